@@ -1,0 +1,321 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test fixes one step of the oracle to a library routine (torch CPU in
+float64), a closed form, an invariant, brute force on tiny inputs, or the
+counts printed in the GQE study note, so that a dropped term, a wrong sign or
+index, or a transposed operand anywhere in the oracle fails at least one test.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+def wl(**kw):
+    base = dict(name="pin", B=2, T=29, d_model=24, H_q=6, H_kv=3, k=1, d_head=8, dtype="f32",
+                seed=7, act_std=1.0, w_std=0.3)
+    base.update(kw)
+    return W.Workload(**base)
+
+def torch_q(w, inp):
+    """All H_q (+ shared) query projections with torch: [B, H, T, d_head], float64."""
+    x = inp["x"].double()                              # [B, T, dm]
+    wq = inp["w_q"].double()                           # [H, dh, dm]
+    return torch.einsum("btm,hdm->bhtd", x, wq)
+
+def torch_sdpa(q, k, v, causal):
+    return F.scaled_dot_product_attention(q, k, v, is_causal=bool(causal))
+
+# ---------------------------------------------------------------- steps 1-4
+
+def test_router_logits_and_group_softmax_match_torch():
+    w = wl(H_q=12, H_kv=3, k=2, zipf_s=1.2)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"], inp["b_router"])
+    s = inp["x"].double().reshape(-1, w.d_model) @ inp["w_router"].double().T + inp["b_router"].double()
+    np.testing.assert_allclose(r["logits"], s.numpy(), rtol=1e-12, atol=1e-12)
+    p = torch.softmax(s.view(-1, w.G, w.E), dim=-1).reshape(-1, w.N)
+    np.testing.assert_allclose(r["probs"], p.numpy(), rtol=1e-12, atol=1e-14)
+
+@pytest.mark.parametrize("E,k", [(2, 1), (4, 2), (4, 3), (3, 1)])
+def test_zero_router_gives_exact_ties_broken_to_lowest_index(E, k):
+    w = wl(H_q=2 * E, H_kv=2, k=k)
+    inp = W.make_inputs(w)
+    r = oracle.route(oracle.desc(w), inp["x"], torch.zeros_like(inp["w_router"]))
+    assert (r["sel"] == np.arange(k, dtype=np.int32)).all()
+    assert (r["ptilde"] == 1.0 / k).all()
+    assert r["tie"].all() == (k < E) and r["tie"].any() == (k < E)
+
+def test_uniform_shift_of_a_groups_logits_changes_nothing():
+    w = wl(H_q=12, H_kv=3, k=2)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    a = oracle.route(d, inp["x"], inp["w_router"])
+    shift = torch.tensor([0.7, -3.0, 11.0], dtype=torch.float64).repeat_interleave(w.E)
+    b = oracle.route(d, inp["x"], inp["w_router"], shift)
+    assert (a["sel"] == b["sel"]).all()
+    np.testing.assert_allclose(a["ptilde"], b["ptilde"], rtol=1e-12)
+
+@pytest.mark.parametrize("E,k", [(4, 2), (5, 2), (5, 3), (3, 1), (4, 4)])
+def test_topk_against_subset_enumeration_with_exact_ties(E, k):
+    # Integer-valued logits make exact ties common; the kept set must maximise
+    # the logit sum and, among maximisers, be the lexicographically smallest.
+    w = wl(H_q=2 * E, H_kv=2, k=k, d_model=3, T=64)
+    g = torch.Generator().manual_seed(E * 10 + k)
+    x = torch.randint(-1, 2, (w.B, w.T, w.d_model), generator=g).double()
+    wr = torch.randint(-2, 3, (w.N, w.d_model), generator=g).double()
+    r = oracle.route(oracle.desc(w), x, wr)
+    s = (x.reshape(-1, w.d_model) @ wr.T).view(-1, w.G, w.E).numpy()
+    n_ties = 0
+    for t in range(s.shape[0]):
+        for gg in range(w.G):
+            best = max(itertools.combinations(range(E), k), key=lambda c: (sum(s[t, gg, list(c)]), [-i for i in c]))
+            assert tuple(r["sel"][t, gg]) == best
+            srt = np.sort(s[t, gg])[::-1]
+            tie = k < E and (srt[k - 1] - srt[k]) < 1e-6
+            assert bool(r["tie"][t, gg]) == tie
+            n_ties += tie
+    assert k == E or n_ties > 0
+
+def test_renormalised_weights_closed_forms():
+    for E, k in [(4, 1), (4, 2), (4, 4), (2, 2)]:
+        w = wl(H_q=2 * E, H_kv=2, k=k)
+        inp = W.make_inputs(w)
+        r = oracle.route(oracle.desc(w), inp["x"], inp["w_router"])
+        np.testing.assert_allclose(r["ptilde"].sum(-1), 1.0, rtol=0, atol=1e-15)
+        p = r["probs"].reshape(-1, w.G, E)
+        if k == 1:
+            assert (r["ptilde"] == 1.0).all()
+        if k == E:
+            assert (r["sel"] == np.arange(E)).all()
+            np.testing.assert_allclose(r["ptilde"], p, rtol=1e-15, atol=1e-16)
+        # p~ = p[S] / sum p[S], with the softmax taken by torch
+        s = inp["x"].double().reshape(-1, w.d_model) @ inp["w_router"].double().T
+        pt = torch.softmax(s.view(-1, w.G, E), -1).gather(-1, torch.as_tensor(r["sel"]).long())
+        pt = pt / pt.sum(-1, keepdim=True)
+        np.testing.assert_allclose(r["ptilde"], pt.numpy(), rtol=1e-12)
+
+# ---------------------------------------------------------------- step 5
+
+def test_compaction_brute_force_and_invariants():
+    w = wl(H_q=12, H_kv=3, k=2, B=3, T=50)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"])
+    c = oracle.compact(d, r["sel"])
+    BT = w.B * w.T
+    buckets = {n: [] for n in range(w.N)}
+    for t in range(BT):
+        for g in range(w.G):
+            for e in r["sel"][t, g]:
+                buckets[g * w.E + int(e)].append(t)
+    assert [len(buckets[n]) for n in range(w.N)] == c["counts"].tolist()
+    assert c["offsets"][0] == 0 and c["offsets"][-1] == BT * w.G * w.k
+    for n in range(w.N):
+        seg = c["rows"][c["offsets"][n]:c["offsets"][n + 1]].tolist()
+        assert seg == buckets[n]
+        assert all(a < b for a, b in zip(seg, seg[1:]))
+    for g in range(w.G):
+        assert c["counts"][g * w.E:(g + 1) * w.E].sum() == BT * w.k
+
+# ---------------------------------------------------------------- step 6
+
+def test_routed_and_shared_projection_match_torch():
+    w = wl(H_q=12, H_kv=3, k=2)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"])
+    qr, qs = oracle.qproj_rows(d, inp["x"], inp["w_q"], r["sel"])
+    qall = torch_q(w, inp).permute(0, 2, 1, 3).reshape(w.B * w.T, w.N + 1, w.d_head)  # [BT, H, dh]
+    n = torch.as_tensor(r["sel"]).long() + (torch.arange(w.G) * w.E).view(1, w.G, 1)
+    exp = qall.gather(1, n.reshape(-1, w.G * w.k, 1).expand(-1, -1, w.d_head)).reshape(-1, w.G, w.k, w.d_head)
+    np.testing.assert_allclose(qr, exp.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(qs, qall[:, w.N].numpy(), rtol=1e-12, atol=1e-13)
+    # a token subset gives the same rows
+    tok = np.array([5, 0, 31, 57])
+    qr2, qs2 = oracle.qproj_rows(d, inp["x"], inp["w_q"], r["sel"], tok)
+    assert np.array_equal(qr2, qr[tok]) and np.array_equal(qs2, qs[tok])
+
+# ---------------------------------------------------------------- step 7-8
+
+@pytest.mark.parametrize("causal", [1, 0])
+@pytest.mark.parametrize("route_mode", [0, 1])
+def test_all_experts_kept_is_dense_gqa(causal, route_mode):
+    """k = E: hard slots are GQA (repeat_interleave + SDPA), weighted slot is sum p*o."""
+    w = wl(H_q=8, H_kv=2, k=4, causal=causal, route_mode=route_mode, n_shared=1)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    res = oracle.prefill(d, inp)
+    q = torch_q(w, inp)
+    kx = inp["k"].double().repeat_interleave(w.E, dim=1)
+    vx = inp["v"].double().repeat_interleave(w.E, dim=1)
+    dense = torch_sdpa(q[:, :w.N], kx, vx, causal)                  # [B, H_q, T, dh]
+    dense = dense.permute(0, 2, 1, 3).reshape(w.B * w.T, w.N, w.d_head)
+    out = res["out"]
+    np.testing.assert_allclose(out[:, :w.N], dense.numpy(), rtol=1e-10, atol=1e-12)
+    s = inp["x"].double().reshape(-1, w.d_model) @ inp["w_router"].double().T
+    p = torch.softmax(s.view(-1, w.G, w.E), -1)                      # [BT, G, E]
+    per_group = (p.unsqueeze(-1) * dense.view(-1, w.G, w.E, w.d_head)).sum(2)   # [BT, G, dh]
+    if route_mode == 0:
+        np.testing.assert_allclose(out[:, w.N], per_group.sum(1).numpy(), rtol=1e-10, atol=1e-12)
+    else:
+        np.testing.assert_allclose(out[:, w.N:w.N + w.G], per_group.numpy(), rtol=1e-10, atol=1e-12)
+    shared = torch_sdpa(q[:, w.N:w.N + 1], inp["k"].double()[:, :1], inp["v"].double()[:, :1], causal)
+    np.testing.assert_allclose(out[:, -1], shared[:, 0].reshape(-1, w.d_head).numpy(), rtol=1e-10, atol=1e-12)
+
+def test_one_query_head_per_group_is_mha_and_one_group_is_mqa():
+    # E = 1 (H_kv = H_q): multi-head attention, every head kept, p~ = 1.
+    w = wl(H_q=4, H_kv=4, k=1)
+    inp = W.make_inputs(w)
+    out = oracle.prefill(oracle.desc(w), inp)["out"]
+    mha = torch_sdpa(torch_q(w, inp)[:, :4], inp["k"].double(), inp["v"].double(), 1)
+    mha = mha.permute(0, 2, 1, 3).reshape(-1, 4, w.d_head)
+    np.testing.assert_allclose(out[:, :4], mha.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(out[:, 4], mha.sum(1).numpy(), rtol=1e-10, atol=1e-12)
+    # G = 1 (H_kv = 1), all kept: multi-query attention.
+    w = wl(H_q=4, H_kv=1, k=4)
+    inp = W.make_inputs(w)
+    out = oracle.prefill(oracle.desc(w), inp)["out"]
+    mqa = torch_sdpa(torch_q(w, inp)[:, :4], inp["k"].double().expand(-1, 4, -1, -1),
+                     inp["v"].double().expand(-1, 4, -1, -1), 1)
+    np.testing.assert_allclose(out[:, :4], mqa.permute(0, 2, 1, 3).reshape(-1, 4, w.d_head).numpy(),
+                               rtol=1e-10, atol=1e-12)
+
+def test_causal_prefix_invariance():
+    w = wl(H_q=8, H_kv=2, k=2, T=40)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    a = oracle.prefill(d, inp)
+    cut = 23
+    pert = dict(inp)
+    g = torch.Generator().manual_seed(99)
+    for key in ("x",):
+        t = inp[key].clone(); t[:, cut:] = torch.randn(t[:, cut:].shape, generator=g); pert[key] = t
+    for key in ("k", "v"):
+        t = inp[key].clone(); t[:, :, cut:] = torch.randn(t[:, :, cut:].shape, generator=g); pert[key] = t
+    b = oracle.prefill(d, pert)
+    keep = np.array([bb * w.T + t for bb in range(w.B) for t in range(cut)])
+    assert np.array_equal(a["out"][keep], b["out"][keep])
+    assert np.array_equal(a["sel"][keep], b["sel"][keep])
+    later = np.array([bb * w.T + t for bb in range(w.B) for t in range(cut, w.T)])
+    assert not np.allclose(a["out"][later], b["out"][later])
+
+def test_attention_closed_forms():
+    w = wl(H_q=6, H_kv=3, k=2, T=17)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    hard = slice(0, w.G * w.k)
+    # position 0 attends only itself: o = v_0 exactly
+    out = oracle.prefill(d, inp)["out"].reshape(w.B, w.T, -1, w.d_head)
+    for b in range(w.B):
+        for g in range(w.G):
+            for j in range(w.k):
+                assert np.array_equal(out[b, 0, g * w.k + j], inp["v"][b, g, 0].double().numpy())
+        assert np.array_equal(out[b, 0, -1], inp["v"][b, 0, 0].double().numpy())
+    # constant V gives that constant everywhere
+    c = torch.randn(w.d_head, dtype=torch.float64)
+    cst = dict(inp, v=c.expand_as(inp["v"]).clone())
+    out = oracle.prefill(d, cst)["out"]
+    np.testing.assert_allclose(out[:, hard], np.broadcast_to(c.numpy(), out[:, hard].shape), rtol=1e-13, atol=1e-14)
+    # zero keys: uniform weights, o_t = mean_{s<=t} v_s
+    zk = dict(inp, k=torch.zeros_like(inp["k"]))
+    out = oracle.prefill(d, zk)["out"].reshape(w.B, w.T, -1, w.d_head)
+    mean = torch.cumsum(inp["v"].double(), 2) / torch.arange(1, w.T + 1, dtype=torch.float64).view(1, 1, -1, 1)
+    for g in range(w.G):
+        for j in range(w.k):
+            np.testing.assert_allclose(out[:, :, g * w.k + j], mean[:, g].numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out[:, :, -1], mean[:, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+def test_shared_slot_is_single_head_attention_on_kv0_and_ignores_router():
+    w = wl(H_q=8, H_kv=4, k=1)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    a = oracle.prefill(d, inp)["out"]
+    q = torch_q(w, inp)[:, w.N:w.N + 1]
+    ref = torch_sdpa(q, inp["k"].double()[:, :1], inp["v"].double()[:, :1], 1)[:, 0].reshape(-1, w.d_head)
+    np.testing.assert_allclose(a[:, -1], ref.numpy(), rtol=1e-10, atol=1e-12)
+    other = dict(inp, w_router=torch.randn(inp["w_router"].shape))
+    b = oracle.prefill(d, other)["out"]
+    assert np.array_equal(a[:, -1], b[:, -1])
+
+def test_top1_weighted_slot_is_sum_of_hard_slots():
+    w = wl(H_q=8, H_kv=4, k=1)
+    inp = W.make_inputs(w)
+    out = oracle.prefill(oracle.desc(w), inp)["out"]
+    acc = np.zeros_like(out[:, 0])
+    for g in range(w.G):
+        acc = acc + out[:, g]
+    assert np.array_equal(out[:, w.G], acc)
+    # one group, top-1: the weighted slot is exactly the single selected output
+    w1 = wl(H_q=3, H_kv=1, k=1)
+    inp1 = W.make_inputs(w1)
+    out1 = oracle.prefill(oracle.desc(w1), inp1)["out"]
+    assert np.array_equal(out1[:, 0], out1[:, 1])
+    # per-group weighted slots with top-1 equal the hard slots bit for bit
+    wm = w.replace(route_mode=1)
+    outm = oracle.prefill(oracle.desc(wm), inp)["out"]
+    assert np.array_equal(outm[:, w.G:2 * w.G], outm[:, :w.G])
+
+def test_permuting_experts_inside_a_group_keeps_weighted_and_shared_slots():
+    w = wl(H_q=12, H_kv=3, k=2)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    a = oracle.prefill(d, inp)["out"]
+    perm = torch.cat([g * w.E + torch.tensor([2, 0, 3, 1]) for g in range(w.G)])
+    q_perm = torch.cat([perm, torch.tensor([w.N])])
+    b = oracle.prefill(d, dict(inp, w_router=inp["w_router"][perm], w_q=inp["w_q"][q_perm]))["out"]
+    np.testing.assert_allclose(a[:, w.G * w.k:], b[:, w.G * w.k:], rtol=1e-12, atol=1e-14)
+    for g in range(w.G):   # hard slots of a group are the same set of vectors
+        sa = np.sort(a[:, g * w.k:(g + 1) * w.k], axis=1)
+        sb = np.sort(b[:, g * w.k:(g + 1) * w.k], axis=1)
+        np.testing.assert_allclose(sa, sb, rtol=1e-12, atol=1e-14)
+
+# ---------------------------------------------------------------- decode
+
+def test_decode_equals_last_prefill_row():
+    w = wl(H_q=8, H_kv=2, k=1, B=3, T=20)
+    inp = W.make_inputs(w)
+    lens = np.array([20, 1, 13], dtype=np.int32)
+    d = oracle.desc(w)
+    full = oracle.route(d, inp["x"], inp["w_router"])
+    tok = np.array([b * w.T + lens[b] - 1 for b in range(w.B)])
+    ref = oracle.prefill_rows(d, inp["x"], inp["w_q"], inp["k"], inp["v"], full["sel"], full["ptilde"], tok)
+    xs = inp["x"][torch.arange(w.B), torch.as_tensor(lens - 1).long()]
+    kc, vc = inp["k"].clone(), inp["v"].clone()
+    for b in range(w.B):       # positions past the length must never be read
+        kc[b, :, lens[b]:] = float("nan"); vc[b, :, lens[b]:] = float("nan")
+    dd = oracle.desc(w, T=1)
+    dec = oracle.decode(dd, xs, inp["w_router"], None, inp["w_q"], kc, vc, lens)
+    assert np.array_equal(dec["out"], ref)
+    assert np.array_equal(dec["sel"], full["sel"][tok])
+    # a one-entry cache returns v_0
+    assert np.array_equal(dec["out"][1, 0], inp["v"][1, 0, 0].double().numpy())
+
+# ---------------------------------------------------------------- printed counts
+
+def test_main_setting_counts_from_the_study_note():
+    g = json.load(open(os.path.join(HERE, "golden", "main_setting.json")))
+    w = W.WORKLOADS["main_250m"]
+    assert (w.H_q, w.H_kv, w.k, w.n_shared) == (g["H_q"], g["H_kv"], g["k"], g["n_shared"])
+    small = w.replace(B=1, T=5, d_model=16, d_head=8, dtype="f32", act_std=1.0, w_std=0.3)
+    d = oracle.desc(small)
+    assert oracle.num_slots(d) == g["output_slots"] == g["hard_slots"] + g["weighted_sum_slots"] + g["shared_slots"]
+    assert oracle.num_slots(oracle.desc(W.dense_variant(small), n_shared=0, route_mode=0)) - 1 == g["dense_output_slots"]
+    inp = W.make_inputs(small)
+    r = oracle.route(d, inp["x"], inp["w_router"])
+    qr, qs = oracle.qproj_rows(d, inp["x"], inp["w_q"], r["sel"])
+    assert qs is not None and qs.shape[0] == small.T
+    assert qr.shape[1] * qr.shape[2] == g["routed_active"]
+    assert qr.shape[1] * qr.shape[2] + 1 == g["computed_query_attentions"]
+    assert small.G * small.E == g["routed_pool"] and small.G == g["groups"] and small.E == g["experts_per_group"]
+    c = oracle.compact(d, r["sel"])
+    assert c["counts"].sum() == small.T * g["routed_active"]
