@@ -1,0 +1,180 @@
+/*
+ * gqe.h -- C ABI of the GQE (Grouped Query Experts) attention forward library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (GQE study note, dimensionstp.github.io, §3-2 (1)-(5)): the H_q
+ * query heads of grouped-query attention form G = H_kv groups of E = H_q / G
+ * query-head "experts".  For every token and group a router scores the E
+ * experts, keeps the top k and renormalises their softmax probabilities over
+ * the kept ones; only the kept experts are projected and attend, causally,
+ * the group's single dense KV head.  The output of a token is the
+ * concatenation of the k*G hard-selected head outputs, a router-weighted sum
+ * of them, and one always-on shared head.
+ *
+ * Conventions used throughout
+ *   G = H_kv, E = H_q / H_kv, N = G * E (routed experts), global expert index
+ *   n = g * E + e (the GQA query-head index of the GQA tutorial, freeguideonline,
+ *   "GQA 核心原理与计算流程" step 3).  BT = B * T.
+ *   S = k*G + (route_mode ? G : 1) + n_shared output slots per token.
+ *   Slot order: hard slots g-major then ascending expert index, weighted
+ *   slot(s), shared slot.  The shared head's projection is W_q row block N
+ *   and it attends KV head 0.  Attention scale is 1/sqrt(d_head).
+ *
+ * Pointers: every tensor pointer is a DEVICE pointer owned by the caller,
+ * contiguous, row-major in the layout given, and 16-byte aligned.  The
+ * library never allocates, frees or synchronises; every call enqueues its
+ * kernels on `stream` (a hipStream_t, NULL = the default stream) and returns.
+ * Outputs are fully overwritten.  Calls keep no state between them and may
+ * be made from several host threads.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued;
+ * a negative gqe_status is returned and nothing runs.  A failed launch
+ * returns GQE_ERR_LAUNCH.  Device-side preconditions that the host cannot
+ * see (decode lengths in 1..L_max, sel values in 0..E-1 handed to gqe_qproj)
+ * are the caller's responsibility.
+ */
+#ifndef GQE_H
+#define GQE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQE_OK = 0,
+    GQE_ERR_INVALID = -1,      /* bad shape, NULL required pointer, k outside 1..E, ... */
+    GQE_ERR_UNSUPPORTED = -2,  /* valid but not built: d_head, dtype, too many experts */
+    GQE_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned */
+    GQE_ERR_LAUNCH = -4,       /* the HIP runtime rejected a launch */
+    GQE_ERR_WORKSPACE = -5     /* workspace missing or smaller than required */
+} gqe_status;
+
+typedef enum { GQE_F32 = 0, GQE_BF16 = 1 } gqe_dtype;
+
+/* Shapes and flags of one call.  Problem statement of the GQE study note §1-1
+ * (H_q, H_kv, G, E) and §3-2 (2) (top-k per group); d_head is the per-head
+ * width d of the attention equation in §1-1. */
+typedef struct {
+    int32_t B;          /* sequences */
+    int32_t T;          /* prefill: tokens per sequence; decode: must be 1 */
+    int32_t d_model;    /* width of x; multiple of 64 for bf16, of 4 for f32 */
+    int32_t H_q;        /* query heads = routed experts N; at most 256 */
+    int32_t H_kv;       /* KV heads = groups G; H_q % H_kv == 0 */
+    int32_t k;          /* experts kept per group and token, 1 <= k <= E, k <= 8 */
+    int32_t d_head;     /* 32, 64 or 128 */
+    int32_t n_shared;   /* 0 or 1: the always-on shared head (reads KV head 0) */
+    int32_t causal;     /* 1: key s is visible to query t iff s <= t; 0: all keys */
+    int32_t route_mode; /* 0: one weighted slot summed over groups (study note
+                           §3-2 (4)); 1: one weighted slot per group */
+    int32_t dtype;      /* gqe_dtype of x, W_router, W_q, q, K, V; outputs are fp32 */
+} gqe_desc;
+
+/* Number of output slots S per token for this descriptor (or -1 if invalid). */
+int gqe_num_slots(const gqe_desc* desc);
+
+/* Human-readable name of a status code (static string). */
+const char* gqe_status_string(int status);
+
+/* Bytes of device workspace gqe_route needs (per-block expert counts). */
+size_t gqe_route_workspace_bytes(const gqe_desc* desc);
+
+/*
+ * gqe_route -- router, in-group softmax, top-k, renormalisation and the
+ * expert compaction, for all B*T tokens.
+ *
+ * Defines (GQE study note §3-2 (2) and (4)):
+ *   s[t,n]  = x[t,:] . W_router[n,:] + b_router[n]          (router score)
+ *   p[t,g,e] = softmax over the E experts of group g
+ *   S[t,g]  = the k largest scores of the group (ties: lower e first),
+ *             written in ascending expert index
+ *   p~[t,g,j] = p[t,g,S_j] / sum_j' p[t,g,S_j']
+ *   counts[n] = tokens that kept expert n;  offsets = exclusive prefix sum,
+ *   offsets[N] = BT*G*k;  rows[offsets[n] + r] = the r-th smallest token id
+ *   (b*T + t) that kept n.
+ *
+ * In:  x [BT, d_model] (dtype), w_router [N, d_model] (dtype),
+ *      b_router [N] fp32 or NULL (no bias).
+ * Out: sel [BT, G, k] int32, p_tilde [BT, G, k] fp32, counts [N] int32,
+ *      offsets [N+1] int32, rows [BT*G*k] int32,
+ *      logits [BT, N] double or NULL (the router scores, for auditing ties).
+ * Workspace: gqe_route_workspace_bytes(desc) bytes of device memory, no
+ *      initialisation needed, contents undefined afterwards.
+ * Scores accumulate exactly-rounded partial sums of at most 32 products in
+ * fp32 into double totals; the comparison that picks the experts is made on
+ * those totals.
+ */
+int gqe_route(const gqe_desc* desc, const void* x, const void* w_router, const float* b_router,
+              int32_t* sel, float* p_tilde, int32_t* counts, int32_t* offsets, int32_t* rows,
+              double* logits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gqe_qproj -- routed query projection (grouped GEMM over the compacted rows)
+ * plus the shared head.  Each kept expert is its own query projection and
+ * unselected experts are never computed (ai-feeds summary of arXiv 2606.20945,
+ * 方法/核心模块; GQE study note §3-2 (2), last sentence; §3-2 (5)).
+ *
+ *   q_routed[b, g, t, j, :] = W_q[g*E + S[t,g]_j] x[b,t,:]     (no bias)
+ *   q_shared[b, t, :]       = W_q[N] x[b,t,:]                  (if n_shared)
+ *
+ * In:  x [BT, d_model]; w_q [N + n_shared, d_head, d_model] (dtype);
+ *      sel, counts, offsets, rows as produced by gqe_route.
+ * Out: q_routed [B, G, T, k, d_head] (dtype; bf16 rounds to nearest even from
+ *      an fp32 accumulator), q_shared [B, T, d_head] or NULL when n_shared = 0.
+ * Within one (b, g) the routed queries form a dense [T*k, d_head] matrix whose
+ * row r belongs to position r / k.
+ */
+int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_t* sel,
+              const int32_t* counts, const int32_t* offsets, const int32_t* rows,
+              void* q_routed, void* q_shared, void* stream);
+
+/*
+ * gqe_attn_prefill -- attention of every routed and shared query row against
+ * its group's dense, unchanged KV head, then slot assembly.
+ *
+ *   o = softmax_s(q . K[b,g,s] / sqrt(d_head)) V[b,g,s],  s <= t if causal
+ *   (attention equation of GQE study note §1-1; scale as IBM "什么是分组查询注意力")
+ *   out[b,t, g*k+j]  = o of routed row (g, j)                 (hard slots, §3-2 (3))
+ *   mode 0: out[b,t,kG] = sum_g sum_j p~[t,g,j] o(g,j)         (§3-2 (4))
+ *   mode 1: out[b,t,kG+g] = sum_j p~[t,g,j] o(g,j)
+ *   out[b,t,S-1] = o of the shared row against KV head 0       (§3-2 (5))
+ *
+ * In:  q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] or NULL,
+ *      k, v [B, H_kv, T, d_head] (dtype), p_tilde [BT, G, k] fp32.
+ * Out: out [B, T, S, d_head] fp32.
+ * bf16: QK^T and PV run on bf16 MFMA with fp32 accumulation; the softmax is
+ * fp32 and the probabilities are rounded to bf16 for the PV product.
+ */
+int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                     const void* k, const void* v, const float* p_tilde, float* out, void* stream);
+
+/* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
+size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
+
+/*
+ * gqe_attn_decode -- one new token per sequence (desc->T == 1) against a KV
+ * cache that already holds that token's K and V (decode reads the whole
+ * cache: GQA tutorial, freeguideonline, "自回归推理中的内存带宽优势").
+ *
+ * In:  q_routed [B, G, 1, k, d_head], q_shared [B, 1, d_head] or NULL,
+ *      k_cache, v_cache [B, H_kv, L_max, d_head] (dtype), lens [B] int32 with
+ *      1 <= lens[b] <= L_max (positions >= lens[b] are never read),
+ *      p_tilde [B, G, k] fp32.
+ * Out: out [B, S, d_head] fp32, slots as in gqe_attn_prefill.
+ * Workspace: gqe_decode_workspace_bytes(desc, L_max) bytes of device memory
+ *      for split-KV partial results; no initialisation needed.
+ * The partial results of fixed-size key chunks are merged in chunk order, so
+ * the result does not depend on scheduling.
+ */
+int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                    const void* k_cache, const void* v_cache, int32_t L_max, const int32_t* lens,
+                    const float* p_tilde, float* out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQE_H */

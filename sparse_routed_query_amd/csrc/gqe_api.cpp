@@ -1,0 +1,193 @@
+// C ABI of the GQE library: argument checks, then kernel launches on the
+// caller's stream.  Nothing here allocates, frees or synchronises.
+#include "gqe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "gqe_launch.h"
+
+namespace {
+
+constexpr int kMaxHq = 64;   // experts a router workgroup keeps in LDS
+constexpr int kMaxK = 8;     // kept experts per group held in registers
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Shape {
+    int B, T, dm, Hq, G, E, k, D, ns, causal, mode, S;
+    bool bf16;
+    long long BT;
+};
+
+// Shared checks of the descriptor.  Returns GQE_OK or a negative status.
+int check_desc(const gqe_desc* d, Shape& s)
+{
+    if (!d) return GQE_ERR_INVALID;
+    if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H_q < 1 || d->H_kv < 1) return GQE_ERR_INVALID;
+    if (d->H_q % d->H_kv != 0) return GQE_ERR_INVALID;
+    const int E = d->H_q / d->H_kv;
+    if (d->k < 1 || d->k > E) return GQE_ERR_INVALID;
+    if (d->n_shared != 0 && d->n_shared != 1) return GQE_ERR_INVALID;
+    if (d->causal != 0 && d->causal != 1) return GQE_ERR_INVALID;
+    if (d->route_mode != 0 && d->route_mode != 1) return GQE_ERR_INVALID;
+    if (d->dtype != GQE_F32 && d->dtype != GQE_BF16) return GQE_ERR_INVALID;
+    if (d->d_head != 32 && d->d_head != 64 && d->d_head != 128) return GQE_ERR_UNSUPPORTED;
+    if (d->H_q > kMaxHq || d->k > kMaxK) return GQE_ERR_UNSUPPORTED;
+    if (d->dtype == GQE_BF16 && d->d_model % 64 != 0) return GQE_ERR_UNSUPPORTED;
+    const long long BT = (long long)d->B * d->T;
+    // every index that reaches an int in a kernel stays below 2^31
+    if (BT * d->H_kv * d->k >= (1ll << 31) || (long long)d->T * d->k >= (1ll << 31) - 256) return GQE_ERR_UNSUPPORTED;
+    s.B = d->B; s.T = d->T; s.dm = d->d_model; s.Hq = d->H_q; s.G = d->H_kv; s.E = E; s.k = d->k;
+    s.D = d->d_head; s.ns = d->n_shared; s.causal = d->causal; s.mode = d->route_mode;
+    s.S = d->k * d->H_kv + (d->route_mode ? d->H_kv : 1) + d->n_shared;
+    s.bf16 = d->dtype == GQE_BF16;
+    s.BT = BT;
+    return GQE_OK;
+}
+
+// A required pointer: non-NULL and 16-byte aligned.
+int need(const void* p)
+{
+    if (!p) return GQE_ERR_INVALID;
+    return aligned16(p) ? GQE_OK : GQE_ERR_ALIGN;
+}
+// An optional pointer: NULL or 16-byte aligned.
+int maybe(const void* p) { return (!p || aligned16(p)) ? GQE_OK : GQE_ERR_ALIGN; }
+
+#define GQE_TRY(expr)                \
+    do {                             \
+        const int _rc = (expr);      \
+        if (_rc != GQE_OK) return _rc; \
+    } while (0)
+
+int launch_status(int rc)
+{
+    if (rc == -2) return GQE_ERR_UNSUPPORTED;
+    return rc == 0 ? GQE_OK : GQE_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqe_num_slots(const gqe_desc* desc)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK) return -1;
+    return s.S;
+}
+
+const char* gqe_status_string(int status)
+{
+    switch (status) {
+    case GQE_OK: return "ok";
+    case GQE_ERR_INVALID: return "invalid argument";
+    case GQE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case GQE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GQE_ERR_LAUNCH: return "kernel launch failed";
+    case GQE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+    }
+}
+
+size_t gqe_route_workspace_bytes(const gqe_desc* desc)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK) return 0;
+    return gqe::route_workspace_bytes((int)s.BT, s.Hq);
+}
+
+int gqe_route(const gqe_desc* desc, const void* x, const void* w_router, const float* b_router, int32_t* sel,
+              float* p_tilde, int32_t* counts, int32_t* offsets, int32_t* rows, double* logits, void* workspace,
+              size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    GQE_TRY(need(counts));
+    GQE_TRY(need(offsets));
+    if (s.BT > 0) {
+        GQE_TRY(need(x));
+        GQE_TRY(need(w_router));
+        GQE_TRY(maybe(b_router));
+        GQE_TRY(need(sel));
+        GQE_TRY(need(p_tilde));
+        GQE_TRY(need(rows));
+        GQE_TRY(maybe(logits));
+        if (!workspace) return GQE_ERR_WORKSPACE;
+        GQE_TRY(need(workspace));
+        if (workspace_bytes < gqe::route_workspace_bytes((int)s.BT, s.Hq)) return GQE_ERR_WORKSPACE;
+    }
+    gqe::RouteArgs a{x, w_router, b_router, sel, p_tilde, counts, offsets, rows, logits, workspace,
+                     (int)s.BT, s.dm, s.G, s.E, s.k, s.bf16};
+    return launch_status(gqe::launch_route(a, (hipStream_t)stream));
+}
+
+int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_t* sel, const int32_t* counts,
+              const int32_t* offsets, const int32_t* rows, void* q_routed, void* q_shared, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(x));
+    GQE_TRY(need(w_q));
+    GQE_TRY(need(sel));
+    GQE_TRY(need(counts));
+    GQE_TRY(need(offsets));
+    GQE_TRY(need(rows));
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    gqe::QprojArgs a{x, w_q, sel, counts, offsets, rows, q_routed, q_shared,
+                     s.B, s.T, s.dm, s.G, s.E, s.k, s.D, s.ns, s.bf16};
+    return launch_status(gqe::launch_qproj(a, (hipStream_t)stream));
+}
+
+int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
+                     const float* p_tilde, float* out, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(out));
+    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out,
+                       s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
+    return launch_status(gqe::launch_prefill(a, (hipStream_t)stream));
+}
+
+size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK || L_max < 1) return 0;
+    return gqe::decode_workspace_bytes(s.B, s.G, s.k, s.ns, s.D, L_max, s.bf16);
+}
+
+int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k_cache,
+                    const void* v_cache, int32_t L_max, const int32_t* lens, const float* p_tilde, float* out,
+                    void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.T != 1 || L_max < 1) return GQE_ERR_INVALID;
+    if ((long long)s.B * s.G * L_max * s.D >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    if (s.B == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k_cache));
+    GQE_TRY(need(v_cache));
+    GQE_TRY(need(lens));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(out));
+    if (!workspace) return GQE_ERR_WORKSPACE;
+    GQE_TRY(need(workspace));
+    if (workspace_bytes < gqe::decode_workspace_bytes(s.B, s.G, s.k, s.ns, s.D, L_max, s.bf16))
+        return GQE_ERR_WORKSPACE;
+    gqe::DecodeArgs a{q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace,
+                      s.B, s.G, s.k, s.D, s.ns, s.mode, s.S, L_max, s.bf16};
+    return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Host-side launch interface between the C ABI layer (gqe_api.cpp) and the
+// kernel files.  Arguments have been validated before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqe {
+
+struct RouteArgs {
+    const void* x;
+    const void* w_router;
+    const float* b_router;
+    int32_t* sel;
+    float* p_tilde;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* rows;
+    double* logits;
+    void* workspace;
+    int BT, d_model, G, E, k;
+    bool bf16;
+};
+size_t route_workspace_bytes(int BT, int N);
+int launch_route(const RouteArgs& a, hipStream_t st);
+
+struct QprojArgs {
+    const void* x;
+    const void* w_q;
+    const int32_t* sel;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* rows;
+    void* q_routed;
+    void* q_shared;
+    int B, T, d_model, G, E, k, d_head, n_shared;
+    bool bf16;
+};
+int launch_qproj(const QprojArgs& a, hipStream_t st);
+
+struct PrefillArgs {
+    const void* q_routed;
+    const void* q_shared;
+    const void* kmat;
+    const void* vmat;
+    const float* p_tilde;
+    float* out;
+    int B, T, G, k, d_head, n_shared, causal, route_mode, S;
+    bool bf16;
+};
+int launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+    const void* q_routed;
+    const void* q_shared;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* lens;
+    const float* p_tilde;
+    float* out;
+    void* workspace;
+    int B, G, k, d_head, n_shared, route_mode, S, L_max;
+    bool bf16;
+};
+size_t decode_workspace_bytes(int B, int G, int k, int n_shared, int d_head, int L_max, bool bf16);
+int launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace gqe

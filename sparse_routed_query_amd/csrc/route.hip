@@ -1,0 +1,266 @@
+// Router (scores, in-group softmax, top-k, renormalisation) and the stable
+// expert compaction, for gfx950.
+//
+// Method: GQE study note (dimensionstp.github.io) §3-2 (2) -- s_{t,g,e} =
+// r_g(x_t)_e, p = softmax over the group's E experts, S = TopK(p, k) -- and
+// §3-2 (4) -- p~ renormalised over the kept experts.  The compaction buckets
+// the kept (token, expert) pairs by expert so the projection and attention
+// touch only kept experts (ai-feeds summary, 方法/核心模块: unselected query
+// heads are skipped).
+//
+// Kernels:
+//   router_kernel   one wave per block of 32 tokens.  Scores come from bf16
+//                   MFMA (16x16x32, exact bf16 products) with every 32-product
+//                   partial sum added into a double accumulator, so the score
+//                   error stays far below the 1e-6 tie margin; fp32 inputs use
+//                   double FMAs.  The wave then selects, renormalises and
+//                   counts kept experts of its block in LDS.
+//   scan_kernel     one workgroup per expert: exclusive scan of the per-block
+//                   counts -> per-block base offsets, and the expert totals.
+//   scatter_kernel  one wave per two blocks: wave ballots give each token its
+//                   rank among the block's tokens that kept the expert, so
+//                   rows[] is ordered by token id without atomics.
+#include "gqe_device.h"
+#include "gqe_launch.h"
+
+namespace gqe {
+
+constexpr int kRouteTok = 32;        // tokens per wave = compaction block
+constexpr int kRouteWaves = 4;       // waves per workgroup
+constexpr int kMaxExperts = 64;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_kernel(
+    const void* __restrict__ xv, const void* __restrict__ wv, const float* __restrict__ bias,
+    int32_t* __restrict__ sel, float* __restrict__ ptilde, double* __restrict__ logits_out,
+    int32_t* __restrict__ blk_counts, int BT, int d_model, int G, int E, int k)
+{
+    const int N = G * E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = blockIdx.x * kRouteWaves + wave;
+    const int tok0 = blk * kRouteTok;
+    // dynamic LDS: per wave, logits [32][N+1] doubles then counters [N] ints
+    extern __shared__ double s_dyn[];
+    double* s_lg = s_dyn + (size_t)wave * kRouteTok * (N + 1);
+    int* s_cnt = (int*)(s_dyn + (size_t)kRouteWaves * kRouteTok * (N + 1)) + wave * N;
+#define LOGIT(tt, n) s_lg[(tt) * (N + 1) + (n)]
+    if (tok0 >= BT) return;  // whole wave leaves together; no block-wide barrier below
+
+    for (int n = lane; n < N; n += 64) s_cnt[n] = 0;
+
+    if constexpr (BF16) {
+        const uint16_t* x = (const uint16_t*)xv;
+        const uint16_t* w = (const uint16_t*)wv;
+        const int nb = (N + 15) / 16;  // 16-expert column blocks (<= 4)
+        double acc[2][4][4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[a][c][r] = 0.0;
+        const int kq = 8 * (lane >> 4);  // k offset of this lane inside a 32-wide step
+        const int t_a0 = tok0 + (lane & 15), t_a1 = tok0 + 16 + (lane & 15);
+        const bool v0 = t_a0 < BT, v1 = t_a1 < BT;
+        const uint16_t* xa0 = x + (size_t)(v0 ? t_a0 : 0) * d_model + kq;
+        const uint16_t* xa1 = x + (size_t)(v1 ? t_a1 : 0) * d_model + kq;
+        const bf16x8 zero8 = {};
+        for (int k0 = 0; k0 < d_model; k0 += 32) {
+            bf16x8 a0 = v0 ? ld_bf16x8(xa0 + k0) : zero8;
+            bf16x8 a1 = v1 ? ld_bf16x8(xa1 + k0) : zero8;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (c < nb) {
+                    const int n = c * 16 + (lane & 15);
+                    bf16x8 b = n < N ? ld_bf16x8(w + (size_t)n * d_model + k0 + kq) : zero8;
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 p0 = mfma16(a0, b, z);
+                    f32x4 p1 = mfma16(a1, b, z);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[0][c][r] += (double)p0[r];
+                        acc[1][c][r] += (double)p1[r];
+                    }
+                }
+            }
+        }
+        // accumulator element r of lane l: token row 4*(l/16) + r, expert column l%16
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int n = c * 16 + (lane & 15);
+                if (c < nb && n < N) {
+                    const double b = bias ? (double)bias[n] : 0.0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) LOGIT(a * 16 + 4 * (lane >> 4) + r, n) = acc[a][c][r] + b;
+                }
+            }
+    } else {
+        const float* x = (const float*)xv;
+        const float* w = (const float*)wv;
+        for (int p = lane; p < kRouteTok * N; p += 64) {
+            const int tt = p / N, n = p % N;
+            const int t = tok0 + tt;
+            double s = 0.0;
+            if (t < BT) {
+                const float* xr = x + (size_t)t * d_model;
+                const float* wr = w + (size_t)n * d_model;
+                for (int i = 0; i < d_model; ++i) s = fma((double)xr[i], (double)wr[i], s);
+                if (bias) s += (double)bias[n];
+            }
+            LOGIT(tt, n) = s;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+
+    // Selection, renormalisation and counting: one (token, group) per lane.
+    for (int p = lane; p < kRouteTok * G; p += 64) {
+        const int tt = p / G, g = p % G;
+        const int t = tok0 + tt;
+        if (t >= BT) continue;
+        const double* s = &LOGIT(tt, g * E);
+        uint64_t chosen = 0;  // E <= 64
+        int kept[8];
+        for (int r = 0; r < k; ++r) {
+            int best = -1;
+            double bv = 0.0;
+            for (int e = 0; e < E; ++e) {
+                if ((chosen >> e) & 1) continue;
+                if (best < 0 || s[e] > bv) { best = e; bv = s[e]; }  // strict: lowest index wins ties
+            }
+            chosen |= 1ull << best;
+        }
+        int j = 0;
+        double mk = -INFINITY;
+        for (int e = 0; e < E; ++e)
+            if ((chosen >> e) & 1) { kept[j++] = e; mk = fmax(mk, s[e]); }
+        float ex[8], den = 0.f;
+        for (j = 0; j < k; ++j) { ex[j] = expf((float)(s[kept[j]] - mk)); den += ex[j]; }
+        const size_t o = ((size_t)t * G + g) * k;
+        for (j = 0; j < k; ++j) {
+            sel[o + j] = kept[j];
+            ptilde[o + j] = ex[j] / den;
+            atomicAdd(&s_cnt[g * E + kept[j]], 1);
+        }
+    }
+    if (logits_out) {
+        for (int p = lane; p < kRouteTok * N; p += 64) {
+            const int tt = p / N, n = p % N;
+            if (tok0 + tt < BT) logits_out[(size_t)(tok0 + tt) * N + n] = LOGIT(tt, n);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    for (int n = lane; n < N; n += 64) blk_counts[(size_t)blk * N + n] = s_cnt[n];
+#undef LOGIT
+}
+
+// Exclusive scan of blk_counts[:, n] into blk_base[:, n]; counts[n] = total.
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blk_counts,
+                                                   int32_t* __restrict__ blk_base,
+                                                   int32_t* __restrict__ counts, int nblk, int N)
+{
+    const int n = blockIdx.x, tid = threadIdx.x;
+    const int per = (nblk + 255) / 256;
+    const int b0 = tid * per, b1 = min(nblk, b0 + per);
+    int local = 0;
+    for (int b = b0; b < b1; ++b) local += blk_counts[(size_t)b * N + n];
+    __shared__ int s[256];
+    s[tid] = local;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over the 256 partial sums
+    for (int o = 1; o < 256; o <<= 1) {
+        int v = tid >= o ? s[tid - o] : 0;
+        __syncthreads();
+        s[tid] += v;
+        __syncthreads();
+    }
+    int run = s[tid] - local;
+    for (int b = b0; b < b1; ++b) {
+        const int c = blk_counts[(size_t)b * N + n];
+        blk_base[(size_t)b * N + n] = run;
+        run += c;
+    }
+    if (tid == 255) counts[n] = s[255];
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ blk_base,
+                                                      const int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ rows, int BT, int G, int E,
+                                                      int k, int nblk)
+{
+    const int N = G * E;
+    __shared__ int s_off[kMaxExperts + 1];
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int n = 0; n < N; ++n) { s_off[n] = run; run += counts[n]; }
+        s_off[N] = run;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int n = threadIdx.x; n <= N; n += blockDim.x) offsets[n] = s_off[n];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, hl = lane & 31;
+    const int blk = (blockIdx.x * 4 + wave) * 2 + half;
+    const int t = blk * kRouteTok + hl;
+    const bool valid = blk < nblk && t < BT;
+    const uint32_t below = (1u << hl) - 1u;
+    for (int g = 0; g < G; ++g) {
+        int kept[8];
+        for (int j = 0; j < k; ++j) kept[j] = valid ? sel[((size_t)t * G + g) * k + j] : -1;
+        for (int e = 0; e < E; ++e) {
+            bool has = false;
+            for (int j = 0; j < k; ++j) has |= kept[j] == e;
+            const uint64_t m = __ballot(has);
+            if (has) {
+                const uint32_t hm = (uint32_t)(m >> (32 * half));
+                const int n = g * E + e;
+                rows[s_off[n] + blk_base[(size_t)blk * N + n] + __popc(hm & below)] = t;
+            }
+        }
+    }
+}
+
+__global__ void zero_i32_kernel(int32_t* __restrict__ a, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a[i] = 0;
+}
+
+size_t route_workspace_bytes(int BT, int N)
+{
+    const size_t nblk = (size_t)(BT + kRouteTok - 1) / kRouteTok;
+    return 2 * nblk * (size_t)N * sizeof(int32_t) + 256;
+}
+
+int launch_route(const RouteArgs& a, hipStream_t st)
+{
+    const int N = a.G * a.E;
+    const int nblk = (a.BT + kRouteTok - 1) / kRouteTok;
+    int32_t* blk_counts = (int32_t*)a.workspace;
+    int32_t* blk_base = blk_counts + (size_t)nblk * N;
+    if (a.BT == 0) {
+        zero_i32_kernel<<<1, 256, 0, st>>>(a.counts, N);
+        zero_i32_kernel<<<1, 256, 0, st>>>(a.offsets, N + 1);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+    const int grid = (nblk + kRouteWaves - 1) / kRouteWaves;
+    const size_t lds = (size_t)kRouteWaves * kRouteTok * (N + 1) * sizeof(double) + (size_t)kRouteWaves * N * sizeof(int);
+    if (a.bf16)
+        router_kernel<true><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
+                                                  blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
+    else
+        router_kernel<false><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
+                                                   blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
+    scan_kernel<<<N, 256, 0, st>>>(blk_counts, blk_base, a.counts, nblk, N);
+    const int sgrid = (nblk + 7) / 8;
+    scatter_kernel<<<sgrid, 256, 0, st>>>(a.sel, blk_base, a.counts, a.offsets, a.rows, a.BT, a.G, a.E, a.k, nblk);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace gqe

@@ -1,0 +1,244 @@
+"""Python binding of libgqe.so: argument marshalling only.
+
+Every function named ``gqe_*`` here calls the C entry point of the same name
+with the tensors' device pointers and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  torch provides device
+memory and streams.  The convenience wrappers ``route``, ``qproj``,
+``attn_prefill``, ``attn_decode``, ``prefill`` and ``decode`` only allocate
+outputs with ``torch.empty`` and call the entry points.
+
+If the library is not built, loading raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqe.so")
+_lib = None
+
+GQE_F32, GQE_BF16 = 0, 1
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3: "pointer not 16-byte aligned",
+           -4: "kernel launch failed", -5: "workspace missing or too small"}
+
+# Every symbol the C header declares (checked by the host tests).
+EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
+           "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode")
+
+
+class GqeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status} ({_STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+class GqeDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "d_model", "H_q", "H_kv", "k", "d_head", "n_shared", "causal", "route_mode", "dtype")]
+
+    @property
+    def G(self) -> int:
+        return self.H_kv
+
+    @property
+    def E(self) -> int:
+        return self.H_q // self.H_kv
+
+    @property
+    def N(self) -> int:
+        return self.H_q
+
+    @property
+    def S(self) -> int:
+        return self.k * self.H_kv + (self.H_kv if self.route_mode else 1) + self.n_shared
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == GQE_BF16 else torch.float32
+
+
+def make_desc(B, T, d_model, H_q, H_kv, k, d_head, n_shared=1, causal=1, route_mode=0, dtype="bf16") -> GqeDesc:
+    dt = {"bf16": GQE_BF16, "f32": GQE_F32, torch.bfloat16: GQE_BF16, torch.float32: GQE_F32}[dtype]
+    return GqeDesc(B, T, d_model, H_q, H_kv, k, d_head, n_shared, causal, route_mode, dt)
+
+
+def desc_from(w, **over) -> GqeDesc:
+    """Descriptor from any object with the shape attributes (e.g. a workload)."""
+    f = dict(B=w.B, T=w.T, d_model=w.d_model, H_q=w.H_q, H_kv=w.H_kv, k=w.k, d_head=w.d_head,
+             n_shared=w.n_shared, causal=w.causal, route_mode=w.route_mode, dtype=w.dtype)
+    f.update(over)
+    return make_desc(**f)
+
+
+def load():
+    """Load libgqe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m sparse_routed_query_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        D = ctypes.POINTER(GqeDesc)
+        lib.gqe_num_slots.argtypes = [D]
+        lib.gqe_num_slots.restype = I
+        lib.gqe_status_string.argtypes = [I]
+        lib.gqe_status_string.restype = ctypes.c_char_p
+        lib.gqe_route_workspace_bytes.argtypes = [D]
+        lib.gqe_route_workspace_bytes.restype = Z
+        lib.gqe_route.argtypes = [D, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.gqe_route.restype = I
+        lib.gqe_qproj.argtypes = [D, P, P, P, P, P, P, P, P, P]
+        lib.gqe_qproj.restype = I
+        lib.gqe_attn_prefill.argtypes = [D, P, P, P, P, P, P, P]
+        lib.gqe_attn_prefill.restype = I
+        lib.gqe_decode_workspace_bytes.argtypes = [D, ctypes.c_int32]
+        lib.gqe_decode_workspace_bytes.restype = Z
+        lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
+        lib.gqe_attn_decode.restype = I
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise GqeError(fn, rc)
+
+
+# ---------------------------------------------------------------- entry points
+
+def gqe_num_slots(desc: GqeDesc) -> int:
+    return load().gqe_num_slots(ctypes.byref(desc))
+
+
+def gqe_route_workspace_bytes(desc: GqeDesc) -> int:
+    return load().gqe_route_workspace_bytes(ctypes.byref(desc))
+
+
+def gqe_decode_workspace_bytes(desc: GqeDesc, L_max: int) -> int:
+    return load().gqe_decode_workspace_bytes(ctypes.byref(desc), L_max)
+
+
+def gqe_route(desc, x, w_router, b_router, sel, p_tilde, counts, offsets, rows, logits, workspace, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_route(ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+                          _ptr(b_router, torch.float32, "b_router"), _ptr(sel, torch.int32, "sel"),
+                          _ptr(p_tilde, torch.float32, "p_tilde"), _ptr(counts, torch.int32, "counts"),
+                          _ptr(offsets, torch.int32, "offsets"), _ptr(rows, torch.int32, "rows"),
+                          _ptr(logits, torch.float64, "logits"), _ptr(workspace, None, "workspace"),
+                          workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                          _stream(stream))
+    _check("gqe_route", rc)
+
+
+def gqe_qproj(desc, x, w_q, sel, counts, offsets, rows, q_routed, q_shared, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_qproj(ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_q, dt, "w_q"), _ptr(sel, torch.int32, "sel"),
+                          _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+                          _ptr(rows, torch.int32, "rows"), _ptr(q_routed, dt, "q_routed"),
+                          _ptr(q_shared, dt, "q_shared"), _stream(stream))
+    _check("gqe_qproj", rc)
+
+
+def gqe_attn_prefill(desc, q_routed, q_shared, k, v, p_tilde, out, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_attn_prefill(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
+                                 _ptr(k, dt, "k"), _ptr(v, dt, "v"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                 _ptr(out, torch.float32, "out"), _stream(stream))
+    _check("gqe_attn_prefill", rc)
+
+
+def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace, stream=None):
+    dt = desc.torch_dtype
+    L_max = k_cache.shape[2]
+    rc = load().gqe_attn_decode(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
+                                _ptr(k_cache, dt, "k_cache"), _ptr(v_cache, dt, "v_cache"), L_max,
+                                _ptr(lens, torch.int32, "lens"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gqe_attn_decode", rc)
+
+
+# ---------------------------------------------------------------- allocating wrappers
+
+def alloc_route(desc: GqeDesc, device, logits: bool = False) -> dict:
+    BT, G, k, N = desc.B * desc.T, desc.G, desc.k, desc.N
+    e = lambda *s, dtype: torch.empty(s, dtype=dtype, device=device)  # noqa: E731
+    return dict(sel=e(BT, G, k, dtype=torch.int32), p_tilde=e(BT, G, k, dtype=torch.float32),
+                counts=e(N, dtype=torch.int32), offsets=e(N + 1, dtype=torch.int32),
+                rows=e(BT * G * k, dtype=torch.int32),
+                logits=e(BT, N, dtype=torch.float64) if logits else None,
+                workspace=e(max(1, gqe_route_workspace_bytes(desc)), dtype=torch.uint8))
+
+
+def alloc_qproj(desc: GqeDesc, device) -> dict:
+    dt = desc.torch_dtype
+    qr = torch.empty((desc.B, desc.G, desc.T, desc.k, desc.d_head), dtype=dt, device=device)
+    qs = torch.empty((desc.B, desc.T, desc.d_head), dtype=dt, device=device) if desc.n_shared else None
+    return dict(q_routed=qr, q_shared=qs)
+
+
+def route(desc, x, w_router, b_router=None, logits=False, bufs=None, stream=None) -> dict:
+    r = bufs if bufs is not None else alloc_route(desc, x.device, logits)
+    gqe_route(desc, x, w_router, b_router, r["sel"], r["p_tilde"], r["counts"], r["offsets"], r["rows"],
+              r["logits"], r["workspace"], stream)
+    return r
+
+
+def qproj(desc, x, w_q, r: dict, bufs=None, stream=None) -> dict:
+    q = bufs if bufs is not None else alloc_qproj(desc, x.device)
+    gqe_qproj(desc, x, w_q, r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"], q["q_shared"], stream)
+    return q
+
+
+def attn_prefill(desc, q: dict, k, v, p_tilde, out=None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((desc.B, desc.T, desc.S, desc.d_head), dtype=torch.float32, device=k.device)
+    gqe_attn_prefill(desc, q["q_routed"], q["q_shared"], k, v, p_tilde, out, stream)
+    return out
+
+
+def attn_decode(desc, q: dict, k_cache, v_cache, lens, p_tilde, out=None, workspace=None, stream=None):
+    if out is None:
+        out = torch.empty((desc.B, desc.S, desc.d_head), dtype=torch.float32, device=k_cache.device)
+    if workspace is None:
+        workspace = torch.empty(gqe_decode_workspace_bytes(desc, k_cache.shape[2]), dtype=torch.uint8,
+                                device=k_cache.device)
+    gqe_attn_decode(desc, q["q_routed"], q["q_shared"], k_cache, v_cache, lens, p_tilde, out, workspace, stream)
+    return out
+
+
+def prefill(desc, x, w_router, b_router, w_q, k, v, logits=False, stream=None) -> dict:
+    """Whole prefill path: route -> compaction -> projection -> attention -> slots."""
+    r = route(desc, x, w_router, b_router, logits=logits, stream=stream)
+    q = qproj(desc, x, w_q, r, stream=stream)
+    out = attn_prefill(desc, q, k, v, r["p_tilde"], stream=stream)
+    return dict(r, **q, out=out)
+
+
+def decode(desc, x, w_router, b_router, w_q, k_cache, v_cache, lens, stream=None) -> dict:
+    """Whole decode step for one new token per sequence (desc.T == 1)."""
+    r = route(desc, x, w_router, b_router, stream=stream)
+    q = qproj(desc, x, w_q, r, stream=stream)
+    out = attn_decode(desc, q, k_cache, v_cache, lens, r["p_tilde"], stream=stream)
+    return dict(r, **q, out=out)

@@ -1,0 +1,154 @@
+"""GPU-vs-oracle parity of the whole GQE path through the C ABI (MI355X only).
+
+Full-size workloads are compared on a stratified sample of tokens (routing
+and compaction on every token); the small shapes below span several tiles
+with ragged tails and the method's degenerate cases, compared on every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_parity_util import (check_out, check_route, full_decode_check, full_prefill_check, gpu_prefill, say,
+                             gpu_decode)
+import sparse_routed_query_amd.gqe as G
+
+pytestmark = pytest.mark.gpu
+
+
+def small(**kw):
+    base = dict(name="small", B=2, T=300, d_model=128, H_q=8, H_kv=2, k=2, d_head=64, dtype="bf16", seed=11,
+                act_std=1.0, w_std=0.02)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_tiny_fp32_both_route_modes():
+    w = W.WORKLOADS["tiny_fp32"]
+    full_prefill_check(w)
+    full_prefill_check(w.replace(route_mode=0, name="tiny_fp32_mode0"))
+
+
+def test_main_250m():
+    full_prefill_check(W.WORKLOADS["main_250m"], n_sample=192)
+
+
+def test_long_32k_gqe_and_dense():
+    w = W.WORKLOADS["long_32k"]
+    full_prefill_check(w, n_sample=96)
+    full_prefill_check(W.dense_variant(w), n_sample=48)
+
+
+def test_wide_zipf():
+    w = W.WORKLOADS["wide_zipf"]
+    inp, gpu, agreed = full_prefill_check(w, n_sample=96)
+    c = agreed["counts"]
+    say(f"[{w.name}] per-expert rows min={c.min()} max={c.max()} mean={c.mean():.0f}")
+    assert c.max() > 1.3 * c.mean()     # the Zipf bias makes the load visibly uneven
+
+
+def test_decode_b64():
+    inp, gpu = full_decode_check(W.WORKLOADS["decode_b64"])
+    assert np.isfinite(gpu["out"].numpy()).all()   # NaN-poisoned cache tails were never read
+
+
+# ---------------------------------------------------------------- small shapes, every token
+
+EDGE = [
+    small(),                                            # 5 query tiles per head, ragged tail
+    small(T=1), small(T=2), small(T=63), small(T=64), small(T=65), small(B=1, T=257),
+    small(H_q=4, H_kv=4, k=1, name="E1_mha"),           # one expert per group
+    small(H_q=8, H_kv=2, k=4, name="k_eq_E"),           # every expert kept = dense GQA
+    small(H_q=4, H_kv=1, k=2, name="G1_mqa"),           # one group
+    small(d_head=32, name="d32"), small(d_head=128, name="d128"),
+    small(causal=0, name="noncausal"),
+    small(n_shared=0, name="no_shared"),
+    small(route_mode=1, name="per_group_slots"),
+    small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="zipf"),
+    small(dtype="f32", T=100, d_model=96, name="f32_d64"),
+    small(dtype="f32", T=70, d_head=128, d_model=64, k=1, name="f32_d128"),
+    small(dtype="f32", T=50, causal=0, route_mode=1, name="f32_noncausal"),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: f"{w.name}-T{w.T}-d{w.d_head}-{w.dtype}")
+def test_small_shapes_every_token(w):
+    full_prefill_check(w)
+
+
+def test_empty_batch():
+    w = small(B=0, name="empty")
+    d = G.desc_from(w)
+    dev = "cuda"
+    r = G.alloc_route(d, dev)
+    r["counts"].fill_(7)
+    r["offsets"].fill_(7)
+    x = torch.empty((0, w.d_model), dtype=torch.bfloat16, device=dev)
+    G.route(d, x, torch.zeros((w.N, w.d_model), dtype=torch.bfloat16, device=dev), bufs=r)
+    q = G.qproj(d, x, torch.zeros((w.N + 1, w.d_head, w.d_model), dtype=torch.bfloat16, device=dev), r)
+    kv = torch.empty((0, w.H_kv, w.T, w.d_head), dtype=torch.bfloat16, device=dev)
+    out = G.attn_prefill(d, q, kv, kv, r["p_tilde"])
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+    assert (r["counts"].cpu() == 0).all() and (r["offsets"].cpu() == 0).all()
+
+
+def test_zero_router_ties_break_to_lowest_index_exactly():
+    w = small(H_q=16, H_kv=4, k=2)
+    inp = W.make_inputs(w)
+    inp["w_router"] = torch.zeros_like(inp["w_router"])
+    gpu = gpu_prefill(w, inp)
+    assert (gpu["sel"] == torch.arange(w.k, dtype=torch.int32)).all()
+    assert (gpu["p_tilde"] == 1.0 / w.k).all()
+    check_route(w, inp, gpu)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = W.WORKLOADS["main_250m"]
+    inp = W.make_inputs(w)
+    a = gpu_prefill(w, inp)
+    b = gpu_prefill(w, inp)
+    for key in ("sel", "p_tilde", "counts", "offsets", "rows", "q_routed", "q_shared", "out"):
+        assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------- decode edges
+
+def decode_case(**kw):
+    base = dict(name="dec", B=5, T=1, d_model=128, H_q=8, H_kv=2, k=1, d_head=64, dtype="bf16", seed=21,
+                act_std=1.0, w_std=0.02, decode=True, L_lo=1, L_hi=700, L_max=700)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+@pytest.mark.parametrize("w", [
+    decode_case(),
+    decode_case(k=2, route_mode=1, name="dec_k2_mode1"),
+    decode_case(d_head=128, H_q=12, H_kv=3, k=3, name="dec_d128_dense"),
+    decode_case(d_head=32, n_shared=0, name="dec_d32_noshared"),
+    decode_case(dtype="f32", name="dec_f32"),
+    decode_case(dtype="f32", d_head=128, L_hi=300, L_max=300, name="dec_f32_d128"),
+], ids=lambda w: w.name)
+def test_decode_shapes(w):
+    drawn = W.make_inputs(w)["lens"]
+    lens = drawn.clone()
+    lens[0], lens[1] = 1, w.L_max               # a one-entry cache and a full cache
+    full_decode_check(w, W.make_inputs(w, lens=lens))
+
+
+def test_decode_matches_last_prefill_row():
+    """Decode of position L-1 equals prefill row L-1 computed by the GPU."""
+    w = small(B=3, T=200, k=1, H_q=8, H_kv=4)
+    inp = W.make_inputs(w)
+    pre = gpu_prefill(w, inp)
+    lens = torch.tensor([200, 37, 1], dtype=torch.int32)
+    dw = w.replace(T=1, decode=True, L_max=200)
+    dinp = dict(x=inp["x"][torch.arange(3), lens.long() - 1].reshape(3, 1, -1), w_router=inp["w_router"],
+                b_router=None, w_q=inp["w_q"], k_cache=inp["k"], v_cache=inp["v"], lens=lens)
+    dec = gpu_decode(dw, dinp)
+    ref = pre["out"][torch.arange(3), lens.long() - 1]
+    check_out(dw, dec["out"].numpy(), ref.double().numpy(), "decode vs prefill row")
+    assert torch.equal(dec["sel"], pre["sel"].reshape(3, 200, w.G, w.k)[torch.arange(3), lens.long() - 1])
+

@@ -110,7 +110,7 @@ def _randn(gen: torch.Generator, shape, std: float) -> torch.Tensor:
     return torch.randn(shape, generator=gen, dtype=torch.float32) * std
 
 
-def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+def make_inputs(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Tensor] = None) -> dict:
     """Draw the seeded inputs of workload ``w`` as CPU tensors.
 
     Returns a dict with ``x`` [B, T, d_model], ``w_router`` [N, d_model],
@@ -118,7 +118,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     (routed experts in global index order g*E + e, shared head last), and
     ``k``/``v`` [B, H_kv, T, d_head] for prefill.  Decode workloads return
     ``k_cache``/``v_cache`` [B, H_kv, L_max, d_head] with every position at or
-    beyond a sequence's length set to NaN, and ``lens`` [B] int32.
+    beyond a sequence's length set to NaN, and ``lens`` [B] int32 (``lens``
+    replaces the drawn lengths when given; the random draws stay the same).
     """
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed if seed is None else seed)
@@ -133,7 +134,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
         shape = (w.B, w.H_kv, w.L_max, w.d_head)
         kc = _randn(gen, shape, w.act_std).to(dt)
         vc = _randn(gen, shape, w.act_std).to(dt)
-        lens = torch.randint(w.L_lo, w.L_hi + 1, (w.B,), generator=gen, dtype=torch.int64).to(torch.int32)
+        drawn = torch.randint(w.L_lo, w.L_hi + 1, (w.B,), generator=gen, dtype=torch.int64).to(torch.int32)
+        lens = drawn if lens is None else lens.to(torch.int32).clone()
         for b in range(w.B):
             kc[b, :, int(lens[b]):, :] = float("nan")
             vc[b, :, int(lens[b]):, :] = float("nan")
