@@ -1,0 +1,284 @@
+"""Benchmark of the GQE attention forward on one MI355X.
+
+A step is one pass of the whole prefill path on the main 250M-scale layer
+shape (B=4, T=4096, d_model=1024, H_q=16, H_kv=8, k=1, shared head,
+d_head=64, bf16): router + compaction (gqe_route), routed and shared query
+projection (gqe_qproj), causal attention and slot assembly
+(gqe_attn_prefill), with every input already resident in HBM.
+
+Printed value: routed prefill throughput in TFLOP/s counted over active
+heads only (attention FLOPs 4*d*B*H_act*T(T+1)/2 with H_act = k*G + 1,
+divided by the whole step's time).  The same JSON line carries:
+  roofline      the attention call (gqe_attn_prefill) timed with HIP events
+                on the stream it is launched on, against the bf16 MFMA peak;
+  decode        the one-token decode step on the decode workload (B=64 cache
+                lengths in [4096, 8192]): gqe_attn_decode timed alone, bytes of
+                K/V it must read over its time, against the HBM peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  long_context  T=32768 GQE vs all-active GQA on the same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-context]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+METRIC = "routed prefill TFLOP/s (active heads) + %MFMA peak; decode GB/s + %HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-context", action="store_true", help="skip the long-context GQE vs dense leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+class Prefill:
+    """Preallocated buffers and the three C-ABI calls of one prefill step."""
+
+    def __init__(self, w, inp, dev):
+        import torch
+        import sparse_routed_query_amd.gqe as G
+        self.G, self.w = G, w
+        self.d = G.desc_from(w)
+        self.x = inp["x"].reshape(-1, w.d_model).to(dev)
+        self.wr = inp["w_router"].to(dev)
+        self.br = inp["b_router"].to(dev) if inp["b_router"] is not None else None
+        self.wq = inp["w_q"].to(dev)
+        self.k = inp["k"].to(dev)
+        self.v = inp["v"].to(dev)
+        self.r = G.alloc_route(self.d, dev)
+        self.q = G.alloc_qproj(self.d, dev)
+        self.out = torch.empty((w.B, w.T, self.d.S, w.d_head), dtype=torch.float32, device=dev)
+
+    def route(self):
+        r = self.r
+        self.G.gqe_route(self.d, self.x, self.wr, self.br, r["sel"], r["p_tilde"], r["counts"], r["offsets"],
+                         r["rows"], None, r["workspace"])
+
+    def qproj(self):
+        r, q = self.r, self.q
+        self.G.gqe_qproj(self.d, self.x, self.wq, r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"],
+                         q["q_shared"])
+
+    def attn(self):
+        self.G.gqe_attn_prefill(self.d, self.q["q_routed"], self.q["q_shared"], self.k, self.v, self.r["p_tilde"],
+                                self.out)
+
+    def step(self):
+        self.route()
+        self.qproj()
+        self.attn()
+
+
+def time_calls(fn_list, n, torch):
+    """Average ms per call of each function, timed with events on the current stream."""
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fn_list]
+          for _ in range(n)]
+    for i in range(n):
+        for j, fn in enumerate(fn_list):
+            ev[i][j][0].record()
+            fn()
+            ev[i][j][1].record()
+    torch.cuda.synchronize()
+    return [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(n)) / n for j in range(len(fn_list))]
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_routed_query_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key: str, src_hash: str):
+    """HBM bytes per launch from committed PMC counters, if taken on this exact source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    e = data.get(kernel_key)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, target_s: float):
+    """The oracle as it stands on a stratified sample of the workload's tokens."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    d = oracle.desc(w)
+    x = inp["x"].reshape(-1, w.d_model)
+
+    def run(tok):
+        t0 = time.perf_counter()
+        r = oracle.route(d, x[tok], inp["w_router"], inp["b_router"])
+        sel_full = np.zeros((w.B * w.T, w.G, w.k), dtype=np.int32)
+        pt_full = np.zeros((w.B * w.T, w.G, w.k))
+        sel_full[tok], pt_full[tok] = r["sel"], r["ptilde"]
+        oracle.prefill_rows(d, inp["x"], inp["w_q"], inp["k"], inp["v"], sel_full, pt_full, tok)
+        return time.perf_counter() - t0
+
+    def flops(tok):
+        t = tok % w.T
+        return float(np.sum(4.0 * w.d_head * w.h_active * (t + 1)))
+
+    probe = W.stratified_rows(w, 128, seed=7).numpy()
+    tp = run(probe)
+    n = int(min(w.B * w.T, max(128, 128 * target_s / max(tp, 1e-3))))
+    tok = W.stratified_rows(w, n, seed=8).numpy()
+    dt = run(tok)
+    return {"value": flops(tok) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(tok)} of {w.B * w.T} tokens of {w.name}, stratified over position; routing of those "
+                      f"tokens plus their projections, causal attention and slots; {dt:.1f} s wall",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def decode_leg(torch, dev, steps):
+    import sparse_routed_query_amd.gqe as G
+    import workloads as W
+    w = W.WORKLOADS["decode_b64"]
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    x = inp["x"].reshape(w.B, w.d_model).to(dev)
+    wr, wq, lens = inp["w_router"].to(dev), inp["w_q"].to(dev), inp["lens"].to(dev)
+    # two cache copies used alternately, so the 256 MB last-level cache cannot serve a step from the previous one
+    caches = [(inp["k_cache"].to(dev), inp["v_cache"].to(dev))]
+    caches.append((caches[0][0].clone(), caches[0][1].clone()))
+    r = G.alloc_route(d, dev)
+    q = G.alloc_qproj(d, dev)
+    out = torch.empty((w.B, d.S, w.d_head), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.gqe_decode_workspace_bytes(d, w.L_max), dtype=torch.uint8, device=dev)
+
+    def route():
+        G.gqe_route(d, x, wr, None, r["sel"], r["p_tilde"], r["counts"], r["offsets"], r["rows"], None,
+                    r["workspace"])
+
+    def qp():
+        G.gqe_qproj(d, x, wq, r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"], q["q_shared"])
+
+    it = [0]
+
+    def attn():
+        kc, vc = caches[it[0] & 1]
+        it[0] += 1
+        G.gqe_attn_decode(d, q["q_routed"], q["q_shared"], kc, vc, lens, r["p_tilde"], out, ws)
+
+    for _ in range(3):
+        route(); qp(); attn()
+    torch.cuda.synchronize()
+    t_route, t_qp, t_attn = time_calls([route, qp, attn], steps, torch)
+    nbytes = W.decode_kv_bytes(w, inp["lens"])
+    gbs = nbytes / (t_attn * 1e-3) / 1e9
+    return {"workload": w.name, "value": gbs, "unit": "GB/s", "metric": "decode attention GB/s (K/V bytes read once)",
+            "attn_us": t_attn * 1e3, "step_us": (t_route + t_qp + t_attn) * 1e3,
+            "route_us": t_route * 1e3, "qproj_us": t_qp * 1e3,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode", source_hash("attn_decode.hip")),
+                         "algorithmic_bytes": nbytes, "kernel": "gqe_attn_decode (split + combine)"}}
+
+
+def long_context_leg(torch, dev, steps):
+    import workloads as W
+    w = W.WORKLOADS["long_32k"]
+    inp = W.make_inputs(w)
+    res = {}
+    for name, ww in (("gqe", w), ("dense", W.dense_variant(w))):
+        p = Prefill(ww, inp, dev)
+        for _ in range(2):
+            p.step()
+        torch.cuda.synchronize()
+        t_route, t_qp, t_attn = time_calls([p.route, p.qproj, p.attn], steps, torch)
+        fl = W.attention_flops(ww)
+        res[name] = {"attn_ms": t_attn, "step_ms": t_route + t_qp + t_attn, "attn_tflops": fl / (t_attn * 1e-3) / 1e12,
+                     "active_heads": ww.h_active}
+        del p
+    res["speedup_attn"] = res["dense"]["attn_ms"] / res["gqe"]["attn_ms"]
+    res["speedup_step"] = res["dense"]["step_ms"] / res["gqe"]["step_ms"]
+    res["ideal_flop_ratio"] = 16 / 9
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU layout is a design note, "
+              f"not a measured path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS["main_250m"]
+    inp = W.make_inputs(w)
+    p = Prefill(w, inp, dev)
+    for _ in range(args.warmup):
+        p.step()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        p.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    fl = W.attention_flops(w)
+    value = fl / (ms_step * 1e-3) / 1e12
+
+    # per-call split, measured in a separate pass with events around each call
+    t_route, t_qp, t_attn = time_calls([p.route, p.qproj, p.attn], max(10, args.steps), torch)
+    attn_tflops = fl / (t_attn * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "d_model": w.d_model, "H_q": w.H_q, "H_kv": w.H_kv,
+                   "k": w.k, "n_shared": w.n_shared, "d_head": w.d_head, "causal": w.causal,
+                   "active_heads": w.h_active, "attention_flops_per_step": fl, "parallelism": "single GPU"},
+        "step_split_us": {"route": t_route * 1e3, "qproj": t_qp * 1e3, "attn_prefill": t_attn * 1e3},
+        "wall_s_timed": wall,
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_for("prefill", source_hash("attn_prefill.hip")),
+                     "kernel": "gqe_attn_prefill (attention + slot assembly)",
+                     "algorithmic_flops_per_launch": fl},
+    }
+    del p
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = decode_leg(torch, dev, max(10, args.steps // 2))
+        torch.cuda.empty_cache()
+    if not args.no_context:
+        line["long_context"] = long_context_leg(torch, dev, 5)
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -59,6 +59,8 @@ def _load():
         lib.ora_decode.restype = ctypes.c_int
         lib.ora_num_slots.argtypes = [P]
         lib.ora_num_slots.restype = ctypes.c_int
+        lib.ora_num_threads.argtypes = []
+        lib.ora_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -82,6 +84,11 @@ def desc(w, **over) -> _Desc:
     f = {n: int(getattr(w, n)) for n, _ in _Desc._fields_}
     f.update({k: int(v) for k, v in over.items()})
     return _Desc(**f)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().ora_num_threads()
 
 
 def num_slots(d: _Desc) -> int:
@@ -192,5 +199,5 @@ def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens):
     return dict(out=out, sel=sel, ptilde=pt, tie=tie.astype(bool))
 
 
-__all__ = ["build", "desc", "num_slots", "route", "compact", "qproj_rows", "prefill_rows", "prefill",
+__all__ = ["build", "desc", "num_slots", "num_threads", "route", "compact", "qproj_rows", "prefill_rows", "prefill",
            "decode", "TIE_MARGIN"]

@@ -35,6 +35,7 @@
  *     weighted slot(s), then the shared slot.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -53,6 +54,9 @@ static int ora_nslots(const ora_desc* D)
 }
 
 int ora_num_slots(const ora_desc* D) { return ora_nslots(D); }
+
+/* Threads an OpenMP parallel region of the oracle uses. */
+int ora_num_threads(void) { return omp_get_max_threads(); }
 
 static double dot(const double* a, const double* b, int64_t n)
 {

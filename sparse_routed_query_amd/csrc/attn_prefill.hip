@@ -69,7 +69,36 @@ __device__ __forceinline__ PfWork pf_map(int id, int B, int T, int G, int k, int
     }
 }
 
-__device__ __forceinline__ int swap_bits23(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two transposing LDS reads give the V^T operand of a 32x32x16 MFMA.  Within
+// each 16-lane group, lane i of ds_read_b64_tr_b16 receives element (i % 4) of
+// the 8-byte chunk addressed by lane 4*j + i/4, as its element j.  Source lane
+// s = 4*j + q therefore points at V[key_j][d0 + 4q .. 4q+3] so that lane i ends
+// up holding V[key_0..3][d0 + i].  The caller folds the per-lane part of that
+// address into `off`.
+__device__ __forceinline__ bf16x8 load_vt(const uint16_t* base, int off, int pitch8)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + pitch8));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Softmax reference threshold: the running reference m_ref only moves when a
+// tile's scores exceed it by more than 2^8, so probabilities stay <= 256 and
+// most tiles need neither a subtraction nor a rescale of the accumulators.
+constexpr float kPfRescale = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(
@@ -77,6 +106,9 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     const uint16_t* __restrict__ vg, float* __restrict__ out, int B, int T, int G, int k, int n_shared, int causal,
     int S, float qscale)
 {
+    constexpr int P = D + kPfPad;           // LDS row pitch (elements)
+    constexpr int NDB = D / 32;
+    constexpr int NCH = kPfBN * D / 8 / 256; // 16-byte chunks per thread for one K or V tile
     const PfWork w = pf_map(blockIdx.x, B, T, G, k, n_shared, causal);
     const bool shared = w.h == G;
     const int kk = shared ? 1 : k;
@@ -92,139 +124,139 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     const int r0 = w.tile * kPfBM;
     const int nkv = pf_nkv(w.tile, kk, R, T, causal);
 
-    // this lane's query row / position
     const int qrow = r0 + wave * 32 + lr;
     const bool qvalid = qrow < R;
-    const int tq = qvalid ? qrow / kk : 0;
-    // key tiles this wave needs (waves of the first rows of a diagonal tile need fewer)
+    const int tq = qvalid ? qrow / kk : 0;   // invalid rows see key 0 only, so they stay finite
     const int wrow_hi = min(R - 1, r0 + wave * 32 + 31);
     const int nkv_w = causal ? (wrow_hi / kk) / kPfBN + 1 : nkv;
     const int t_lo_w = (r0 + wave * 32) / kk;
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kPfBN][D + kPfPad];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[D][kPfBN + kPfPad];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPfBN * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPfBN * P];
 
-    // Q^T operand: lane holds query column lr, d = 16c + 8*lh .. +8, scaled.
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
+        bf16x8 v = {};
         if (qvalid) {
             const u32x4 raw = ld_u32x4(Q + (size_t)qrow * D + 16 * c + 8 * lh);
-            bf16x8 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[2 * i] = f2bf(bf2f((uint16_t)(raw[i] & 0xffff)) * qscale);
                 v[2 * i + 1] = f2bf(bf2f((uint16_t)(raw[i] >> 16)) * qscale);
             }
-            qf[c] = v;
-        } else {
-            qf[c] = bf16x8{};
         }
+        qf[c] = v;
     }
 
-    constexpr int NCH = kPfBN * D / 8 / 256;  // 16-byte chunks per thread for one K or V tile
     u32x4 rk[NCH], rv[NCH];
+    // Keys past T are loaded from row T-1 instead: their scores are masked, so
+    // their probabilities are exactly 0 and the (finite) values never count.
     auto load = [&](int kt) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256, s = c / (D / 8), d0 = (c % (D / 8)) * 8;
-            const int pos = kt * kPfBN + s;
-            if (pos < T) {
-                rk[i] = ld_u32x4(K + (size_t)pos * D + d0);
-                rv[i] = ld_u32x4(V + (size_t)pos * D + d0);
-            } else {
-                rk[i] = u32x4{0, 0, 0, 0};
-                rv[i] = u32x4{0, 0, 0, 0};
-            }
+            const int pos = min(kt * kPfBN + s, T - 1);
+            rk[i] = ld_u32x4(K + (size_t)pos * D + d0);
+            rv[i] = ld_u32x4(V + (size_t)pos * D + d0);
         }
     };
-    auto store = [&]() {
+    auto store = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256, s = c / (D / 8), d0 = (c % (D / 8)) * 8;
-            *(u32x4*)&sK[s][d0] = rk[i];
-            const int sp = swap_bits23(s);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sV[d0 + 2 * e][sp] = (uint16_t)(rv[i][e] & 0xffff);
-                sV[d0 + 2 * e + 1][sp] = (uint16_t)(rv[i][e] >> 16);
-            }
+            *(u32x4*)&sK[buf][s * P + d0] = rk[i];
+            *(u32x4*)&sV[buf][s * P + d0] = rv[i];
         }
     };
+    // per-lane parts of the LDS addresses
+    const int k_off = lr * P + 8 * lh;                                       // K row lr, d half lh
+    const int s16 = lane & 15;
+    const int v_off = (4 * lh + (s16 >> 2)) * P + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
 
-    constexpr int NDB = D / 32;
     f32x16 o[NDB];
 #pragma unroll
     for (int j = 0; j < NDB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-    float m_run = -INFINITY, l_half = 0.f;
+    float m_ref = 0.f, l_half = 0.f;
+    f32x16 cneg;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cneg[r] = 0.f;
 
     load(0);
+    store(0);
+    __syncthreads();
     for (int kt = 0; kt < nkv; ++kt) {
-        __syncthreads();
-        store();
-        __syncthreads();
+        const int buf = kt & 1;
         if (kt + 1 < nkv) load(kt + 1);
-        if (kt >= nkv_w) continue;
-
-        // S^T = K Q^T for two 32-key blocks
-        f32x16 s[2];
+        if (kt < nkv_w) {
+            const uint16_t* bK = sK[buf];
+            const uint16_t* bV = sV[buf];
+            // S^T - m_ref = K Q^T + cneg for two 32-key blocks
+            f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
+                s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P), qf[0], cneg);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-            for (int c = 0; c < D / 16; ++c) {
-                const bf16x8 a = ld_bf16x8(&sK[kb * 32 + lr][16 * c + 8 * lh]);
-                s[kb] = mfma32(a, qf[c], s[kb]);
+                for (int c = 1; c < D / 16; ++c) s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P + 16 * c), qf[c], s[kb]);
             }
-        }
-        // mask: keys past the causal edge, or past T
-        const int s0 = kt * kPfBN;
-        const bool need_mask = causal ? (s0 + kPfBN - 1 > t_lo_w) : (s0 + kPfBN > T);
-        if (need_mask) {
-            const int lim = causal ? tq : T - 1;
+            const int s0 = kt * kPfBN;
+            const bool need_mask = causal ? (s0 + kPfBN - 1 > t_lo_w) : (s0 + kPfBN > T);
+            if (need_mask) {
+                // key of element r in block kb is s0 + 4*lh + (kb*32 + 8*(r/4) + r%4)
+                const int lim = (causal ? tq : T - 1) - s0 - 4 * lh;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
+            }
+            float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[0][r], s[0][r + 1]));
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[1][r], s[1][r + 1]));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            // first tile: set the reference; later tiles: move it only on a large jump
+            const bool move = kt == 0 ? true : mt > kPfRescale;
+            if (__ballot(move)) {
+                const float shift = move ? mt : 0.f;
+                const float alpha = kt == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
+#pragma unroll
+                for (int j = 0; j < NDB; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+                l_half *= alpha;
+                m_ref += shift;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+            }
+            // P = exp2(S - m_ref), packed to bf16; the row sum uses the rounded values
+            uint32_t pw[16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = s0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    if (key > lim) s[kb][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; r += 2)
+                    pw[kb * 8 + r / 2] = pk_bf16(__builtin_amdgcn_exp2f(s[kb][r]), __builtin_amdgcn_exp2f(s[kb][r + 1]));
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) l_half = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, l_half, false);
+            // O^T += V^T P^T over the four 16-key steps
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 pv = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+                for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * P + 32 * j, 8 * P), pb, o[j]);
+            }
         }
-        float mt = s[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float ls = 0.f;
-        bf16x8 pb[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
-                ls += p;
-                pb[kb * 2 + (r >> 3)][r & 7] = f2bf(p);
-            }
-        l_half = l_half * alpha + ls;
-#pragma unroll
-        for (int j = 0; j < NDB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-        // O^T += V^T P^T over the four 16-key steps
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int j = 0; j < NDB; ++j) {
-                const bf16x8 a = ld_bf16x8(&sV[j * 32 + lr][16 * c + 8 * lh]);
-                o[j] = mfma32(a, pb[c], o[j]);
-            }
+        if (kt + 1 < nkv) store(buf ^ 1);
+        __syncthreads();
     }
 
     if (!qvalid) return;
