@@ -11,9 +11,9 @@
 //                 registers (k kept rows, plus the shared row on group 0), so
 //                 each cached byte is read once.  It writes (max, sum, o) of
 //                 the chunk in base-2 units.
-// combine kernel: one workgroup per sequence merges the chunks of each row in
-//                 chunk order (deterministic), writes the hard and shared
-//                 slots and the weighted slot(s).
+// merge kernel:   one wave per (row, sequence) merges that row's chunks in
+//                 chunk order (deterministic) into its hard or shared slot;
+//                 the slot-assembly kernel then forms the weighted slot(s).
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
@@ -130,48 +130,42 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
     }
 }
 
+// One wave per (query row, sequence): merges the chunk partials of that row.
+// The maximum and the sum of the chunk weights are wave reductions; the value
+// rows are summed in chunk order, so the result does not depend on timing.
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part,
-                                                             const int32_t* __restrict__ lens,
-                                                             const float* __restrict__ p_tilde,
-                                                             float* __restrict__ out, int G, int k, int n_shared,
-                                                             int route_mode, int S, int nch, int CH)
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ lens, float* __restrict__ out,
+                                                          int G, int k, int n_shared, int S, int nch, int CH)
 {
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int row = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const int kG = G * k;
+    const int g = row < kG ? row / k : 0;
+    const int r = row < kG ? row % k : k;
+    const int RG = k + n_shared;
     const int L = min(max(lens[b], 0), nch * CH);
     const int nc = (L + CH - 1) / CH;
-    const int RG = k + n_shared;
-    const int kG = G * k;
-    const int nrows = kG + n_shared;
-    extern __shared__ float s_h[];  // [nrows][D] merged rows
-    for (int idx = tid; idx < nrows * D; idx += 256) {
-        const int row = idx / D, d = idx % D;
-        const int g = row < kG ? row / k : 0;
-        const int r = row < kG ? row % k : k;
-        const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
-        float M = -INFINITY;
-        for (int c = 0; c < nc; ++c) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
-        float Ls = 0.f, O = 0.f;
-        for (int c = 0; c < nc; ++c) {
-            const float* q = pp + (size_t)c * (D + 2);
-            const float wgt = __builtin_amdgcn_exp2f(q[0] - M);
-            Ls = fmaf(q[1], wgt, Ls);
-            O = fmaf(q[2 + d], wgt, O);
+    const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
+    float M = -INFINITY;
+    for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
+    M = wave_max(M);
+    float Ls = 0.f;
+    for (int c = lane; c < nc; c += 64) Ls += pp[(size_t)c * (D + 2) + 1] * __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
+    Ls = wave_sum(Ls);
+    const float inv = 1.f / Ls;
+    float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
+#pragma unroll
+    for (int d0 = 0; d0 < D; d0 += 64) {
+        const int d = d0 + lane;
+        if (d < D) {
+            float O = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < nc; ++c) {
+                const float* q = pp + (size_t)c * (D + 2);
+                O = fmaf(q[2 + d], __builtin_amdgcn_exp2f(q[0] - M), O);
+            }
+            dst[d] = O * inv;
         }
-        const float val = O / Ls;
-        s_h[row * D + d] = val;
-        out[((size_t)b * S + (row < kG ? row : S - 1)) * D + d] = val;
-    }
-    __syncthreads();
-    const float* pt = p_tilde + (size_t)b * G * k;
-    const int nroute = route_mode ? G : 1;
-    for (int idx = tid; idx < nroute * D; idx += 256) {
-        const int gg = idx / D, d = idx % D;
-        float acc = 0.f;
-        const int g_lo = route_mode ? gg : 0, g_hi = route_mode ? gg + 1 : G;
-        for (int g = g_lo; g < g_hi; ++g)
-            for (int j = 0; j < k; ++j) acc = fmaf(pt[g * k + j], s_h[(g * k + j) * D + d], acc);
-        out[((size_t)b * S + kG + gg) * D + d] = acc;
     }
 }
 
@@ -204,9 +198,10 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t st)
     decode_split_kernel<ET, D><<<grid, 256, 0, st>>>((const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache,
                                                      (const ET*)a.v_cache, a.lens, (float*)a.workspace, a.G, a.k,
                                                      a.n_shared, a.L_max, nch, qscale);
-    const size_t lds = (size_t)(a.G * a.k + a.n_shared) * D * sizeof(float);
-    decode_combine_kernel<D><<<a.B, 256, lds, st>>>((const float*)a.workspace, a.lens, a.p_tilde, a.out, a.G, a.k,
-                                                    a.n_shared, a.route_mode, a.S, nch, CH);
+    dim3 mgrid(a.G * a.k + a.n_shared, a.B);
+    decode_merge_kernel<D><<<mgrid, 64, 0, st>>>((const float*)a.workspace, a.lens, a.out, a.G, a.k, a.n_shared, a.S,
+                                                 nch, CH);
+    launch_assemble(a.p_tilde, a.out, a.B, a.G, a.k, D, a.S, a.route_mode, st);
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t st)

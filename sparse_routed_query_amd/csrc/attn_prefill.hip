@@ -89,6 +89,12 @@ __device__ __forceinline__ bf16x8 load_vt(const uint16_t* base, int off, int pit
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Lanes l and l^32 own the same query column.  (v_permlane32_swap would avoid
+// the LDS round trip, but inside this loop it returned stale values on gfx950
+// with this compiler, so the exchange goes through ds_bpermute.)
+__device__ __forceinline__ float half_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float half_sum(float v) { return v + __shfl_xor(v, 32); }
+
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
 {
     const f32x2 v = {a, b};
@@ -212,12 +218,15 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
                     for (int r = 0; r < 16; ++r)
                         s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
             }
-            float mt = fmaxf(s[0][0], s[0][1]);
+            // chained form so the compiler emits v_max3_f32
+            float mt = s[0][0];
 #pragma unroll
-            for (int r = 2; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[0][r], s[0][r + 1]));
+            for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[0][r]), s[0][r + 1]);
+            mt = fmaxf(fmaxf(mt, s[0][15]), s[1][0]);
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[1][r], s[1][r + 1]));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
+            mt = fmaxf(mt, s[1][15]);
+            mt = half_max(mt);
             // first tile: set the reference; later tiles: move it only on a large jump
             const bool move = kt == 0 ? true : mt > kPfRescale;
             if (__ballot(move)) {
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     }
 
     if (!qvalid) return;
-    const float l = l_half + __shfl_xor(l_half, 32);
+    const float l = half_sum(l_half);
     const float inv = 1.f / l;
     const int t = qrow / kk, jj = qrow - t * kk;
     float* dst = out + (((size_t)w.b * T + t) * S + slot0 + jj) * D;

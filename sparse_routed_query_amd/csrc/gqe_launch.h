@@ -50,6 +50,9 @@ struct PrefillArgs {
     bool bf16;
 };
 int launch_prefill(const PrefillArgs& a, hipStream_t st);
+// Weighted slot(s) of n_tok output rows [n_tok, S, D] from their hard slots.
+int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, int k, int D, int S, int route_mode,
+                    hipStream_t st);
 
 struct DecodeArgs {
     const void* q_routed;

@@ -9,12 +9,12 @@
 // heads are skipped).
 //
 // Kernels:
-//   router_kernel   one wave per block of 32 tokens.  Scores come from bf16
-//                   MFMA (16x16x32, exact bf16 products) with every 32-product
-//                   partial sum added into a double accumulator, so the score
-//                   error stays far below the 1e-6 tie margin; fp32 inputs use
-//                   double FMAs.  The wave then selects, renormalises and
-//                   counts kept experts of its block in LDS.
+//   router_kernel   one workgroup per block of 32 tokens.  Scores come from
+//                   bf16 MFMA (16x16x32, exact bf16 products) with every
+//                   32-product partial sum added into a double accumulator, so
+//                   the score error stays far below the 1e-6 tie margin; fp32
+//                   inputs use double FMAs.  The workgroup then selects,
+//                   renormalises and counts kept experts of its block in LDS.
 //   scan_kernel     one workgroup per expert: exclusive scan of the per-block
 //                   counts -> per-block base offsets, and the expert totals.
 //   scatter_kernel  one wave per two blocks: wave ballots give each token its
@@ -26,37 +26,40 @@
 namespace gqe {
 
 constexpr int kRouteTok = 32;        // tokens per wave = compaction block
-constexpr int kRouteWaves = 4;       // waves per workgroup
 constexpr int kMaxExperts = 64;
 
-template <bool BF16>
+// One workgroup per block of 32 tokens.  bf16: the four waves take every
+// fourth 32-wide step of d_model, issue the loads of 8 steps before their
+// MFMAs (the kernel is bound by load latency, not math), and add each
+// 32-product partial into a double accumulator; the four partial sums are
+// then added in a fixed order.  fp32: one double FMA chain per score.
+template <bool BF16, int NB>
 __global__ __launch_bounds__(256) void router_kernel(
     const void* __restrict__ xv, const void* __restrict__ wv, const float* __restrict__ bias,
     int32_t* __restrict__ sel, float* __restrict__ ptilde, double* __restrict__ logits_out,
     int32_t* __restrict__ blk_counts, int BT, int d_model, int G, int E, int k)
 {
     const int N = G * E;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int blk = blockIdx.x * kRouteWaves + wave;
+    constexpr int nb = NB;         // 16-expert column blocks (<= 4)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int blk = blockIdx.x;
     const int tok0 = blk * kRouteTok;
-    // dynamic LDS: per wave, logits [32][N+1] doubles then counters [N] ints
+    // dynamic LDS: logits [32][N+1] doubles, then per-wave partials [4][2][nb][4][64] doubles, then counters [N]
     extern __shared__ double s_dyn[];
-    double* s_lg = s_dyn + (size_t)wave * kRouteTok * (N + 1);
-    int* s_cnt = (int*)(s_dyn + (size_t)kRouteWaves * kRouteTok * (N + 1)) + wave * N;
+    double* s_lg = s_dyn;
+    double* s_part = s_dyn + (size_t)kRouteTok * (N + 1);
+    int* s_cnt = (int*)(s_part + (BF16 ? (size_t)4 * 2 * nb * 4 * 64 : 0));
 #define LOGIT(tt, n) s_lg[(tt) * (N + 1) + (n)]
-    if (tok0 >= BT) return;  // whole wave leaves together; no block-wide barrier below
-
-    for (int n = lane; n < N; n += 64) s_cnt[n] = 0;
+    for (int n = tid; n < N; n += 256) s_cnt[n] = 0;
 
     if constexpr (BF16) {
         const uint16_t* x = (const uint16_t*)xv;
         const uint16_t* w = (const uint16_t*)wv;
-        const int nb = (N + 15) / 16;  // 16-expert column blocks (<= 4)
-        double acc[2][4][4];
+        double acc[2][NB][4];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < NB; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[a][c][r] = 0.0;
         const int kq = 8 * (lane >> 4);  // k offset of this lane inside a 32-wide step
@@ -65,41 +68,58 @@ __global__ __launch_bounds__(256) void router_kernel(
         const uint16_t* xa0 = x + (size_t)(v0 ? t_a0 : 0) * d_model + kq;
         const uint16_t* xa1 = x + (size_t)(v1 ? t_a1 : 0) * d_model + kq;
         const bf16x8 zero8 = {};
-        for (int k0 = 0; k0 < d_model; k0 += 32) {
-            bf16x8 a0 = v0 ? ld_bf16x8(xa0 + k0) : zero8;
-            bf16x8 a1 = v1 ? ld_bf16x8(xa1 + k0) : zero8;
+        const int nsteps = d_model / 32;
+        constexpr int U = NB <= 2 ? 8 : 4;
+        for (int s0 = wave; s0 < nsteps; s0 += 4 * U) {
+            bf16x8 a0[U], a1[U], bw[U][NB];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (c < nb) {
+            for (int u = 0; u < U; ++u) {
+                const int st = s0 + 4 * u;
+                const int k0 = st * 32;
+                const bool live = st < nsteps;
+                a0[u] = (v0 && live) ? ld_bf16x8(xa0 + k0) : zero8;
+                a1[u] = (v1 && live) ? ld_bf16x8(xa1 + k0) : zero8;
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
                     const int n = c * 16 + (lane & 15);
-                    bf16x8 b = n < N ? ld_bf16x8(w + (size_t)n * d_model + k0 + kq) : zero8;
+                    bw[u][c] = (n < N && live) ? ld_bf16x8(w + (size_t)n * d_model + k0 + kq) : zero8;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
                     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    f32x4 p0 = mfma16(a0, b, z);
-                    f32x4 p1 = mfma16(a1, b, z);
+                    const f32x4 p0 = mfma16(a0[u], bw[u][c], z);
+                    const f32x4 p1 = mfma16(a1[u], bw[u][c], z);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         acc[0][c][r] += (double)p0[r];
                         acc[1][c][r] += (double)p1[r];
                     }
                 }
-            }
         }
-        // accumulator element r of lane l: token row 4*(l/16) + r, expert column l%16
+        // partials to LDS, then a fixed-order sum over the four waves
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int n = c * 16 + (lane & 15);
-                if (c < nb && n < N) {
-                    const double b = bias ? (double)bias[n] : 0.0;
+            for (int c = 0; c < NB; ++c)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) LOGIT(a * 16 + 4 * (lane >> 4) + r, n) = acc[a][c][r] + b;
-                }
-            }
+                for (int r = 0; r < 4; ++r) s_part[(((wave * 2 + a) * nb + c) * 4 + r) * 64 + lane] = acc[a][c][r];
+        __syncthreads();
+        // accumulator element r of lane l: token row 4*(l/16) + r, expert column l%16
+        for (int i = tid; i < 2 * nb * 4 * 64; i += 256) {
+            const int l = i & 63, r = (i >> 6) & 3, c = (i >> 8) % nb, a = (i >> 8) / nb;
+            const int n = c * 16 + (l & 15);
+            if (n >= N) continue;
+            double v = 0.0;
+            for (int wv2 = 0; wv2 < 4; ++wv2) v += s_part[(((wv2 * 2 + a) * nb + c) * 4 + r) * 64 + l];
+            LOGIT(a * 16 + 4 * (l >> 4) + r, n) = v + (bias ? (double)bias[n] : 0.0);
+        }
     } else {
         const float* x = (const float*)xv;
         const float* w = (const float*)wv;
-        for (int p = lane; p < kRouteTok * N; p += 64) {
+        for (int p = tid; p < kRouteTok * N; p += 256) {
             const int tt = p / N, n = p % N;
             const int t = tok0 + tt;
             double s = 0.0;
@@ -112,12 +132,10 @@ __global__ __launch_bounds__(256) void router_kernel(
             LOGIT(tt, n) = s;
         }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
+    __syncthreads();
 
-    // Selection, renormalisation and counting: one (token, group) per lane.
-    for (int p = lane; p < kRouteTok * G; p += 64) {
+    // Selection, renormalisation and counting: one (token, group) per thread.
+    for (int p = tid; p < kRouteTok * G; p += 256) {
         const int tt = p / G, g = p % G;
         const int t = tok0 + tt;
         if (t >= BT) continue;
@@ -147,15 +165,13 @@ __global__ __launch_bounds__(256) void router_kernel(
         }
     }
     if (logits_out) {
-        for (int p = lane; p < kRouteTok * N; p += 64) {
+        for (int p = tid; p < kRouteTok * N; p += 256) {
             const int tt = p / N, n = p % N;
             if (tok0 + tt < BT) logits_out[(size_t)(tok0 + tt) * N + n] = LOGIT(tt, n);
         }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    for (int n = lane; n < N; n += 64) blk_counts[(size_t)blk * N + n] = s_cnt[n];
+    __syncthreads();
+    for (int n = tid; n < N; n += 256) blk_counts[(size_t)blk * N + n] = s_cnt[n];
 #undef LOGIT
 }
 
@@ -249,14 +265,24 @@ int launch_route(const RouteArgs& a, hipStream_t st)
         zero_i32_kernel<<<1, 256, 0, st>>>(a.offsets, N + 1);
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
-    const int grid = (nblk + kRouteWaves - 1) / kRouteWaves;
-    const size_t lds = (size_t)kRouteWaves * kRouteTok * (N + 1) * sizeof(double) + (size_t)kRouteWaves * N * sizeof(int);
-    if (a.bf16)
-        router_kernel<true><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
-                                                  blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
-    else
-        router_kernel<false><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
-                                                   blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
+    const int grid = nblk;
+    const int nb = (N + 15) / 16;
+    const size_t lds = (size_t)kRouteTok * (N + 1) * sizeof(double) +
+                       (a.bf16 ? (size_t)4 * 2 * nb * 4 * 64 * sizeof(double) : 0) + (size_t)N * sizeof(int);
+    if (a.bf16) {
+#define GQE_ROUTER(NBV) router_kernel<true, NBV><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, \
+        a.p_tilde, a.logits, blk_counts, a.BT, a.d_model, a.G, a.E, a.k)
+        switch (nb) {
+        case 1: GQE_ROUTER(1); break;
+        case 2: GQE_ROUTER(2); break;
+        case 3: GQE_ROUTER(3); break;
+        default: GQE_ROUTER(4); break;
+        }
+#undef GQE_ROUTER
+    } else {
+        router_kernel<false, 1><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
+                                                      blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
+    }
     scan_kernel<<<N, 256, 0, st>>>(blk_counts, blk_base, a.counts, nblk, N);
     const int sgrid = (nblk + 7) / 8;
     scatter_kernel<<<sgrid, 256, 0, st>>>(a.sel, blk_base, a.counts, a.offsets, a.rows, a.BT, a.G, a.E, a.k, nblk);
