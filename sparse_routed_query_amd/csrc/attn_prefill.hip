@@ -38,12 +38,12 @@ struct PfWork {
 };
 
 // Key tiles needed by query tile i of a head with kk rows per position.
-__device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal)
+__device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal, int bn = kPfBN)
 {
-    if (!causal) return (T + kPfBN - 1) / kPfBN;
+    if (!causal) return (T + bn - 1) / bn;
     const int last_row = min(R - 1, (i + 1) * kPfBM - 1);
     const int t_hi = last_row / kk;
-    return t_hi / kPfBN + 1;
+    return t_hi / bn + 1;
 }
 
 // Map a workgroup id to (b, head, tile), ordering tiles by decreasing work.
@@ -105,6 +105,7 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
 // tile's scores exceed it by more than 2^8, so probabilities stay <= 256 and
 // most tiles need neither a subtraction nor a rescale of the accumulators.
 constexpr float kPfRescale = 8.0f;
+constexpr float kPfRescaleSum = 256.0f;   // 2^kPfRescale
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(
@@ -137,8 +138,11 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     const int nkv_w = causal ? (wrow_hi / kk) / kPfBN + 1 : nkv;
     const int t_lo_w = (r0 + wave * 32) / kk;
 
+    // V rows get 32 elements of padding: the transposing reads are then free of
+    // bank conflicts (16 for K rows, read with 16-byte loads).
+    constexpr int PV = D + 32;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPfBN * P];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPfBN * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPfBN * PV];
 
     bf16x8 qf[D / 16];
 #pragma unroll
@@ -172,13 +176,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + i * 256, s = c / (D / 8), d0 = (c % (D / 8)) * 8;
             *(u32x4*)&sK[buf][s * P + d0] = rk[i];
-            *(u32x4*)&sV[buf][s * P + d0] = rv[i];
+            *(u32x4*)&sV[buf][s * PV + d0] = rv[i];
         }
     };
     // per-lane parts of the LDS addresses
     const int k_off = lr * P + 8 * lh;                                       // K row lr, d half lh
     const int s16 = lane & 15;
-    const int v_off = (4 * lh + (s16 >> 2)) * P + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    const int v_off = (4 * lh + (s16 >> 2)) * PV + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
 
     f32x16 o[NDB];
 #pragma unroll
@@ -218,50 +222,67 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
                     for (int r = 0; r < 16; ++r)
                         s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
             }
-            // chained form so the compiler emits v_max3_f32
-            float mt = s[0][0];
-#pragma unroll
-            for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[0][r]), s[0][r + 1]);
-            mt = fmaxf(fmaxf(mt, s[0][15]), s[1][0]);
-#pragma unroll
-            for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
-            mt = fmaxf(mt, s[1][15]);
-            mt = half_max(mt);
-            // first tile: set the reference; later tiles: move it only on a large jump
-            const bool move = kt == 0 ? true : mt > kPfRescale;
-            if (__ballot(move)) {
-                const float shift = move ? mt : 0.f;
-                const float alpha = kt == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+            // P = exp2(S - m_ref), packed to bf16; the row sum uses the rounded values.
+            // If no lane's partial row sum exceeds 2^8, no probability does, so the
+            // reference stays and the row max is never computed.  The first tile,
+            // and any tile whose sum trips that check, take the exact path: row
+            // max, move the reference if it jumped by more than 2^8, recompute.
+            uint32_t pw[16];
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+            auto probs = [&]() {
+                float ls = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
+                    for (int r = 0; r < 16; r += 2)
+                        pw[kb * 8 + r / 2] = pk_bf16(__builtin_amdgcn_exp2f(s[kb][r]), __builtin_amdgcn_exp2f(s[kb][r + 1]));
 #pragma unroll
-                for (int j = 0; j < NDB; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-                l_half *= alpha;
-                m_ref += shift;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                for (int i = 0; i < 16; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, ls, false);
+                return ls;
+            };
+            bool exact = kt == 0;
+            if (!exact) {
+                const float ls = probs();
+                exact = __ballot(!(ls <= kPfRescaleSum)) != 0;
+                if (!exact) l_half += ls;
             }
-            // P = exp2(S - m_ref), packed to bf16; the row sum uses the rounded values
-            uint32_t pw[16];
+            if (exact) {
+                // chained form so the compiler emits v_max3_f32
+                float mt = s[0][0];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[0][r]), s[0][r + 1]);
+                mt = fmaxf(fmaxf(mt, s[0][15]), s[1][0]);
 #pragma unroll
-                for (int r = 0; r < 16; r += 2)
-                    pw[kb * 8 + r / 2] = pk_bf16(__builtin_amdgcn_exp2f(s[kb][r]), __builtin_amdgcn_exp2f(s[kb][r + 1]));
-            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+                for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
+                mt = fmaxf(mt, s[1][15]);
+                mt = half_max(mt);
+                // first tile: set the reference; later tiles: move it only on a large jump
+                const bool move = kt == 0 ? true : mt > kPfRescale;
+                if (__ballot(move)) {
+                    const float shift = move ? mt : 0.f;
+                    const float alpha = kt == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) l_half = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, l_half, false);
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
+#pragma unroll
+                    for (int j = 0; j < NDB; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+                    l_half *= alpha;
+                    m_ref += shift;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                }
+                l_half += probs();
+            }
             // O^T += V^T P^T over the four 16-key steps
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const u32x4 pv = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
 #pragma unroll
-                for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * P + 32 * j, 8 * P), pb, o[j]);
+                for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * PV + 32 * j, 8 * PV), pb, o[j]);
             }
         }
         if (kt + 1 < nkv) store(buf ^ 1);
@@ -282,6 +303,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
             *(f32x4*)(dst + d) = v;
         }
 }
+
 
 // fp32 path: one thread per query row, online softmax in fp32.
 template <int D>
