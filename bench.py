@@ -17,7 +17,8 @@ divided by the whole step's time).  The same JSON line carries:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   long_context  T=32768 GQE vs all-active GQA on the same inputs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-context]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-context] [--no-decode]
+       python bench.py --only {prefill,decode,copy} --steps K   (profiler runs)
 """
 from __future__ import annotations
 
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--no-context", action="store_true", help="skip the long-context GQE vs dense leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
 
 
@@ -108,8 +111,8 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key: str, src_hash: str):
-    """HBM bytes per launch from committed PMC counters, if taken on this exact source."""
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from committed PMC counters, if taken on the current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -118,7 +121,7 @@ def traffic_for(kernel_key: str, src_hash: str):
     except ValueError:
         return None
     e = data.get(kernel_key)
-    if not e or e.get("source_hash") != src_hash:
+    if not e or e.get("source_hash") != source_hash(*e.get("source_files", [])):
         return None
     return e.get("bytes_per_launch")
 
@@ -195,7 +198,7 @@ def decode_leg(torch, dev, steps):
             "attn_us": t_attn * 1e3, "step_us": (t_route + t_qp + t_attn) * 1e3,
             "route_us": t_route * 1e3, "qproj_us": t_qp * 1e3,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode", source_hash("attn_decode.hip")),
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),
                          "algorithmic_bytes": nbytes, "kernel": "gqe_attn_decode (split + combine)"}}
 
 
@@ -220,6 +223,40 @@ def long_context_leg(torch, dev, steps):
     return res
 
 
+def only(args, torch):
+    """One call repeated, for rocprofv3 counter runs: the prefill attention call
+    on the main shape, the decode attention call, or a plain 256 MiB device copy
+    (the calibration kernel for FETCH_SIZE / WRITE_SIZE)."""
+    import workloads as W
+    import sparse_routed_query_amd.gqe as G
+    dev = "cuda:0"
+    if args.only == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+    elif args.only == "prefill":
+        w = W.WORKLOADS["main_250m"]
+        p = Prefill(w, W.make_inputs(w), dev)
+        p.route()
+        p.qproj()
+        for _ in range(args.steps):
+            p.attn()
+    else:
+        w = W.WORKLOADS["decode_b64"]
+        inp = W.make_inputs(w)
+        d = G.desc_from(w)
+        x = inp["x"].reshape(w.B, w.d_model).to(dev)
+        r = G.route(d, x, inp["w_router"].to(dev))
+        q = G.qproj(d, x, inp["w_q"].to(dev), r)
+        kc, vc, lens = inp["k_cache"].to(dev), inp["v_cache"].to(dev), inp["lens"].to(dev)
+        out = torch.empty((w.B, d.S, w.d_head), dtype=torch.float32, device=dev)
+        ws = torch.empty(G.gqe_decode_workspace_bytes(d, w.L_max), dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            G.gqe_attn_decode(d, q["q_routed"], q["q_shared"], kc, vc, lens, r["p_tilde"], out, ws)
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -230,6 +267,9 @@ def main():
     import workloads as W
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.only:
+        only(args, torch)
+        return
     w = W.WORKLOADS["main_250m"]
     inp = W.make_inputs(w)
     p = Prefill(w, inp, dev)
@@ -263,7 +303,7 @@ def main():
         "wall_s_timed": wall,
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_for("prefill", source_hash("attn_prefill.hip")),
+                     "traffic": traffic_for("prefill"),
                      "kernel": "gqe_attn_prefill (attention + slot assembly)",
                      "algorithmic_flops_per_launch": fl},
     }
