@@ -61,7 +61,7 @@ typedef struct {
     int32_t B;          /* sequences */
     int32_t T;          /* prefill: tokens per sequence; decode: must be 1 */
     int32_t d_model;    /* width of x; multiple of 64 for bf16, of 4 for f32 */
-    int32_t H_q;        /* query heads = routed experts N; at most 256 */
+    int32_t H_q;        /* query heads = routed experts N; at most 64 */
     int32_t H_kv;       /* KV heads = groups G; H_q % H_kv == 0 */
     int32_t k;          /* experts kept per group and token, 1 <= k <= E, k <= 8 */
     int32_t d_head;     /* 32, 64 or 128 */
