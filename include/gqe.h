@@ -150,6 +150,28 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
 int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared,
                      const void* k, const void* v, const float* p_tilde, float* out, void* stream);
 
+/*
+ * gqe_attn_prefill_heads -- the attention part of gqe_attn_prefill alone
+ * (same definition, GQE study note §1-1 and §3-2 (3), (5)): writes the hard
+ * slots out[b,t,g*k+j] and the shared slot out[b,t,S-1]; the weighted slot(s)
+ * of `out` are left as they were.  Together with gqe_assemble it computes
+ * exactly what gqe_attn_prefill computes (bitwise).
+ * In/Out: as gqe_attn_prefill, without p_tilde.
+ */
+int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                           const void* k, const void* v, float* out, void* stream);
+
+/*
+ * gqe_assemble -- the weighted slot(s) of B*T output rows from their hard
+ * slots (GQE study note §3-2 (4)):
+ *   mode 0: out[t, kG]   = sum_g sum_j p~[t,g,j] out[t, g*k+j]
+ *   mode 1: out[t, kG+g] = sum_j p~[t,g,j] out[t, g*k+j]
+ * summed in fp32 in that fixed order (g, then j).  Reads only the hard slots.
+ * In:  p_tilde [B*T, G, k] fp32.  In/Out: out [B*T, S, d_head] fp32.
+ * Works for decode outputs too (T = 1).
+ */
+int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
+
 /* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
 

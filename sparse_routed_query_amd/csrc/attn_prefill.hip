@@ -385,10 +385,10 @@ int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, in
     const long long n = n_tok * D;
     if (n == 0) return 0;
     assemble_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p_tilde, out, n_tok, G, k, D, S, route_mode);
-    return 0;
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_prefill(const PrefillArgs& a, hipStream_t st)
+int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
 {
     const long long BT = (long long)a.B * a.T;
     if (BT == 0) return 0;
@@ -421,9 +421,14 @@ int launch_prefill(const PrefillArgs& a, hipStream_t st)
         default: return -2;
         }
     }
-    if (hipGetLastError() != hipSuccess) return -1;
-    launch_assemble(a.p_tilde, a.out, BT, a.G, a.k, a.d_head, a.S, a.route_mode, st);
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_prefill(const PrefillArgs& a, hipStream_t st)
+{
+    const int rc = launch_prefill_heads(a, st);
+    if (rc != 0) return rc;
+    return launch_assemble(a.p_tilde, a.out, (long long)a.B * a.T, a.G, a.k, a.d_head, a.S, a.route_mode, st);
 }
 
 }  // namespace gqe

@@ -66,6 +66,24 @@ int launch_status(int rc)
     return rc == 0 ? GQE_OK : GQE_ERR_LAUNCH;
 }
 
+int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
+                   const float* p_tilde, float* out, void* stream, bool assemble)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    if (assemble) GQE_TRY(need(p_tilde));
+    GQE_TRY(need(out));
+    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out,
+                       s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
+    return launch_status(assemble ? gqe::launch_prefill(a, (hipStream_t)stream)
+                                  : gqe::launch_prefill_heads(a, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,18 +162,23 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
 int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
                      const float* p_tilde, float* out, void* stream)
 {
+    return prefill_common(desc, q_routed, q_shared, k, v, p_tilde, out, stream, true);
+}
+
+int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                           const void* v, float* out, void* stream)
+{
+    return prefill_common(desc, q_routed, q_shared, k, v, nullptr, out, stream, false);
+}
+
+int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream)
+{
     Shape s;
     GQE_TRY(check_desc(desc, s));
     if (s.BT == 0) return GQE_OK;
-    GQE_TRY(need(q_routed));
-    if (s.ns) GQE_TRY(need(q_shared));
-    GQE_TRY(need(k));
-    GQE_TRY(need(v));
     GQE_TRY(need(p_tilde));
     GQE_TRY(need(out));
-    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out,
-                       s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
-    return launch_status(gqe::launch_prefill(a, (hipStream_t)stream));
+    return launch_status(gqe::launch_assemble(p_tilde, out, s.BT, s.G, s.k, s.D, s.S, s.mode, (hipStream_t)stream));
 }
 
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max)

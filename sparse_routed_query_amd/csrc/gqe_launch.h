@@ -49,6 +49,9 @@ struct PrefillArgs {
     int B, T, G, k, d_head, n_shared, causal, route_mode, S;
     bool bf16;
 };
+// Attention only: hard and shared slots of `out`; the weighted slots are not written.
+int launch_prefill_heads(const PrefillArgs& a, hipStream_t st);
+// Attention, then the weighted slots.
 int launch_prefill(const PrefillArgs& a, hipStream_t st);
 // Weighted slot(s) of n_tok output rows [n_tok, S, D] from their hard slots.
 int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, int k, int D, int S, int route_mode,

@@ -26,7 +26,8 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 
 # Every symbol the C header declares (checked by the host tests).
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
-           "gqe_attn_prefill", "gqe_decode_workspace_bytes", "gqe_attn_decode")
+           "gqe_attn_prefill", "gqe_attn_prefill_heads", "gqe_assemble", "gqe_decode_workspace_bytes",
+           "gqe_attn_decode")
 
 
 class GqeError(RuntimeError):
@@ -94,6 +95,10 @@ def load():
         lib.gqe_qproj.restype = I
         lib.gqe_attn_prefill.argtypes = [D, P, P, P, P, P, P, P]
         lib.gqe_attn_prefill.restype = I
+        lib.gqe_attn_prefill_heads.argtypes = [D, P, P, P, P, P, P]
+        lib.gqe_attn_prefill_heads.restype = I
+        lib.gqe_assemble.argtypes = [D, P, P, P]
+        lib.gqe_assemble.restype = I
         lib.gqe_decode_workspace_bytes.argtypes = [D, ctypes.c_int32]
         lib.gqe_decode_workspace_bytes.restype = Z
         lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
@@ -166,6 +171,20 @@ def gqe_attn_prefill(desc, q_routed, q_shared, k, v, p_tilde, out, stream=None):
                                  _ptr(k, dt, "k"), _ptr(v, dt, "v"), _ptr(p_tilde, torch.float32, "p_tilde"),
                                  _ptr(out, torch.float32, "out"), _stream(stream))
     _check("gqe_attn_prefill", rc)
+
+
+def gqe_attn_prefill_heads(desc, q_routed, q_shared, k, v, out, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_attn_prefill_heads(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"),
+                                       _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"), _ptr(v, dt, "v"),
+                                       _ptr(out, torch.float32, "out"), _stream(stream))
+    _check("gqe_attn_prefill_heads", rc)
+
+
+def gqe_assemble(desc, p_tilde, out, stream=None):
+    rc = load().gqe_assemble(ctypes.byref(desc), _ptr(p_tilde, torch.float32, "p_tilde"),
+                             _ptr(out, torch.float32, "out"), _stream(stream))
+    _check("gqe_assemble", rc)
 
 
 def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace, stream=None):

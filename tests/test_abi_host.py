@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -100,6 +100,13 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert lib.gqe_attn_prefill(by(d), A16, A16, A16, None, A16, A16, None) == INVALID
     assert lib.gqe_attn_prefill(by(main(d_head=48)), A16, A16, A16, A16, A16, A16, None) == UNSUPPORTED
     assert lib.gqe_attn_prefill(by(d), A16, A16, A16, A16, A16, MIS, None) == ALIGN
+    assert lib.gqe_attn_prefill(by(d), A16, A16, A16, A16, None, A16, None) == INVALID     # p_tilde needed
+    assert lib.gqe_attn_prefill_heads(by(d), A16, None, A16, A16, A16, None) == INVALID    # shared head needs q_shared
+    assert lib.gqe_attn_prefill_heads(by(main(d_head=48)), A16, A16, A16, A16, A16, None) == UNSUPPORTED
+    assert lib.gqe_attn_prefill_heads(by(d), A16, A16, A16, A16, MIS, None) == ALIGN
+    assert lib.gqe_assemble(by(d), None, A16, None) == INVALID
+    assert lib.gqe_assemble(by(d), A16, MIS, None) == ALIGN
+    assert lib.gqe_assemble(by(main(H_q=15)), A16, A16, None) == INVALID
     dd = main(B=64, T=1)
     ws = G.gqe_decode_workspace_bytes(dd, 8192)
     dec = lambda desc, L=8192, lens=A16, w=A16, wb=ws: lib.gqe_attn_decode(  # noqa: E731

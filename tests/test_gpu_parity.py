@@ -114,6 +114,28 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(dtype="f32", d_head=32)],
+                         ids=lambda w: f"{w.name}-{w.dtype}")
+def test_heads_then_assemble_equals_attn_prefill(w):
+    """gqe_attn_prefill_heads + gqe_assemble give exactly gqe_attn_prefill's output."""
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    di = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    x = di["x"].reshape(-1, w.d_model)
+    r = G.route(d, x, di["w_router"], di["b_router"])
+    q = G.qproj(d, x, di["w_q"], r)
+    ref = G.attn_prefill(d, q, di["k"], di["v"], r["p_tilde"])
+    out = torch.full_like(ref, float("nan"))
+    G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out)
+    kG = w.k * w.G
+    n_w = w.G if w.route_mode else 1
+    torch.cuda.synchronize()
+    assert torch.isnan(out[:, :, kG:kG + n_w]).all(), "heads call wrote the weighted slots"
+    G.gqe_assemble(d, r["p_tilde"], out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 # ---------------------------------------------------------------- decode edges
 
 def decode_case(**kw):
