@@ -11,17 +11,16 @@
 // the token's kept experts of group g.  The shared head is expert index N
 // with the identity row list.
 //
-// Workgroups walk (row tile, expert) with the row tile as the major index, so
-// workgroups resident at the same time read overlapping token ranges of x.
-// Tiles past an expert's row count exit at once: the grid is sized for the
-// largest possible bucket, and the counts never leave the device.
+// The bucket sizes stay on the device: every workgroup derives its (expert,
+// tile) from the counts (qp_plan below), so the grid is sized by an upper
+// bound and the few workgroups past the last tile exit at once.  The order
+// keeps the k*G+1 reads of each x row inside one XCD's L2.
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
 namespace gqe {
 
 constexpr int kQpBM = 128;   // rows per tile (4 waves x 32)
-constexpr int kQpBK = 64;    // d_model slice per LDS stage
 constexpr int kQpPad = 8;    // bf16 elements of row padding in LDS (16 bytes)
 
 // Destination element offset of row r of expert n's bucket.
@@ -37,7 +36,98 @@ __device__ __forceinline__ size_t qp_dst(int n, int N, int tok, const int32_t* _
     return ((((size_t)b * G + g) * T + t) * k + j) * d_head;
 }
 
-template <int D>
+// Work order.  Expert n has c_n = ceil(M_n / kQpBM) row tiles (M_N = B*T for
+// the shared head).  Tiles are ordered in rounds r = 0..R-1, R = max c_n:
+// expert n contributes ceil((r+1) c_n / R) - ceil(r c_n / R) tiles to round
+// r, so a round covers about the same token range in every expert (buckets
+// are sorted by token).  Logical item L then goes to the workgroup with
+// blockIdx % 8 == L / chunk: workgroups are dealt round-robin to the eight
+// XCDs, so each XCD walks a contiguous range of rounds and its L2 serves the
+// k*G+1 reads of every x row.  Computed by one wave from the device-side
+// counts; returns false for workgroups past the last item.
+__device__ __forceinline__ int qp_before(int c, int r, int R)
+{
+    // ceil(r * c / R), exact: the quotient is an integer or at least 1/R away from one
+    return (int)ceil((double)r * (double)c / (double)R);
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ int wave_scan_i(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__device__ bool qp_plan(int bid, int nbid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, int lane,
+                        int& n_out, int& tile_out)
+{
+    auto ntiles = [&](int n) {
+        if (n >= n_exp) return 0;
+        const int M = n < N ? counts[n] : BT;
+        return (M + kQpBM - 1) / kQpBM;
+    };
+    const int c0 = ntiles(lane), c1 = ntiles(lane + 64);
+    const int U = wave_sum_i(c0 + c1);
+    const int R = wave_max_i(max(c0, c1));
+    const int chunk = (U + 7) / 8;
+    const int L = (bid % 8) * chunk + bid / 8;
+    if (bid / 8 >= chunk || L >= U) return false;
+    (void)nbid;
+    auto S = [&](int r) { return wave_sum_i(qp_before(c0, r, R) + qp_before(c1, r, R)); };
+    // S(r) lies in [r U / R, r U / R + n_exp): start from the estimate and walk
+    int r = (int)(((long long)L * R) / U);
+    while (r > 0 && S(r) > L) --r;
+    while (r + 1 < R && S(r + 1) <= L) ++r;
+    int rem = L - S(r);
+    const int b0 = qp_before(c0, r, R), b1 = qp_before(c1, r, R);
+    const int k0 = qp_before(c0, r + 1, R) - b0, k1 = qp_before(c1, r + 1, R) - b1;
+    const int p0 = wave_scan_i(k0, lane);
+    const int t0 = __shfl(p0, 63);
+    int n, tile;
+    if (rem < t0) {
+        const unsigned long long m = __ballot(p0 > rem);
+        const int ln = __ffsll((long long)m) - 1;
+        n = ln;
+        tile = __shfl(b0, ln) + rem - (__shfl(p0, ln) - __shfl(k0, ln));
+    } else {
+        rem -= t0;
+        const int p1 = wave_scan_i(k1, lane);
+        const unsigned long long m = __ballot(p1 > rem);
+        const int ln = __ffsll((long long)m) - 1;
+        n = ln + 64;
+        tile = __shfl(b1, ln) + rem - (__shfl(p1, ln) - __shfl(k1, ln));
+    }
+    n_out = n;
+    tile_out = tile;
+    return true;
+}
+
+// One workgroup computes a 128-row tile of one expert: Q = X[rows] W_q[n]^T,
+// each of the four waves 32 rows.  Per stage of BK columns of d_model the x
+// rows and the weight slice are loaded with 16-byte coalesced loads (16 lanes
+// per 256-byte row segment) into registers while the previous stage is
+// multiplied out of LDS, then stored to LDS between two barriers.  Rows past
+// the bucket's end reload its last row and are not stored, so every load is
+// unconditional.
+template <int D, int BK>
 __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
@@ -45,91 +135,93 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     int k, int n_shared)
 {
     const int N = G * E, BT = B * T, n_exp = N + n_shared;
-    const int n = blockIdx.x % n_exp;
-    const int row0 = (blockIdx.x / n_exp) * kQpBM;
-    const int M = n < N ? counts[n] : BT;
-    if (row0 >= M) return;
-    const int base = n < N ? offsets[n] : 0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kQpBM][kQpBK + kQpPad];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[D][kQpBK + kQpPad];
-    __shared__ int s_tok[kQpBM];
-    __shared__ size_t s_dst[kQpBM];
-
-    if (tid < kQpBM) {
-        const int r = row0 + tid;
-        int tok = -1;
-        if (r < M) tok = n < N ? rows[base + r] : r;
-        s_tok[tid] = tok;
-        s_dst[tid] = tok >= 0 ? qp_dst(n, N, tok, sel, T, G, E, k, D) : 0;
+    __shared__ int s_item[2];
+    if (wave == 0) {
+        int pn = -1, pt = 0;
+        if (!qp_plan(blockIdx.x, gridDim.x, counts, N, n_exp, BT, lane, pn, pt)) pn = -1;
+        if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
     }
     __syncthreads();
+    const int n = s_item[0];
+    if (n < 0) return;
+    const int row0 = s_item[1] * kQpBM;
+    const int M = n < N ? counts[n] : BT;
+    const int base = n < N ? offsets[n] : 0;
+    constexpr int P = BK + kQpPad;
+    constexpr int NB = D / 32;
+    constexpr int CPR = BK / 8;                           // 16-byte chunks per row of a stage
+    constexpr int ACH = kQpBM * CPR / 256;                // A chunks per thread
+    constexpr int BCH = D * CPR / 256;                    // B chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kQpBM * P];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[D * P];
 
-    // global -> register staging: A is 128 rows x 64 cols = 1024 16-byte chunks (4 per thread),
-    // B is D rows x 64 cols = D*8 chunks.
-    constexpr int kAch = kQpBM * kQpBK / 8 / 256;
-    constexpr int kBch = D * kQpBK / 8 / 256 > 0 ? D * kQpBK / 8 / 256 : 1;
-    const uint16_t* wn = wq + (size_t)n * D * d_model;
-    u32x4 ra[kAch], rb[kBch];
+    // row pointers of this thread's A chunks (rows tid / CPR + i * 256 / CPR)
+    const int col = (tid % CPR) * 8;
+    const uint16_t* pa[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        const int rr = min(row0 + tid / CPR + i * (256 / CPR), M - 1);
+        const int tok = n < N ? rows[base + rr] : rr;
+        pa[i] = x + (size_t)tok * d_model + col;
+    }
+    const uint16_t* pb = wq + (size_t)n * D * d_model + (size_t)(tid / CPR) * d_model + col;
+    u32x4 ra[ACH], rb[BCH];
     auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < kAch; ++i) {
-            const int c = tid + i * 256, r = c >> 3, col = (c & 7) * 8;
-            const int tok = s_tok[r];
-            ra[i] = tok >= 0 ? ld_u32x4(x + (size_t)tok * d_model + k0 + col) : u32x4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < ACH; ++i) ra[i] = ld_u32x4(pa[i] + k0);
 #pragma unroll
-        for (int i = 0; i < kBch; ++i) {
-            const int c = tid + i * 256, r = c >> 3, col = (c & 7) * 8;
-            if (r < D) rb[i] = ld_u32x4(wn + (size_t)r * d_model + k0 + col);
-        }
+        for (int i = 0; i < BCH; ++i) rb[i] = ld_u32x4(pb + (size_t)i * (256 / CPR) * d_model + k0);
     };
+    const int w_off = (tid / CPR) * P + col;
     auto store = [&]() {
 #pragma unroll
-        for (int i = 0; i < kAch; ++i) {
-            const int c = tid + i * 256, r = c >> 3, col = (c & 7) * 8;
-            *(u32x4*)&sA[r][col] = ra[i];
-        }
+        for (int i = 0; i < ACH; ++i) *(u32x4*)&sA[w_off + i * (256 / CPR) * P] = ra[i];
 #pragma unroll
-        for (int i = 0; i < kBch; ++i) {
-            const int c = tid + i * 256, r = c >> 3, col = (c & 7) * 8;
-            if (r < D) *(u32x4*)&sB[r][col] = rb[i];
-        }
+        for (int i = 0; i < BCH; ++i) *(u32x4*)&sB[w_off + i * (256 / CPR) * P] = rb[i];
     };
 
-    constexpr int NB = D / 32;
     f32x16 acc[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
+    const int nst = d_model / BK;
+    const int a_off = (wave * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+    const int b_off = (lane & 31) * P + 8 * (lane >> 5);
     load(0);
-    for (int k0 = 0; k0 < d_model; k0 += kQpBK) {
+    for (int st = 0; st < nst; ++st) {
         __syncthreads();
         store();
         __syncthreads();
-        if (k0 + kQpBK < d_model) load(k0 + kQpBK);
+        if (st + 1 < nst) load((st + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < kQpBK; kk += 16) {
-            const bf16x8 a = ld_bf16x8(&sA[wave * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+        for (int kk = 0; kk < BK; kk += 16) {
+            const bf16x8 a = ld_bf16x8(&sA[a_off + kk]);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const bf16x8 b = ld_bf16x8(&sB[j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
-                acc[j] = mfma32(a, b, acc[j]);
-            }
+            for (int j = 0; j < NB; ++j) acc[j] = mfma32(a, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
         }
     }
 
+    // destinations of the tile's rows; rows past the bucket are not stored
+    __shared__ size_t s_dst[kQpBM];
+    const int m = wave * 32 + (lane & 31);
+    if (lane < 32) {
+        const int r = row0 + m;
+        size_t o = ~(size_t)0;
+        if (r < M) o = qp_dst(n, N, n < N ? rows[base + r] : r, sel, T, G, E, k, D);
+        s_dst[m] = o;
+    }
+    __syncthreads();
     uint16_t* dst = n < N ? q_routed : q_shared;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (s_tok[m] < 0) continue;
-        const size_t o = s_dst[m];
+    for (int e = 0; e < 16; ++e) {
+        const int mm = wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const size_t o = s_dst[mm];
+        if (o == ~(size_t)0) continue;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) dst[o + j * 32 + (lane & 31)] = __builtin_bit_cast(uint16_t, f2bf(acc[j][r]));
+        for (int j = 0; j < NB; ++j) dst[o + j * 32 + (lane & 31)] = __builtin_bit_cast(uint16_t, f2bf(acc[j][e]));
     }
 }
 
@@ -166,17 +258,23 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
     if (BT == 0) return 0;
     const int tiles = (BT + kQpBM - 1) / kQpBM;
     const int grid = tiles * n_exp;
+    // bf16: an upper bound on the number of tiles over all buckets, rounded to the 8 XCDs
+    const long long umax = (long long)BT * a.G * a.k / kQpBM + N + (long long)a.n_shared * tiles;
+    const int grid_bf16 = (int)(8 * ((umax + 7) / 8));
     if (a.bf16) {
         const uint16_t* x = (const uint16_t*)a.x;
         const uint16_t* w = (const uint16_t*)a.w_q;
         uint16_t* qr = (uint16_t*)a.q_routed;
         uint16_t* qs = (uint16_t*)a.q_shared;
-        switch (a.d_head) {
-        case 32: qproj_bf16_kernel<32><<<grid, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, a.B, a.T, a.d_model, a.G, a.E, a.k, a.n_shared); break;
-        case 64: qproj_bf16_kernel<64><<<grid, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, a.B, a.T, a.d_model, a.G, a.E, a.k, a.n_shared); break;
-        case 128: qproj_bf16_kernel<128><<<grid, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, a.B, a.T, a.d_model, a.G, a.E, a.k, a.n_shared); break;
+#define GQE_QP(D) qproj_bf16_kernel<D, 64><<<grid_bf16, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, \
+                                                                  a.B, a.T, a.d_model, a.G, a.E, a.k, a.n_shared)
+        switch (a.d_head) {   // d_model is a multiple of the 64-wide stage (checked by the API)
+        case 32: GQE_QP(32); break;
+        case 64: GQE_QP(64); break;
+        case 128: GQE_QP(128); break;
         default: return -2;
         }
+#undef GQE_QP
     } else {
         qproj_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, (const float*)a.w_q, a.sel, a.counts, a.offsets,
                                                a.rows, (float*)a.q_routed, (float*)a.q_shared, a.B, a.T, a.d_model,
