@@ -354,35 +354,51 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
     for (int d = 0; d < D; ++d) dst[d] = acc[d] / l;
 }
 
-// Weighted slot(s): sum over g then j of p~ times the hard slots, fp32.
+// Weighted slot(s): sum over g then j of p~ times the hard slots, fp32, in
+// that fixed order.  One thread per 4 consecutive d of a token (16-byte
+// accesses); the loads of up to 8 hard slots are issued before their FMAs.
 __global__ __launch_bounds__(256) void assemble_kernel(const float* __restrict__ p_tilde, float* __restrict__ out,
                                                        long long n_tok, int G, int k, int D, int S, int route_mode)
 {
+    const int DQ = D / 4;
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= n_tok * D) return;
-    const long long tok = gid / D;
-    const int d = (int)(gid % D);
-    float* row = out + (size_t)tok * S * D;
+    if (gid >= n_tok * DQ) return;
+    const long long tok = gid / DQ;
+    const int d = (int)(gid % DQ) * 4;
+    float* row = out + (size_t)tok * S * D + d;
     const float* pt = p_tilde + (size_t)tok * G * k;
     const int kG = k * G;
-    if (route_mode == 0) {
-        float acc = 0.f;
-        for (int g = 0; g < G; ++g)
-            for (int j = 0; j < k; ++j) acc = fmaf(pt[g * k + j], row[(size_t)(g * k + j) * D + d], acc);
-        row[(size_t)kG * D + d] = acc;
-    } else {
-        for (int g = 0; g < G; ++g) {
-            float acc = 0.f;
-            for (int j = 0; j < k; ++j) acc = fmaf(pt[g * k + j], row[(size_t)(g * k + j) * D + d], acc);
-            row[(size_t)(kG + g) * D + d] = acc;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h0 = 0; h0 < kG; h0 += 8) {
+        f32x4 v[8];
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int h = min(h0 + i, kG - 1);
+            v[i] = *(const f32x4*)(row + (size_t)h * D);
+            w[i] = pt[h];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int h = h0 + i;
+            if (h >= kG) break;
+            acc[0] = fmaf(w[i], v[i][0], acc[0]);
+            acc[1] = fmaf(w[i], v[i][1], acc[1]);
+            acc[2] = fmaf(w[i], v[i][2], acc[2]);
+            acc[3] = fmaf(w[i], v[i][3], acc[3]);
+            if (route_mode == 1 && (h + 1) % k == 0) {    // end of group h / k
+                *(f32x4*)(row + (size_t)(kG + h / k) * D) = acc;
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
+    if (route_mode == 0) *(f32x4*)(row + (size_t)kG * D) = acc;
 }
 
 int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, int k, int D, int S, int route_mode,
                     hipStream_t st)
 {
-    const long long n = n_tok * D;
+    const long long n = n_tok * (D / 4);
     if (n == 0) return 0;
     assemble_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p_tilde, out, n_tok, G, k, D, S, route_mode);
     return hipGetLastError() == hipSuccess ? 0 : -1;

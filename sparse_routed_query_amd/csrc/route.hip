@@ -243,6 +243,97 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
     }
 }
 
+// Compaction in one pass for small block tables (nblk * N <= kFusedMax):
+// every workgroup reads the whole table of per-block counts (L2-resident),
+// forms the expert totals, the offsets and the prefix of its own blocks, and
+// scatters its blocks' tokens like scatter_kernel.  Integer sums, so the
+// result is the same as the scan + scatter pair.
+constexpr int kFusedMax = 1 << 14;
+constexpr int kCmpWaves = 4;                       // waves per workgroup, two token blocks each
+
+__global__ __launch_bounds__(64 * kCmpWaves) void compact_kernel(const int32_t* __restrict__ sel,
+                                                                 const int32_t* __restrict__ blk_counts,
+                                                                 int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ rows, int BT, int G, int E,
+                                                                 int k, int nblk)
+{
+    constexpr int NT = 64 * kCmpWaves, BPW = 2 * kCmpWaves;
+    const int N = G * E, tid = threadIdx.x;
+    const int blk0 = blockIdx.x * BPW;
+    __shared__ int s_tot[NT], s_pre[NT];
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_base[BPW][kMaxExperts];
+    // 1. per-expert totals and the prefix before this workgroup's first block
+    const int R = NT / N;                        // thread rows, one expert per column
+    int tot = 0, pre = 0;
+    if (tid < R * N) {
+        const int n = tid % N;
+        // 16 independent loads in flight per step
+        for (int b0 = tid / N; b0 < nblk; b0 += 16 * R) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int b = b0 + i * R;
+                c[i] = b < nblk ? blk_counts[(size_t)b * N + n] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                tot += c[i];
+                pre += b0 + i * R < blk0 ? c[i] : 0;
+            }
+        }
+    }
+    s_tot[tid] = tot;
+    s_pre[tid] = pre;
+    __syncthreads();
+    if (tid < N) {
+        int t = 0, q = 0;
+        for (int r = 0; r < R; ++r) { t += s_tot[r * N + tid]; q += s_pre[r * N + tid]; }
+        s_tot[tid] = t;          // row 0 of the table is only read by its own thread
+        s_pre[tid] = q;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int n = 0; n < N; ++n) { s_off[n] = run; run += s_tot[n]; }
+        s_off[N] = run;
+    }
+    __syncthreads();
+    if (tid < N) {
+        int run = s_off[tid] + s_pre[tid];
+        for (int i = 0; i < BPW; ++i) {
+            s_base[i][tid] = run;
+            if (blk0 + i < nblk) run += blk_counts[(size_t)(blk0 + i) * N + tid];
+        }
+        if (blockIdx.x == 0) counts[tid] = s_tot[tid];
+    }
+    if (blockIdx.x == 0)
+        for (int n = tid; n <= N; n += NT) offsets[n] = s_off[n];
+    __syncthreads();
+    // 2. scatter: lanes 0-31 and 32-63 of a wave take one block each
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, hl = lane & 31;
+    const int bi = wave * 2 + half;
+    const int blk = blk0 + bi;
+    const int t = blk * kRouteTok + hl;
+    const bool valid = blk < nblk && t < BT;
+    const uint32_t below = (1u << hl) - 1u;
+    for (int g = 0; g < G; ++g) {
+        int kept[8];
+        for (int j = 0; j < k; ++j) kept[j] = valid ? sel[((size_t)t * G + g) * k + j] : -1;
+        for (int e = 0; e < E; ++e) {
+            bool has = false;
+            for (int j = 0; j < k; ++j) has |= kept[j] == e;
+            const uint64_t m = __ballot(has);
+            if (has) {
+                const uint32_t hm = (uint32_t)(m >> (32 * half));
+                rows[s_base[bi][g * E + e] + __popc(hm & below)] = t;
+            }
+        }
+    }
+}
+
 __global__ void zero_i32_kernel(int32_t* __restrict__ a, int n)
 {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) a[i] = 0;
@@ -283,9 +374,16 @@ int launch_route(const RouteArgs& a, hipStream_t st)
         router_kernel<false, 1><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
                                                       blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
     }
-    scan_kernel<<<N, 256, 0, st>>>(blk_counts, blk_base, a.counts, nblk, N);
-    const int sgrid = (nblk + 7) / 8;
-    scatter_kernel<<<sgrid, 256, 0, st>>>(a.sel, blk_base, a.counts, a.offsets, a.rows, a.BT, a.G, a.E, a.k, nblk);
+    if ((long long)nblk * N <= kFusedMax) {
+        const int cgrid = (nblk + 2 * kCmpWaves - 1) / (2 * kCmpWaves);
+        compact_kernel<<<cgrid, 64 * kCmpWaves, 0, st>>>(a.sel, blk_counts, a.counts, a.offsets, a.rows, a.BT, a.G,
+                                                         a.E, a.k, nblk);
+    } else {
+        scan_kernel<<<N, 256, 0, st>>>(blk_counts, blk_base, a.counts, nblk, N);
+        const int sgrid = (nblk + 7) / 8;
+        scatter_kernel<<<sgrid, 256, 0, st>>>(a.sel, blk_base, a.counts, a.offsets, a.rows, a.BT, a.G, a.E, a.k,
+                                              nblk);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

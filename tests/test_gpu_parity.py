@@ -114,6 +114,20 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("BT,H_q,k", [(33000, 64, 2), (4097, 16, 1), (31, 64, 8)], ids=lambda v: str(v))
+def test_route_compaction_both_paths(BT, H_q, k):
+    """Routing and compaction, bit-exact after tie substitution, for block tables on both sides of the
+    single-pass limit (33000 tokens x 64 experts takes the scan + scatter pair)."""
+    w = W.Workload("route_only", B=1, T=BT, d_model=64, H_q=H_q, H_kv=8, k=k, d_head=32, dtype="bf16", seed=31,
+                   act_std=1.0, w_std=0.05)   # score std 0.4, inside the range the tie margin is set for
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    x = inp["x"].reshape(-1, w.d_model).cuda()
+    r = G.route(d, x, inp["w_router"].cuda(), None, logits=True)
+    torch.cuda.synchronize()
+    check_route(w, inp, {key: (v.cpu() if isinstance(v, torch.Tensor) else v) for key, v in r.items()})
+
+
 @pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(dtype="f32", d_head=32)],
                          ids=lambda w: f"{w.name}-{w.dtype}")
 def test_heads_then_assemble_equals_attn_prefill(w):
