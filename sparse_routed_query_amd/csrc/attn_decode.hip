@@ -11,9 +11,9 @@
 //                 registers (k kept rows, plus the shared row on group 0), so
 //                 each cached byte is read once.  It writes (max, sum, o) of
 //                 the chunk in base-2 units.
-// merge kernel:   one wave per (row, sequence) merges that row's chunks in
-//                 chunk order (deterministic) into its hard or shared slot;
-//                 the slot-assembly kernel then forms the weighted slot(s).
+// merge kernel:   one workgroup per sequence merges each row's chunks in
+//                 chunk order (deterministic) into its hard or shared slot
+//                 and then forms the weighted slot(s) from those hard slots.
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
@@ -61,8 +61,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
     for (int i = 0; i < kDcPasses; ++i) {
         const int pos = c0 + i * PPP + pp;
         if (pos < L) {
-            kr[i] = ld_u32x4(K + (size_t)pos * D + dq);
-            vr[i] = ld_u32x4(V + (size_t)pos * D + dq);
+            // the cache is read once per step: non-temporal loads keep it from
+            // displacing other data in the caches
+            kr[i] = __builtin_nontemporal_load((const u32x4*)(K + (size_t)pos * D + dq));
+            vr[i] = __builtin_nontemporal_load((const u32x4*)(V + (size_t)pos * D + dq));
         } else {
             kr[i] = u32x4{0, 0, 0, 0};
             vr[i] = u32x4{0, 0, 0, 0};
@@ -130,41 +132,67 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
     }
 }
 
-// One wave per (query row, sequence): merges the chunk partials of that row.
-// The maximum and the sum of the chunk weights are wave reductions; the value
-// rows are summed in chunk order, so the result does not depend on timing.
+// One workgroup per sequence: each wave merges the chunk partials of some of
+// the sequence's query rows (in chunk order, so the result does not depend on
+// timing) into their hard or shared slot, keeping the hard slots in LDS; the
+// weighted slot(s) are then summed from LDS in fixed g-then-j order, exactly
+// as the slot-assembly kernel does from memory.
+constexpr int kDcMergeWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
-                                                          const int32_t* __restrict__ lens, float* __restrict__ out,
-                                                          int G, int k, int n_shared, int S, int nch, int CH)
+__global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ lens, const float* __restrict__ p_tilde,
+    float* __restrict__ out, int G, int k, int n_shared, int S, int route_mode, int nch, int CH)
 {
-    const int row = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    extern __shared__ float s_hard[];       // [k*G][D]
+    const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kG = G * k;
-    const int g = row < kG ? row / k : 0;
-    const int r = row < kG ? row % k : k;
     const int RG = k + n_shared;
     const int L = min(max(lens[b], 0), nch * CH);
     const int nc = (L + CH - 1) / CH;
-    const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
-    float M = -INFINITY;
-    for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
-    M = wave_max(M);
-    float Ls = 0.f;
-    for (int c = lane; c < nc; c += 64) Ls += pp[(size_t)c * (D + 2) + 1] * __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
-    Ls = wave_sum(Ls);
-    const float inv = 1.f / Ls;
-    float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
+    for (int row = wave; row < kG + n_shared; row += kDcMergeWaves) {
+        const int g = row < kG ? row / k : 0;
+        const int r = row < kG ? row % k : k;
+        const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
+        float M = -INFINITY;
+        for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
+        M = wave_max(M);
+        float Ls = 0.f;
+        for (int c = lane; c < nc; c += 64) Ls += pp[(size_t)c * (D + 2) + 1] * __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
+        Ls = wave_sum(Ls);
+        const float inv = 1.f / Ls;
+        float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
 #pragma unroll
-    for (int d0 = 0; d0 < D; d0 += 64) {
-        const int d = d0 + lane;
-        if (d < D) {
-            float O = 0.f;
+        for (int d0 = 0; d0 < D; d0 += 64) {
+            const int d = d0 + lane;
+            if (d < D) {
+                float O = 0.f;
 #pragma unroll 8
-            for (int c = 0; c < nc; ++c) {
-                const float* q = pp + (size_t)c * (D + 2);
-                O = fmaf(q[2 + d], __builtin_amdgcn_exp2f(q[0] - M), O);
+                for (int c = 0; c < nc; ++c) {
+                    const float* q = pp + (size_t)c * (D + 2);
+                    O = fmaf(q[2 + d], __builtin_amdgcn_exp2f(q[0] - M), O);
+                }
+                O *= inv;
+                dst[d] = O;
+                if (row < kG) s_hard[row * D + d] = O;
             }
-            dst[d] = O * inv;
+        }
+    }
+    __syncthreads();
+    // weighted slot(s)
+    const float* pt = p_tilde + (size_t)b * kG;
+    float* orow = out + (size_t)b * S * D;
+    for (int d = threadIdx.x; d < D; d += 64 * kDcMergeWaves) {
+        if (route_mode == 0) {
+            float acc = 0.f;
+            for (int h = 0; h < kG; ++h) acc = fmaf(pt[h], s_hard[h * D + d], acc);
+            orow[(size_t)kG * D + d] = acc;
+        } else {
+            for (int g = 0; g < G; ++g) {
+                float acc = 0.f;
+                for (int j = 0; j < k; ++j) acc = fmaf(pt[g * k + j], s_hard[(g * k + j) * D + d], acc);
+                orow[(size_t)(kG + g) * D + d] = acc;
+            }
         }
     }
 }
@@ -198,10 +226,9 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t st)
     decode_split_kernel<ET, D><<<grid, 256, 0, st>>>((const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache,
                                                      (const ET*)a.v_cache, a.lens, (float*)a.workspace, a.G, a.k,
                                                      a.n_shared, a.L_max, nch, qscale);
-    dim3 mgrid(a.G * a.k + a.n_shared, a.B);
-    decode_merge_kernel<D><<<mgrid, 64, 0, st>>>((const float*)a.workspace, a.lens, a.out, a.G, a.k, a.n_shared, a.S,
-                                                 nch, CH);
-    launch_assemble(a.p_tilde, a.out, a.B, a.G, a.k, D, a.S, a.route_mode, st);
+    const size_t lds = (size_t)a.G * a.k * D * sizeof(float);
+    decode_merge_kernel<D><<<a.B, 64 * kDcMergeWaves, lds, st>>>((const float*)a.workspace, a.lens, a.p_tilde, a.out,
+                                                                 a.G, a.k, a.n_shared, a.S, a.route_mode, nch, CH);
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t st)
