@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
 // timing) into their hard or shared slot, keeping the hard slots in LDS; the
 // weighted slot(s) are then summed from LDS in fixed g-then-j order, exactly
 // as the slot-assembly kernel does from memory.
-constexpr int kDcMergeWaves = 4;
+constexpr int kDcMergeWaves = 16;
 
 template <int D>
 __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
@@ -154,11 +154,32 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
         const int g = row < kG ? row / k : 0;
         const int r = row < kG ? row % k : k;
         const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
+        // pass 1: the largest chunk maximum
         float M = -INFINITY;
         for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
         M = wave_max(M);
+        // pass 2, 64 chunks at a time: lane c forms chunk c's weight; the
+        // weighted value rows are added in chunk order
         float Ls = 0.f;
-        for (int c = lane; c < nc; c += 64) Ls += pp[(size_t)c * (D + 2) + 1] * __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
+        float O[(D + 63) / 64];
+#pragma unroll
+        for (int i = 0; i < (D + 63) / 64; ++i) O[i] = 0.f;
+        for (int c0 = 0; c0 < nc; c0 += 64) {
+            const int c = c0 + lane;
+            float wgt = 0.f;
+            if (c < nc) {
+                wgt = __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
+                Ls += pp[(size_t)c * (D + 2) + 1] * wgt;
+            }
+            const int n = min(64, nc - c0);
+            for (int i = 0; i < n; ++i) {
+                const float wi = __shfl(wgt, i);
+                const float* q = pp + (size_t)(c0 + i) * (D + 2) + 2;
+#pragma unroll
+                for (int d0 = 0; d0 < D; d0 += 64)
+                    if (d0 + lane < D) O[d0 / 64] = fmaf(q[d0 + lane], wi, O[d0 / 64]);
+            }
+        }
         Ls = wave_sum(Ls);
         const float inv = 1.f / Ls;
         float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
@@ -166,15 +187,9 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
         for (int d0 = 0; d0 < D; d0 += 64) {
             const int d = d0 + lane;
             if (d < D) {
-                float O = 0.f;
-#pragma unroll 8
-                for (int c = 0; c < nc; ++c) {
-                    const float* q = pp + (size_t)c * (D + 2);
-                    O = fmaf(q[2 + d], __builtin_amdgcn_exp2f(q[0] - M), O);
-                }
-                O *= inv;
-                dst[d] = O;
-                if (row < kG) s_hard[row * D + d] = O;
+                const float v = O[d0 / 64] * inv;
+                dst[d] = v;
+                if (row < kG) s_hard[row * D + d] = v;
             }
         }
     }
