@@ -3,21 +3,26 @@
 A step is one pass of the whole prefill path on the main 250M-scale layer
 shape (B=4, T=4096, d_model=1024, H_q=16, H_kv=8, k=1, shared head,
 d_head=64, bf16): router + compaction (gqe_route), routed and shared query
-projection (gqe_qproj), causal attention and slot assembly
-(gqe_attn_prefill), with every input already resident in HBM.
+projection (gqe_qproj), causal attention (gqe_attn_prefill_heads) and slot
+assembly (gqe_assemble) -- together the work of gqe_attn_prefill -- with
+every input already resident in HBM.
 
 Printed value: routed prefill throughput in TFLOP/s counted over active
 heads only (attention FLOPs 4*d*B*H_act*T(T+1)/2 with H_act = k*G + 1,
 divided by the whole step's time).  The same JSON line carries:
-  roofline      the attention call (gqe_attn_prefill) timed with HIP events
-                on the stream it is launched on, against the bf16 MFMA peak;
+  roofline      the attention kernel alone (the one kernel of
+                gqe_attn_prefill_heads) timed with HIP events on the stream it
+                is launched on, against the bf16 MFMA peak;
   decode        the one-token decode step on the decode workload (B=64 cache
                 lengths in [4096, 8192]): gqe_attn_decode timed alone, bytes of
                 K/V it must read over its time, against the HBM peak;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
   long_context  T=32768 GQE vs all-active GQA on the same inputs.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-context] [--no-decode]
+--graph also times the step replayed from one HIP graph of the four calls
+(on this stack replaying is not faster than launching them one by one).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu] [--no-context] [--no-decode]
        python bench.py --only {prefill,decode,copy} --steps K   (profiler runs)
 """
 from __future__ import annotations
@@ -47,6 +52,7 @@ def parse():
     ap.add_argument("--no-context", action="store_true", help="skip the long-context GQE vs dense leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--graph", action="store_true", help="also time the step replayed from one HIP graph")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
@@ -282,15 +288,33 @@ def main():
         p.step()
     torch.cuda.synchronize()
 
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
-        p.step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    def timed(fn, n):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n, time.perf_counter() - t0
+
+    ms_step, wall = timed(p.step, args.steps)
+    ms_graph = None
+    if args.graph:
+        # the four calls captured once into a HIP graph and replayed (the
+        # library never allocates or syncs, so the step is capturable)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            p.step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            p.step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_graph, _ = timed(graph.replay, args.steps)
     fl = W.attention_flops(w)
     value = fl / (ms_step * 1e-3) / 1e12
 
@@ -304,6 +328,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "d_model": w.d_model, "H_q": w.H_q, "H_kv": w.H_kv,
                    "k": w.k, "n_shared": w.n_shared, "d_head": w.d_head, "causal": w.causal,
                    "active_heads": w.h_active, "attention_flops_per_step": fl, "parallelism": "single GPU"},
+        "ms_per_step_hip_graph": ms_graph,
         "step_split_us": {"route": t_route * 1e3, "qproj": t_qp * 1e3, "attn_prefill_heads": t_attn * 1e3,
                           "assemble": t_asm * 1e3},
         "wall_s_timed": wall,

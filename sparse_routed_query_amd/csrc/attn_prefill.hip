@@ -320,19 +320,18 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
     const int b = (int)(gid / per_b);
     long long r = gid % per_b;
     const float* q;
-    int h, kk, slot, t;
+    int h, slot, t;
     if (r < (long long)G * Rr) {
         h = (int)(r / Rr);
         const int rr = (int)(r % Rr);
-        kk = k; t = rr / k;
+        t = rr / k;
         slot = h * k + rr % k;
         q = q_routed + (((size_t)b * G + h) * Rr + rr) * D;
     } else {
-        h = 0; kk = 1; t = (int)(r - (long long)G * Rr);
+        h = 0; t = (int)(r - (long long)G * Rr);
         slot = S - 1;
         q = q_shared + ((size_t)b * T + t) * D;
     }
-    (void)kk;
     const float* K = kg + ((size_t)b * G + h) * (size_t)T * D;
     const float* V = vg + ((size_t)b * G + h) * (size_t)T * D;
     const float scale = 1.f / sqrtf((float)D);

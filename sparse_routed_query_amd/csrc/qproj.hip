@@ -76,7 +76,7 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane)
     return v;
 }
 
-__device__ bool qp_plan(int bid, int nbid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, int lane,
+__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, int lane,
                         int& n_out, int& tile_out)
 {
     auto ntiles = [&](int n) {
@@ -90,7 +90,6 @@ __device__ bool qp_plan(int bid, int nbid, const int32_t* __restrict__ counts, i
     const int chunk = (U + 7) / 8;
     const int L = (bid % 8) * chunk + bid / 8;
     if (bid / 8 >= chunk || L >= U) return false;
-    (void)nbid;
     auto S = [&](int r) { return wave_sum_i(qp_before(c0, r, R) + qp_before(c1, r, R)); };
     // S(r) lies in [r U / R, r U / R + n_exp): start from the estimate and walk
     int r = (int)(((long long)L * R) / U);
@@ -139,7 +138,7 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     __shared__ int s_item[2];
     if (wave == 0) {
         int pn = -1, pt = 0;
-        if (!qp_plan(blockIdx.x, gridDim.x, counts, N, n_exp, BT, lane, pn, pt)) pn = -1;
+        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, lane, pn, pt)) pn = -1;
         if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
     }
     __syncthreads();

@@ -150,6 +150,47 @@ def test_heads_then_assemble_equals_attn_prefill(w):
     assert torch.equal(out, ref)
 
 
+def test_graph_replay_matches_eager():
+    """The four prefill calls captured into a HIP graph give the eager results on every replay."""
+    w = small(B=2, T=700, k=1, name="graph")
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    di = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    x = di["x"].reshape(-1, w.d_model)
+    r = G.alloc_route(d, x.device)
+    q = G.alloc_qproj(d, x.device)
+    out = torch.empty((w.B, w.T, d.S, w.d_head), dtype=torch.float32, device=x.device)
+
+    def step():
+        G.gqe_route(d, x, di["w_router"], di["b_router"], r["sel"], r["p_tilde"], r["counts"], r["offsets"],
+                    r["rows"], None, r["workspace"])
+        G.gqe_qproj(d, x, di["w_q"], r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"], q["q_shared"])
+        G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out)
+        G.gqe_assemble(d, r["p_tilde"], out)
+
+    step()
+    torch.cuda.synchronize()
+    bufs = dict(sel=r["sel"], p_tilde=r["p_tilde"], counts=r["counts"], offsets=r["offsets"], rows=r["rows"],
+                q_routed=q["q_routed"], q_shared=q["q_shared"], out=out)
+    ref = {k: v.clone() for k, v in bufs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for v in bufs.values():                 # eager work between replays
+            v.fill_(-7 if v.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in bufs.items():
+            assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager run"
+
+
 # ---------------------------------------------------------------- decode edges
 
 def decode_case(**kw):
