@@ -144,19 +144,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPfBN * P];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPfBN * PV];
 
-    bf16x8 qf[D / 16];
+    // Q loads (rows past R read row R-1 and are zeroed) are issued together
+    // with the first K/V tile's, so the prologue waits for memory once
+    u32x4 qraw[D / 16];
+    {
+        const uint16_t* qsrc = Q + (size_t)min(qrow, R - 1) * D + 8 * lh;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        bf16x8 v = {};
-        if (qvalid) {
-            const u32x4 raw = ld_u32x4(Q + (size_t)qrow * D + 16 * c + 8 * lh);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = f2bf(bf2f((uint16_t)(raw[i] & 0xffff)) * qscale);
-                v[2 * i + 1] = f2bf(bf2f((uint16_t)(raw[i] >> 16)) * qscale);
-            }
-        }
-        qf[c] = v;
+        for (int c = 0; c < D / 16; ++c) qraw[c] = ld_u32x4(qsrc + 16 * c);
     }
 
     u32x4 rk[NCH], rv[NCH];
@@ -195,6 +189,20 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     for (int r = 0; r < 16; ++r) cneg[r] = 0.f;
 
     load(0);
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        bf16x8 v = {};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = f2bf(bf2f((uint16_t)(qraw[c][i] & 0xffff)) * qscale);
+            v[2 * i + 1] = f2bf(bf2f((uint16_t)(qraw[c][i] >> 16)) * qscale);
+        }
+        qf[c] = qvalid ? v : bf16x8{};
+        // pin the Q fragments here, ahead of the first tile's store: the Q loads
+        // are then in flight together with the tile loads, not issued after them
+        asm volatile("" ::"v"(qf[c]));
+    }
     store(0);
     __syncthreads();
     for (int kt = 0; kt < nkv; ++kt) {
