@@ -138,6 +138,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
 // weighted slot(s) are then summed from LDS in fixed g-then-j order, exactly
 // as the slot-assembly kernel does from memory.
 constexpr int kDcMergeWaves = 16;
+constexpr int kDcMergeRegs = 32;          // value registers per lane for merging a row from registers
 
 template <int D>
 __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
@@ -154,30 +155,61 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
         const int g = row < kG ? row / k : 0;
         const int r = row < kG ? row % k : k;
         const float* pp = part + (((size_t)b * G + g) * RG + r) * (size_t)nch * (D + 2);
-        // pass 1: the largest chunk maximum
-        float M = -INFINITY;
-        for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
-        M = wave_max(M);
-        // pass 2, 64 chunks at a time: lane c forms chunk c's weight; the
-        // weighted value rows are added in chunk order
+        constexpr int ND = (D + 63) / 64;          // value columns per lane
+        constexpr int FAST = kDcMergeRegs / ND;    // rows with at most this many chunks merge from registers
         float Ls = 0.f;
-        float O[(D + 63) / 64];
+        float O[ND];
 #pragma unroll
-        for (int i = 0; i < (D + 63) / 64; ++i) O[i] = 0.f;
-        for (int c0 = 0; c0 < nc; c0 += 64) {
-            const int c = c0 + lane;
-            float wgt = 0.f;
-            if (c < nc) {
-                wgt = __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
-                Ls += pp[(size_t)c * (D + 2) + 1] * wgt;
+        for (int i = 0; i < ND; ++i) O[i] = 0.f;
+        if (nc <= FAST) {
+            // every partial of the row is loaded at once (one memory round trip):
+            // lane c holds chunk c's (max, sum); value rows of every chunk are
+            // held per lane (chunks past nc repeat chunk nc-1 and are not used)
+            float m = -INFINITY, l = 0.f;
+            if (lane < nc) {
+                m = pp[(size_t)lane * (D + 2)];
+                l = pp[(size_t)lane * (D + 2) + 1];
             }
-            const int n = min(64, nc - c0);
-            for (int i = 0; i < n; ++i) {
-                const float wi = __shfl(wgt, i);
-                const float* q = pp + (size_t)(c0 + i) * (D + 2) + 2;
+            float ov[FAST][ND];
 #pragma unroll
-                for (int d0 = 0; d0 < D; d0 += 64)
-                    if (d0 + lane < D) O[d0 / 64] = fmaf(q[d0 + lane], wi, O[d0 / 64]);
+            for (int c = 0; c < FAST; ++c)
+#pragma unroll
+                for (int i = 0; i < ND; ++i) {
+                    const int d = min(64 * i + lane, D - 1);
+                    ov[c][i] = pp[(size_t)min(c, nc - 1) * (D + 2) + 2 + d];
+                }
+            const float M = wave_max(m);
+            const float wgt = lane < nc ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+            Ls = l * wgt;
+#pragma unroll
+            for (int c = 0; c < FAST; ++c) {
+                if (c >= nc) break;
+                const float wi = __shfl(wgt, c);
+#pragma unroll
+                for (int i = 0; i < ND; ++i) O[i] = fmaf(ov[c][i], wi, O[i]);
+            }
+        } else {
+            // pass 1: the largest chunk maximum
+            float M = -INFINITY;
+            for (int c = lane; c < nc; c += 64) M = fmaxf(M, pp[(size_t)c * (D + 2)]);
+            M = wave_max(M);
+            // pass 2, 64 chunks at a time: lane c forms chunk c's weight; the
+            // weighted value rows are added in chunk order
+            for (int c0 = 0; c0 < nc; c0 += 64) {
+                const int c = c0 + lane;
+                float wgt = 0.f;
+                if (c < nc) {
+                    wgt = __builtin_amdgcn_exp2f(pp[(size_t)c * (D + 2)] - M);
+                    Ls += pp[(size_t)c * (D + 2) + 1] * wgt;
+                }
+                const int n = min(64, nc - c0);
+                for (int i = 0; i < n; ++i) {
+                    const float wi = __shfl(wgt, i);
+                    const float* q = pp + (size_t)(c0 + i) * (D + 2) + 2;
+#pragma unroll
+                    for (int d0 = 0; d0 < D; d0 += 64)
+                        if (d0 + lane < D) O[d0 / 64] = fmaf(q[d0 + lane], wi, O[d0 / 64]);
+                }
             }
         }
         Ls = wave_sum(Ls);

@@ -207,6 +207,8 @@ def decode_case(**kw):
     decode_case(d_head=32, n_shared=0, name="dec_d32_noshared"),
     decode_case(dtype="f32", name="dec_f32"),
     decode_case(dtype="f32", d_head=128, L_hi=300, L_max=300, name="dec_f32_d128"),
+    # up to 33 chunks of 128 keys: more than the merge holds in registers at d_head 128
+    decode_case(d_head=128, H_q=8, H_kv=4, L_lo=1500, L_hi=4200, L_max=4200, name="dec_d128_long"),
 ], ids=lambda w: w.name)
 def test_decode_shapes(w):
     drawn = W.make_inputs(w)["lens"]
