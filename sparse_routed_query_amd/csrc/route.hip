@@ -259,26 +259,45 @@ __global__ __launch_bounds__(64 * kCmpWaves) void compact_kernel(const int32_t* 
                                                                  int k, int nblk)
 {
     constexpr int NT = 64 * kCmpWaves, BPW = 2 * kCmpWaves;
+    constexpr int SELR = 16;                     // kept entries per token staged through registers
     const int N = G * E, tid = threadIdx.x;
     const int blk0 = blockIdx.x * BPW;
     __shared__ int s_tot[NT], s_pre[NT];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_base[BPW][kMaxExperts];
+    __shared__ int s_sel[BPW * kRouteTok][SELR];
+    // this lane's token of the scatter (lanes 0-31 and 32-63 of a wave take one block each)
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, hl = lane & 31;
+    const int bi = wave * 2 + half;
+    const int blk = blk0 + bi;
+    const int t = blk * kRouteTok + hl;
+    const bool valid = blk < nblk && t < BT;
+    const int Gk = G * k;
+    const bool staged = Gk <= SELR;
+    // Every global load of the kernel is issued up front: the token's kept
+    // experts, its workgroup's own block counts, then the whole count table.
+    int sv[SELR];
+#pragma unroll
+    for (int h = 0; h < SELR; ++h) sv[h] = (staged && valid) ? sel[(size_t)t * Gk + min(h, Gk - 1)] : -1;
+    int own[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) own[i] = (tid < N && blk0 + i < nblk) ? blk_counts[(size_t)(blk0 + i) * N + tid] : 0;
     // 1. per-expert totals and the prefix before this workgroup's first block
     const int R = NT / N;                        // thread rows, one expert per column
     int tot = 0, pre = 0;
     if (tid < R * N) {
         const int n = tid % N;
-        // 16 independent loads in flight per step
-        for (int b0 = tid / N; b0 < nblk; b0 += 16 * R) {
-            int c[16];
+        // 32 independent loads in flight per step (one step for tables up to 8192 entries)
+        for (int b0 = tid / N; b0 < nblk; b0 += 32 * R) {
+            int c[32];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 32; ++i) {
                 const int b = b0 + i * R;
                 c[i] = b < nblk ? blk_counts[(size_t)b * N + n] : 0;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 32; ++i) {
                 tot += c[i];
                 pre += b0 + i * R < blk0 ? c[i] : 0;
             }
@@ -286,11 +305,13 @@ __global__ __launch_bounds__(64 * kCmpWaves) void compact_kernel(const int32_t* 
     }
     s_tot[tid] = tot;
     s_pre[tid] = pre;
+#pragma unroll
+    for (int h = 0; h < SELR; ++h) s_sel[bi * kRouteTok + hl][h] = sv[h];
     __syncthreads();
     if (tid < N) {
-        int t = 0, q = 0;
-        for (int r = 0; r < R; ++r) { t += s_tot[r * N + tid]; q += s_pre[r * N + tid]; }
-        s_tot[tid] = t;          // row 0 of the table is only read by its own thread
+        int tt = 0, q = 0;
+        for (int r = 0; r < R; ++r) { tt += s_tot[r * N + tid]; q += s_pre[r * N + tid]; }
+        s_tot[tid] = tt;         // row 0 of the table is only read by its own thread
         s_pre[tid] = q;
     }
     __syncthreads();
@@ -302,26 +323,23 @@ __global__ __launch_bounds__(64 * kCmpWaves) void compact_kernel(const int32_t* 
     __syncthreads();
     if (tid < N) {
         int run = s_off[tid] + s_pre[tid];
+#pragma unroll
         for (int i = 0; i < BPW; ++i) {
             s_base[i][tid] = run;
-            if (blk0 + i < nblk) run += blk_counts[(size_t)(blk0 + i) * N + tid];
+            run += own[i];
         }
         if (blockIdx.x == 0) counts[tid] = s_tot[tid];
     }
     if (blockIdx.x == 0)
         for (int n = tid; n <= N; n += NT) offsets[n] = s_off[n];
     __syncthreads();
-    // 2. scatter: lanes 0-31 and 32-63 of a wave take one block each
-    const int lane = tid & 63, wave = tid >> 6;
-    const int half = lane >> 5, hl = lane & 31;
-    const int bi = wave * 2 + half;
-    const int blk = blk0 + bi;
-    const int t = blk * kRouteTok + hl;
-    const bool valid = blk < nblk && t < BT;
+    // 2. scatter: wave ballots rank the token among its block's tokens that kept each expert
     const uint32_t below = (1u << hl) - 1u;
+    const int* my_sel = s_sel[bi * kRouteTok + hl];
     for (int g = 0; g < G; ++g) {
         int kept[8];
-        for (int j = 0; j < k; ++j) kept[j] = valid ? sel[((size_t)t * G + g) * k + j] : -1;
+        for (int j = 0; j < k; ++j)
+            kept[j] = !valid ? -1 : staged ? my_sel[g * k + j] : sel[((size_t)t * G + g) * k + j];
         for (int e = 0; e < E; ++e) {
             bool has = false;
             for (int j = 0; j < k; ++j) has |= kept[j] == e;
