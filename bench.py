@@ -23,7 +23,7 @@ divided by the whole step's time).  The same JSON line carries:
 (on this stack replaying is not faster than launching them one by one).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu] [--no-context] [--no-decode]
-       python bench.py --only {prefill,decode,copy} --steps K   (profiler runs)
+       python bench.py --only {step,prefill,decode,copy} --steps K   (profiler runs)
 """
 from __future__ import annotations
 
@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="also time the step replayed from one HIP graph")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["step", "prefill", "decode", "copy"], default=None,
                     help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
 
@@ -234,9 +234,10 @@ def long_context_leg(torch, dev, steps):
 
 
 def only(args, torch):
-    """One call repeated, for rocprofv3 counter runs: the prefill attention call
-    on the main shape, the decode attention call, or a plain 256 MiB device copy
-    (the calibration kernel for FETCH_SIZE / WRITE_SIZE)."""
+    """One call repeated, for rocprofv3 counter runs: the whole prefill step, the
+    prefill attention and assembly calls on the main shape, the decode attention
+    call, or a plain 256 MiB device copy (the calibration kernel for FETCH_SIZE /
+    WRITE_SIZE)."""
     import workloads as W
     import sparse_routed_query_amd.gqe as G
     dev = "cuda:0"
@@ -245,6 +246,11 @@ def only(args, torch):
         dst = torch.empty_like(src)
         for _ in range(args.steps):
             dst.copy_(src)
+    elif args.only == "step":
+        w = W.WORKLOADS["main_250m"]
+        p = Prefill(w, W.make_inputs(w), dev)
+        for _ in range(args.steps):
+            p.step()
     elif args.only == "prefill":
         w = W.WORKLOADS["main_250m"]
         p = Prefill(w, W.make_inputs(w), dev)
