@@ -75,6 +75,8 @@ class Prefill:
         self.r = G.alloc_route(self.d, dev)
         self.q = G.alloc_qproj(self.d, dev)
         self.out = torch.empty((w.B, w.T, self.d.S, w.d_head), dtype=torch.float32, device=dev)
+        n_ws = G.gqe_attn_prefill_workspace_bytes(self.d)   # zeroed once; every call leaves it zeroed
+        self.ws = torch.zeros(n_ws, dtype=torch.uint8, device=dev) if n_ws else None
 
     def route(self):
         r = self.r
@@ -88,7 +90,8 @@ class Prefill:
 
     def attn(self):
         """Attention only (hard and shared slots): the dominant kernel."""
-        self.G.gqe_attn_prefill_heads(self.d, self.q["q_routed"], self.q["q_shared"], self.k, self.v, self.out)
+        self.G.gqe_attn_prefill_heads(self.d, self.q["q_routed"], self.q["q_shared"], self.k, self.v, self.out,
+                                      self.ws)
 
     def assemble(self):
         self.G.gqe_assemble(self.d, self.r["p_tilde"], self.out)

@@ -131,6 +131,41 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
               void* q_routed, void* q_shared, void* stream);
 
 /*
+ * Bytes of device workspace that lets gqe_attn_prefill / gqe_attn_prefill_heads
+ * split the longest causal query tiles (bf16 only; 0 when no tile would be
+ * split: f32, non-causal or short sequences).
+ *
+ * With a workspace, each causal query tile that needs more than 32 key tiles
+ * of 64 keys is computed by two workgroups over the two halves of its key
+ * range; the one that finishes second merges the two partial softmax states
+ * (running reference, row sum, unnormalised output), adding part 0's term
+ * first, so the result does not depend on which half finished first.  It
+ * differs from the unsplit result only by that regrouping of fp32 sums.  The
+ * split keeps the launch's longest workgroups near the average load of a
+ * workgroup slot (the causal tile with the most keys otherwise sets the
+ * kernel's end).
+ *
+ * Layout: one int32 counter per split tile (padded to 256 bytes), then the
+ * partial states.  The counters must hold even values (zero) before the first
+ * call with a buffer -- allocate it zeroed once -- and every completed call
+ * leaves them at zero.  Calls that share a workspace must not overlap.
+ */
+size_t gqe_attn_prefill_workspace_bytes(const gqe_desc* desc);
+
+/*
+ * gqe_attn_prefill_plan -- the work items of one bf16 prefill attention launch,
+ * in launch order (for inspection and host tests; computes nothing on the GPU).
+ * split != 0 gives the plan used with a workspace.  Writes at most max_items
+ * items of 5 int32 each to `items` (host memory, may be NULL):
+ *   b, head (H_kv = the shared head), query tile (128 rows), part (-1 whole
+ *   tile, 0 / 1 first / second half of its key tiles), split-pair index (-1
+ *   for a whole tile).
+ * Items are ordered by decreasing number of key tiles.  Returns the number of
+ * items (the launch's workgroup count) or a negative status.
+ */
+int64_t gqe_attn_prefill_plan(const gqe_desc* desc, int split, int32_t* items, int64_t max_items);
+
+/*
  * gqe_attn_prefill -- attention of every routed and shared query row against
  * its group's dense, unchanged KV head, then slot assembly.
  *
@@ -144,22 +179,28 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
  * In:  q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] or NULL,
  *      k, v [B, H_kv, T, d_head] (dtype), p_tilde [BT, G, k] fp32.
  * Out: out [B, T, S, d_head] fp32.
+ * Workspace: NULL (no split tiles) or gqe_attn_prefill_workspace_bytes(desc)
+ *      bytes of device memory prepared as described there; a smaller size
+ *      returns GQE_ERR_WORKSPACE.
  * bf16: QK^T and PV run on bf16 MFMA with fp32 accumulation; the softmax is
  * fp32 and the probabilities are rounded to bf16 for the PV product.
  */
 int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared,
-                     const void* k, const void* v, const float* p_tilde, float* out, void* stream);
+                     const void* k, const void* v, const float* p_tilde, float* out,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gqe_attn_prefill_heads -- the attention part of gqe_attn_prefill alone
  * (same definition, GQE study note §1-1 and §3-2 (3), (5)): writes the hard
  * slots out[b,t,g*k+j] and the shared slot out[b,t,S-1]; the weighted slot(s)
  * of `out` are left as they were.  Together with gqe_assemble it computes
- * exactly what gqe_attn_prefill computes (bitwise).
- * In/Out: as gqe_attn_prefill, without p_tilde.
+ * exactly what gqe_attn_prefill computes with the same workspace choice
+ * (bitwise).
+ * In/Out/Workspace: as gqe_attn_prefill, without p_tilde.
  */
 int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const void* q_shared,
-                           const void* k, const void* v, float* out, void* stream);
+                           const void* k, const void* v, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * gqe_assemble -- the weighted slot(s) of B*T output rows from their hard

@@ -23,7 +23,12 @@
 //     rescale needs no exchange either.
 //   * Workgroups are issued longest-first (causal work grows with the query
 //     tile) over both the routed tiles (k rows per position) and the shared
-//     tiles (one row per position).
+//     tiles (one row per position).  With a workspace, the causal tiles that
+//     need more than a threshold of key tiles are cut into two work items
+//     over the two halves of their key range, so that no workgroup is much
+//     longer than the average load of a workgroup slot; both halves write
+//     their partial softmax state (reference, row sum, unnormalised output),
+//     and the one that finishes second merges the two (no waiting).
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
@@ -33,41 +38,140 @@ constexpr int kPfBM = 128;   // query rows per workgroup (4 waves x 32)
 constexpr int kPfBN = 64;    // keys per iteration
 constexpr int kPfPad = 8;    // LDS row padding in bf16 elements
 
-struct PfWork {
-    int b, h, tile;          // h == G means the shared head
+// Key tiles needed by query tile i of a head with kk rows per position.
+__host__ __device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal)
+{
+    if (!causal) return (T + kPfBN - 1) / kPfBN;
+    const int last_row = min(R - 1, (i + 1) * kPfBM - 1);
+    return (last_row / kk) / kPfBN + 1;
+}
+
+// Work schedule of one launch.  A routed head has ntr query tiles (k rows per
+// position), the shared head nts (one row per position).  Tiles i >= isr
+// (routed) and i >= iss (shared) are split: part 0 takes key tiles [0, h),
+// part 1 [h, nkv), h = nkv / 2.  Work items are ordered by decreasing size
+// (key tiles of the item; for a split tile, the larger part), then routed
+// before shared, split before whole, and by decreasing tile index.
+struct PfSched {
+    int B, T, G, k, n_shared, causal;
+    int ntr, nts;   // query tiles per routed / shared head
+    int isr, iss;   // first split tile (== ntr / nts: none)
+    int nkv_max;    // key tiles of the longest tile
+};
+struct PfItem {
+    int b, h, tile;   // h == G means the shared head
+    int part;         // -1: whole tile; 0, 1: first / second half of its keys
+    int pair;         // split tiles: index of the (part 0, part 1) pair; else -1
 };
 
-// Key tiles needed by query tile i of a head with kk rows per position.
-__device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal, int bn = kPfBN)
+// Smallest tile index in [0, nt] whose key-tile count is at least n
+// (nkv is non-decreasing in the tile index).
+__host__ __device__ __forceinline__ int pf_first_ge(int n, int kk, int R, int nt, int T, int causal)
 {
-    if (!causal) return (T + bn - 1) / bn;
-    const int last_row = min(R - 1, (i + 1) * kPfBM - 1);
-    const int t_hi = last_row / kk;
-    return t_hi / bn + 1;
+    if (!causal) return n <= (T + kPfBN - 1) / kPfBN ? 0 : nt;
+    if (n <= 1) return 0;
+    // nkv(i) >= n  <=>  min(R - 1, 128 i + 127) >= 64 kk (n - 1)
+    const long long need = (long long)kPfBN * kk * (n - 1);
+    if (need > R - 1) return nt;
+    return (int)min((long long)nt, need / kPfBM);
 }
 
-// Map a workgroup id to (b, head, tile), ordering tiles by decreasing work.
-// Routed tiles (B*G of them per tile index) and shared tiles (B per index)
-// are merged like two sorted lists.
-__device__ __forceinline__ PfWork pf_map(int id, int B, int T, int G, int k, int n_shared, int causal)
+// Number of work items whose size is at least s.
+__host__ __device__ __forceinline__ long long pf_count_ge(const PfSched& p, int s)
 {
-    const int Rr = T * k, Rs = T;
-    int ir = (Rr + kPfBM - 1) / kPfBM - 1;
-    int is = n_shared ? (Rs + kPfBM - 1) / kPfBM - 1 : -1;
-    PfWork w{0, 0, 0};
-    while (true) {
-        const int cr = ir >= 0 ? pf_nkv(ir, k, Rr, T, causal) : -1;
-        const int cs = is >= 0 ? pf_nkv(is, 1, Rs, T, causal) : -1;
-        if (cr >= cs) {
-            const int n = B * G;
-            if (id < n) { w.b = id / G; w.h = id % G; w.tile = ir; return w; }
-            id -= n; --ir;
-        } else {
-            if (id < B) { w.b = id; w.h = G; w.tile = is; return w; }
-            id -= B; --is;
+    long long n = 0;
+#pragma unroll
+    for (int l = 0; l < 2; ++l) {
+        const int kk = l ? 1 : p.k, nt = l ? p.nts : p.ntr, is = l ? p.iss : p.isr;
+        const long long cnt = l ? (p.n_shared ? p.B : 0) : (long long)p.B * p.G;
+        const int R = p.T * kk;
+        const int whole = max(0, is - pf_first_ge(s, kk, R, nt, p.T, p.causal));
+        const int split = max(0, nt - max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal)));
+        n += (whole + 2ll * split) * cnt;
+    }
+    return n;
+}
+
+// The id-th work item, given the size s of that item: the largest s with
+// pf_count_ge(p, s) > id.
+__host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, long long id, int s)
+{
+    id -= pf_count_ge(p, s + 1);
+    PfItem w{0, 0, 0, -1, -1};
+    for (int l = 0; l < 2; ++l) {
+        const int kk = l ? 1 : p.k, nt = l ? p.nts : p.ntr, is = l ? p.iss : p.isr;
+        const long long cnt = l ? (p.n_shared ? p.B : 0) : (long long)p.B * p.G;
+        const int R = p.T * kk;
+        for (int sp = 1; sp >= 0; --sp) {
+            // tiles of this group whose item size is exactly s: [a, e)
+            int a, e;
+            if (sp) {
+                a = max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal));
+                e = max(is, pf_first_ge(2 * s + 1, kk, R, nt, p.T, p.causal));
+            } else {
+                a = min(is, pf_first_ge(s, kk, R, nt, p.T, p.causal));
+                e = min(is, pf_first_ge(s + 1, kk, R, nt, p.T, p.causal));
+            }
+            const long long per = cnt * (sp ? 2 : 1);
+            const long long n = (long long)max(0, e - a) * per;
+            if (id < n) {
+                const int i = e - 1 - (int)(id / per);
+                const int rem = (int)(id % per);
+                const int bh = sp ? rem >> 1 : rem;
+                w.tile = i;
+                // the two halves of a pair go to neighbouring workgroups, which the
+                // hardware hands to different XCDs; alternate their order so that
+                // part 1 (the diagonal tiles) does not always land on the same XCDs
+                w.part = sp ? (rem ^ (rem >> 1)) & 1 : -1;
+                if (l == 0) {
+                    w.b = bh / p.G; w.h = bh % p.G;
+                } else {
+                    w.b = bh; w.h = p.G;
+                }
+                w.pair = !sp ? -1 : l == 0 ? (i - is) * p.B * p.G + bh
+                                           : (p.ntr - p.isr) * p.B * p.G + (i - is) * p.B + bh;
+                return w;
+            }
+            id -= n;
         }
     }
+    return w;   // not reached for id < pf_count_ge(p, 1)
 }
+
+// The id-th work item (0 <= id < pf_count_ge(p, 1)), by binary search.
+__host__ __device__ __forceinline__ PfItem pf_item(const PfSched& p, long long id)
+{
+    int lo = 1, hi = p.nkv_max;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (pf_count_ge(p, mid) > id) lo = mid; else hi = mid - 1;
+    }
+    return pf_item_of_size(p, id, lo);
+}
+
+// The same on the GPU, by the 64 lanes of a wave at once: lane l tests a
+// candidate size, and since pf_count_ge is non-increasing in s the lanes that
+// pass form a prefix.  Two rounds (stride, then within the stride) cover up
+// to 4096 key tiles.  Keeps the search off the scalar unit, which all waves
+// of a compute unit share.
+__device__ __forceinline__ PfItem pf_item_wave(const PfSched& p, long long id, int lane)
+{
+    const int stride = (p.nkv_max + 63) / 64;
+    const int s1 = 1 + lane * stride;
+    const bool ok1 = s1 <= p.nkv_max && pf_count_ge(p, s1) > id;
+    int s = 1 + (__popcll(__ballot(ok1)) - 1) * stride;
+    if (stride > 1) {
+        const int s2 = s + lane;
+        const bool ok2 = lane < stride && s2 <= p.nkv_max && pf_count_ge(p, s2) > id;
+        s += __popcll(__ballot(ok2)) - 1;
+    }
+    return pf_item_of_size(p, id, s);
+}
+
+// Floats of one part's partial state: per thread, the output accumulators
+// (D / 2) and (reference, half row sum).
+template <int D>
+__host__ __device__ constexpr int pf_part_floats() { return 256 * (D / 2 + 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -107,16 +211,33 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b)
 constexpr float kPfRescale = 8.0f;
 constexpr float kPfRescaleSum = 256.0f;   // 2^kPfRescale
 
+struct PfParams {
+    const uint16_t* q_routed;
+    const uint16_t* q_shared;
+    const uint16_t* kg;
+    const uint16_t* vg;
+    float* out;
+    int* ctr;      // one counter per split pair (even before a launch, even after)
+    float* part;   // pf_part_floats<D>() floats per part of each split pair
+    int S;
+    float qscale;  // log2(e) / sqrt(d)
+    PfSched sc;
+};
+
+// One work item: attention of a query tile over its key tiles [kt0, kt1).
 template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(
-    const uint16_t* __restrict__ q_routed, const uint16_t* __restrict__ q_shared, const uint16_t* __restrict__ kg,
-    const uint16_t* __restrict__ vg, float* __restrict__ out, int B, int T, int G, int k, int n_shared, int causal,
-    int S, float qscale)
+__device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 {
     constexpr int P = D + kPfPad;           // LDS row pitch (elements)
     constexpr int NDB = D / 32;
     constexpr int NCH = kPfBN * D / 8 / 256; // 16-byte chunks per thread for one K or V tile
-    const PfWork w = pf_map(blockIdx.x, B, T, G, k, n_shared, causal);
+    const int T = p.sc.T, G = p.sc.G, k = p.sc.k, causal = p.sc.causal, S = p.S;
+    const float qscale = p.qscale;
+    const uint16_t* __restrict__ q_routed = p.q_routed;
+    const uint16_t* __restrict__ q_shared = p.q_shared;
+    const uint16_t* __restrict__ kg = p.kg;
+    const uint16_t* __restrict__ vg = p.vg;
+    float* __restrict__ out = p.out;
     const bool shared = w.h == G;
     const int kk = shared ? 1 : k;
     const int R = T * kk;
@@ -130,10 +251,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     const int lr = lane & 31, lh = lane >> 5;
     const int r0 = w.tile * kPfBM;
     const int nkv = pf_nkv(w.tile, kk, R, T, causal);
+    // key tiles of this work item: [kt0, kt1)
+    const int kt0 = w.part == 1 ? nkv / 2 : 0;
+    const int kt1 = w.part == 0 ? nkv / 2 : nkv;
 
     const int qrow = r0 + wave * 32 + lr;
     const bool qvalid = qrow < R;
-    const int tq = qvalid ? qrow / kk : 0;   // invalid rows see key 0 only, so they stay finite
+    const int tq = qvalid ? qrow / kk : T - 1;   // rows past R see every key, so they stay finite
     const int wrow_hi = min(R - 1, r0 + wave * 32 + 31);
     const int nkv_w = causal ? (wrow_hi / kk) / kPfBN + 1 : nkv;
     const int t_lo_w = (r0 + wave * 32) / kk;
@@ -188,7 +312,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) cneg[r] = 0.f;
 
-    load(0);
+    load(kt0);
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
@@ -205,9 +329,9 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     }
     store(0);
     __syncthreads();
-    for (int kt = 0; kt < nkv; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkv) load(kt + 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        if (kt + 1 < kt1) load(kt + 1);
         if (kt < nkv_w) {
             const uint16_t* bK = sK[buf];
             const uint16_t* bV = sV[buf];
@@ -248,7 +372,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
                 for (int i = 0; i < 16; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, ls, false);
                 return ls;
             };
-            bool exact = kt == 0;
+            bool exact = kt == kt0;
             if (!exact) {
                 const float ls = probs();
                 exact = __ballot(!(ls <= kPfRescaleSum)) != 0;
@@ -265,10 +389,10 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
                 mt = fmaxf(mt, s[1][15]);
                 mt = half_max(mt);
                 // first tile: set the reference; later tiles: move it only on a large jump
-                const bool move = kt == 0 ? true : mt > kPfRescale;
+                const bool move = kt == kt0 ? true : mt > kPfRescale;
                 if (__ballot(move)) {
                     const float shift = move ? mt : 0.f;
-                    const float alpha = kt == 0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+                    const float alpha = kt == kt0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -293,8 +417,60 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
                 for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * PV + 32 * j, 8 * PV), pb, o[j]);
             }
         }
-        if (kt + 1 < nkv) store(buf ^ 1);
+        if (kt + 1 < kt1) store(buf ^ 1);
         __syncthreads();
+    }
+
+    if (w.part >= 0) {
+        // Split tile: publish this part's state, then take a ticket; the part
+        // that draws the second ticket merges, the first one is done.  The
+        // state moves with agent-scope stores and loads, each coherent across
+        // the XCDs' L2 caches on its own, so no fence has to write back or
+        // invalidate a whole L2; the wait below makes the stores complete
+        // before the ticket is taken.
+        __shared__ int s_ticket;
+        typedef unsigned long long u64;
+        constexpr int NQ = D / 4;   // 8-byte words of output accumulators per thread
+        auto word = [&](int c) {    // accumulators 2c, 2c+1 of this thread
+            const f32x2 v = {o[(2 * c) >> 4][(2 * c) & 15], o[(2 * c) >> 4][(2 * c + 1) & 15]};
+            return __builtin_bit_cast(u64, v);
+        };
+        u64* mine = (u64*)(p.part + ((size_t)w.pair * 2 + w.part) * pf_part_floats<D>());
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+            __hip_atomic_store(mine + c * 256 + tid, word(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + NQ * 256 + tid, __builtin_bit_cast(u64, f32x2{m_ref, l_half}), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) s_ticket = __hip_atomic_fetch_add(p.ctr + w.pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if ((s_ticket & 1) == 0) return;
+        const u64* other = (const u64*)(p.part + ((size_t)w.pair * 2 + (w.part ^ 1)) * pf_part_floats<D>());
+        u64 ov[NQ + 1];
+#pragma unroll
+        for (int c = 0; c <= NQ; ++c)
+            ov[c] = __hip_atomic_load(other + c * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // part 0's term first, whichever part merges, so the result does not
+        // depend on which part finished last
+        const f32x2 ml = __builtin_bit_cast(f32x2, ov[NQ]);
+        const float m_o = ml[0], l_o = ml[1];
+        const float mm = fmaxf(m_ref, m_o);
+        const float a_me = __builtin_amdgcn_exp2f(m_ref - mm), a_o = __builtin_amdgcn_exp2f(m_o - mm);
+        const bool first = w.part == 0;
+        const float a0 = first ? a_me : a_o, a1 = first ? a_o : a_me;
+        l_half = fmaf(first ? l_half : l_o, a0, (first ? l_o : l_half) * a1);
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+            const f32x2 y = __builtin_bit_cast(f32x2, ov[c]);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int f = 2 * c + e;
+                const float x = o[f >> 4][f & 15];
+                o[f >> 4][f & 15] = fmaf(first ? x : y[e], a0, (first ? y[e] : x) * a1);
+            }
+        }
+        if (tid == 0) __hip_atomic_store(p.ctr + w.pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     if (!qvalid) return;
@@ -310,6 +486,12 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
             f32x4 v = {o[j][4 * g4] * inv, o[j][4 * g4 + 1] * inv, o[j][4 * g4 + 2] * inv, o[j][4 * g4 + 3] * inv};
             *(f32x4*)(dst + d) = v;
         }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_bf16_kernel(const PfParams p)
+{
+    pf_item_run<D>(p, pf_item_wave(p.sc, blockIdx.x, threadIdx.x & 63));
 }
 
 
@@ -411,23 +593,103 @@ int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, in
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// Causal query tiles that need more than this many key tiles are split in two
+// when a workspace is given ...
+constexpr int kPfSplitTiles = 32;
+// ... and the longest tile needs more key tiles than the average load of a
+// workgroup slot (3 resident workgroups on each of the 256 compute units);
+// otherwise longest-first order alone balances the launch.
+constexpr int kPfSlots = 3 * 256;
+
+// First split tile of a head: the split tiles are the suffix of tiles that
+// need more than kPfSplitTiles key tiles and whose first row sees the first
+// key of part 1 (so both parts start from a finite reference).
+static int pf_split_start(int nt, int kk, int T, int causal)
+{
+    if (!causal) return nt;
+    const int R = T * kk;
+    int i = nt;
+    while (i > 0) {
+        const int j = i - 1, n = pf_nkv(j, kk, R, T, causal);
+        const long long t0 = (long long)j * kPfBM / kk;
+        if (n > kPfSplitTiles && (long long)kPfBN * (n / 2) <= t0) i = j; else break;
+    }
+    return i;
+}
+
+static PfSched pf_sched(int B, int T, int G, int k, int n_shared, int causal, bool split)
+{
+    PfSched sc;
+    sc.B = B; sc.T = T; sc.G = G; sc.k = k; sc.n_shared = n_shared; sc.causal = causal;
+    sc.ntr = (T * k + kPfBM - 1) / kPfBM;
+    sc.nts = n_shared ? (T + kPfBM - 1) / kPfBM : 0;
+    if (split && causal) {
+        long long units = 0;   // key tiles over all query tiles
+        for (int i = 0; i < sc.ntr; ++i) units += (long long)pf_nkv(i, k, T * k, T, causal) * B * G;
+        for (int i = 0; i < sc.nts; ++i) units += (long long)pf_nkv(i, 1, T, T, causal) * B;
+        split = (long long)((T + kPfBN - 1) / kPfBN) * kPfSlots > units;
+    }
+    sc.isr = split ? pf_split_start(sc.ntr, k, T, causal) : sc.ntr;
+    sc.iss = split ? pf_split_start(sc.nts, 1, T, causal) : sc.nts;
+    sc.nkv_max = (T + kPfBN - 1) / kPfBN;
+    return sc;
+}
+
+static long long pf_pairs(const PfSched& sc)
+{
+    return (long long)(sc.ntr - sc.isr) * sc.B * sc.G + (long long)(sc.nts - sc.iss) * sc.B;
+}
+
+// One counter per split pair.
+static size_t pf_ctr_bytes(long long pairs) { return (size_t)((pairs * 4 + 255) / 256 * 256); }
+
+size_t prefill_workspace_bytes(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool bf16)
+{
+    if (!bf16 || (long long)B * T == 0) return 0;
+    const long long pairs = pf_pairs(pf_sched(B, T, G, k, n_shared, causal, true));
+    if (pairs == 0) return 0;
+    const int pf = d_head == 32 ? pf_part_floats<32>() : d_head == 64 ? pf_part_floats<64>() : pf_part_floats<128>();
+    return pf_ctr_bytes(pairs) + (size_t)pairs * 2 * pf * sizeof(float);
+}
+
+long long prefill_plan(int B, int T, int G, int k, int n_shared, int causal, bool split, int32_t* items,
+                       long long max_items)
+{
+    const PfSched sc = pf_sched(B, T, G, k, n_shared, causal, split);
+    const long long n = (long long)B * T == 0 ? 0 : pf_count_ge(sc, 1);
+    for (long long i = 0; items && i < n && i < max_items; ++i) {
+        const PfItem w = pf_item(sc, i);
+        const int32_t v[5] = {w.b, w.h, w.tile, w.part, w.pair};
+        for (int j = 0; j < 5; ++j) items[i * 5 + j] = v[j];
+    }
+    return n;
+}
+
 int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
 {
     const long long BT = (long long)a.B * a.T;
     if (BT == 0) return 0;
     if (a.bf16) {
-        const int ntr = (a.T * a.k + kPfBM - 1) / kPfBM;
-        const int nts = a.n_shared ? (a.T + kPfBM - 1) / kPfBM : 0;
-        const int grid = a.B * (a.G * ntr + nts);
-        const float qscale = 1.4426950408889634f / sqrtf((float)a.d_head);
-        const uint16_t* qr = (const uint16_t*)a.q_routed;
-        const uint16_t* qs = (const uint16_t*)a.q_shared;
-        const uint16_t* k = (const uint16_t*)a.kmat;
-        const uint16_t* v = (const uint16_t*)a.vmat;
+        const bool split = a.workspace != nullptr &&
+                           prefill_workspace_bytes(a.B, a.T, a.G, a.k, a.d_head, a.n_shared, a.causal, true) > 0;
+        PfParams prm;
+        prm.q_routed = (const uint16_t*)a.q_routed;
+        prm.q_shared = (const uint16_t*)a.q_shared;
+        prm.kg = (const uint16_t*)a.kmat;
+        prm.vg = (const uint16_t*)a.vmat;
+        prm.out = a.out;
+        prm.sc = pf_sched(a.B, a.T, a.G, a.k, a.n_shared, a.causal, split);
+        prm.ctr = split ? (int*)a.workspace : nullptr;
+        prm.part = split ? (float*)((char*)a.workspace + pf_ctr_bytes(pf_pairs(prm.sc))) : nullptr;
+        prm.S = a.S;
+        prm.qscale = 1.4426950408889634f / sqrtf((float)a.d_head);
+        const long long items = pf_count_ge(prm.sc, 1);
+        if (items >= (1ll << 31)) return -2;
+        const int grid = (int)items;
         switch (a.d_head) {
-        case 32: prefill_bf16_kernel<32><<<grid, 256, 0, st>>>(qr, qs, k, v, a.out, a.B, a.T, a.G, a.k, a.n_shared, a.causal, a.S, qscale); break;
-        case 64: prefill_bf16_kernel<64><<<grid, 256, 0, st>>>(qr, qs, k, v, a.out, a.B, a.T, a.G, a.k, a.n_shared, a.causal, a.S, qscale); break;
-        case 128: prefill_bf16_kernel<128><<<grid, 256, 0, st>>>(qr, qs, k, v, a.out, a.B, a.T, a.G, a.k, a.n_shared, a.causal, a.S, qscale); break;
+        case 32: prefill_bf16_kernel<32><<<grid, 256, 0, st>>>(prm); break;
+        case 64: prefill_bf16_kernel<64><<<grid, 256, 0, st>>>(prm); break;
+        case 128: prefill_bf16_kernel<128><<<grid, 256, 0, st>>>(prm); break;
         default: return -2;
         }
     } else {

@@ -66,8 +66,14 @@ int launch_status(int rc)
     return rc == 0 ? GQE_OK : GQE_ERR_LAUNCH;
 }
 
+size_t prefill_ws_bytes(const Shape& s)
+{
+    return gqe::prefill_workspace_bytes(s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.bf16);
+}
+
 int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
-                   const float* p_tilde, float* out, void* stream, bool assemble)
+                   const float* p_tilde, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                   bool assemble)
 {
     Shape s;
     GQE_TRY(check_desc(desc, s));
@@ -78,7 +84,9 @@ int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_sha
     GQE_TRY(need(v));
     if (assemble) GQE_TRY(need(p_tilde));
     GQE_TRY(need(out));
-    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out,
+    GQE_TRY(maybe(workspace));
+    if (workspace && workspace_bytes < prefill_ws_bytes(s)) return GQE_ERR_WORKSPACE;
+    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out, workspace,
                        s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
     return launch_status(assemble ? gqe::launch_prefill(a, (hipStream_t)stream)
                                   : gqe::launch_prefill_heads(a, (hipStream_t)stream));
@@ -159,16 +167,33 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
     return launch_status(gqe::launch_qproj(a, (hipStream_t)stream));
 }
 
-int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
-                     const float* p_tilde, float* out, void* stream)
+size_t gqe_attn_prefill_workspace_bytes(const gqe_desc* desc)
 {
-    return prefill_common(desc, q_routed, q_shared, k, v, p_tilde, out, stream, true);
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK) return 0;
+    return prefill_ws_bytes(s);
+}
+
+int64_t gqe_attn_prefill_plan(const gqe_desc* desc, int split, int32_t* items, int64_t max_items)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!s.bf16) return GQE_ERR_UNSUPPORTED;
+    if (max_items < 0) return GQE_ERR_INVALID;
+    return gqe::prefill_plan(s.B, s.T, s.G, s.k, s.ns, s.causal, split != 0 && prefill_ws_bytes(s) > 0, items,
+                             max_items);
+}
+
+int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
+                     const float* p_tilde, float* out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return prefill_common(desc, q_routed, q_shared, k, v, p_tilde, out, workspace, workspace_bytes, stream, true);
 }
 
 int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
-                           const void* v, float* out, void* stream)
+                           const void* v, float* out, void* workspace, size_t workspace_bytes, void* stream)
 {
-    return prefill_common(desc, q_routed, q_shared, k, v, nullptr, out, stream, false);
+    return prefill_common(desc, q_routed, q_shared, k, v, nullptr, out, workspace, workspace_bytes, stream, false);
 }
 
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream)

@@ -46,9 +46,15 @@ struct PrefillArgs {
     const void* vmat;
     const float* p_tilde;
     float* out;
+    void* workspace;   // NULL: no split tiles; else prefill_workspace_bytes() bytes, counters even
     int B, T, G, k, d_head, n_shared, causal, route_mode, S;
     bool bf16;
 };
+size_t prefill_workspace_bytes(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool bf16);
+// The launch's work items in launch order, 5 ints each (b, h, tile, part, pair);
+// returns their number and writes at most max_items of them.
+long long prefill_plan(int B, int T, int G, int k, int n_shared, int causal, bool split, int32_t* items,
+                       long long max_items);
 // Attention only: hard and shared slots of `out`; the weighted slots are not written.
 int launch_prefill_heads(const PrefillArgs& a, hipStream_t st);
 // Attention, then the weighted slots.

@@ -26,8 +26,8 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 
 # Every symbol the C header declares (checked by the host tests).
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
-           "gqe_attn_prefill", "gqe_attn_prefill_heads", "gqe_assemble", "gqe_decode_workspace_bytes",
-           "gqe_attn_decode")
+           "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
+           "gqe_attn_prefill_heads", "gqe_assemble", "gqe_decode_workspace_bytes", "gqe_attn_decode")
 
 
 class GqeError(RuntimeError):
@@ -93,9 +93,13 @@ def load():
         lib.gqe_route.restype = I
         lib.gqe_qproj.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.gqe_qproj.restype = I
-        lib.gqe_attn_prefill.argtypes = [D, P, P, P, P, P, P, P]
+        lib.gqe_attn_prefill_workspace_bytes.argtypes = [D]
+        lib.gqe_attn_prefill_workspace_bytes.restype = Z
+        lib.gqe_attn_prefill_plan.argtypes = [D, I, P, ctypes.c_int64]
+        lib.gqe_attn_prefill_plan.restype = ctypes.c_int64
+        lib.gqe_attn_prefill.argtypes = [D, P, P, P, P, P, P, P, Z, P]
         lib.gqe_attn_prefill.restype = I
-        lib.gqe_attn_prefill_heads.argtypes = [D, P, P, P, P, P, P]
+        lib.gqe_attn_prefill_heads.argtypes = [D, P, P, P, P, P, P, Z, P]
         lib.gqe_attn_prefill_heads.restype = I
         lib.gqe_assemble.argtypes = [D, P, P, P]
         lib.gqe_assemble.restype = I
@@ -165,19 +169,43 @@ def gqe_qproj(desc, x, w_q, sel, counts, offsets, rows, q_routed, q_shared, stre
     _check("gqe_qproj", rc)
 
 
-def gqe_attn_prefill(desc, q_routed, q_shared, k, v, p_tilde, out, stream=None):
+def gqe_attn_prefill_workspace_bytes(desc: GqeDesc) -> int:
+    return int(load().gqe_attn_prefill_workspace_bytes(ctypes.byref(desc)))
+
+
+def gqe_attn_prefill_plan(desc: GqeDesc, split: bool = True):
+    """Work items of one bf16 prefill attention launch: int32 array [n, 5] of
+    (b, head, query tile, part, pair) in launch order."""
+    import numpy as np
+    lib = load()
+    n = lib.gqe_attn_prefill_plan(ctypes.byref(desc), int(split), None, 0)
+    _check("gqe_attn_prefill_plan", min(int(n), 0))
+    items = np.zeros((max(int(n), 1), 5), dtype=np.int32)
+    lib.gqe_attn_prefill_plan(ctypes.byref(desc), int(split), items.ctypes.data_as(ctypes.c_void_p), int(n))
+    return items[: int(n)]
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def gqe_attn_prefill(desc, q_routed, q_shared, k, v, p_tilde, out, workspace=None, stream=None):
     dt = desc.torch_dtype
+    wp, wb = _ws(workspace)
     rc = load().gqe_attn_prefill(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
                                  _ptr(k, dt, "k"), _ptr(v, dt, "v"), _ptr(p_tilde, torch.float32, "p_tilde"),
-                                 _ptr(out, torch.float32, "out"), _stream(stream))
+                                 _ptr(out, torch.float32, "out"), wp, wb, _stream(stream))
     _check("gqe_attn_prefill", rc)
 
 
-def gqe_attn_prefill_heads(desc, q_routed, q_shared, k, v, out, stream=None):
+def gqe_attn_prefill_heads(desc, q_routed, q_shared, k, v, out, workspace=None, stream=None):
     dt = desc.torch_dtype
+    wp, wb = _ws(workspace)
     rc = load().gqe_attn_prefill_heads(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"),
                                        _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"), _ptr(v, dt, "v"),
-                                       _ptr(out, torch.float32, "out"), _stream(stream))
+                                       _ptr(out, torch.float32, "out"), wp, wb, _stream(stream))
     _check("gqe_attn_prefill_heads", rc)
 
 
@@ -230,10 +258,29 @@ def qproj(desc, x, w_q, r: dict, bufs=None, stream=None) -> dict:
     return q
 
 
-def attn_prefill(desc, q: dict, k, v, p_tilde, out=None, stream=None) -> torch.Tensor:
+_prefill_ws = {}
+
+
+def prefill_workspace(desc: GqeDesc, device) -> Optional[torch.Tensor]:
+    """A zeroed workspace for the prefill attention of `desc` on `device`, kept
+    and reused (each call leaves its counters at zero), or None if the shape
+    splits no query tile.  Calls that use it must not overlap in time."""
+    n = gqe_attn_prefill_workspace_bytes(desc)
+    if n == 0:
+        return None
+    dev = torch.device(device)
+    ws = _prefill_ws.get(dev)
+    if ws is None or ws.numel() < n:
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+        _prefill_ws[dev] = ws
+    return ws
+
+
+def attn_prefill(desc, q: dict, k, v, p_tilde, out=None, split=True, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty((desc.B, desc.T, desc.S, desc.d_head), dtype=torch.float32, device=k.device)
-    gqe_attn_prefill(desc, q["q_routed"], q["q_shared"], k, v, p_tilde, out, stream)
+    ws = prefill_workspace(desc, k.device) if split else None
+    gqe_attn_prefill(desc, q["q_routed"], q["q_shared"], k, v, p_tilde, out, ws, stream)
     return out
 
 

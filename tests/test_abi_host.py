@@ -23,13 +23,13 @@ MIS = P(0x10008)      # 8-byte aligned only
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "gqe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gqe_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|size_t|const char\*)\s+(gqe_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -97,13 +97,22 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert lib.gqe_qproj(by(d), None, A16, A16, A16, A16, A16, A16, A16, None) == INVALID
     assert lib.gqe_qproj(by(d), A16, A16, A16, A16, A16, A16, A16, None, None) == INVALID   # shared head needs q_shared
     assert lib.gqe_qproj(by(d), A16, MIS, A16, A16, A16, A16, A16, A16, None) == ALIGN
-    assert lib.gqe_attn_prefill(by(d), A16, A16, A16, None, A16, A16, None) == INVALID
-    assert lib.gqe_attn_prefill(by(main(d_head=48)), A16, A16, A16, A16, A16, A16, None) == UNSUPPORTED
-    assert lib.gqe_attn_prefill(by(d), A16, A16, A16, A16, A16, MIS, None) == ALIGN
-    assert lib.gqe_attn_prefill(by(d), A16, A16, A16, A16, None, A16, None) == INVALID     # p_tilde needed
-    assert lib.gqe_attn_prefill_heads(by(d), A16, None, A16, A16, A16, None) == INVALID    # shared head needs q_shared
-    assert lib.gqe_attn_prefill_heads(by(main(d_head=48)), A16, A16, A16, A16, A16, None) == UNSUPPORTED
-    assert lib.gqe_attn_prefill_heads(by(d), A16, A16, A16, A16, MIS, None) == ALIGN
+    pws = G.gqe_attn_prefill_workspace_bytes(d)
+    pf = lambda desc, q=A16, qs=A16, v=A16, pt=A16, out=A16, w=A16, wb=pws: lib.gqe_attn_prefill(  # noqa: E731
+        by(desc), q, qs, A16, v, pt, out, w, wb, None)
+    hd = lambda desc, qs=A16, out=A16, w=A16, wb=pws: lib.gqe_attn_prefill_heads(  # noqa: E731
+        by(desc), A16, qs, A16, A16, out, w, wb, None)
+    assert pf(d, v=None) == INVALID
+    assert pf(main(d_head=48)) == UNSUPPORTED
+    assert pf(d, out=MIS) == ALIGN
+    assert pf(d, pt=None) == INVALID                 # p_tilde needed
+    assert pf(d, w=MIS) == ALIGN
+    assert pf(d, wb=pws - 1) == WORKSPACE
+    assert hd(d, qs=None) == INVALID                 # shared head needs q_shared
+    assert hd(main(d_head=48)) == UNSUPPORTED
+    assert hd(d, out=MIS) == ALIGN
+    assert hd(d, w=MIS) == ALIGN
+    assert hd(d, wb=0) == WORKSPACE
     assert lib.gqe_assemble(by(d), None, A16, None) == INVALID
     assert lib.gqe_assemble(by(d), A16, MIS, None) == ALIGN
     assert lib.gqe_assemble(by(main(H_q=15)), A16, A16, None) == INVALID
@@ -125,3 +134,83 @@ def test_python_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         G.gqe_route(d, torch.zeros(4, 64), torch.zeros(4, 64), None, torch.zeros(4, 2, 1, dtype=torch.int32),
                     None, None, None, None, None, None)
+
+
+# ------------------------------------------------------------- prefill schedule
+
+def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=768):
+    """Work items of the prefill attention launch, written out directly: every
+    query tile of 128 rows, cut in two when it is causal, needs more than 32 key
+    tiles of 64 and its first row sees key 64*(nkv//2), provided the longest
+    tile needs more key tiles than the average load of 768 workgroup slots;
+    sorted by item size (larger part), routed before shared, split before
+    whole, tile descending."""
+    def nkv_of(i, kk):
+        if not causal:
+            return -(-T // 64)
+        return (min(T * kk - 1, 128 * (i + 1) - 1) // kk) // 64 + 1
+    units = sum(nkv_of(i, k) * B * G_ for i in range(-(-T * k // 128)))
+    units += sum(nkv_of(i, 1) * B for i in range(-(-T // 128))) if n_shared else 0
+    split = split and causal and -(-T // 64) * slots > units
+    items = []
+    n_pairs_r = 0
+    for lst, (kk, heads) in enumerate(((k, [(b, g) for b in range(B) for g in range(G_)]),
+                                       (1, [(b, G_) for b in range(B)] if n_shared else []))):
+        R = T * kk
+        nt = -(-R // 128)
+        def nkv(i):
+            if not causal:
+                return -(-T // 64)
+            return (min(R - 1, 128 * (i + 1) - 1) // kk) // 64 + 1
+        def can(i):
+            return causal and nkv(i) > split_tiles and 64 * (nkv(i) // 2) <= (128 * i) // kk
+        first_split = nt
+        while split and first_split > 0 and can(first_split - 1):
+            first_split -= 1
+        for i in range(nt):
+            n = nkv(i)
+            for hi, (b, h) in enumerate(heads):
+                if i >= first_split:
+                    pair = (n_pairs_r if lst else 0) + (i - first_split) * len(heads) + hi
+                    for slot in (0, 1):   # the halves of every other pair come in the opposite order
+                        part = slot ^ (hi & 1)
+                        items.append(((-(n - n // 2), lst, 0, -i, hi, slot), (b, h, i, part, pair)))
+                else:
+                    items.append(((-n, lst, 1, -i, hi, 0), (b, h, i, -1, -1)))
+        if lst == 0:
+            n_pairs_r = (nt - first_split) * len(heads)
+    items.sort()
+    return [it for _, it in items]
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=4, T=4096, k=1, n_shared=1, causal=1),     # the 250M-model shape
+    dict(B=1, T=32768, k=1, n_shared=1, causal=1),    # long: longest-first order is enough, nothing split
+    dict(B=2, T=4000, k=3, n_shared=1, causal=1),     # ragged rows, three kept experts
+    dict(B=1, T=8192, k=2, n_shared=0, causal=1),
+    dict(B=3, T=2100, k=1, n_shared=1, causal=0),     # non-causal: nothing split
+    dict(B=2, T=300, k=2, n_shared=1, causal=1),      # short: nothing split
+    dict(B=1, T=1, k=1, n_shared=1, causal=1),
+])
+def test_prefill_plan_matches_its_definition(shape):
+    d = main(B=shape["B"], T=shape["T"], k=shape["k"], H_q=8 * max(2, shape["k"]), n_shared=shape["n_shared"],
+             causal=shape["causal"])
+    for split in (False, True):
+        got = [tuple(int(x) for x in r) for r in G.gqe_attn_prefill_plan(d, split)]
+        want = plan_reference(shape["B"], shape["T"], 8, shape["k"], shape["n_shared"], shape["causal"], split)
+        assert got == want, (split, len(got), len(want))
+    plan = G.gqe_attn_prefill_plan(d, True)
+    pairs = sorted((int(r[4]), int(r[3])) for r in plan if r[3] >= 0)
+    n_pairs = len(pairs) // 2
+    assert pairs == [(p, part) for p in range(n_pairs) for part in (0, 1)]
+    want_bytes = 0 if n_pairs == 0 else -(-n_pairs * 4 // 256) * 256 + n_pairs * 2 * 256 * (64 // 2 + 2) * 4
+    assert G.gqe_attn_prefill_workspace_bytes(d) == want_bytes
+
+
+def test_prefill_workspace_only_for_split_shapes():
+    assert G.gqe_attn_prefill_workspace_bytes(main()) > 0
+    assert G.gqe_attn_prefill_workspace_bytes(main(causal=0)) == 0
+    assert G.gqe_attn_prefill_workspace_bytes(main(T=2048)) == 0           # at most 32 key tiles
+    assert G.gqe_attn_prefill_workspace_bytes(main(B=1, T=32768)) == 0     # balanced without splitting
+    assert G.gqe_attn_prefill_workspace_bytes(main(dtype="f32")) == 0
+    assert G.load().gqe_attn_prefill_plan(ctypes.byref(main(dtype="f32")), 1, None, 0) == UNSUPPORTED

@@ -128,19 +128,68 @@ def test_route_compaction_both_paths(BT, H_q, k):
     check_route(w, inp, {key: (v.cpu() if isinstance(v, torch.Tensor) else v) for key, v in r.items()})
 
 
-@pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(dtype="f32", d_head=32)],
-                         ids=lambda w: f"{w.name}-{w.dtype}")
-def test_heads_then_assemble_equals_attn_prefill(w):
-    """gqe_attn_prefill_heads + gqe_assemble give exactly gqe_attn_prefill's output."""
+# ---------------------------------------------------------------- split query tiles
+
+SPLIT = [
+    small(B=1, T=2500, name="split_k2"),                # E = 4, k = 2: 5000 routed rows per head, ragged tail
+    small(B=2, T=2200, H_q=4, H_kv=2, k=1, d_head=32, name="split_d32"),
+    small(B=1, T=2300, H_q=4, H_kv=4, k=1, d_head=128, route_mode=1, name="split_d128_mode1"),
+    small(B=1, T=3000, k=3, H_q=8, H_kv=2, n_shared=0, name="split_k3_noshared"),
+]
+
+
+@pytest.mark.parametrize("w", SPLIT, ids=lambda w: w.name)
+def test_split_tiles_every_token(w):
+    """Query tiles whose key range is cut in two and merged by the later half, on every token."""
+    d = G.desc_from(w)
+    plan = G.gqe_attn_prefill_plan(d, True)
+    assert G.gqe_attn_prefill_workspace_bytes(d) > 0 and (plan[:, 3] >= 0).any()
+    full_prefill_check(w)
+
+
+def prefill_inputs_on_gpu(w):
     inp = W.make_inputs(w)
     d = G.desc_from(w)
     di = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     x = di["x"].reshape(-1, w.d_model)
     r = G.route(d, x, di["w_router"], di["b_router"])
     q = G.qproj(d, x, di["w_q"], r)
+    return d, di, r, q
+
+
+def test_split_merge_is_deterministic_and_resets_its_counters():
+    w = SPLIT[0]
+    d, di, r, q = prefill_inputs_on_gpu(w)
+    n_pairs = int((G.gqe_attn_prefill_plan(d, True)[:, 3] >= 0).sum()) // 2
+    ws = torch.zeros(G.gqe_attn_prefill_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    ctr = ws[: n_pairs * 4].view(torch.int32)              # one counter per split pair
+    run = lambda w_: G.attn_prefill(d, q, di["k"], di["v"], r["p_tilde"], split=False) if w_ is None else (  # noqa
+        G.gqe_attn_prefill(d, q["q_routed"], q["q_shared"], di["k"], di["v"], r["p_tilde"], out, w_))
+    out = torch.empty((w.B, w.T, d.S, w.d_head), dtype=torch.float32, device="cuda")
+    run(ws)
+    a = out.clone()
+    torch.cuda.synchronize()
+    assert (ctr == 0).all(), "counters not reset"
+    ctr.copy_(2 * torch.arange(n_pairs, dtype=torch.int32, device="cuda"))   # any even start works
+    run(ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a), "split result depends on the run"
+    assert (ctr == 0).all()
+    whole = run(None)
+    torch.cuda.synchronize()
+    err = (whole - a).abs()
+    say(f"[{w.name}] split vs whole: max-abs={float(err.max()):.3e} mean-abs={float(err.mean()):.3e}")
+    assert float(err.max()) <= 1e-2 and float(err.mean()) <= 1e-4
+
+
+@pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(dtype="f32", d_head=32),
+                               SPLIT[0]], ids=lambda w: f"{w.name}-{w.dtype}")
+def test_heads_then_assemble_equals_attn_prefill(w):
+    """gqe_attn_prefill_heads + gqe_assemble give exactly gqe_attn_prefill's output (same workspace)."""
+    d, di, r, q = prefill_inputs_on_gpu(w)
     ref = G.attn_prefill(d, q, di["k"], di["v"], r["p_tilde"])
     out = torch.full_like(ref, float("nan"))
-    G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out)
+    G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out, G.prefill_workspace(d, "cuda"))
     kG = w.k * w.G
     n_w = w.G if w.route_mode else 1
     torch.cuda.synchronize()
@@ -150,9 +199,11 @@ def test_heads_then_assemble_equals_attn_prefill(w):
     assert torch.equal(out, ref)
 
 
-def test_graph_replay_matches_eager():
-    """The four prefill calls captured into a HIP graph give the eager results on every replay."""
-    w = small(B=2, T=700, k=1, name="graph")
+@pytest.mark.parametrize("T", [700, 2500])
+def test_graph_replay_matches_eager(T):
+    """The four prefill calls captured into a HIP graph give the eager results on every replay
+    (T = 2500 splits its longest query tiles: the merge counters reset themselves)."""
+    w = small(B=2, T=T, k=1, name="graph")
     inp = W.make_inputs(w)
     d = G.desc_from(w)
     di = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
@@ -160,12 +211,14 @@ def test_graph_replay_matches_eager():
     r = G.alloc_route(d, x.device)
     q = G.alloc_qproj(d, x.device)
     out = torch.empty((w.B, w.T, d.S, w.d_head), dtype=torch.float32, device=x.device)
+    ws = G.prefill_workspace(d, x.device)
+    assert (ws is not None) == (T > 2176)
 
     def step():
         G.gqe_route(d, x, di["w_router"], di["b_router"], r["sel"], r["p_tilde"], r["counts"], r["offsets"],
                     r["rows"], None, r["workspace"])
         G.gqe_qproj(d, x, di["w_q"], r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"], q["q_shared"])
-        G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out)
+        G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out, ws)
         G.gqe_assemble(d, r["p_tilde"], out)
 
     step()
