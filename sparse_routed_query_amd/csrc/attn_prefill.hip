@@ -354,23 +354,26 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                     for (int r = 0; r < 16; ++r)
                         s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
             }
-            // P = exp2(S - m_ref), packed to bf16; the row sum uses the rounded values.
+            // P = exp2(S - m_ref), packed to bf16 for the PV product.  The row sum
+            // adds the fp32 values with plain adds (v_dot2 on the packed values
+            // does not run alongside other waves' MFMAs; adds do).
             // If no lane's partial row sum exceeds 2^8, no probability does, so the
             // reference stays and the row max is never computed.  The first tile,
             // and any tile whose sum trips that check, take the exact path: row
             // max, move the reference if it jumped by more than 2^8, recompute.
             uint32_t pw[16];
-            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
             auto probs = [&]() {
-                float ls = 0.f;
+                float la = 0.f, lb = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2)
-                        pw[kb * 8 + r / 2] = pk_bf16(__builtin_amdgcn_exp2f(s[kb][r]), __builtin_amdgcn_exp2f(s[kb][r + 1]));
-#pragma unroll
-                for (int i = 0; i < 16; ++i) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[i]), ones, ls, false);
-                return ls;
+                    for (int r = 0; r < 16; r += 2) {
+                        const float e0 = __builtin_amdgcn_exp2f(s[kb][r]), e1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
+                        pw[kb * 8 + r / 2] = pk_bf16(e0, e1);
+                        la += e0;
+                        lb += e1;
+                    }
+                return la + lb;
             };
             bool exact = kt == kt0;
             if (!exact) {
@@ -488,8 +491,10 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         }
 }
 
+// At most 168 VGPRs for d <= 64 keeps three waves on each SIMD (the LDS of
+// three workgroups fits a compute unit); d = 128 runs two.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(const PfParams p)
+__global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void prefill_bf16_kernel(const PfParams p)
 {
     pf_item_run<D>(p, pf_item_wave(p.sc, blockIdx.x, threadIdx.x & 63));
 }
