@@ -265,8 +265,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     // V rows get 32 elements of padding: the transposing reads are then free of
     // bank conflicts (16 for K rows, read with 16-byte loads).
     constexpr int PV = D + 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPfBN * P];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPfBN * PV];
+    constexpr int KVSZ = kPfBN * (P + PV);   // one stage: K rows, then V rows
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * KVSZ];
 
     // Q loads (rows past R read row R-1 and are zeroed) are issued together
     // with the first K/V tile's, so the prologue waits for memory once
@@ -278,23 +278,32 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     }
 
     u32x4 rk[NCH], rv[NCH];
-    // Keys past T are loaded from row T-1 instead: their scores are masked, so
-    // their probabilities are exactly 0 and the (finite) values never count.
+    // Thread tid moves 16-byte chunks tid + 256 i of a tile: key row
+    // srow + i * RPP, elements scol .. scol + 7.  A tile is contiguous in
+    // memory, so its chunks sit at tid * 8 + i * 256 * 8 from the tile start.
+    constexpr int RPP = 256 / (D / 8);       // key rows per 256 chunks
+    const int srow = tid / (D / 8), scol = (tid % (D / 8)) * 8;
+    // Buffer loads: the resource starts at the tile and covers the rest of the
+    // head, so rows past T fall outside it and read as zero (their scores are
+    // masked, so their probabilities are exactly 0).
     auto load = [&](int kt) {
+        const int p0 = kt * kPfBN;
+        const int bytes = (T - p0) * D * 2;
+        const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)(K + (size_t)p0 * D), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)p0 * D), 0, bytes, 0x00020000);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * 256, s = c / (D / 8), d0 = (c % (D / 8)) * 8;
-            const int pos = min(kt * kPfBN + s, T - 1);
-            rk[i] = ld_u32x4(K + (size_t)pos * D + d0);
-            rv[i] = ld_u32x4(V + (size_t)pos * D + d0);
+            rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, tid * 16 + i * 4096, 0, 0));
+            rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, tid * 16 + i * 4096, 0, 0));
         }
     };
+    const int k_st = srow * P + scol, v_st = kPfBN * P + srow * PV + scol;   // store offsets in a stage
     auto store = [&](int buf) {
+        uint16_t* stage = sKV + buf * KVSZ;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            const int c = tid + i * 256, s = c / (D / 8), d0 = (c % (D / 8)) * 8;
-            *(u32x4*)&sK[buf][s * P + d0] = rk[i];
-            *(u32x4*)&sV[buf][s * PV + d0] = rv[i];
+            *(u32x4*)(stage + k_st + i * RPP * P) = rk[i];
+            *(u32x4*)(stage + v_st + i * RPP * PV) = rv[i];
         }
     };
     // per-lane parts of the LDS addresses
@@ -333,8 +342,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         const int buf = (kt - kt0) & 1;
         if (kt + 1 < kt1) load(kt + 1);
         if (kt < nkv_w) {
-            const uint16_t* bK = sK[buf];
-            const uint16_t* bV = sV[buf];
+            const uint16_t* bK = sKV + buf * KVSZ;
+            const uint16_t* bV = bK + kPfBN * P;
             // S^T - m_ref = K Q^T + cneg for two 32-key blocks
             f32x16 s[2];
 #pragma unroll
