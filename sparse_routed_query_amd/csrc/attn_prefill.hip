@@ -247,7 +247,9 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     const uint16_t* V = vg + ((size_t)w.b * G + kvh) * (size_t)T * D;
     const int slot0 = shared ? S - 1 : w.h * k;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform, so that the per-wave tile limits and mask tests stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lh = lane >> 5;
     const int r0 = w.tile * kPfBM;
     const int nkv = pf_nkv(w.tile, kk, R, T, causal);
@@ -259,8 +261,11 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     const bool qvalid = qrow < R;
     const int tq = qvalid ? qrow / kk : T - 1;   // rows past R see every key, so they stay finite
     const int wrow_hi = min(R - 1, r0 + wave * 32 + 31);
-    const int nkv_w = causal ? (wrow_hi / kk) / kPfBN + 1 : nkv;
-    const int t_lo_w = (r0 + wave * 32) / kk;
+    const int nkv_w = __builtin_amdgcn_readfirstlane(causal ? (wrow_hi / kk) / kPfBN + 1 : nkv);
+    const int t_lo_w = __builtin_amdgcn_readfirstlane((r0 + wave * 32) / kk);
+    // key tiles starting after this position need a mask: some key is past
+    // the wave's first row (causal) or past T
+    const int mask_after = causal ? t_lo_w - kPfBN + 1 : T - kPfBN;
 
     // V rows get 32 elements of padding: the transposing reads are then free of
     // bank conflicts (16 for K rows, read with 16-byte loads).
@@ -353,7 +358,7 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                 for (int c = 1; c < D / 16; ++c) s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P + 16 * c), qf[c], s[kb]);
             }
             const int s0 = kt * kPfBN;
-            const bool need_mask = causal ? (s0 + kPfBN - 1 > t_lo_w) : (s0 + kPfBN > T);
+            const bool need_mask = s0 > mask_after;
             if (need_mask) {
                 // key of element r in block kb is s0 + 4*lh + (kb*32 + 8*(r/4) + r%4)
                 const int lim = (causal ? tq : T - 1) - s0 - 4 * lh;
