@@ -51,7 +51,8 @@ __host__ __device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int 
 // (routed) and i >= iss (shared) are split: part 0 takes key tiles [0, h),
 // part 1 [h, nkv), h = nkv / 2.  Work items are ordered by decreasing size
 // (key tiles of the item; for a split tile, the larger part), then routed
-// before shared, split before whole, and by decreasing tile index.
+// before shared, split before whole, by decreasing tile index, and split
+// tiles by part, then head.
 struct PfSched {
     int B, T, G, k, n_shared, causal;
     int ntr, nts;   // query tiles per routed / shared head
@@ -117,12 +118,13 @@ __host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, lon
             if (id < n) {
                 const int i = e - 1 - (int)(id / per);
                 const int rem = (int)(id % per);
-                const int bh = sp ? rem >> 1 : rem;
+                // split tiles come part-major (all part 0s, then all part 1s):
+                // workgroup j runs on XCD j mod 8, so with cnt a multiple of 8
+                // both halves and the whole tiles of a head keep to the same
+                // XCDs, whose L2 then serves the head's K/V to all of them
+                const int bh = sp ? rem % (int)cnt : rem;
                 w.tile = i;
-                // the two halves of a pair go to neighbouring workgroups, which the
-                // hardware hands to different XCDs; alternate their order so that
-                // part 1 (the diagonal tiles) does not always land on the same XCDs
-                w.part = sp ? (rem ^ (rem >> 1)) & 1 : -1;
+                w.part = sp ? rem / (int)cnt : -1;
                 if (l == 0) {
                     w.b = bh / p.G; w.h = bh % p.G;
                 } else {

@@ -144,7 +144,7 @@ def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=7
     tiles of 64 and its first row sees key 64*(nkv//2), provided the longest
     tile needs more key tiles than the average load of 768 workgroup slots;
     sorted by item size (larger part), routed before shared, split before
-    whole, tile descending."""
+    whole, tile descending, split tiles by part then head."""
     def nkv_of(i, kk):
         if not causal:
             return -(-T // 64)
@@ -172,9 +172,8 @@ def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=7
             for hi, (b, h) in enumerate(heads):
                 if i >= first_split:
                     pair = (n_pairs_r if lst else 0) + (i - first_split) * len(heads) + hi
-                    for slot in (0, 1):   # the halves of every other pair come in the opposite order
-                        part = slot ^ (hi & 1)
-                        items.append(((-(n - n // 2), lst, 0, -i, hi, slot), (b, h, i, part, pair)))
+                    for part in (0, 1):   # part-major: all part 0s of a tile, then all part 1s
+                        items.append(((-(n - n // 2), lst, 0, -i, part, hi), (b, h, i, part, pair)))
                 else:
                     items.append(((-n, lst, 1, -i, hi, 0), (b, h, i, -1, -1)))
         if lst == 0:
