@@ -47,7 +47,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the GPU needs ~30 ms of load to reach its steady clock")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-context", action="store_true", help="skip the long-context GQE vs dense leg")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
@@ -101,6 +102,20 @@ class Prefill:
         self.qproj()
         self.attn()
         self.assemble()
+
+
+def warm(fns, torch, ms=30.0, min_calls=3):
+    """Run the calls until at least `ms` of wall time has passed: the first
+    tens of milliseconds of load run at a lower clock than the steady state."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < min_calls or (time.perf_counter() - t0) * 1e3 < ms:
+        for fn in fns:
+            fn()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def time_calls(fn_list, n, torch):
@@ -201,9 +216,7 @@ def decode_leg(torch, dev, steps):
         it[0] += 1
         G.gqe_attn_decode(d, q["q_routed"], q["q_shared"], kc, vc, lens, r["p_tilde"], out, ws)
 
-    for _ in range(3):
-        route(); qp(); attn()
-    torch.cuda.synchronize()
+    warm([route, qp, attn], torch)
     t_route, t_qp, t_attn = time_calls([route, qp, attn], steps, torch)
     nbytes = W.decode_kv_bytes(w, inp["lens"])
     gbs = nbytes / (t_attn * 1e-3) / 1e9
@@ -212,7 +225,7 @@ def decode_leg(torch, dev, steps):
             "route_us": t_route * 1e3, "qproj_us": t_qp * 1e3,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),
-                         "algorithmic_bytes": nbytes, "kernel": "gqe_attn_decode (split + combine)"}}
+                         "algorithmic_bytes": nbytes, "kernel": "gqe_attn_decode (split KV chunks + merge)"}}
 
 
 def long_context_leg(torch, dev, steps):
@@ -222,9 +235,7 @@ def long_context_leg(torch, dev, steps):
     res = {}
     for name, ww in (("gqe", w), ("dense", W.dense_variant(w))):
         p = Prefill(ww, inp, dev)
-        for _ in range(2):
-            p.step()
-        torch.cuda.synchronize()
+        warm([p.step], torch)
         t_route, t_qp, t_attn, t_asm = time_calls([p.route, p.qproj, p.attn, p.assemble], steps, torch)
         fl = W.attention_flops(ww)
         res[name] = {"attn_ms": t_attn, "step_ms": t_route + t_qp + t_attn + t_asm,
