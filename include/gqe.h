@@ -120,9 +120,13 @@ int gqe_route(const gqe_desc* desc, const void* x, const void* w_router, const f
  *   q_shared[b, t, :]       = W_q[N] x[b,t,:]                  (if n_shared)
  *
  * In:  x [BT, d_model]; w_q [N + n_shared, d_head, d_model] (dtype);
- *      sel, counts, offsets, rows as produced by gqe_route.
+ *      sel, counts, offsets, rows as produced by gqe_route (only read, and only
+ *      required, when q_routed is given).
  * Out: q_routed [B, G, T, k, d_head] (dtype; bf16 rounds to nearest even from
- *      an fp32 accumulator), q_shared [B, T, d_head] or NULL when n_shared = 0.
+ *      an fp32 accumulator), q_shared [B, T, d_head].
+ * Either output may be NULL: that part is then not computed by this call (with
+ * n_shared = 0 q_shared is ignored).  The shared head needs no routing, so a
+ * caller can project it on a second stream while gqe_route runs.
  * Within one (b, g) the routed queries form a dense [T*k, d_head] matrix whose
  * row r belongs to position r / k.
  */
@@ -148,7 +152,9 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
  * Layout: one int32 counter per split tile (padded to 256 bytes), then the
  * partial states.  The counters must hold even values (zero) before the first
  * call with a buffer -- allocate it zeroed once -- and every completed call
- * leaves them at zero.  Calls that share a workspace must not overlap.
+ * leaves them at zero.  Calls that share a workspace must not overlap, except
+ * a routed-only and a shared-only call of the same shape (see
+ * gqe_attn_prefill_heads).
  */
 size_t gqe_attn_prefill_workspace_bytes(const gqe_desc* desc);
 
@@ -176,8 +182,9 @@ int64_t gqe_attn_prefill_plan(const gqe_desc* desc, int split, int32_t* items, i
  *   mode 1: out[b,t,kG+g] = sum_j p~[t,g,j] o(g,j)
  *   out[b,t,S-1] = o of the shared row against KV head 0       (§3-2 (5))
  *
- * In:  q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] or NULL,
- *      k, v [B, H_kv, T, d_head] (dtype), p_tilde [BT, G, k] fp32.
+ * In:  q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] or NULL (the
+ *      shared slot is then not written), k, v [B, H_kv, T, d_head] (dtype),
+ *      p_tilde [BT, G, k] fp32.
  * Out: out [B, T, S, d_head] fp32.
  * Workspace: NULL (no split tiles) or gqe_attn_prefill_workspace_bytes(desc)
  *      bytes of device memory prepared as described there; a smaller size
@@ -196,7 +203,10 @@ int gqe_attn_prefill(const gqe_desc* desc, const void* q_routed, const void* q_s
  * of `out` are left as they were.  Together with gqe_assemble it computes
  * exactly what gqe_attn_prefill computes with the same workspace choice
  * (bitwise).
- * In/Out/Workspace: as gqe_attn_prefill, without p_tilde.
+ * In/Out/Workspace: as gqe_attn_prefill, without p_tilde; here q_routed may be
+ * NULL too.  A call with only q_routed and one with only q_shared compute
+ * exactly what one call with both computes, and may run at the same time on
+ * two streams with one workspace (their split tiles use disjoint parts of it).
  */
 int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const void* q_shared,
                            const void* k, const void* v, float* out, void* workspace,

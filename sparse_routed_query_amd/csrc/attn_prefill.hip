@@ -58,7 +58,14 @@ struct PfSched {
     int ntr, nts;   // query tiles per routed / shared head
     int isr, iss;   // first split tile (== ntr / nts: none)
     int nkv_max;    // key tiles of the longest tile
+    int routed, shared;   // which heads this launch computes (the split and the
+                          // pair numbering always follow the whole shape)
 };
+
+__host__ __device__ __forceinline__ long long pf_heads(const PfSched& p, int l)
+{
+    return l ? ((p.n_shared && p.shared) ? p.B : 0) : (p.routed ? (long long)p.B * p.G : 0);
+}
 struct PfItem {
     int b, h, tile;   // h == G means the shared head
     int part;         // -1: whole tile; 0, 1: first / second half of its keys
@@ -84,7 +91,7 @@ __host__ __device__ __forceinline__ long long pf_count_ge(const PfSched& p, int 
 #pragma unroll
     for (int l = 0; l < 2; ++l) {
         const int kk = l ? 1 : p.k, nt = l ? p.nts : p.ntr, is = l ? p.iss : p.isr;
-        const long long cnt = l ? (p.n_shared ? p.B : 0) : (long long)p.B * p.G;
+        const long long cnt = pf_heads(p, l);
         const int R = p.T * kk;
         const int whole = max(0, is - pf_first_ge(s, kk, R, nt, p.T, p.causal));
         const int split = max(0, nt - max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal)));
@@ -101,7 +108,7 @@ __host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, lon
     PfItem w{0, 0, 0, -1, -1};
     for (int l = 0; l < 2; ++l) {
         const int kk = l ? 1 : p.k, nt = l ? p.nts : p.ntr, is = l ? p.iss : p.isr;
-        const long long cnt = l ? (p.n_shared ? p.B : 0) : (long long)p.B * p.G;
+        const long long cnt = pf_heads(p, l);
         const int R = p.T * kk;
         for (int sp = 1; sp >= 0; --sp) {
             // tiles of this group whose item size is exactly s: [a, e)
@@ -533,12 +540,14 @@ __global__ __launch_bounds__(128) void prefill_f32_kernel(const float* __restric
     const float* q;
     int h, slot, t;
     if (r < (long long)G * Rr) {
+        if (!q_routed) return;
         h = (int)(r / Rr);
         const int rr = (int)(r % Rr);
         t = rr / k;
         slot = h * k + rr % k;
         q = q_routed + (((size_t)b * G + h) * Rr + rr) * D;
     } else {
+        if (!q_shared) return;
         h = 0; t = (int)(r - (long long)G * Rr);
         slot = S - 1;
         q = q_shared + ((size_t)b * T + t) * D;
@@ -638,10 +647,12 @@ static int pf_split_start(int nt, int kk, int T, int causal)
     return i;
 }
 
-static PfSched pf_sched(int B, int T, int G, int k, int n_shared, int causal, bool split)
+static PfSched pf_sched(int B, int T, int G, int k, int n_shared, int causal, bool split, bool routed = true,
+                        bool shared = true)
 {
     PfSched sc;
     sc.B = B; sc.T = T; sc.G = G; sc.k = k; sc.n_shared = n_shared; sc.causal = causal;
+    sc.routed = routed; sc.shared = shared;
     sc.ntr = (T * k + kPfBM - 1) / kPfBM;
     sc.nts = n_shared ? (T + kPfBM - 1) / kPfBM : 0;
     if (split && causal) {
@@ -699,13 +710,15 @@ int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
         prm.kg = (const uint16_t*)a.kmat;
         prm.vg = (const uint16_t*)a.vmat;
         prm.out = a.out;
-        prm.sc = pf_sched(a.B, a.T, a.G, a.k, a.n_shared, a.causal, split);
+        prm.sc = pf_sched(a.B, a.T, a.G, a.k, a.n_shared, a.causal, split, a.q_routed != nullptr,
+                          a.q_shared != nullptr);
         prm.ctr = split ? (int*)a.workspace : nullptr;
         prm.part = split ? (float*)((char*)a.workspace + pf_ctr_bytes(pf_pairs(prm.sc))) : nullptr;
         prm.S = a.S;
         prm.qscale = 1.4426950408889634f / sqrtf((float)a.d_head);
         const long long items = pf_count_ge(prm.sc, 1);
         if (items >= (1ll << 31)) return -2;
+        if (items == 0) return 0;
         const int grid = (int)items;
         switch (a.d_head) {
         case 32: prefill_bf16_kernel<32><<<grid, 256, 0, st>>>(prm); break;

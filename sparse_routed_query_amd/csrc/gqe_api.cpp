@@ -78,15 +78,20 @@ int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_sha
     Shape s;
     GQE_TRY(check_desc(desc, s));
     if (s.BT == 0) return GQE_OK;
-    GQE_TRY(need(q_routed));
-    if (s.ns) GQE_TRY(need(q_shared));
+    // a NULL q_routed / q_shared leaves that part out of this call; the
+    // weighted slots need the routed hard slots
+    if (assemble) GQE_TRY(need(q_routed));
+    GQE_TRY(maybe(q_routed));
+    GQE_TRY(maybe(q_shared));
+    const bool shared = s.ns && q_shared;
+    if (!q_routed && !shared) return GQE_OK;
     GQE_TRY(need(k));
     GQE_TRY(need(v));
     if (assemble) GQE_TRY(need(p_tilde));
     GQE_TRY(need(out));
     GQE_TRY(maybe(workspace));
     if (workspace && workspace_bytes < prefill_ws_bytes(s)) return GQE_ERR_WORKSPACE;
-    gqe::PrefillArgs a{q_routed, q_shared, k, v, p_tilde, out, workspace,
+    gqe::PrefillArgs a{q_routed, shared ? q_shared : nullptr, k, v, p_tilde, out, workspace,
                        s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
     return launch_status(assemble ? gqe::launch_prefill(a, (hipStream_t)stream)
                                   : gqe::launch_prefill_heads(a, (hipStream_t)stream));
@@ -154,15 +159,20 @@ int gqe_qproj(const gqe_desc* desc, const void* x, const void* w_q, const int32_
     Shape s;
     GQE_TRY(check_desc(desc, s));
     if (s.BT == 0) return GQE_OK;
+    // a NULL q_routed / q_shared leaves that part out of this call
+    GQE_TRY(maybe(q_routed));
+    GQE_TRY(maybe(q_shared));
+    const bool shared = s.ns && q_shared;
+    if (!q_routed && !shared) return GQE_OK;
     GQE_TRY(need(x));
     GQE_TRY(need(w_q));
-    GQE_TRY(need(sel));
-    GQE_TRY(need(counts));
-    GQE_TRY(need(offsets));
-    GQE_TRY(need(rows));
-    GQE_TRY(need(q_routed));
-    if (s.ns) GQE_TRY(need(q_shared));
-    gqe::QprojArgs a{x, w_q, sel, counts, offsets, rows, q_routed, q_shared,
+    if (q_routed) {
+        GQE_TRY(need(sel));
+        GQE_TRY(need(counts));
+        GQE_TRY(need(offsets));
+        GQE_TRY(need(rows));
+    }
+    gqe::QprojArgs a{x, w_q, sel, counts, offsets, rows, q_routed, shared ? q_shared : nullptr,
                      s.B, s.T, s.dm, s.G, s.E, s.k, s.D, s.ns, s.bf16};
     return launch_status(gqe::launch_qproj(a, (hipStream_t)stream));
 }

@@ -32,16 +32,16 @@ struct QprojArgs {
     const int32_t* counts;
     const int32_t* offsets;
     const int32_t* rows;
-    void* q_routed;
-    void* q_shared;
+    void* q_routed;   // NULL: the routed experts are not projected by this call
+    void* q_shared;   // NULL: the shared head is not projected by this call
     int B, T, d_model, G, E, k, d_head, n_shared;
     bool bf16;
 };
 int launch_qproj(const QprojArgs& a, hipStream_t st);
 
 struct PrefillArgs {
-    const void* q_routed;
-    const void* q_shared;
+    const void* q_routed;   // NULL: the routed heads are not computed by this call
+    const void* q_shared;   // NULL: the shared head is not computed by this call
     const void* kmat;
     const void* vmat;
     const float* p_tilde;

@@ -76,11 +76,11 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane)
     return v;
 }
 
-__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, int lane,
+__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, bool routed, int lane,
                         int& n_out, int& tile_out)
 {
     auto ntiles = [&](int n) {
-        if (n >= n_exp) return 0;
+        if (n >= n_exp || (n < N && !routed)) return 0;
         const int M = n < N ? counts[n] : BT;
         return (M + kQpBM - 1) / kQpBM;
     };
@@ -133,12 +133,13 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     uint16_t* __restrict__ q_routed, uint16_t* __restrict__ q_shared, int B, int T, int d_model, int G, int E,
     int k, int n_shared)
 {
+    // q_routed == NULL: only the shared head; n_shared == 0: only the routed experts
     const int N = G * E, BT = B * T, n_exp = N + n_shared;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int s_item[2];
     if (wave == 0) {
         int pn = -1, pt = 0;
-        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, lane, pn, pt)) pn = -1;
+        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, q_routed != nullptr, lane, pn, pt)) pn = -1;
         if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
     }
     __syncthreads();
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(
 {
     const int N = G * E, BT = B * T, n_exp = N + n_shared;
     const int n = blockIdx.x % n_exp;
+    if (n < N && !q_routed) return;
     const int row0 = (blockIdx.x / n_exp) * kQpBM;
     const int M = n < N ? counts[n] : BT;
     if (row0 >= M) return;
@@ -253,12 +255,15 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(
 
 int launch_qproj(const QprojArgs& a, hipStream_t st)
 {
-    const int N = a.G * a.E, BT = a.B * a.T, n_exp = N + a.n_shared;
-    if (BT == 0) return 0;
+    // a NULL q_shared leaves the shared head out of this call (n_shared = 0 below)
+    const int ns = a.q_shared ? a.n_shared : 0;
+    const bool routed = a.q_routed != nullptr;
+    const int N = a.G * a.E, BT = a.B * a.T, n_exp = N + ns;
+    if (BT == 0 || (!routed && ns == 0)) return 0;
     const int tiles = (BT + kQpBM - 1) / kQpBM;
     const int grid = tiles * n_exp;
     // bf16: an upper bound on the number of tiles over all buckets, rounded to the 8 XCDs
-    const long long umax = (long long)BT * a.G * a.k / kQpBM + N + (long long)a.n_shared * tiles;
+    const long long umax = (routed ? (long long)BT * a.G * a.k / kQpBM + N : 0) + (long long)ns * tiles;
     const int grid_bf16 = (int)(8 * ((umax + 7) / 8));
     if (a.bf16) {
         const uint16_t* x = (const uint16_t*)a.x;
@@ -266,7 +271,7 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
         uint16_t* qr = (uint16_t*)a.q_routed;
         uint16_t* qs = (uint16_t*)a.q_shared;
 #define GQE_QP(D) qproj_bf16_kernel<D, 64><<<grid_bf16, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, \
-                                                                  a.B, a.T, a.d_model, a.G, a.E, a.k, a.n_shared)
+                                                                  a.B, a.T, a.d_model, a.G, a.E, a.k, ns)
         switch (a.d_head) {   // d_model is a multiple of the 64-wide stage (checked by the API)
         case 32: GQE_QP(32); break;
         case 64: GQE_QP(64); break;
@@ -277,7 +282,7 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
     } else {
         qproj_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, (const float*)a.w_q, a.sel, a.counts, a.offsets,
                                                a.rows, (float*)a.q_routed, (float*)a.q_shared, a.B, a.T, a.d_model,
-                                               a.G, a.E, a.k, a.d_head, a.n_shared);
+                                               a.G, a.E, a.k, a.d_head, ns);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -95,8 +95,10 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     d = main()
     by = ctypes.byref
     assert lib.gqe_qproj(by(d), None, A16, A16, A16, A16, A16, A16, A16, None) == INVALID
-    assert lib.gqe_qproj(by(d), A16, A16, A16, A16, A16, A16, A16, None, None) == INVALID   # shared head needs q_shared
     assert lib.gqe_qproj(by(d), A16, MIS, A16, A16, A16, A16, A16, A16, None) == ALIGN
+    assert lib.gqe_qproj(by(d), A16, A16, None, A16, A16, A16, A16, None, None) == INVALID   # routed part needs sel
+    assert lib.gqe_qproj(by(d), A16, A16, A16, A16, A16, A16, MIS, None, None) == ALIGN
+    assert lib.gqe_qproj(by(d), None, None, None, None, None, None, None, None, None) == OK  # nothing to compute
     pws = G.gqe_attn_prefill_workspace_bytes(d)
     pf = lambda desc, q=A16, qs=A16, v=A16, pt=A16, out=A16, w=A16, wb=pws: lib.gqe_attn_prefill(  # noqa: E731
         by(desc), q, qs, A16, v, pt, out, w, wb, None)
@@ -108,7 +110,8 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert pf(d, pt=None) == INVALID                 # p_tilde needed
     assert pf(d, w=MIS) == ALIGN
     assert pf(d, wb=pws - 1) == WORKSPACE
-    assert hd(d, qs=None) == INVALID                 # shared head needs q_shared
+    assert pf(d, q=None) == INVALID                  # the weighted slots need the routed hard slots
+    assert lib.gqe_attn_prefill_heads(by(d), None, None, None, None, None, None, 0, None) == OK  # nothing to compute
     assert hd(main(d_head=48)) == UNSUPPORTED
     assert hd(d, out=MIS) == ALIGN
     assert hd(d, w=MIS) == ALIGN

@@ -284,3 +284,37 @@ def test_decode_matches_last_prefill_row():
     check_out(dw, dec["out"].numpy(), ref.double().numpy(), "decode vs prefill row")
     assert torch.equal(dec["sel"], pre["sel"].reshape(3, 200, w.G, w.k)[torch.arange(3), lens.long() - 1])
 
+
+
+def test_two_stream_step_matches_one_stream():
+    """The shared head projected and attended on a side stream (calls with q_routed = NULL) while the main
+    stream routes and handles the kept experts (calls with q_shared = NULL), sharing one workspace, gives the
+    one-stream results bit for bit."""
+    w = small(B=2, T=2500, k=1, name="two_streams")
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    di = {key: (v.cuda() if v is not None else None) for key, v in inp.items()}
+    x = di["x"].reshape(-1, w.d_model)
+    ws = G.prefill_workspace(d, "cuda")
+    assert ws is not None
+    r = G.route(d, x, di["w_router"], di["b_router"])
+    q1 = G.qproj(d, x, di["w_q"], r)
+    out1 = torch.full((w.B, w.T, d.S, w.d_head), float("nan"), device="cuda")
+    G.gqe_attn_prefill_heads(d, q1["q_routed"], q1["q_shared"], di["k"], di["v"], out1, ws)
+    G.gqe_assemble(d, r["p_tilde"], out1)
+    q2 = G.alloc_qproj(d, "cuda")
+    out2 = torch.full_like(out1, float("nan"))
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            G.gqe_qproj(d, x, di["w_q"], None, None, None, None, None, q2["q_shared"])
+            G.gqe_attn_prefill_heads(d, None, q2["q_shared"], di["k"], di["v"], out2, ws)
+        G.gqe_qproj(d, x, di["w_q"], r["sel"], r["counts"], r["offsets"], r["rows"], q2["q_routed"], None)
+        G.gqe_attn_prefill_heads(d, q2["q_routed"], None, di["k"], di["v"], out2, ws)
+        G.gqe_assemble(d, r["p_tilde"], out2)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(q2["q_routed"], q1["q_routed"]) and torch.equal(q2["q_shared"], q1["q_shared"])
+        assert torch.equal(out2, out1), f"round {rep}: two-stream result differs"
