@@ -196,11 +196,30 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
         store();
         __syncthreads();
         if (st + 1 < nst) load((st + 1) * BK);
+        if constexpr (D >= 128) {
+            // all fragments of the stage first, so the reads overlap each other
+            // and the MFMAs wait only for their own operands (at d = 64 the
+            // extra registers cost a wave per SIMD, which costs more)
+            bf16x8 fa[BK / 16], fb[BK / 16][NB];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const bf16x8 a = ld_bf16x8(&sA[a_off + kk]);
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                fa[kk] = ld_bf16x8(&sA[a_off + 16 * kk]);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[j] = mfma32(a, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
+                for (int j = 0; j < NB; ++j) fb[kk][j] = ld_bf16x8(&sB[b_off + j * 32 * P + 16 * kk]);
+            }
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa[kk], fb[kk][j], acc[j]);
+            __builtin_amdgcn_sched_group_barrier(0x100, (BK / 16) * (NB + 1), 0);   // the LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, (BK / 16) * NB, 0);         // then the MFMAs
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 16) {
+                const bf16x8 a = ld_bf16x8(&sA[a_off + kk]);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[j] = mfma32(a, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
+            }
         }
     }
 
