@@ -55,6 +55,8 @@ def _load():
         lib.ora_qproj_rows.restype = None
         lib.ora_prefill_rows.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, P, P]
         lib.ora_prefill_rows.restype = None
+        lib.ora_attend_rows.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P]
+        lib.ora_attend_rows.restype = None
         lib.ora_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
         lib.ora_decode.restype = ctypes.c_int
         lib.ora_num_slots.argtypes = [P]
@@ -160,6 +162,21 @@ def prefill_rows(d: _Desc, x, w_q, K, V, sel, ptilde, tok=None):
     out = np.empty((tok.shape[0], S, d.d_head))
     lib.ora_prefill_rows(ctypes.byref(d), _ptr(x), _ptr(wq), _ptr(K), _ptr(V), _ptr(sel), _ptr(pt),
                          tok.shape[0], _ptr(tok), _ptr(out))
+    return out
+
+
+def attend_rows(d: _Desc, q_routed, q_shared, K, V, ptilde, tok=None):
+    """Attention and slot assembly for tokens ``tok`` given their query rows
+    (q_routed [n, G, k, d_head], q_shared [n, d_head] or None, as qproj_rows
+    returns them).  Returns out [n, S, d_head] float64."""
+    lib = _load()
+    qr = _f64(q_routed)
+    n = qr.shape[0]
+    tok = np.arange(n, dtype=np.int64) if tok is None else np.ascontiguousarray(np.asarray(tok, dtype=np.int64))
+    qs = _f64(q_shared) if (d.n_shared and q_shared is not None) else None
+    K, V, pt = _f64(K), _f64(V), _f64(ptilde)
+    out = np.empty((n, num_slots(d), d.d_head))
+    lib.ora_attend_rows(ctypes.byref(d), _ptr(qr), _ptr(qs), _ptr(K), _ptr(V), _ptr(pt), n, _ptr(tok), _ptr(out))
     return out
 
 

@@ -277,6 +277,43 @@ void ora_prefill_rows(const ora_desc* D, const double* x, const double* w_q, con
 }
 
 /*
+ * Steps 7-8 for a list of tokens given their query rows (as ora_qproj_rows
+ * returns them): q_routed [n_list, G, k, d_head], q_shared [n_list, d_head]
+ * (or NULL without a shared head).  The same attention and slot assembly as
+ * ora_prefill_rows, for callers whose queries were rounded (a bf16 projection
+ * output) before attending.  out [n_list, S, d_head].
+ */
+void ora_attend_rows(const ora_desc* D, const double* q_routed, const double* q_shared, const double* K,
+                     const double* V, const double* ptilde, int64_t n_list, const int64_t* tok, double* out)
+{
+    const int G = D->H_kv, k = D->k, dh = D->d_head, T = D->T;
+    const int S = ora_nslots(D);
+#pragma omp parallel
+    {
+        double* o_r = (double*)malloc(sizeof(double) * (size_t)G * k * dh);
+        double* o_sh = (double*)malloc(sizeof(double) * dh);
+        double* w = (double*)malloc(sizeof(double) * (size_t)T);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_list; ++i) {
+            const int64_t tk = tok[i];
+            const int64_t b = tk / T, t = tk % T;
+            const int64_t n_keys = D->causal ? t + 1 : T;
+            for (int g = 0; g < G; ++g) {
+                const double* Kh = K + (b * G + g) * (int64_t)T * dh;
+                const double* Vh = V + (b * G + g) * (int64_t)T * dh;
+                for (int j = 0; j < k; ++j)
+                    attend(q_routed + ((i * G + g) * k + j) * dh, Kh, Vh, n_keys, dh, o_r + (g * k + j) * dh, w);
+            }
+            if (D->n_shared)
+                attend(q_shared + i * dh, K + b * G * (int64_t)T * dh, V + b * G * (int64_t)T * dh, n_keys, dh,
+                       o_sh, w);
+            assemble(D, o_r, o_sh, ptilde + tk * G * k, out + i * (int64_t)S * dh);
+        }
+        free(o_r); free(o_sh); free(w);
+    }
+}
+
+/*
  * Decode: one new token per sequence against a KV cache that already holds
  * it.  x [B, d_model]; k_cache, v_cache [B, H_kv, L_max, d_head]; lens[b] in
  * 1..L_max counts the valid positions of sequence b.  Routing runs on the one

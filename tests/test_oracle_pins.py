@@ -147,6 +147,31 @@ def test_routed_and_shared_projection_match_torch():
 
 # ---------------------------------------------------------------- step 7-8
 
+def test_attention_given_queries_equals_prefill_rows_and_torch():
+    """attend_rows (steps 7-8 from given query rows) is prefill_rows on the oracle's own projection, bit for
+    bit, and on other queries (rounded ones) each hard and shared slot is torch's causal attention of that query."""
+    w = wl(H_q=12, H_kv=3, k=2, route_mode=1)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"])
+    tok = np.array([0, 3, 28, 29, 57, 40])
+    qr, qs = oracle.qproj_rows(d, inp["x"], inp["w_q"], r["sel"], tok)
+    ref = oracle.prefill_rows(d, inp["x"], inp["w_q"], inp["k"], inp["v"], r["sel"], r["ptilde"], tok)
+    assert np.array_equal(oracle.attend_rows(d, qr, qs, inp["k"], inp["v"], r["ptilde"], tok), ref)
+    qr2, qs2 = np.round(qr * 8) / 8, np.round(qs * 8) / 8
+    got = oracle.attend_rows(d, qr2, qs2, inp["k"], inp["v"], r["ptilde"], tok)
+    K, V = inp["k"].double(), inp["v"].double()
+    for i, t in enumerate(tok):
+        b, tt = divmod(int(t), w.T)
+        def att(q, h):
+            sc = (torch.as_tensor(q) @ K[b, h, : tt + 1].T) / np.sqrt(w.d_head)
+            return (torch.softmax(sc, -1) @ V[b, h, : tt + 1]).numpy()
+        for g in range(w.G):
+            for j in range(w.k):
+                np.testing.assert_allclose(got[i, g * w.k + j], att(qr2[i, g, j], g), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(got[i, -1], att(qs2[i], 0), rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("causal", [1, 0])
 @pytest.mark.parametrize("route_mode", [0, 1])
 def test_all_experts_kept_is_dense_gqa(causal, route_mode):
