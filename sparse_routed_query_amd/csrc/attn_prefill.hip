@@ -358,89 +358,160 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         if (kt < nkv_w) {
             const uint16_t* bK = sKV + buf * KVSZ;
             const uint16_t* bV = bK + kPfBN * P;
-            // S^T - m_ref = K Q^T + cneg for two 32-key blocks
-            f32x16 s[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P), qf[0], cneg);
-#pragma unroll
-                for (int c = 1; c < D / 16; ++c) s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P + 16 * c), qf[c], s[kb]);
-            }
             const int s0 = kt * kPfBN;
             const bool need_mask = s0 > mask_after;
-            if (need_mask) {
-                // key of element r in block kb is s0 + 4*lh + (kb*32 + 8*(r/4) + r%4)
-                const int lim = (causal ? tq : T - 1) - s0 - 4 * lh;
+            bool done = false;
+            if (!need_mask && kt != kt0) {
+                // Fast path, per 32-key block: block 0's probabilities are formed
+                // while block 1's scores are in the matrix cores, and block 1's
+                // while block 0's PV is.  A block whose row sums could exceed 2^8
+                // falls back: block 0 to the general path below (nothing has been
+                // accumulated yet), block 1 to moving the reference on its own
+                // (which rescales what block 0 already added).
+                f32x16 sb0, sb1;
+                sb0 = mfma32(ld_bf16x8(bK + k_off), qf[0], cneg);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int c = 1; c < D / 16; ++c) sb0 = mfma32(ld_bf16x8(bK + k_off + 16 * c), qf[c], sb0);
+                sb1 = mfma32(ld_bf16x8(bK + k_off + 32 * P), qf[0], cneg);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
-            }
-            // P = exp2(S - m_ref), packed to bf16 for the PV product.  The row sum
-            // adds the fp32 values with plain adds (v_dot2 on the packed values
-            // does not run alongside other waves' MFMAs; adds do).
-            // If no lane's partial row sum exceeds 2^8, no probability does, so the
-            // reference stays and the row max is never computed.  The first tile,
-            // and any tile whose sum trips that check, take the exact path: row
-            // max, move the reference if it jumped by more than 2^8, recompute.
-            uint32_t pw[16];
-            auto probs = [&]() {
-                float la = 0.f, lb = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int c = 1; c < D / 16; ++c) sb1 = mfma32(ld_bf16x8(bK + k_off + 32 * P + 16 * c), qf[c], sb1);
+                uint32_t pb0[8], pb1[8];
+                auto probs_block = [&](const f32x16& sv, uint32_t (&pw8)[8]) {
+                    float la = 0.f, lb = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
-                        const float e0 = __builtin_amdgcn_exp2f(s[kb][r]), e1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
-                        pw[kb * 8 + r / 2] = pk_bf16(e0, e1);
+                        const float e0 = __builtin_amdgcn_exp2f(sv[r]), e1 = __builtin_amdgcn_exp2f(sv[r + 1]);
+                        pw8[r / 2] = pk_bf16(e0, e1);
                         la += e0;
                         lb += e1;
                     }
-                return la + lb;
-            };
-            bool exact = kt == kt0;
-            if (!exact) {
-                const float ls = probs();
-                exact = __ballot(!(ls <= kPfRescaleSum)) != 0;
-                if (!exact) l_half += ls;
+                    return la + lb;
+                };
+                // O^T += V^T P^T over 16-key steps c0, c0 + 1
+                auto pv_steps = [&](const uint32_t (&pw8)[8], int c0) {
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const u32x4 pv = {pw8[4 * c], pw8[4 * c + 1], pw8[4 * c + 2], pw8[4 * c + 3]};
+                        const bf16x8 pbv = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+                        for (int j = 0; j < NDB; ++j)
+                            o[j] = mfma32(load_vt(bV, v_off + 16 * (c0 + c) * PV + 32 * j, 8 * PV), pbv, o[j]);
+                    }
+                };
+                const float ls0 = probs_block(sb0, pb0);
+                if (__ballot(!(ls0 <= kPfRescaleSum)) == 0) {
+                    l_half += ls0;
+                    pv_steps(pb0, 0);
+                    float ls1 = probs_block(sb1, pb1);
+                    if (__ballot(!(ls1 <= kPfRescaleSum)) != 0) {
+                        float mt = sb1[0];
+#pragma unroll
+                        for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, sb1[r]), sb1[r + 1]);
+                        mt = half_max(fmaxf(mt, sb1[15]));
+                        const float shift = mt > kPfRescale ? mt : 0.f;
+                        const float alpha = __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sb1[r] -= shift;
+#pragma unroll
+                        for (int j = 0; j < NDB; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+                        l_half *= alpha;
+                        m_ref += shift;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                        ls1 = probs_block(sb1, pb1);
+                    }
+                    l_half += ls1;
+                    pv_steps(pb1, 2);
+                    done = true;
+                }
             }
-            if (exact) {
-                // chained form so the compiler emits v_max3_f32
-                float mt = s[0][0];
+            if (!done) {
+                // General path: the first tile of the item, tiles that need a
+                // mask, and tiles whose first block failed the check above.
+                // S^T - m_ref = K Q^T + cneg for two 32-key blocks
+                f32x16 s[2];
 #pragma unroll
-                for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[0][r]), s[0][r + 1]);
-                mt = fmaxf(fmaxf(mt, s[0][15]), s[1][0]);
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P), qf[0], cneg);
 #pragma unroll
-                for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
-                mt = fmaxf(mt, s[1][15]);
-                mt = half_max(mt);
-                // first tile: set the reference; later tiles: move it only on a large jump
-                const bool move = kt == kt0 ? true : mt > kPfRescale;
-                if (__ballot(move)) {
-                    const float shift = move ? mt : 0.f;
-                    const float alpha = kt == kt0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+                    for (int c = 1; c < D / 16; ++c) s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P + 16 * c), qf[c], s[kb]);
+                }
+                if (need_mask) {
+                    // key of element r in block kb is s0 + 4*lh + (kb*32 + 8*(r/4) + r%4)
+                    const int lim = (causal ? tq : T - 1) - s0 - 4 * lh;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
-#pragma unroll
-                    for (int j = 0; j < NDB; ++j)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-                    l_half *= alpha;
-                    m_ref += shift;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                        for (int r = 0; r < 16; ++r)
+                            s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
                 }
-                l_half += probs();
-            }
-            // O^T += V^T P^T over the four 16-key steps
+                // P = exp2(S - m_ref), packed to bf16 for the PV product.  The row sum
+                // adds the fp32 values with plain adds (v_dot2 on the packed values
+                // does not run alongside other waves' MFMAs; adds do).
+                // If no lane's partial row sum exceeds 2^8, no probability does, so the
+                // reference stays and the row max is never computed.  The first tile,
+                // and any tile whose sum trips that check, take the exact path: row
+                // max, move the reference if it jumped by more than 2^8, recompute.
+                uint32_t pw[16];
+                auto probs = [&]() {
+                    float la = 0.f, lb = 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 pv = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
-                const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * PV + 32 * j, 8 * PV), pb, o[j]);
+                        for (int r = 0; r < 16; r += 2) {
+                            const float e0 = __builtin_amdgcn_exp2f(s[kb][r]), e1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
+                            pw[kb * 8 + r / 2] = pk_bf16(e0, e1);
+                            la += e0;
+                            lb += e1;
+                        }
+                    return la + lb;
+                };
+                bool exact = kt == kt0;
+                if (!exact) {
+                    const float ls = probs();
+                    exact = __ballot(!(ls <= kPfRescaleSum)) != 0;
+                    if (!exact) l_half += ls;
+                }
+                if (exact) {
+                    // chained form so the compiler emits v_max3_f32
+                    float mt = s[0][0];
+#pragma unroll
+                    for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[0][r]), s[0][r + 1]);
+                    mt = fmaxf(fmaxf(mt, s[0][15]), s[1][0]);
+#pragma unroll
+                    for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
+                    mt = fmaxf(mt, s[1][15]);
+                    mt = half_max(mt);
+                    // first tile: set the reference; later tiles: move it only on a large jump
+                    const bool move = kt == kt0 ? true : mt > kPfRescale;
+                    if (__ballot(move)) {
+                        const float shift = move ? mt : 0.f;
+                        const float alpha = kt == kt0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
+#pragma unroll
+                        for (int j = 0; j < NDB; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+                        l_half *= alpha;
+                        m_ref += shift;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                    }
+                    l_half += probs();
+                }
+                // O^T += V^T P^T over the four 16-key steps
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 pv = {pw[4 * c], pw[4 * c + 1], pw[4 * c + 2], pw[4 * c + 3]};
+                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pv);
+#pragma unroll
+                    for (int j = 0; j < NDB; ++j) o[j] = mfma32(load_vt(bV, v_off + 16 * c * PV + 32 * j, 8 * PV), pb, o[j]);
+                }
             }
         }
         if (kt + 1 < kt1) store(buf ^ 1);

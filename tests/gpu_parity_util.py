@@ -117,6 +117,26 @@ def check_prefill(w: W.Workload, inp: dict, gpu: dict, agreed: dict, tok: np.nda
     check_out(w, got, ref, f"prefill out ({len(tok)} tokens)")
 
 
+def kernel_query(q: torch.Tensor, d_head: int) -> np.ndarray:
+    """The query the bf16 attention kernel multiplies with: q pre-scaled by log2(e)/sqrt(d) in fp32 and
+    rounded to bf16 (so its softmax is a bare exp2), mapped back to natural units in float64."""
+    c = np.float32(1.4426950408889634) / np.sqrt(np.float32(d_head))
+    qs = (q.float() * torch.tensor(c, dtype=torch.float32)).to(torch.bfloat16)
+    return qs.double().numpy() / np.float64(c)
+
+
+def check_prefill_given_q(w: W.Workload, inp: dict, gpu: dict, agreed: dict, tok: np.ndarray):
+    """Attention and slots against the oracle's attention of the GPU's own query rows, as the attention
+    kernel uses them (kernel_query), so that only the softmax and accumulation arithmetic is compared."""
+    d = oracle.desc(w)
+    b, t = tok // w.T, tok % w.T
+    qr = kernel_query(gpu["q_routed"][b, :, t], w.d_head)              # [n, G, k, dh]
+    qs = kernel_query(gpu["q_shared"][b, t], w.d_head) if w.n_shared else None
+    ref = oracle.attend_rows(d, qr, qs, inp["k"], inp["v"], agreed["ptilde"], tok)
+    got = gpu["out"].reshape(w.B * w.T, -1, w.d_head).numpy()[tok]
+    check_out(w, got, ref, f"prefill out given the GPU's queries ({len(tok)} tokens)")
+
+
 def full_prefill_check(w: W.Workload, n_sample: int = 0):
     say(f"case {w}")
     inp = W.make_inputs(w)

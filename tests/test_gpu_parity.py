@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_parity_util import (check_out, check_route, full_decode_check, full_prefill_check, gpu_prefill, say,
-                             gpu_decode)
+from gpu_parity_util import (check_out, check_prefill_given_q, check_qproj, check_route, full_decode_check,
+                             full_prefill_check, gpu_decode, gpu_prefill, say)
 import sparse_routed_query_amd.gqe as G
 
 pytestmark = pytest.mark.gpu
@@ -318,3 +318,23 @@ def test_two_stream_step_matches_one_stream():
         torch.cuda.synchronize()
         assert torch.equal(q2["q_routed"], q1["q_routed"]) and torch.equal(q2["q_shared"], q1["q_shared"])
         assert torch.equal(out2, out1), f"round {rep}: two-stream result differs"
+
+
+def test_large_scores_move_the_softmax_reference():
+    """Scores spread over tens of log2 units and growing along the keys, so new row maxima keep arriving:
+    the lazy softmax reference moves on the first tile, on the first and on the second 32-key block of
+    later tiles, and across the two halves of split query tiles (T = 2500), on every token.  With scores
+    this large (|s| up to ~40 log2 units) the bf16 roundings of the query -- by the projection, and of the
+    query pre-scaled by log2(e)/sqrt(d) that the kernel multiplies with -- move outputs by up to ~0.1, so
+    the attention is compared with the oracle's attention of exactly that query (kernel_query)."""
+    w = small(B=1, T=2500, k=1, w_std=0.35, name="large_scores")
+    inp = W.make_inputs(w)
+    ramp = 1.0 + 3.0 * torch.arange(w.T, dtype=torch.float32) / w.T
+    inp["k"] = (inp["k"].float() * ramp[None, None, :, None]).to(inp["k"].dtype)
+    # router scores back to the spread the routing tolerances are set for (std ~0.4)
+    inp["w_router"] = (inp["w_router"].float() * 0.1).to(inp["w_router"].dtype)
+    gpu = gpu_prefill(w, inp)
+    agreed = check_route(w, inp, gpu)
+    tok = np.arange(w.B * w.T)
+    check_qproj(w, inp, gpu, agreed, tok)
+    check_prefill_given_q(w, inp, gpu, agreed, tok)
