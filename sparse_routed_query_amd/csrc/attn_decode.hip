@@ -19,22 +19,78 @@
 
 namespace gqe {
 
-constexpr int kDcPasses = 8;   // 16-byte loads per thread for each of K and V
+constexpr int kDcPasses = 12;  // 16-byte loads per thread for each of K and V
 
 template <typename ET, int D>
 struct DcShape {
     static constexpr int VEC = 16 / sizeof(ET);    // elements per 16-byte load
-    static constexpr int LPP = D / VEC;            // lanes per key position
-    static constexpr int PPP = 256 / LPP;          // positions per pass
+    static constexpr int LPP = D / VEC;            // lanes per key position (4 .. 32)
+    static constexpr int PPW = 64 / LPP;           // positions per wave and pass
+    static constexpr int PPP = 4 * PPW;            // positions per pass
     static constexpr int CH = PPP * kDcPasses;     // keys per chunk
 };
+
+typedef __bf16 dc_bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float elem(const u32x4& v, int i, const uint16_t*)
 {
     const uint32_t w = v[i >> 1];
-    return bf2f((uint16_t)((i & 1) ? (w >> 16) : (w & 0xffff)));
+    return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 __device__ __forceinline__ float elem(const u32x4& v, int i, const float*) { return __uint_as_float(v[i]); }
+
+// q . k over one 16-byte slice: bf16 pairs through the two-term dot product
+// with fp32 accumulation, fp32 through fused multiply-adds
+__device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k, const uint16_t*)
+{
+    // (elements are copied out before the bit cast: a bit cast of a vector
+    // element in place reads element 0 with this compiler)
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t qj = q[j], kj = k[j];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2, qj), __builtin_bit_cast(dc_bf16x2, kj), acc,
+                                              false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float slice_dot(const u32x4& q, const u32x4& k, const float*)
+{
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = fmaf(__uint_as_float(q[j]), __uint_as_float(k[j]), acc);
+    return acc;
+}
+
+// Value of the lane whose index differs in bit O (O a power of two); below 16
+// through DPP (quad permutes, then the 8- and 16-lane mirrors).  The mirrors
+// pair lane i with 7-i (15-i), which is an exchange across bit 2 (bit 3) for
+// values already equal within groups of 4 (8) lanes, as they are in the
+// butterflies below, which take the bits in increasing order.
+template <int O>
+__device__ __forceinline__ float lane_partner(float v)
+{
+    const int x = __builtin_bit_cast(int, v);
+    if constexpr (O == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+    else if constexpr (O == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+    else if constexpr (O == 4) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true));
+    else if constexpr (O == 8) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true));
+    else return __shfl_xor(v, O);
+}
+// sum / max over the lanes that differ in bits FROM..TO-1 (values already
+// equal within groups of FROM lanes); every lane gets the same result
+template <int FROM, int TO>
+__device__ __forceinline__ float lanes_sum(float v)
+{
+    if constexpr (FROM < TO) return lanes_sum<FROM * 2, TO>(v + lane_partner<FROM>(v));
+    else return v;
+}
+template <int FROM, int TO>
+__device__ __forceinline__ float lanes_max(float v)
+{
+    if constexpr (FROM < TO) return lanes_max<FROM * 2, TO>(fmaxf(v, lane_partner<FROM>(v)));
+    else return v;
+}
 
 template <typename ET, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict__ q_routed,
@@ -45,14 +101,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
                                                            float qscale)
 {
     using SH = DcShape<ET, D>;
-    constexpr int VEC = SH::VEC, LPP = SH::LPP, PPP = SH::PPP, CH = SH::CH;
+    constexpr int VEC = SH::VEC, LPP = SH::LPP, PPW = SH::PPW, PPP = SH::PPP, CH = SH::CH;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = min(max(lens[b], 0), L_max);   // never read outside the cache
     const int c0 = c * CH;
     if (c0 >= L) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int dq = (tid % LPP) * VEC;
-    const int pp = tid / LPP;
+    const int dq = (lane % LPP) * VEC;
+    const int pp = tid / LPP;                    // = wave * PPW + position slot in the wave
     const ET* K = kc + ((size_t)b * G + g) * (size_t)L_max * D;
     const ET* V = vc + ((size_t)b * G + g) * (size_t)L_max * D;
 
@@ -71,64 +127,72 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
         }
     }
 
-    __shared__ float s_red[4][D + 2];
+    // Each wave forms (max, sum, o) over its own positions; after one barrier
+    // per row, D threads rescale the four waves' terms to the chunk maximum and
+    // add them in wave order.  Rows alternate between two LDS buffers: the
+    // barrier of row r+1 is passed only after every thread has finished
+    // combining row r, so row r+2 may overwrite row r's buffer.
+    __shared__ __attribute__((aligned(16))) float s_acc[2][4 * PPW * D];
+    __shared__ float s_ml[2][8];
     const int RG = k + n_shared;
     const int nrows = k + ((g == 0 && n_shared) ? 1 : 0);
     for (int row = 0; row < nrows; ++row) {
+        const int buf = row & 1;
         const ET* q = row < k ? q_routed + (((size_t)b * G + g) * k + row) * D : q_shared + (size_t)b * D;
-        float qv[VEC];
-        {
-            const u32x4 raw = ld_u32x4(q + dq);
+        const u32x4 qr = ld_u32x4(q + dq);
+        // most workgroups serve one row: keep the unpacking of V inside the
+        // row loop rather than holding every unpacked value in registers
 #pragma unroll
-            for (int v = 0; v < VEC; ++v) qv[v] = elem(raw, v, (const ET*)nullptr) * qscale;
-        }
+        for (int i = 0; i < kDcPasses; ++i) asm volatile("" : "+v"(vr[i]));
         float sc[kDcPasses];
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < kDcPasses; ++i) {
-            float dot = 0.f;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) dot = fmaf(qv[v], elem(kr[i], v, (const ET*)nullptr), dot);
-#pragma unroll
-            for (int o = 1; o < LPP; o <<= 1) dot += __shfl_xor(dot, o);
-            const int pos = c0 + i * PPP + pp;
-            sc[i] = pos < L ? dot : -INFINITY;
+            const float dot = lanes_sum<1, LPP>(slice_dot(qr, kr[i], (const ET*)nullptr)) * qscale;
+            sc[i] = c0 + i * PPP + pp < L ? dot : -INFINITY;
             m = fmaxf(m, sc[i]);
         }
-#pragma unroll
-        for (int o = LPP; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        if (lane == 0) s_red[wave][D] = m;
-        __syncthreads();
-        m = fmaxf(fmaxf(s_red[0][D], s_red[1][D]), fmaxf(s_red[2][D], s_red[3][D]));
+        m = lanes_max<LPP, 64>(m);
+        const float mu = m == -INFINITY ? 0.f : m;   // a wave past the end of the cache adds nothing
         float l = 0.f, acc[VEC];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 #pragma unroll
         for (int i = 0; i < kDcPasses; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sc[i] - m);
+            const float p = __builtin_amdgcn_exp2f(sc[i] - mu);
             l += p;
 #pragma unroll
             for (int v = 0; v < VEC; ++v) acc[v] = fmaf(p, elem(vr[i], v, (const ET*)nullptr), acc[v]);
         }
+        l = lanes_sum<LPP, 64>(l);
+        float* sa = &s_acc[buf][pp * D + dq];
 #pragma unroll
-        for (int o = LPP; o < 64; o <<= 1) {
-            l += __shfl_xor(l, o);
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) acc[v] += __shfl_xor(acc[v], o);
-        }
-        if (lane < LPP) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) s_red[wave][dq + v] = acc[v];
-        }
-        if (lane == 0) s_red[wave][D + 1] = l;
-        __syncthreads();
-        float* dst = part + ((((size_t)b * G + g) * RG + row) * nch + c) * (D + 2);
-        if (tid < D) dst[2 + tid] = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
-        if (tid == 0) {
-            dst[0] = m;
-            dst[1] = s_red[0][D + 1] + s_red[1][D + 1] + s_red[2][D + 1] + s_red[3][D + 1];
+        for (int v = 0; v < VEC; v += 4) *(f32x4*)(sa + v) = f32x4{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]};
+        if (lane == 0) {
+            s_ml[buf][wave] = m;
+            s_ml[buf][4 + wave] = l;
         }
         __syncthreads();
+        if (tid < D) {
+            const float* ml = s_ml[buf];
+            const float M = fmaxf(fmaxf(ml[0], ml[1]), fmaxf(ml[2], ml[3]));
+            float o = 0.f, ls = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = __builtin_amdgcn_exp2f(ml[w] - M);
+                float ow = 0.f;
+#pragma unroll
+                for (int s = 0; s < PPW; ++s) ow += s_acc[buf][(w * PPW + s) * D + tid];
+                o = fmaf(f, ow, o);
+                ls = fmaf(f, ml[4 + w], ls);
+            }
+            float* dst = part + ((((size_t)b * G + g) * RG + row) * nch + c) * (D + 2);
+            dst[2 + tid] = o;
+            if (tid == 0) {
+                dst[0] = M;
+                dst[1] = ls;
+            }
+        }
     }
 }
 
