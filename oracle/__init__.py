@@ -57,6 +57,10 @@ def _load():
         lib.ora_prefill_rows.restype = None
         lib.ora_attend_rows.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P]
         lib.ora_attend_rows.restype = None
+        lib.ora_assemble_rows.argtypes = [P, P, ctypes.c_int64, P]
+        lib.ora_assemble_rows.restype = None
+        lib.ora_out_proj_rows.argtypes = [P, P, P, ctypes.c_int64, P]
+        lib.ora_out_proj_rows.restype = None
         lib.ora_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
         lib.ora_decode.restype = ctypes.c_int
         lib.ora_num_slots.argtypes = [P]
@@ -180,6 +184,33 @@ def attend_rows(d: _Desc, q_routed, q_shared, K, V, ptilde, tok=None):
     return out
 
 
+def assemble_rows(d: _Desc, slots, ptilde):
+    """The weighted slot(s) of token rows whose hard and shared slots are given.
+
+    slots [n, S, d_head] (the weighted slot(s) are ignored), ptilde [n, G, k].
+    Returns a float64 copy of ``slots`` with the weighted slot(s) filled.
+    """
+    lib = _load()
+    out = np.array(_f64(slots), dtype=np.float64, copy=True).reshape(-1, num_slots(d), d.d_head)
+    pt = _f64(ptilde).reshape(out.shape[0], d.H_kv, d.k)
+    lib.ora_assemble_rows(ctypes.byref(d), _ptr(pt), out.shape[0], _ptr(out))
+    return out
+
+
+def out_proj_rows(d: _Desc, slots, w_o):
+    """The attention output projection y = h W_o^T of token rows.
+
+    slots [n, S, d_head] (all slots filled), w_o [d_model, S*d_head].
+    Returns y [n, d_model] float64.
+    """
+    lib = _load()
+    h = _f64(slots).reshape(-1, num_slots(d), d.d_head)
+    wo = _f64(w_o).reshape(d.d_model, num_slots(d) * d.d_head)
+    y = np.empty((h.shape[0], d.d_model))
+    lib.ora_out_proj_rows(ctypes.byref(d), _ptr(h), _ptr(wo), h.shape[0], _ptr(y))
+    return y
+
+
 def prefill(d: _Desc, inputs: dict, tok=None, routing=None):
     """Full prefill forward from a dict of inputs (x, w_router, b_router, w_q, k, v).
 
@@ -217,4 +248,5 @@ def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens):
 
 
 __all__ = ["build", "desc", "num_slots", "num_threads", "route", "compact", "qproj_rows", "prefill_rows", "prefill",
+           "assemble_rows", "out_proj_rows",
            "decode", "TIE_MARGIN"]

@@ -314,6 +314,47 @@ void ora_attend_rows(const ora_desc* D, const double* q_routed, const double* q_
 }
 
 /*
+ * Step 8 alone for n_list rows whose hard and shared slots are given: fills
+ * the weighted slot(s) of slots [n_list, S, d_head] in place from the hard
+ * slots, exactly as the prefill rows path does.  ptilde [n_list, G, k].
+ */
+void ora_assemble_rows(const ora_desc* D, const double* ptilde, int64_t n_list, double* slots)
+{
+    const int G = D->H_kv, k = D->k, dh = D->d_head;
+    const int S = ora_nslots(D), nroute = D->route_mode ? G : 1;
+#pragma omp parallel
+    {
+        double* tmp = (double*)malloc(sizeof(double) * (size_t)S * dh);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n_list; ++i) {
+            double* row = slots + i * (int64_t)S * dh;
+            const double* o_sh = D->n_shared ? row + ((int64_t)G * k + nroute) * dh : NULL;
+            assemble(D, row, o_sh, ptilde + i * (int64_t)G * k, tmp);
+            memcpy(row, tmp, sizeof(double) * (size_t)S * dh);
+        }
+        free(tmp);
+    }
+}
+
+/*
+ * The attention output projection of n_list tokens: the S slots of a token,
+ * concatenated in slot order into h_t of width S*d_head, times W_o
+ * ([tut] "GQA 核心原理与计算流程", step 5: the head outputs are concatenated
+ * and projected by one final linear map; [note] §3-2 (5) and (7): in GQE the
+ * concatenation is of the kG+2 slots, so W_o is kG+2 slots wide).  No bias
+ * (the pages name none).
+ *   y[i, c] = sum_s sum_d slots[i, s, d] * w_o[c, s*d_head + d]
+ * slots [n_list, S, d_head]; w_o [d_model, S*d_head]; y [n_list, d_model].
+ */
+void ora_out_proj_rows(const ora_desc* D, const double* slots, const double* w_o, int64_t n_list, double* y)
+{
+    const int64_t width = (int64_t)ora_nslots(D) * D->d_head;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_list; ++i)
+        for (int c = 0; c < D->d_model; ++c) y[i * D->d_model + c] = dot(slots + i * width, w_o + c * width, width);
+}
+
+/*
  * Decode: one new token per sequence against a KV cache that already holds
  * it.  x [B, d_model]; k_cache, v_cache [B, H_kv, L_max, d_head]; lens[b] in
  * 1..L_max counts the valid positions of sequence b.  Routing runs on the one

@@ -304,6 +304,59 @@ def test_permuting_experts_inside_a_group_keeps_weighted_and_shared_slots():
         sb = np.sort(b[:, g * w.k:(g + 1) * w.k], axis=1)
         np.testing.assert_allclose(sa, sb, rtol=1e-12, atol=1e-14)
 
+# ---------------------------------------------------------------- output projection
+
+@pytest.mark.parametrize("route_mode", [0, 1])
+def test_assemble_rows_restores_the_weighted_slots(route_mode):
+    # given the hard and shared slots of the prefill rows path, the weighted
+    # slot(s) come back bit for bit, and equal p~-weighted sums of the hard slots
+    w = wl(H_q=12, H_kv=3, k=2, route_mode=route_mode)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    ref = oracle.prefill(d, inp)
+    out = ref["out"]
+    G, k, dh = w.G, w.k, w.d_head
+    nr = G if route_mode else 1
+    garbled = out.copy()
+    garbled[:, G * k:G * k + nr] = np.nan
+    got = oracle.assemble_rows(d, garbled, ref["ptilde"])
+    assert np.array_equal(got, out)
+    hard = out[:, :G * k].reshape(-1, G, k, dh)
+    per_group = np.einsum("tgj,tgjd->tgd", ref["ptilde"], hard)
+    want = per_group if route_mode else per_group.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(got[:, G * k:G * k + nr], want, rtol=1e-12, atol=1e-15)
+
+def test_output_projection_closed_forms_and_torch():
+    # [tut] step 5 / [note] §3-2 (5), (7): y = concat(slots) W_o^T over S*d_head inputs
+    w = wl(H_q=6, H_kv=3, k=1)                       # S = 3 hard + 1 weighted + 1 shared = 5
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    h = oracle.prefill(d, inp)["out"]
+    n, S, dh = h.shape
+    width = S * dh
+    flat = h.reshape(n, width)
+    # identity: d_model = S*d_head, W_o = I gives the concatenation back exactly
+    di = oracle.desc(w, d_model=width)
+    assert np.array_equal(oracle.out_proj_rows(di, h, np.eye(width)), flat)
+    # a permutation matrix picks slot entries: output c is input perm[c]
+    perm = np.random.default_rng(3).permutation(width)
+    assert np.array_equal(oracle.out_proj_rows(di, h, np.eye(width)[perm]), flat[:, perm])
+    # a block selector returns one slot (here the shared one, slot S-1)
+    sel_blk = np.zeros((dh, width)); sel_blk[:, (S - 1) * dh:] = np.eye(dh)
+    assert np.array_equal(oracle.out_proj_rows(oracle.desc(w, d_model=dh), h, sel_blk), h[:, S - 1])
+    # a general W_o (d_model != width, so a transposed operand cannot pass) against torch
+    wo = torch.randn(w.d_model, width, dtype=torch.float64, generator=torch.Generator().manual_seed(5))
+    y = oracle.out_proj_rows(d, h, wo)
+    ref = torch.from_numpy(flat) @ wo.T
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-13)
+    # per-group weighted slots widen the input to S = kG + G + 1
+    wm = w.replace(route_mode=1)
+    dm = oracle.desc(wm)
+    hm = oracle.prefill(dm, inp)["out"]
+    wom = torch.randn(w.d_model, hm.shape[1] * dh, dtype=torch.float64, generator=torch.Generator().manual_seed(6))
+    np.testing.assert_allclose(oracle.out_proj_rows(dm, hm, wom), (torch.from_numpy(hm.reshape(n, -1)) @ wom.T).numpy(),
+                               rtol=1e-12, atol=1e-13)
+
 # ---------------------------------------------------------------- decode
 
 def test_decode_equals_last_prefill_row():
