@@ -223,6 +223,28 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
  */
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
 
+/*
+ * gqe_out_proj -- the attention output projection, fused with slot assembly.
+ * The S slots of a token are concatenated in slot order into h_t (width
+ * S*d_head) and passed through one linear map, y_t = W_o h_t, no bias (GQA
+ * tutorial, freeguideonline, "GQA 核心原理与计算流程" step 5: concatenate the
+ * head outputs, then one final linear projection; GQE study note §3-2 (5) and
+ * (7): in GQE the concatenation is of the kG+2 slots).  The weighted slot(s)
+ * are not read: they are formed from the hard slots inside the call exactly
+ * as gqe_assemble forms them.
+ * In:  out [B*T, S, d_head] fp32 with the hard and shared slots written (as
+ *      gqe_attn_prefill_heads or gqe_attn_decode leave them);
+ *      p_tilde [B*T, G, k] fp32; w_o [d_model, S*d_head] (dtype), row-major.
+ * Out: y [B*T, d_model] fp32.  With write_weighted = 1 the weighted slot(s)
+ *      of `out` are written too, bit for bit what gqe_assemble writes; with 0
+ *      `out` is only read.
+ * bf16: each slot value is rounded to bf16 (nearest even) before the product,
+ * which accumulates in fp32; fp32: fp32 throughout.  Works for decode outputs
+ * too (T = 1).  d_model * S * d_head must stay below 2^31.
+ */
+int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
+                 int32_t write_weighted, void* stream);
+
 /* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
 

@@ -216,6 +216,25 @@ int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* s
     return launch_status(gqe::launch_assemble(p_tilde, out, s.BT, s.G, s.k, s.D, s.S, s.mode, (hipStream_t)stream));
 }
 
+int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
+                 int32_t write_weighted, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (write_weighted != 0 && write_weighted != 1) return GQE_ERR_INVALID;
+    if ((long long)s.dm * s.S * s.D >= (1ll << 31)) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(out));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(w_o));
+    GQE_TRY(need(y));
+    gqe::OutProjArgs a;
+    a.out = out; a.p_tilde = p_tilde; a.w_o = w_o; a.y = y; a.BT = s.BT;
+    a.d_model = s.dm; a.G = s.G; a.k = s.k; a.d_head = s.D; a.n_shared = s.ns; a.route_mode = s.mode; a.S = s.S;
+    a.write_weighted = write_weighted; a.bf16 = s.bf16;
+    return launch_status(gqe::launch_out_proj(a, (hipStream_t)stream));
+}
+
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max)
 {
     Shape s;

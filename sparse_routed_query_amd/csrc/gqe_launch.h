@@ -63,6 +63,17 @@ int launch_prefill(const PrefillArgs& a, hipStream_t st);
 int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, int k, int D, int S, int route_mode,
                     hipStream_t st);
 
+struct OutProjArgs {
+    float* out;            // [BT, S, d_head] fp32: hard and shared slots read, weighted slot(s) optionally written
+    const float* p_tilde;  // [BT, G, k] fp32
+    const void* w_o;       // [d_model, S * d_head] (dtype)
+    float* y;              // [BT, d_model] fp32
+    long long BT;
+    int d_model, G, k, d_head, n_shared, route_mode, S, write_weighted;
+    bool bf16;
+};
+int launch_out_proj(const OutProjArgs& a, hipStream_t st);
+
 struct DecodeArgs {
     const void* q_routed;
     const void* q_shared;

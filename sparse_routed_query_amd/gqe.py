@@ -27,7 +27,7 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 # Every symbol the C header declares (checked by the host tests).
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
-           "gqe_attn_prefill_heads", "gqe_assemble", "gqe_decode_workspace_bytes", "gqe_attn_decode")
+           "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode")
 
 
 class GqeError(RuntimeError):
@@ -103,6 +103,8 @@ def load():
         lib.gqe_attn_prefill_heads.restype = I
         lib.gqe_assemble.argtypes = [D, P, P, P]
         lib.gqe_assemble.restype = I
+        lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
+        lib.gqe_out_proj.restype = I
         lib.gqe_decode_workspace_bytes.argtypes = [D, ctypes.c_int32]
         lib.gqe_decode_workspace_bytes.restype = Z
         lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
@@ -215,6 +217,13 @@ def gqe_assemble(desc, p_tilde, out, stream=None):
     _check("gqe_assemble", rc)
 
 
+def gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted=False, stream=None):
+    rc = load().gqe_out_proj(ctypes.byref(desc), _ptr(out, torch.float32, "out"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                             _ptr(w_o, desc.torch_dtype, "w_o"), _ptr(y, torch.float32, "y"), int(bool(write_weighted)),
+                             _stream(stream))
+    _check("gqe_out_proj", rc)
+
+
 def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace, stream=None):
     dt = desc.torch_dtype
     L_max = k_cache.shape[2]
@@ -292,6 +301,14 @@ def attn_decode(desc, q: dict, k_cache, v_cache, lens, p_tilde, out=None, worksp
                                 device=k_cache.device)
     gqe_attn_decode(desc, q["q_routed"], q["q_shared"], k_cache, v_cache, lens, p_tilde, out, workspace, stream)
     return out
+
+
+def out_proj(desc, out, p_tilde, w_o, y=None, write_weighted=False, stream=None) -> torch.Tensor:
+    """y = W_o h_t over the concatenated slots of every token (weighted slot(s) formed inside)."""
+    if y is None:
+        y = torch.empty((desc.B * desc.T, desc.d_model), dtype=torch.float32, device=out.device)
+    gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted, stream)
+    return y
 
 
 def prefill(desc, x, w_router, b_router, w_q, k, v, logits=False, stream=None) -> dict:

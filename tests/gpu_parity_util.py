@@ -175,3 +175,42 @@ def full_decode_check(w: W.Workload, inp: dict | None = None):
         keep = np.ones(w.B, dtype=bool)
     check_out(w, gpu["out"].numpy()[keep], orc["out"][keep], f"decode out ({int(keep.sum())} sequences)")
     return inp, gpu
+
+
+def gpu_out_proj(w: W.Workload, out_slots: torch.Tensor, p_tilde: torch.Tensor, w_o: torch.Tensor,
+                 write_weighted: bool = True, dev="cuda"):
+    """gqe_out_proj on the given slots [B*T, S, d_head] with the weighted slot(s) set to NaN first, so
+    that a read of them would show in y.  Returns (y, slots after the call) on the CPU."""
+    d = G.desc_from(w)
+    kG, nr = w.k * w.G, (w.G if w.route_mode else 1)
+    o = out_slots.reshape(w.B * w.T, d.S, w.d_head).clone()
+    o[:, kG:kG + nr] = float("nan")
+    od = o.to(dev)
+    y = G.out_proj(d, od, p_tilde.reshape(w.B * w.T, w.G, w.k).to(dev), w_o.to(dev), write_weighted=write_weighted)
+    torch.cuda.synchronize()
+    return y.cpu(), od.cpu()
+
+
+def check_out_proj(w: W.Workload, slots: torch.Tensor, p_tilde: torch.Tensor, w_o: torch.Tensor,
+                   y: torch.Tensor, tok: np.ndarray):
+    """y of tokens ``tok`` against the oracle's projection of the same hard and shared slots (its own
+    fp64 weighted sum), element by element within the bound the arithmetic gives: bf16 rounding of each
+    slot value (relative 2^-9), fp32 accumulation over the K = S*d_head terms and the fp32 weighted sum
+    (K + kG + 1 roundings of 2^-24), each relative to sum_i |h_i| |W_o[c, i]|."""
+    d = oracle.desc(w)
+    S = oracle.num_slots(d)
+    h_gpu = slots.reshape(-1, S, w.d_head)[tok].double().numpy()
+    pt = p_tilde.reshape(-1, w.G, w.k)[tok].double().numpy()
+    h = oracle.assemble_rows(d, h_gpu, pt)
+    y_ref = oracle.out_proj_rows(d, h, w_o)
+    h_abs = oracle.assemble_rows(d, np.abs(h_gpu), pt)        # weighted part: sum p~ |hard| bounds its error too
+    mag = h_abs.reshape(len(tok), -1) @ np.abs(w_o.double().numpy()).T
+    K = S * w.d_head
+    eps = (2.0 ** -9 if w.dtype == "bf16" else 0.0) + (K + w.k * w.G + 1) * 2.0 ** -24
+    got = y.reshape(-1, w.d_model)[tok].double().numpy()
+    err = np.abs(got - y_ref)
+    ratio = float((err / (eps * mag + 1e-30)).max())
+    say(f"[{w.name}] out_proj ({len(tok)} tokens): max-abs={err.max():.3e} mean-abs={err.mean():.3e} "
+        f"max|ref|={np.abs(y_ref).max():.3e} max err/bound={ratio:.3f}")
+    assert np.isfinite(got).all()
+    assert ratio <= 1.0

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -120,6 +120,15 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert lib.gqe_assemble(by(d), None, A16, None) == INVALID
     assert lib.gqe_assemble(by(d), A16, MIS, None) == ALIGN
     assert lib.gqe_assemble(by(main(H_q=15)), A16, A16, None) == INVALID
+    op = lambda desc, out=A16, pt=A16, wo=A16, y=A16, ww=0: lib.gqe_out_proj(  # noqa: E731
+        by(desc), out, pt, wo, y, ww, None)
+    assert op(d, out=None) == INVALID
+    assert op(d, pt=None) == INVALID             # the weighted slot(s) need p~
+    assert op(d, wo=None) == INVALID
+    assert op(d, y=MIS) == ALIGN
+    assert op(d, ww=2) == INVALID
+    assert op(main(d_head=48)) == UNSUPPORTED
+    assert op(main(B=0), out=None, pt=None, wo=None, y=None) == OK   # nothing to compute
     dd = main(B=64, T=1)
     ws = G.gqe_decode_workspace_bytes(dd, 8192)
     dec = lambda desc, L=8192, lens=A16, w=A16, wb=ws: lib.gqe_attn_decode(  # noqa: E731

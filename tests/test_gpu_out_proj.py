@@ -1,0 +1,82 @@
+"""GPU parity of the attention output projection fused with slot assembly (gqe_out_proj).
+
+y_t = W_o h_t over the S concatenated slots (GQA tutorial, "GQA 核心原理与计算流程" step 5; GQE study
+note §3-2 (5), (7)).  The GPU's own hard and shared slots are the input of both sides, so the
+comparison isolates the projection: the oracle forms the weighted slot(s) in fp64 and projects in fp64;
+the bound per element follows from bf16 rounding of the slots and fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_parity_util import check_out_proj, gpu_decode, gpu_out_proj, gpu_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+
+def small(**kw):
+    base = dict(name="op_small", B=2, T=300, d_model=128, H_q=8, H_kv=2, k=2, d_head=64, dtype="bf16", seed=21,
+                act_std=1.0, w_std=0.02)
+    base.update(kw)
+    return W.Workload(**base)
+
+
+def run_and_check(w, tok=None):
+    inp = W.make_inputs(w)
+    gpu = gpu_prefill(w, inp)
+    wo = W.make_w_o(w)
+    slots = gpu["out"].reshape(w.B * w.T, -1, w.d_head)
+    y, after = gpu_out_proj(w, slots, gpu["p_tilde"], wo)
+    # the weighted slot(s) written back are gqe_assemble's bits; the other slots are untouched
+    assert torch.equal(after, slots)
+    assert torch.isfinite(y).all()
+    tok = np.arange(w.B * w.T) if tok is None else tok
+    check_out_proj(w, slots, gpu["p_tilde"], wo, y, tok)
+    return gpu, wo, slots, y
+
+
+SHAPES = [
+    small(),                                              # ragged token tile (600 = 4 x 128 + 88)
+    small(d_model=320, name="ragged_cols"),               # a 64-wide last column tile
+    small(d_head=32, name="d32"), small(d_head=128, name="d128"),
+    small(route_mode=1, name="per_group_slots"),
+    small(n_shared=0, name="no_shared"),
+    small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="kG8"),
+    small(H_q=4, H_kv=1, k=2, name="G1"),
+    small(T=1, name="T1"),
+    small(B=1, T=64, d_model=1024, name="d_model1024"),
+    small(dtype="f32", T=100, d_model=96, name="f32"),
+    small(dtype="f32", T=70, d_head=128, d_model=64, k=1, route_mode=1, name="f32_d128_mode1"),
+]
+
+
+@pytest.mark.parametrize("w", SHAPES, ids=lambda w: f"{w.name}-d{w.d_head}-{w.dtype}")
+def test_out_proj_every_token(w):
+    run_and_check(w)
+
+
+def test_out_proj_main_250m_sampled():
+    w = W.WORKLOADS["main_250m"]
+    BT = w.B * w.T
+    rng = np.random.default_rng(0)
+    tok = np.unique(np.concatenate([np.arange(0, BT, BT // 256), rng.integers(0, BT, 128), [0, BT - 1]]))
+    run_and_check(w, tok)
+
+
+def test_out_proj_after_decode_and_without_write_back():
+    w = W.WORKLOADS["decode_b64"]
+    inp = W.make_inputs(w)
+    dec = gpu_decode(w, inp)
+    wo = W.make_w_o(w)
+    slots = dec["out"].reshape(w.B, -1, w.d_head)
+    y, after = gpu_out_proj(w, slots, dec["p_tilde"], wo)
+    assert torch.equal(after, slots)
+    check_out_proj(w, slots, dec["p_tilde"], wo, y, np.arange(w.B))
+    # without write-back the slots stay as given (NaN where the weighted ones were) and y is the same bits
+    y2, after2 = gpu_out_proj(w, slots, dec["p_tilde"], wo, write_weighted=False)
+    assert torch.equal(y2, y)
+    kG = w.k * w.G
+    assert torch.isnan(after2[:, kG]).all()
+    assert torch.equal(after2[:, :kG], slots[:, :kG]) and torch.equal(after2[:, kG + 1:], slots[:, kG + 1:])
+    say(f"[{w.name}] out_proj after decode ok")

@@ -151,6 +151,23 @@ def make_inputs(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Te
     return out
 
 
+def make_w_o(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
+    """Draw the output-projection weight [d_model, S * d_head] of workload ``w``,
+    N(0, w_std^2) in the workload dtype, from a generator of its own (seed +
+    1000003), so the draws of ``make_inputs`` are unchanged."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((w.seed if seed is None else seed) + 1000003)
+    S = w.k * w.G + (w.G if w.route_mode else 1) + w.n_shared
+    return _randn(gen, (w.d_model, S * w.d_head), w.w_std).to(torch_dtype(w))
+
+
+def out_proj_flops(w: Workload, n_tok: Optional[int] = None) -> float:
+    """Output-projection FLOPs: 2 * tokens * d_model * S * d_head."""
+    S = w.k * w.G + (w.G if w.route_mode else 1) + w.n_shared
+    n = w.B * w.T if n_tok is None else n_tok
+    return 2.0 * n * w.d_model * S * w.d_head
+
+
 def attention_flops(w: Workload, lens=None) -> float:
     """Active-head attention FLOPs (QK^T and PV multiply-adds, 2 FLOPs each).
 
