@@ -17,13 +17,16 @@ divided by the whole step's time).  The same JSON line carries:
                 lengths in [4096, 8192]): gqe_attn_decode timed alone, bytes of
                 K/V it must read over its time, against the HBM peak;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
-  long_context  T=32768 GQE vs all-active GQA on the same inputs.
+  long_context  T=32768 GQE vs all-active GQA on the same inputs;
+  out_proj      the next step after the path, outside the timed step: the
+                output projection over the kG+2 slots fused with slot assembly
+                (gqe_out_proj) on the step's own slots, against the bf16 peak.
 
 --graph also times the step replayed from one HIP graph of the four calls
 (on this stack replaying is not faster than launching them one by one).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu] [--no-context] [--no-decode]
-       python bench.py --only {step,prefill,decode,copy} --steps K   (profiler runs)
+       python bench.py --only {step,prefill,outproj,decode,copy} --steps K   (profiler runs)
 """
 from __future__ import annotations
 
@@ -54,7 +57,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="also time the step replayed from one HIP graph")
-    ap.add_argument("--only", choices=["step", "prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["step", "prefill", "outproj", "decode", "copy"], default=None,
                     help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
 
@@ -228,6 +231,36 @@ def decode_leg(torch, dev, steps):
                          "algorithmic_bytes": nbytes, "kernel": "gqe_attn_decode (split KV chunks + merge)"}}
 
 
+def out_proj_leg(p, torch, steps):
+    """The attention output projection fused with slot assembly (gqe_out_proj) on the step's own slots:
+    y = W_o h over the S = kG+2 concatenated slots, bf16 MFMA with fp32 accumulation.  Timed beside it,
+    for context only, hipBLASLt's plain bf16 GEMM (torch.mm) of slots that were already assembled and
+    cast to bf16, with a bf16 result: it does neither the assembly nor the fp32 output."""
+    import workloads as W
+    w, G = p.w, p.G
+    wo = W.make_w_o(w).to(p.x.device)
+    BT = w.B * w.T
+    y = torch.empty((BT, w.d_model), dtype=torch.float32, device=p.x.device)
+    slots = p.out.view(BT, -1)
+
+    def op():
+        G.gqe_out_proj(p.d, p.out, p.r["p_tilde"], wo, y, False)
+
+    hb = slots.to(torch.bfloat16)
+    wt = wo.t()
+
+    def lib():
+        torch.mm(hb, wt)
+
+    warm([op, lib], torch)
+    t_op, t_lib = time_calls([op, lib], steps, torch)
+    fl = W.out_proj_flops(w)
+    tf = fl / (t_op * 1e-3) / 1e12
+    return {"workload": w.name, "kernel": f"out_proj_bf16_kernel<{w.d_head}> (gqe_out_proj)", "us": t_op * 1e3,
+            "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl, "shape_mnk": [BT, w.d_model, slots.shape[1]],
+            "context_torch_mm_bf16_us": t_lib * 1e3}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
@@ -273,6 +306,14 @@ def only(args, torch):
         for _ in range(args.steps):
             p.attn()
             p.assemble()
+    elif args.only == "outproj":
+        w = W.WORKLOADS["main_250m"]
+        p = Prefill(w, W.make_inputs(w), dev)
+        p.step()
+        wo = W.make_w_o(w).to(dev)
+        y = torch.empty((w.B * w.T, w.d_model), dtype=torch.float32, device=dev)
+        for _ in range(args.steps):
+            G.gqe_out_proj(p.d, p.out, p.r["p_tilde"], wo, y, False)
     else:
         w = W.WORKLOADS["decode_b64"]
         inp = W.make_inputs(w)
@@ -358,6 +399,7 @@ def main():
                      "kernel": f"prefill_bf16_kernel<{w.d_head}> (the one kernel of gqe_attn_prefill_heads)",
                      "algorithmic_flops_per_launch": fl},
     }
+    line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
     del p
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -28,14 +28,17 @@ namespace gqe {
 constexpr int kOpBN = 128;   // output features per tile
 constexpr int kOpPad = 8;    // bf16 elements of LDS row padding (16 bytes)
 
-// Tile shape per d_head: BM tokens, TPR threads per token, each holding AV
-// fp32 values of a slot row and of the weighted sum (at d_head = 128 two
-// threads per token would need 128 such registers and spill).
+// Tile shape per d_head.  A slot row of a token (D fp32 values) is read by
+// LPR = D/4 consecutive lanes with 16-byte loads, RPP = 256/LPR rows per
+// pass, NP passes for the tile's BM tokens; a thread then holds NP x 4 values
+// of the slot and of the weighted sum (BM = 64 at d_head = 128 keeps that at
+// 32 registers each).
 template <int D>
 struct OpTile {
     static constexpr int BM = D >= 128 ? 64 : 128;
-    static constexpr int TPR = 256 / BM;
-    static constexpr int AV = D / TPR;
+    static constexpr int LPR = D / 4;
+    static constexpr int RPP = 256 / LPR;
+    static constexpr int NP = BM / RPP;
     static constexpr int RB = BM / 64;   // 32-row blocks per wave
 };
 
@@ -57,7 +60,8 @@ __global__ __launch_bounds__(256, 2) void out_proj_bf16_kernel(float* __restrict
                                                                long long BT, int d_model, int G, int k, int n_shared,
                                                                int mode, int S, int nM, int nN, int write_weighted)
 {
-    constexpr int BM = OpTile<D>::BM, TPR = OpTile<D>::TPR, AV = OpTile<D>::AV, RB = OpTile<D>::RB;
+    constexpr int BM = OpTile<D>::BM, LPR = OpTile<D>::LPR, RPP = OpTile<D>::RPP, NP = OpTile<D>::NP;
+    constexpr int RB = OpTile<D>::RB;
     constexpr int PA = D + kOpPad;
     constexpr int BCH = kOpBN * D / 8 / 256;   // 16-byte W_o chunks per thread and stage
     __shared__ __attribute__((aligned(16))) uint16_t sA[BM * PA];
@@ -76,23 +80,32 @@ __global__ __launch_bounds__(256, 2) void out_proj_bf16_kernel(float* __restrict
     const int nroute = mode ? G : 1;
     const size_t Ktot = (size_t)S * D;
 
-    // this thread's token row and part of the slot (A side)
-    const int arow = tid / TPR, acol = (tid % TPR) * AV;
-    const long long tok = m0 + arow;
-    const bool tok_ok = tok < BT;
-    const long long tl = tok_ok ? tok : BT - 1;
-    const float* arow_p = out + (size_t)tl * S * D + acol;
-    const float* pt = p_tilde + (size_t)tl * kG;
+    // A side: this thread's rows arow0 + RPP p (p < NP), values acol .. acol+3.
+    // Buffer loads over the tile's rows only: 32-bit offsets, and rows past
+    // B*T fall outside the resource and read as zero (they are never stored).
+    const int arow0 = tid / LPR, acol = (tid % LPR) * 4;
+    const int rows = (int)(BT - m0 < BM ? BT - m0 : BM);
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(out + (size_t)m0 * S * D), 0,
+                                                                         rows * S * D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc((void*)(p_tilde + (size_t)m0 * kG), 0,
+                                                                         rows * kG * 4, 0x00020000);
 
-    f32x4 ra[AV / 4];
-    float rp = 0.f;
+    f32x4 ra[NP];
+    float rp[NP];
     u32x4 rb[BCH];
     auto load = [&](int i) {
         const int sl = op_slot(i, G, k, mode);
         if (sl < kG || sl >= kG + nroute) {
 #pragma unroll
-            for (int q = 0; q < AV / 4; ++q) ra[q] = *(const f32x4*)(arow_p + (size_t)sl * D + 4 * q);
-            if (sl < kG) rp = pt[sl];
+            for (int p = 0; p < NP; ++p)
+                ra[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rA, ((arow0 + RPP * p) * S * D + sl * D + acol) * 4, 0, 0));
+            if (sl < kG) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    rp[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rP, ((arow0 + RPP * p) * kG + sl) * 4, 0, 0));
+            }
         }
 #pragma unroll
         for (int c = 0; c < BCH; ++c) {
@@ -102,45 +115,42 @@ __global__ __launch_bounds__(256, 2) void out_proj_bf16_kernel(float* __restrict
         }
     };
 
-    float wacc[AV];
+    f32x4 wacc[NP];
 #pragma unroll
-    for (int v = 0; v < AV; ++v) wacc[v] = 0.f;
+    for (int p = 0; p < NP; ++p) wacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // stage i into LDS: the slot as bf16 (a hard slot also adds into the
     // weighted sum; the weighted stage uses that sum and may write it back)
     auto store = [&](int i) {
         const int sl = op_slot(i, G, k, mode);
-        float av[AV];
+        f32x4 av[NP];
         if (sl < kG) {
 #pragma unroll
-            for (int q = 0; q < AV / 4; ++q)
+            for (int p = 0; p < NP; ++p) {
+                av[p] = ra[p];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    av[4 * q + e] = ra[q][e];
-                    wacc[4 * q + e] = fmaf(rp, ra[q][e], wacc[4 * q + e]);
-                }
+                for (int e = 0; e < 4; ++e) wacc[p][e] = fmaf(rp[p], ra[p][e], wacc[p][e]);
+            }
         } else if (sl < kG + nroute) {
 #pragma unroll
-            for (int v = 0; v < AV; ++v) av[v] = wacc[v];
-            if (write_weighted && tn == 0 && tok_ok) {
-                float* dst = out + (size_t)tok * S * D + (size_t)sl * D + acol;
+            for (int p = 0; p < NP; ++p) av[p] = wacc[p];
+            if (write_weighted && tn == 0) {
 #pragma unroll
-                for (int q = 0; q < AV / 4; ++q)
-                    *(f32x4*)(dst + 4 * q) = f32x4{wacc[4 * q], wacc[4 * q + 1], wacc[4 * q + 2], wacc[4 * q + 3]};
+                for (int p = 0; p < NP; ++p) {
+                    const long long t = m0 + arow0 + RPP * p;
+                    if (t < BT) *(f32x4*)(out + (size_t)t * S * D + (size_t)sl * D + acol) = wacc[p];
+                }
             }
 #pragma unroll
-            for (int v = 0; v < AV; ++v) wacc[v] = 0.f;
+            for (int p = 0; p < NP; ++p) wacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
         } else {
 #pragma unroll
-            for (int q = 0; q < AV / 4; ++q)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) av[4 * q + e] = ra[q][e];
+            for (int p = 0; p < NP; ++p) av[p] = ra[p];
         }
 #pragma unroll
-        for (int q = 0; q < AV / 8; ++q) {
-            const u32x4 pk = {pack_bf2(av[8 * q], av[8 * q + 1]), pack_bf2(av[8 * q + 2], av[8 * q + 3]),
-                              pack_bf2(av[8 * q + 4], av[8 * q + 5]), pack_bf2(av[8 * q + 6], av[8 * q + 7])};
-            *(u32x4*)&sA[arow * PA + acol + 8 * q] = pk;
+        for (int p = 0; p < NP; ++p) {
+            const uint32_t lo = pack_bf2(av[p][0], av[p][1]), hi = pack_bf2(av[p][2], av[p][3]);
+            *(uint2*)&sA[(arow0 + RPP * p) * PA + acol] = make_uint2(lo, hi);
         }
 #pragma unroll
         for (int c = 0; c < BCH; ++c) {
