@@ -47,10 +47,18 @@ typedef struct {
     int32_t B, T, d_model, H_q, H_kv, k, d_head, n_shared, causal, route_mode;
 } ora_desc;
 
+/* Weighted slots: route_mode 0 one summed over groups ([note] §3-2 (4)), 1 one
+ * per group, 2 none (the "hard concat only" row of the [note] §5-1 ablation
+ * table). */
+static int ora_nroute(const ora_desc* D)
+{
+    return D->route_mode == 0 ? 1 : D->route_mode == 1 ? D->H_kv : 0;
+}
+
 static int ora_nslots(const ora_desc* D)
 {
     int G = D->H_kv;
-    return D->k * G + (D->route_mode ? G : 1) + D->n_shared;
+    return D->k * G + ora_nroute(D) + D->n_shared;
 }
 
 int ora_num_slots(const ora_desc* D) { return ora_nslots(D); }
@@ -214,6 +222,7 @@ static void attend(const double* q, const double* Kh, const double* Vh, int64_t 
  *   out[g*k + j]        hard slot: o_{t,g,e} of the j-th kept expert (not averaged)
  *   mode 0: out[kG]     h_route = sum_g sum_j ptilde * o, summed g then j
  *   mode 1: out[kG + g] per-group weighted sum sum_j ptilde * o
+ *   mode 2: no weighted slot
  *   out[last]           the shared head (when present)
  * o_r [G*k, dh] holds the kept-expert outputs in hard-slot order.
  */
@@ -221,11 +230,11 @@ static void assemble(const ora_desc* D, const double* o_r, const double* o_sh, c
                      double* out)
 {
     const int G = D->H_kv, k = D->k, dh = D->d_head;
-    const int nroute = D->route_mode ? G : 1;
+    const int nroute = ora_nroute(D);
     memcpy(out, o_r, sizeof(double) * (size_t)G * k * dh);
     double* route = out + (int64_t)G * k * dh;
     for (int i = 0; i < nroute * dh; ++i) route[i] = 0.0;
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G && nroute; ++g)
         for (int j = 0; j < k; ++j) {
             double* dst = route + (D->route_mode ? g : 0) * dh;
             for (int d = 0; d < dh; ++d) dst[d] += pt[g * k + j] * o_r[(g * k + j) * dh + d];
@@ -321,7 +330,7 @@ void ora_attend_rows(const ora_desc* D, const double* q_routed, const double* q_
 void ora_assemble_rows(const ora_desc* D, const double* ptilde, int64_t n_list, double* slots)
 {
     const int G = D->H_kv, k = D->k, dh = D->d_head;
-    const int S = ora_nslots(D), nroute = D->route_mode ? G : 1;
+    const int S = ora_nslots(D), nroute = ora_nroute(D);
 #pragma omp parallel
     {
         double* tmp = (double*)malloc(sizeof(double) * (size_t)S * dh);

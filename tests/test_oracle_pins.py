@@ -290,6 +290,18 @@ def test_top1_weighted_slot_is_sum_of_hard_slots():
     outm = oracle.prefill(oracle.desc(wm), inp)["out"]
     assert np.array_equal(outm[:, w.G:2 * w.G], outm[:, :w.G])
 
+def test_hard_concat_only_drops_the_weighted_slot():
+    # route mode 2 ("hard concat only", [note] §5-1 ablation table): the same hard and shared slots,
+    # bit for bit, and no weighted slot in between
+    w = wl(H_q=12, H_kv=3, k=2)
+    inp = W.make_inputs(w)
+    a = oracle.prefill(oracle.desc(w), inp)["out"]
+    d2 = oracle.desc(w.replace(route_mode=2))
+    b = oracle.prefill(d2, inp)["out"]
+    kG = w.G * w.k
+    assert oracle.num_slots(d2) == kG + 1 and b.shape[1] == kG + 1
+    assert np.array_equal(b[:, :kG], a[:, :kG]) and np.array_equal(b[:, kG], a[:, kG + 1])
+
 def test_permuting_experts_inside_a_group_keeps_weighted_and_shared_slots():
     w = wl(H_q=12, H_kv=3, k=2)
     inp = W.make_inputs(w)
