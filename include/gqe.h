@@ -15,7 +15,8 @@
  *   G = H_kv, E = H_q / H_kv, N = G * E (routed experts), global expert index
  *   n = g * E + e (the GQA query-head index of the GQA tutorial, freeguideonline,
  *   "GQA 核心原理与计算流程" step 3).  BT = B * T.
- *   S = k*G + (route_mode ? G : 1) + n_shared output slots per token.
+ *   S = k*G + R + n_shared output slots per token, R = 1, G or 0 weighted
+ *   slots for route_mode 0, 1 or 2.
  *   Slot order: hard slots g-major then ascending expert index, weighted
  *   slot(s), shared slot.  The shared head's projection is W_q row block N
  *   and it attends KV head 0.  Attention scale is 1/sqrt(d_head).
@@ -68,7 +69,9 @@ typedef struct {
     int32_t n_shared;   /* 0 or 1: the always-on shared head (reads KV head 0) */
     int32_t causal;     /* 1: key s is visible to query t iff s <= t; 0: all keys */
     int32_t route_mode; /* 0: one weighted slot summed over groups (study note
-                           §3-2 (4)); 1: one weighted slot per group */
+                           §3-2 (4)); 1: one weighted slot per group; 2: no
+                           weighted slot (the "hard concat only" row of the
+                           study note's §5-1 ablation table) */
     int32_t dtype;      /* gqe_dtype of x, W_router, W_q, q, K, V; outputs are fp32 */
 } gqe_desc;
 

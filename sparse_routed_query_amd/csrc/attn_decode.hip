@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
             float acc = 0.f;
             for (int h = 0; h < kG; ++h) acc = fmaf(pt[h], s_hard[h * D + d], acc);
             orow[(size_t)kG * D + d] = acc;
-        } else {
+        } else if (route_mode == 1) {
             for (int g = 0; g < G; ++g) {
                 float acc = 0.f;
                 for (int j = 0; j < k; ++j) acc = fmaf(pt[g * k + j], s_hard[(g * k + j) * D + d], acc);

@@ -689,7 +689,7 @@ int launch_assemble(const float* p_tilde, float* out, long long n_tok, int G, in
                     hipStream_t st)
 {
     const long long n = n_tok * (D / 4);
-    if (n == 0) return 0;
+    if (n == 0 || route_mode == 2) return 0;   // mode 2 has no weighted slot
     assemble_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p_tilde, out, n_tok, G, k, D, S, route_mode);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -29,7 +29,7 @@ int check_desc(const gqe_desc* d, Shape& s)
     if (d->k < 1 || d->k > E) return GQE_ERR_INVALID;
     if (d->n_shared != 0 && d->n_shared != 1) return GQE_ERR_INVALID;
     if (d->causal != 0 && d->causal != 1) return GQE_ERR_INVALID;
-    if (d->route_mode != 0 && d->route_mode != 1) return GQE_ERR_INVALID;
+    if (d->route_mode < 0 || d->route_mode > 2) return GQE_ERR_INVALID;
     if (d->dtype != GQE_F32 && d->dtype != GQE_BF16) return GQE_ERR_INVALID;
     if (d->d_head != 32 && d->d_head != 64 && d->d_head != 128) return GQE_ERR_UNSUPPORTED;
     if (d->H_q > kMaxHq || d->k > kMaxK) return GQE_ERR_UNSUPPORTED;
@@ -39,7 +39,7 @@ int check_desc(const gqe_desc* d, Shape& s)
     if (BT * d->H_kv * d->k >= (1ll << 31) || (long long)d->T * d->k >= (1ll << 31) - 256) return GQE_ERR_UNSUPPORTED;
     s.B = d->B; s.T = d->T; s.dm = d->d_model; s.Hq = d->H_q; s.G = d->H_kv; s.E = E; s.k = d->k;
     s.D = d->d_head; s.ns = d->n_shared; s.causal = d->causal; s.mode = d->route_mode;
-    s.S = d->k * d->H_kv + (d->route_mode ? d->H_kv : 1) + d->n_shared;
+    s.S = d->k * d->H_kv + (d->route_mode == 0 ? 1 : d->route_mode == 1 ? d->H_kv : 0) + d->n_shared;
     s.bf16 = d->dtype == GQE_BF16;
     s.BT = BT;
     return GQE_OK;

@@ -42,12 +42,16 @@ struct OpTile {
     static constexpr int RB = BM / 64;   // 32-row blocks per wave
 };
 
-// Slot read at K stage i (0 <= i < S).  Mode 0: slot order (hard, weighted,
-// shared).  Mode 1: each group's hard slots, then that group's weighted slot,
-// so the weighted sum is complete when its stage comes; the shared slot last.
+// Weighted slots of a route mode: one (0), one per group (1) or none (2).
+__device__ __forceinline__ int op_nroute(int G, int mode) { return mode == 0 ? 1 : mode == 1 ? G : 0; }
+
+// Slot read at K stage i (0 <= i < S).  Modes 0 and 2: slot order (hard,
+// weighted if any, shared).  Mode 1: each group's hard slots, then that
+// group's weighted slot, so the weighted sum is complete when its stage
+// comes; the shared slot last.
 __device__ __forceinline__ int op_slot(int i, int G, int k, int mode)
 {
-    if (mode == 0) return i;
+    if (mode != 1) return i;
     const int kG = G * k;
     if (i >= (k + 1) * G) return i;   // the shared slot, S - 1
     const int g = i / (k + 1), r = i - g * (k + 1);
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void out_proj_bf16_kernel(float* __restrict
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kG = G * k;
-    const int nroute = mode ? G : 1;
+    const int nroute = op_nroute(G, mode);
     const size_t Ktot = (size_t)S * D;
 
     // A side: this thread's rows arow0 + RPP p (p < NP), values acol .. acol+3.
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(float* __restrict__ o
     if (gid >= BT * d_model) return;
     const long long t = gid / d_model;
     const int n = (int)(gid % d_model);
-    const int kG = G * k, nroute = mode ? G : 1;
+    const int kG = G * k, nroute = op_nroute(G, mode);
     float* row = out + (size_t)t * S * D;
     const float* pt = p_tilde + (size_t)t * kG;
     const float* wr = w_o + (size_t)n * S * D;

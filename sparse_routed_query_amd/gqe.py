@@ -54,7 +54,7 @@ class GqeDesc(ctypes.Structure):
 
     @property
     def S(self) -> int:
-        return self.k * self.H_kv + (self.H_kv if self.route_mode else 1) + self.n_shared
+        return self.k * self.H_kv + (1, self.H_kv, 0)[self.route_mode] + self.n_shared
 
     @property
     def torch_dtype(self) -> torch.dtype:

@@ -182,7 +182,7 @@ def gpu_out_proj(w: W.Workload, out_slots: torch.Tensor, p_tilde: torch.Tensor, 
     """gqe_out_proj on the given slots [B*T, S, d_head] with the weighted slot(s) set to NaN first, so
     that a read of them would show in y.  Returns (y, slots after the call) on the CPU."""
     d = G.desc_from(w)
-    kG, nr = w.k * w.G, (w.G if w.route_mode else 1)
+    kG, nr = w.k * w.G, (1, w.G, 0)[w.route_mode]
     o = out_slots.reshape(w.B * w.T, d.S, w.d_head).clone()
     o[:, kG:kG + nr] = float("nan")
     od = o.to(dev)

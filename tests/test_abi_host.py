@@ -52,6 +52,9 @@ def test_num_slots_and_workspace_sizes():
     assert G.gqe_num_slots(main(route_mode=1)) == 17            # 8 hard + 8 per-group + shared
     assert G.gqe_num_slots(main(k=2, n_shared=0)) == 17         # dense: 16 hard + weighted
     assert G.gqe_num_slots(main(H_q=15)) == -1
+    assert G.gqe_num_slots(main(route_mode=2)) == 9             # 8 hard + shared ("hard concat only")
+    assert G.gqe_num_slots(main(route_mode=2, n_shared=0)) == 8
+    assert G.gqe_num_slots(main(route_mode=3)) == -1
     nblk = (4 * 4096 + 31) // 32
     assert G.gqe_route_workspace_bytes(main()) >= 2 * nblk * 16 * 4
     dd = main(B=64, T=1)
@@ -67,7 +70,7 @@ def test_num_slots_and_workspace_sizes():
     (dict(k=3), INVALID),                    # k > E = 2
     (dict(n_shared=2), INVALID),
     (dict(causal=5), INVALID),
-    (dict(route_mode=2), INVALID),
+    (dict(route_mode=3), INVALID),
     (dict(B=-1), INVALID),
     (dict(d_head=96), UNSUPPORTED),
     (dict(d_model=1000), UNSUPPORTED),       # bf16 needs d_model % 64 == 0

@@ -41,6 +41,7 @@ SHAPES = [
     small(d_model=320, name="ragged_cols"),               # a 64-wide last column tile
     small(d_head=32, name="d32"), small(d_head=128, name="d128"),
     small(route_mode=1, name="per_group_slots"),
+    small(route_mode=2, name="hard_only"),
     small(n_shared=0, name="no_shared"),
     small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="kG8"),
     small(H_q=4, H_kv=1, k=2, name="G1"),

@@ -66,6 +66,7 @@ EDGE = [
     small(causal=0, name="noncausal"),
     small(n_shared=0, name="no_shared"),
     small(route_mode=1, name="per_group_slots"),
+    small(route_mode=2, name="hard_only"), small(route_mode=2, n_shared=0, k=1, name="hard_only_no_shared"),
     small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="zipf"),
     small(dtype="f32", T=100, d_model=96, name="f32_d64"),
     small(dtype="f32", T=70, d_head=128, d_model=64, k=1, name="f32_d128"),
@@ -182,7 +183,8 @@ def test_split_merge_is_deterministic_and_resets_its_counters():
     assert float(err.max()) <= 1e-2 and float(err.mean()) <= 1e-4
 
 
-@pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(dtype="f32", d_head=32),
+@pytest.mark.parametrize("w", [small(), small(route_mode=1, name="small_mode1"), small(route_mode=2, name="small_mode2"),
+                               small(dtype="f32", d_head=32),
                                SPLIT[0]], ids=lambda w: f"{w.name}-{w.dtype}")
 def test_heads_then_assemble_equals_attn_prefill(w):
     """gqe_attn_prefill_heads + gqe_assemble give exactly gqe_attn_prefill's output (same workspace)."""
@@ -191,7 +193,7 @@ def test_heads_then_assemble_equals_attn_prefill(w):
     out = torch.full_like(ref, float("nan"))
     G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out, G.prefill_workspace(d, "cuda"))
     kG = w.k * w.G
-    n_w = w.G if w.route_mode else 1
+    n_w = (1, w.G, 0)[w.route_mode]
     torch.cuda.synchronize()
     assert torch.isnan(out[:, :, kG:kG + n_w]).all(), "heads call wrote the weighted slots"
     G.gqe_assemble(d, r["p_tilde"], out)
@@ -256,6 +258,7 @@ def decode_case(**kw):
 @pytest.mark.parametrize("w", [
     decode_case(),
     decode_case(k=2, route_mode=1, name="dec_k2_mode1"),
+    decode_case(k=2, route_mode=2, name="dec_k2_hard_only"),
     decode_case(d_head=128, H_q=12, H_kv=3, k=3, name="dec_d128_dense"),
     decode_case(d_head=32, n_shared=0, name="dec_d32_noshared"),
     decode_case(dtype="f32", name="dec_f32"),
