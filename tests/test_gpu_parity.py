@@ -79,6 +79,18 @@ def test_small_shapes_every_token(w):
     full_prefill_check(w)
 
 
+# Sweeps of the expert pool E and of k (the study note's E/k sweeps; k chosen at inference is just a
+# descriptor value), every token, both with the summed and the per-group weighted slots.
+EK = [(2, 1), (4, 1), (4, 2), (4, 3), (8, 2), (8, 5), (16, 4), (16, 8)]
+
+
+@pytest.mark.parametrize("E,k", EK, ids=lambda v: str(v))
+def test_expert_pool_and_k_sweep(E, k):
+    G = 64 // E if E > 4 else 4
+    w = small(B=1, T=200, H_q=G * E, H_kv=G, k=k, route_mode=int(E % 2 == 0 and k % 2 == 1), name=f"E{E}k{k}")
+    full_prefill_check(w)
+
+
 def test_empty_batch():
     w = small(B=0, name="empty")
     d = G.desc_from(w)
