@@ -219,12 +219,26 @@ def decode_leg(torch, dev, steps):
         it[0] += 1
         G.gqe_attn_decode(d, q["q_routed"], q["q_shared"], kc, vc, lens, r["p_tilde"], out, ws)
 
-    warm([route, qp, attn], torch)
-    t_route, t_qp, t_attn = time_calls([route, qp, attn], steps, torch)
+    # the same caches in pages of 16 positions, stored in a random order (two copies alternated as above)
+    PAGE = 16
+    pages = [W.make_paged_cache(w, inp, PAGE, seed=s) for s in (w.seed, w.seed + 1)]
+    pages = [{k: v.to(dev) for k, v in pg.items()} for pg in pages]
+    ws_p = torch.empty(G.gqe_decode_workspace_bytes(d, pages[0]["block_table"].shape[1] * PAGE), dtype=torch.uint8,
+                       device=dev)
+
+    def attn_paged():
+        pg = pages[it[0] & 1]
+        it[0] += 1
+        G.gqe_attn_decode_paged(d, q["q_routed"], q["q_shared"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                lens, r["p_tilde"], out, ws_p)
+
+    warm([route, qp, attn, attn_paged], torch)
+    t_route, t_qp, t_attn, t_paged = time_calls([route, qp, attn, attn_paged], steps, torch)
     nbytes = W.decode_kv_bytes(w, inp["lens"])
     gbs = nbytes / (t_attn * 1e-3) / 1e9
     return {"workload": w.name, "value": gbs, "unit": "GB/s", "metric": "decode attention GB/s (K/V bytes read once)",
             "attn_us": t_attn * 1e3, "step_us": (t_route + t_qp + t_attn) * 1e3,
+            "paged16_attn_us": t_paged * 1e3, "paged16_gbs": nbytes / (t_paged * 1e-3) / 1e9,
             "route_us": t_route * 1e3, "qproj_us": t_qp * 1e3,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": traffic_for("decode"),

@@ -248,6 +248,30 @@ int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* s
 int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
                  int32_t write_weighted, void* stream);
 
+/*
+ * gqe_attn_decode_paged -- gqe_attn_decode over a paged KV cache, the layout
+ * of paged attention (GQA tutorial, freeguideonline, "推理优化：连续批处理与
+ * 分页注意力": GQA pairs with continuous batching and paged attention, the
+ * cache being stored per KV group).  Same definition and outputs as
+ * gqe_attn_decode; only where the keys and values live differs.
+ * In:  k_pages, v_pages [num_pages, H_kv, page_size, d_head] (dtype): each page
+ *      holds page_size consecutive positions of every KV head;
+ *      block_table [B, max_pages] int32: position p of sequence b is row
+ *      p % page_size of page block_table[b, p / page_size];
+ *      lens [B] int32 with 1 <= lens[b] <= max_pages * page_size;
+ *      q_routed, q_shared, p_tilde as for gqe_attn_decode.
+ * page_size is a power of two from 8 to 4096.  Page ids outside
+ * 0 .. num_pages-1 are clamped into that range (a bad table gives wrong
+ * results, never an access outside the pages).
+ * Out: out [B, S, d_head] fp32.
+ * Workspace: gqe_decode_workspace_bytes(desc, max_pages * page_size) bytes.
+ */
+int gqe_attn_decode_paged(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                          const void* k_pages, const void* v_pages, int32_t num_pages, int32_t page_size,
+                          int32_t max_pages, const int32_t* block_table, const int32_t* lens,
+                          const float* p_tilde, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
 

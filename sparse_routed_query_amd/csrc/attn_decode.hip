@@ -92,25 +92,65 @@ __device__ __forceinline__ float lanes_max(float v)
     else return v;
 }
 
-template <typename ET, int D>
+// PAGED != 0: the cache is [num_pages, G, page_size, D] and position pos of
+// sequence b is row pos % page_size of page block_table[b][pos / page_size]
+// (page ids outside 0 .. num_pages-1 are clamped, so a bad table reads wrong
+// data but never outside the pages); PAGED == 0: dense [B, G, L_max, D].
+// PAGED == 1 when a page holds at least the PPW positions a wave reads per
+// pass, 2 otherwise (see row_of below).
+template <typename ET, int D, int PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict__ q_routed,
                                                            const ET* __restrict__ q_shared,
                                                            const ET* __restrict__ kc, const ET* __restrict__ vc,
                                                            const int32_t* __restrict__ lens, float* __restrict__ part,
                                                            int G, int k, int n_shared, int L_max, int nch,
-                                                           float qscale)
+                                                           float qscale, const int32_t* __restrict__ block_table,
+                                                           int page_shift, int max_pages, int num_pages)
 {
     using SH = DcShape<ET, D>;
     constexpr int VEC = SH::VEC, LPP = SH::LPP, PPW = SH::PPW, PPP = SH::PPP, CH = SH::CH;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int L = min(max(lens[b], 0), L_max);   // never read outside the cache
     const int c0 = c * CH;
-    if (c0 >= L) return;
+    const int L = min(max(lens[b], 0), L_max);   // never read outside the cache
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int dq = (lane % LPP) * VEC;
     const int pp = tid / LPP;                    // = wave * PPW + position slot in the wave
-    const ET* K = kc + ((size_t)b * G + g) * (size_t)L_max * D;
-    const ET* V = vc + ((size_t)b * G + g) * (size_t)L_max * D;
+    // Paged: a wave's PPW positions of a pass start at a multiple of PPW, so
+    // when pages hold at least PPW positions (PAGED == 1) they lie in one page
+    // and the wave looks its page up once, with a scalar load.  Those loads
+    // take the table column clamped to its width (a pass past the end uses
+    // no page), not a bound from the sequence's length, so they are all
+    // issued at once, together with the length's load, without branches.
+    // Smaller pages (PAGED == 2) are looked up per lane.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int32_t* bt = PAGED ? block_table + (size_t)b * max_pages : nullptr;
+    int wpage[kDcPasses];
+    if constexpr (PAGED == 1) {
+#pragma unroll
+        for (int i = 0; i < kDcPasses; ++i) {
+            const int pos_w = c0 + i * PPP + wave_u * PPW;
+            wpage[i] = bt[min(pos_w >> page_shift, max_pages - 1)];
+        }
+        // keep the lookups here: left to itself the compiler moves each into
+        // its pass's branch below and waits for it there, one pass at a time
+#pragma unroll
+        for (int i = 0; i < kDcPasses; ++i) asm volatile("" : "+s"(wpage[i]));
+    }
+    if (c0 >= L) return;
+    auto row_of = [&](int i, int pos) -> size_t {   // element offset of position pos's row (pass i)
+        if constexpr (PAGED != 0) {
+            int id;
+            if constexpr (PAGED == 1) {
+                id = wpage[i];
+            } else {
+                id = bt[pos >> page_shift];
+            }
+            const int pg = min(max(id, 0), num_pages - 1);
+            return (((size_t)pg * G + g) << page_shift) + (pos & ((1 << page_shift) - 1));
+        } else {
+            return ((size_t)b * G + g) * (size_t)L_max + pos;
+        }
+    };
 
     u32x4 kr[kDcPasses], vr[kDcPasses];
 #pragma unroll
@@ -119,8 +159,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const ET* __restrict_
         if (pos < L) {
             // the cache is read once per step: non-temporal loads keep it from
             // displacing other data in the caches
-            kr[i] = __builtin_nontemporal_load((const u32x4*)(K + (size_t)pos * D + dq));
-            vr[i] = __builtin_nontemporal_load((const u32x4*)(V + (size_t)pos * D + dq));
+            const size_t r = row_of(i, pos) * D + dq;
+            kr[i] = __builtin_nontemporal_load((const u32x4*)(kc + r));
+            vr[i] = __builtin_nontemporal_load((const u32x4*)(vc + r));
         } else {
             kr[i] = u32x4{0, 0, 0, 0};
             vr[i] = u32x4{0, 0, 0, 0};
@@ -334,9 +375,20 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t st)
     const int nch = (a.L_max + CH - 1) / CH;
     const float qscale = 1.4426950408889634f / sqrtf((float)D);
     dim3 grid(nch, a.G, a.B);
-    decode_split_kernel<ET, D><<<grid, 256, 0, st>>>((const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache,
-                                                     (const ET*)a.v_cache, a.lens, (float*)a.workspace, a.G, a.k,
-                                                     a.n_shared, a.L_max, nch, qscale);
+    if (a.block_table && (1 << a.page_shift) >= DcShape<ET, D>::PPW)
+        decode_split_kernel<ET, D, 1><<<grid, 256, 0, st>>>(
+            (const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache, (const ET*)a.v_cache, a.lens,
+            (float*)a.workspace, a.G, a.k, a.n_shared, a.L_max, nch, qscale, a.block_table, a.page_shift, a.max_pages,
+            a.num_pages);
+    else if (a.block_table)
+        decode_split_kernel<ET, D, 2><<<grid, 256, 0, st>>>(
+            (const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache, (const ET*)a.v_cache, a.lens,
+            (float*)a.workspace, a.G, a.k, a.n_shared, a.L_max, nch, qscale, a.block_table, a.page_shift, a.max_pages,
+            a.num_pages);
+    else
+        decode_split_kernel<ET, D, 0><<<grid, 256, 0, st>>>(
+            (const ET*)a.q_routed, (const ET*)a.q_shared, (const ET*)a.k_cache, (const ET*)a.v_cache, a.lens,
+            (float*)a.workspace, a.G, a.k, a.n_shared, a.L_max, nch, qscale, nullptr, 0, 0, 0);
     const size_t lds = (size_t)a.G * a.k * D * sizeof(float);
     decode_merge_kernel<D><<<a.B, 64 * kDcMergeWaves, lds, st>>>((const float*)a.workspace, a.lens, a.p_tilde, a.out,
                                                                  a.G, a.k, a.n_shared, a.S, a.route_mode, nch, CH);

@@ -267,4 +267,37 @@ int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_sh
     return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
 }
 
+int gqe_attn_decode_paged(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k_pages,
+                          const void* v_pages, int32_t num_pages, int32_t page_size, int32_t max_pages,
+                          const int32_t* block_table, const int32_t* lens, const float* p_tilde, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.T != 1 || num_pages < 1 || max_pages < 1) return GQE_ERR_INVALID;
+    if (page_size < 8 || page_size > 4096 || (page_size & (page_size - 1)) != 0) return GQE_ERR_INVALID;
+    const long long L_max = (long long)max_pages * page_size;
+    if (L_max >= (1ll << 30) || (long long)num_pages * s.G * page_size * s.D >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    if (s.B == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k_pages));
+    GQE_TRY(need(v_pages));
+    GQE_TRY(need(block_table));
+    GQE_TRY(need(lens));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(out));
+    if (!workspace) return GQE_ERR_WORKSPACE;
+    GQE_TRY(need(workspace));
+    if (workspace_bytes < gqe::decode_workspace_bytes(s.B, s.G, s.k, s.ns, s.D, (int)L_max, s.bf16))
+        return GQE_ERR_WORKSPACE;
+    gqe::DecodeArgs a{q_routed, q_shared, k_pages, v_pages, lens, p_tilde, out, workspace,
+                      s.B, s.G, s.k, s.D, s.ns, s.mode, s.S, (int)L_max, s.bf16};
+    a.block_table = block_table;
+    a.page_shift = __builtin_ctz((unsigned)page_size);
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

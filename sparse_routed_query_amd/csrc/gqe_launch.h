@@ -85,6 +85,11 @@ struct DecodeArgs {
     void* workspace;
     int B, G, k, d_head, n_shared, route_mode, S, L_max;
     bool bf16;
+    // paged cache (block_table != NULL): k_cache / v_cache are [num_pages, G, page_size, d_head],
+    // position p of sequence b is row p % page_size of page block_table[b * max_pages + p / page_size];
+    // L_max = max_pages * page_size.  page_size is a power of two.
+    const int32_t* block_table = nullptr;
+    int page_shift = 0, max_pages = 0, num_pages = 0;
 };
 size_t decode_workspace_bytes(int B, int G, int k, int n_shared, int d_head, int L_max, bool bf16);
 int launch_decode(const DecodeArgs& a, hipStream_t st);

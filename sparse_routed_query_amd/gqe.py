@@ -27,7 +27,8 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 # Every symbol the C header declares (checked by the host tests).
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
-           "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode")
+           "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
+           "gqe_attn_decode_paged")
 
 
 class GqeError(RuntimeError):
@@ -109,6 +110,9 @@ def load():
         lib.gqe_decode_workspace_bytes.restype = Z
         lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
         lib.gqe_attn_decode.restype = I
+        i32 = ctypes.c_int32
+        lib.gqe_attn_decode_paged.argtypes = [D, P, P, P, P, i32, i32, i32, P, P, P, P, P, Z, P]
+        lib.gqe_attn_decode_paged.restype = I
         _lib = lib
     return _lib
 
@@ -233,6 +237,19 @@ def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, o
                                 _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check("gqe_attn_decode", rc)
+
+
+def gqe_attn_decode_paged(desc, q_routed, q_shared, k_pages, v_pages, block_table, lens, p_tilde, out, workspace,
+                          stream=None):
+    """k_pages, v_pages [num_pages, H_kv, page_size, d_head]; block_table [B, max_pages] int32."""
+    dt = desc.torch_dtype
+    rc = load().gqe_attn_decode_paged(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
+                                      _ptr(k_pages, dt, "k_pages"), _ptr(v_pages, dt, "v_pages"), k_pages.shape[0],
+                                      k_pages.shape[2], block_table.shape[1], _ptr(block_table, torch.int32, "block_table"),
+                                      _ptr(lens, torch.int32, "lens"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                      _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gqe_attn_decode_paged", rc)
 
 
 # ---------------------------------------------------------------- allocating wrappers

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -142,6 +142,18 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert dec(dd, w=None) == WORKSPACE
     assert dec(dd, wb=ws - 1) == WORKSPACE
     assert dec(dd, lens=MIS) == ALIGN
+    pws_ = G.gqe_decode_workspace_bytes(dd, 512 * 16)
+    pg = lambda desc, npg=100, P=16, mp=512, bt=A16, w=A16, wb=pws_: lib.gqe_attn_decode_paged(  # noqa: E731
+        by(desc), A16, A16, A16, A16, npg, P, mp, bt, A16, A16, A16, w, wb, None)
+    assert pg(main(B=64, T=2)) == INVALID       # one token per sequence
+    assert pg(dd, P=24) == INVALID              # page size must be a power of two ...
+    assert pg(dd, P=4) == INVALID               # ... from 8
+    assert pg(dd, npg=0) == INVALID
+    assert pg(dd, mp=0) == INVALID
+    assert pg(dd, bt=None) == INVALID
+    assert pg(dd, bt=MIS) == ALIGN
+    assert pg(dd, wb=pws_ - 1) == WORKSPACE     # sized for max_pages * page_size positions
+    assert pg(main(B=0, T=1), bt=None, w=None) == OK
 
 
 def test_python_binding_refuses_host_tensors():

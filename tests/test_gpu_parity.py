@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
 from gpu_parity_util import (check_out, check_prefill_given_q, check_qproj, check_route, full_decode_check,
                              full_prefill_check, gpu_decode, gpu_prefill, say)
@@ -353,3 +354,50 @@ def test_large_scores_move_the_softmax_reference():
     tok = np.arange(w.B * w.T)
     check_qproj(w, inp, gpu, agreed, tok)
     check_prefill_given_q(w, inp, gpu, agreed, tok)
+
+
+# ---------------------------------------------------------------- paged decode
+
+def paged_and_dense(w, page_size):
+    """gqe_attn_decode over the dense cache and gqe_attn_decode_paged over the same cache cut into pages
+    stored in a random order (unused pages and positions NaN), with the same routing and queries."""
+    inp = W.make_inputs(w)
+    pg = W.make_paged_cache(w, inp, page_size)
+    d = G.desc_from(w)
+    dev = "cuda"
+    x = inp["x"].reshape(w.B, w.d_model).to(dev)
+    br = inp["b_router"].to(dev) if inp["b_router"] is not None else None
+    r = G.route(d, x, inp["w_router"].to(dev), br)
+    q = G.qproj(d, x, inp["w_q"].to(dev), r)
+    lens = inp["lens"].to(dev)
+    dense = G.attn_decode(d, q, inp["k_cache"].to(dev), inp["v_cache"].to(dev), lens, r["p_tilde"])
+    out = torch.full_like(dense, float("nan"))
+    L_cap = pg["block_table"].shape[1] * page_size
+    ws = torch.empty(G.gqe_decode_workspace_bytes(d, L_cap), dtype=torch.uint8, device=dev)
+    G.gqe_attn_decode_paged(d, q["q_routed"], q["q_shared"], pg["k_pages"].to(dev), pg["v_pages"].to(dev),
+                            pg["block_table"].to(dev), lens, r["p_tilde"], out, ws)
+    torch.cuda.synchronize()
+    return inp, r, dense.cpu(), out.cpu()
+
+
+@pytest.mark.parametrize("w,page_size", [
+    (decode_case(), 8), (decode_case(), 64), (decode_case(), 4096),
+    (decode_case(k=2, route_mode=1, name="dec_k2_mode1"), 16),
+    (decode_case(d_head=128, H_q=12, H_kv=3, k=3, name="dec_d128"), 32),
+    (decode_case(dtype="f32", name="dec_f32"), 16),
+    (W.WORKLOADS["decode_b64"], 16), (W.WORKLOADS["decode_b64"], 256),
+], ids=lambda v: v.name if isinstance(v, W.Workload) else f"page{v}")
+def test_paged_decode_equals_dense(w, page_size):
+    """Only where K and V live differs, so the outputs are the dense call's, bit for bit."""
+    _, _, dense, paged = paged_and_dense(w, page_size)
+    assert torch.isfinite(paged).all()          # no NaN page row or spare page was read
+    assert torch.equal(paged, dense)
+
+
+def test_paged_decode_against_the_oracle():
+    w = decode_case(B=7, L_lo=1, L_hi=300, L_max=300, name="dec_paged_oracle")
+    inp, r, _, paged = paged_and_dense(w, 32)
+    orc = oracle.decode(oracle.desc(w), inp["x"].reshape(w.B, w.d_model), inp["w_router"], inp["b_router"],
+                        inp["w_q"], inp["k_cache"], inp["v_cache"], inp["lens"])
+    assert np.array_equal(r["sel"].cpu().numpy(), orc["sel"]) or orc["tie"].any()
+    check_out(w, paged.numpy(), orc["out"], "paged decode out")

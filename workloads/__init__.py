@@ -151,6 +151,38 @@ def make_inputs(w: Workload, seed: Optional[int] = None, lens: Optional[torch.Te
     return out
 
 
+def make_paged_cache(w: Workload, inp: dict, page_size: int, spare: int = 3, seed: Optional[int] = None) -> dict:
+    """The decode caches of ``inp`` cut into pages of ``page_size`` positions and stored in a random order.
+
+    Returns ``k_pages``/``v_pages`` [num_pages, H_kv, page_size, d_head] and ``block_table`` [B, max_pages]
+    int32 (max_pages = L_max / page_size rounded up): page j of sequence b holds positions
+    j*page_size .. (j+1)*page_size-1 of ``inp``'s cache.  Only pages that hold positions below the
+    sequence's length are stored; ``spare`` more pages and the positions past each length are NaN, and
+    table entries past a sequence's last page point at random pages, so a read of anything outside the
+    sequence shows.  A pure rearrangement of the dense draws (generator seed + 2000003).
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((w.seed if seed is None else seed) + 2000003)
+    kc, vc, lens = inp["k_cache"], inp["v_cache"], inp["lens"]
+    B, H, L_max, D = kc.shape
+    max_pages = -(-L_max // page_size)
+    used = [-(-int(l) // page_size) for l in lens]
+    num_pages = sum(used) + spare
+    order = torch.randperm(num_pages, generator=gen)
+    kp = torch.full((num_pages, H, page_size, D), float("nan"), dtype=kc.dtype)
+    vp = torch.full_like(kp, float("nan"))
+    table = torch.randint(0, num_pages, (B, max_pages), generator=gen, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for j in range(used[b]):
+            pg = int(order[nxt]); nxt += 1
+            table[b, j] = pg
+            lo, hi = j * page_size, min((j + 1) * page_size, L_max)
+            kp[pg, :, :hi - lo] = kc[b, :, lo:hi]
+            vp[pg, :, :hi - lo] = vc[b, :, lo:hi]
+    return dict(k_pages=kp, v_pages=vp, block_table=table)
+
+
 def make_w_o(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
     """Draw the output-projection weight [d_model, S * d_head] of workload ``w``,
     N(0, w_std^2) in the workload dtype, from a generator of its own (seed +
