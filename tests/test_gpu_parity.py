@@ -401,3 +401,53 @@ def test_paged_decode_against_the_oracle():
                         inp["w_q"], inp["k_cache"], inp["v_cache"], inp["lens"])
     assert np.array_equal(r["sel"].cpu().numpy(), orc["sel"]) or orc["tie"].any()
     check_out(w, paged.numpy(), orc["out"], "paged decode out")
+
+
+def test_decode_and_out_proj_graph_replay_and_repeat():
+    """A decode step on a paged cache followed by the output projection, captured into one HIP graph,
+    gives the eager results on every replay; and repeated eager calls give the same bits."""
+    w = decode_case(B=6, L_lo=1, L_hi=500, L_max=500, name="dec_graph")
+    inp = W.make_inputs(w)
+    pg = {k: v.cuda() for k, v in W.make_paged_cache(w, inp, 32).items()}
+    d = G.desc_from(w)
+    x = inp["x"].reshape(w.B, w.d_model).cuda()
+    wr, wq, lens = inp["w_router"].cuda(), inp["w_q"].cuda(), inp["lens"].cuda()
+    wo = W.make_w_o(w).cuda()
+    r = G.alloc_route(d, x.device)
+    q = G.alloc_qproj(d, x.device)
+    out = torch.empty((w.B, d.S, w.d_head), dtype=torch.float32, device=x.device)
+    y = torch.empty((w.B, w.d_model), dtype=torch.float32, device=x.device)
+    ws = torch.empty(G.gqe_decode_workspace_bytes(d, pg["block_table"].shape[1] * 32), dtype=torch.uint8,
+                     device=x.device)
+
+    def step():
+        G.gqe_route(d, x, wr, None, r["sel"], r["p_tilde"], r["counts"], r["offsets"], r["rows"], None,
+                    r["workspace"])
+        G.gqe_qproj(d, x, wq, r["sel"], r["counts"], r["offsets"], r["rows"], q["q_routed"], q["q_shared"])
+        G.gqe_attn_decode_paged(d, q["q_routed"], q["q_shared"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                lens, r["p_tilde"], out, ws)
+        G.gqe_out_proj(d, out, r["p_tilde"], wo, y, True)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {"out": out.clone(), "y": y.clone()}
+    for _ in range(2):                           # repeated eager calls: the same bits
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref["out"]) and torch.equal(y, ref["y"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        out.fill_(float("nan"))                  # eager work between replays
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref["out"]), f"replay {rep}: out differs from the eager run"
+        assert torch.equal(y, ref["y"]), f"replay {rep}: y differs from the eager run"
