@@ -20,7 +20,7 @@
 
 namespace gqe {
 
-constexpr int kQpBM = 128;   // rows per tile (4 waves x 32)
+constexpr int kQpBM = 128;   // rows per tile of the fp32 kernel
 constexpr int kQpPad = 8;    // bf16 elements of row padding in LDS (16 bytes)
 
 // Destination element offset of row r of expert n's bucket.
@@ -36,7 +36,7 @@ __device__ __forceinline__ size_t qp_dst(int n, int N, int tok, const int32_t* _
     return ((((size_t)b * G + g) * T + t) * k + j) * d_head;
 }
 
-// Work order.  Expert n has c_n = ceil(M_n / kQpBM) row tiles (M_N = B*T for
+// Work order.  Expert n has c_n = ceil(M_n / BM) row tiles (M_N = B*T for
 // the shared head).  Tiles are ordered in rounds r = 0..R-1, R = max c_n:
 // expert n contributes ceil((r+1) c_n / R) - ceil(r c_n / R) tiles to round
 // r, so a round covers about the same token range in every expert (buckets
@@ -76,13 +76,13 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane)
     return v;
 }
 
-__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, bool routed, int lane,
-                        int& n_out, int& tile_out)
+__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, bool routed, int BM,
+                        int lane, int& n_out, int& tile_out)
 {
     auto ntiles = [&](int n) {
         if (n >= n_exp || (n < N && !routed)) return 0;
         const int M = n < N ? counts[n] : BT;
-        return (M + kQpBM - 1) / kQpBM;
+        return (M + BM - 1) / BM;
     };
     const int c0 = ntiles(lane), c1 = ntiles(lane + 64);
     const int U = wave_sum_i(c0 + c1);
@@ -119,41 +119,50 @@ __device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int 
     return true;
 }
 
-// One workgroup computes a 128-row tile of one expert: Q = X[rows] W_q[n]^T,
-// each of the four waves 32 rows.  Per stage of BK columns of d_model the x
-// rows and the weight slice are loaded with 16-byte coalesced loads (16 lanes
-// per 256-byte row segment) into registers while the previous stage is
-// multiplied out of LDS, then stored to LDS between two barriers.  Rows past
-// the bucket's end reload its last row and are not stored, so every load is
-// unconditional.
+// Threads and rows of a bf16 tile (one 32-row block per wave): at d_head =
+// 128 eight waves share a 256-row tile, so each expert's W_q slice is read
+// from L2 half as often (6 % faster on the d_head = 128 workload; at d_head
+// <= 64 the fewer, larger workgroups were slower).
+template <int D>
+struct QpNT {
+    static constexpr int NT = D >= 128 ? 512 : 256;
+    static constexpr int BM = NT / 2;
+};
+// One workgroup computes a BM-row tile of one expert: Q = X[rows] W_q[n]^T,
+// each wave 32 rows.  Per stage of BK columns of d_model the x rows and the
+// weight slice are loaded with 16-byte coalesced loads (16 lanes per 256-byte
+// row segment) into registers while the previous stage is multiplied out of
+// LDS, then stored to LDS between two barriers.  Rows past the bucket's end
+// reload its last row and are not stored, so every load is unconditional.
 template <int D, int BK>
-__global__ __launch_bounds__(256) void qproj_bf16_kernel(
+__global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
     uint16_t* __restrict__ q_routed, uint16_t* __restrict__ q_shared, int B, int T, int d_model, int G, int E,
     int k, int n_shared)
 {
     // q_routed == NULL: only the shared head; n_shared == 0: only the routed experts
+    constexpr int NT = QpNT<D>::NT, BM = QpNT<D>::BM;
     const int N = G * E, BT = B * T, n_exp = N + n_shared;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int s_item[2];
     if (wave == 0) {
         int pn = -1, pt = 0;
-        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, q_routed != nullptr, lane, pn, pt)) pn = -1;
+        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, q_routed != nullptr, BM, lane, pn, pt)) pn = -1;
         if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
     }
     __syncthreads();
     const int n = s_item[0];
     if (n < 0) return;
-    const int row0 = s_item[1] * kQpBM;
+    const int row0 = s_item[1] * BM;
     const int M = n < N ? counts[n] : BT;
     const int base = n < N ? offsets[n] : 0;
     constexpr int P = BK + kQpPad;
     constexpr int NB = D / 32;
     constexpr int CPR = BK / 8;                           // 16-byte chunks per row of a stage
-    constexpr int ACH = kQpBM * CPR / 256;                // A chunks per thread
-    constexpr int BCH = D * CPR / 256;                    // B chunks per thread
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kQpBM * P];
+    constexpr int ACH = BM * CPR / NT;                    // A chunks per thread
+    constexpr int BCH = D * CPR / NT;                     // B chunks per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * P];
     __shared__ __attribute__((aligned(16))) uint16_t sB[D * P];
 
     // row pointers of this thread's A chunks (rows tid / CPR + i * 256 / CPR)
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     const uint16_t* pa[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int rr = min(row0 + tid / CPR + i * (256 / CPR), M - 1);
+        const int rr = min(row0 + tid / CPR + i * (NT / CPR), M - 1);
         const int tok = n < N ? rows[base + rr] : rr;
         pa[i] = x + (size_t)tok * d_model + col;
     }
@@ -171,14 +180,14 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < ACH; ++i) ra[i] = ld_u32x4(pa[i] + k0);
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) rb[i] = ld_u32x4(pb + (size_t)i * (256 / CPR) * d_model + k0);
+        for (int i = 0; i < BCH; ++i) rb[i] = ld_u32x4(pb + (size_t)i * (NT / CPR) * d_model + k0);
     };
     const int w_off = (tid / CPR) * P + col;
     auto store = [&]() {
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) *(u32x4*)&sA[w_off + i * (256 / CPR) * P] = ra[i];
+        for (int i = 0; i < ACH; ++i) *(u32x4*)&sA[w_off + i * (NT / CPR) * P] = ra[i];
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) *(u32x4*)&sB[w_off + i * (256 / CPR) * P] = rb[i];
+        for (int i = 0; i < BCH; ++i) *(u32x4*)&sB[w_off + i * (NT / CPR) * P] = rb[i];
     };
 
     f32x16 acc[NB];
@@ -224,7 +233,7 @@ __global__ __launch_bounds__(256) void qproj_bf16_kernel(
     }
 
     // destinations of the tile's rows; rows past the bucket are not stored
-    __shared__ size_t s_dst[kQpBM];
+    __shared__ size_t s_dst[BM];
     const int m = wave * 32 + (lane & 31);
     if (lane < 32) {
         const int r = row0 + m;
@@ -282,14 +291,16 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
     const int tiles = (BT + kQpBM - 1) / kQpBM;
     const int grid = tiles * n_exp;
     // bf16: an upper bound on the number of tiles over all buckets, rounded to the 8 XCDs
-    const long long umax = (routed ? (long long)BT * a.G * a.k / kQpBM + N : 0) + (long long)ns * tiles;
-    const int grid_bf16 = (int)(8 * ((umax + 7) / 8));
+    auto grid_bf16_for = [&](int BM) {
+        const long long um = (routed ? (long long)BT * a.G * a.k / BM + N : 0) + (long long)ns * ((BT + BM - 1) / BM);
+        return (int)(8 * ((um + 7) / 8));
+    };
     if (a.bf16) {
         const uint16_t* x = (const uint16_t*)a.x;
         const uint16_t* w = (const uint16_t*)a.w_q;
         uint16_t* qr = (uint16_t*)a.q_routed;
         uint16_t* qs = (uint16_t*)a.q_shared;
-#define GQE_QP(D) qproj_bf16_kernel<D, 64><<<grid_bf16, 256, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, \
+#define GQE_QP(D) qproj_bf16_kernel<D, 64><<<grid_bf16_for(QpNT<D>::BM), QpNT<D>::NT, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, \
                                                                   a.B, a.T, a.d_model, a.G, a.E, a.k, ns)
         switch (a.d_head) {   // d_model is a multiple of the 64-wide stage (checked by the API)
         case 32: GQE_QP(32); break;
