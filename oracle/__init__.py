@@ -57,6 +57,8 @@ def _load():
         lib.ora_prefill_rows.restype = None
         lib.ora_attend_rows.argtypes = [P, P, P, P, P, P, ctypes.c_int64, P, P]
         lib.ora_attend_rows.restype = None
+        lib.ora_kv_proj.argtypes = [P, P, P, P]
+        lib.ora_kv_proj.restype = None
         lib.ora_assemble_rows.argtypes = [P, P, ctypes.c_int64, P]
         lib.ora_assemble_rows.restype = None
         lib.ora_out_proj_rows.argtypes = [P, P, P, ctypes.c_int64, P]
@@ -184,6 +186,17 @@ def attend_rows(d: _Desc, q_routed, q_shared, K, V, ptilde, tok=None):
     return out
 
 
+def kv_proj(d: _Desc, x, w):
+    """One of the K / V projections: x [B*T, d_model] (or [B, T, d_model]), w [H_kv, d_head, d_model].
+    Returns [B, H_kv, T, d_head] float64."""
+    lib = _load()
+    x = _f64(x).reshape(d.B * d.T, d.d_model)
+    w = _f64(w).reshape(d.H_kv, d.d_head, d.d_model)
+    out = np.empty((d.B, d.H_kv, d.T, d.d_head))
+    lib.ora_kv_proj(ctypes.byref(d), _ptr(x), _ptr(w), _ptr(out))
+    return out
+
+
 def assemble_rows(d: _Desc, slots, ptilde):
     """The weighted slot(s) of token rows whose hard and shared slots are given.
 
@@ -248,5 +261,5 @@ def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens):
 
 
 __all__ = ["build", "desc", "num_slots", "num_threads", "route", "compact", "qproj_rows", "prefill_rows", "prefill",
-           "assemble_rows", "out_proj_rows",
+           "assemble_rows", "out_proj_rows", "kv_proj",
            "decode", "TIE_MARGIN"]

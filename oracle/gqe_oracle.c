@@ -194,6 +194,24 @@ void ora_qproj_rows(const ora_desc* D, int64_t n_list, const int64_t* tok, const
 }
 
 /*
+ * The K and V projections ahead of the path ([tut] "GQA 核心原理与计算流程",
+ * step 2: the input is projected linearly to K and V, split into g = H_kv
+ * heads each as wide as a query head).  x [B*T, d_model]; w [H_kv, d_head,
+ * d_model]; out[b, h, t, :] = w[h] x[b*T + t], out [B, H_kv, T, d_head].
+ * Called once with W_k and once with W_v.
+ */
+void ora_kv_proj(const ora_desc* D, const double* x, const double* w, double* out)
+{
+    const int G = D->H_kv, dh = D->d_head, T = D->T;
+    const int64_t BT = (int64_t)D->B * T;
+#pragma omp parallel for schedule(static)
+    for (int64_t tk = 0; tk < BT; ++tk) {
+        const int64_t b = tk / T, t = tk % T;
+        for (int h = 0; h < G; ++h) project(D, x + tk * D->d_model, w, h, out + ((b * G + h) * T + t) * dh);
+    }
+}
+
+/*
  * Step 7, one query row: scaled dot-product attention over n_keys keys
  * ([note] §1-1, Attention(Q,K,V) = softmax(QK^T / sqrt(d)) V; scale
  * 1/sqrt(d_k) as in [ibm]).  Kh, Vh point at key 0 of one KV head, rows

@@ -316,6 +316,27 @@ def test_permuting_experts_inside_a_group_keeps_weighted_and_shared_slots():
         sb = np.sort(b[:, g * w.k:(g + 1) * w.k], axis=1)
         np.testing.assert_allclose(sa, sb, rtol=1e-12, atol=1e-14)
 
+# ---------------------------------------------------------------- K / V projection
+
+def test_kv_projection_closed_form_and_torch():
+    # [tut] step 2: x projected to K and V, split into H_kv heads of d_head
+    w = wl(B=2, T=11, d_model=8, d_head=8, H_q=6, H_kv=3)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    x = inp["x"].reshape(-1, w.d_model)
+    # scaled identities: head h of K is (h + 1) * x exactly
+    eye = torch.stack([torch.eye(8, dtype=torch.float64) * (h + 1) for h in range(3)])
+    k = oracle.kv_proj(d, x, eye)
+    for h in range(3):
+        assert np.array_equal(k[:, h], (h + 1) * inp["x"].double().numpy())
+    # a general W (d_model != d_head, so a transposed operand cannot pass) against torch, head h at [:, h]
+    w2 = wl(B=2, T=11, d_model=24, d_head=8, H_q=6, H_kv=3)
+    inp2 = W.make_inputs(w2)
+    wk = torch.randn(3, 8, 24, dtype=torch.float64, generator=torch.Generator().manual_seed(4))
+    got = oracle.kv_proj(oracle.desc(w2), inp2["x"], wk)
+    ref = torch.einsum("btm,hdm->bhtd", inp2["x"].double(), wk)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+
 # ---------------------------------------------------------------- output projection
 
 @pytest.mark.parametrize("route_mode", [0, 1])
