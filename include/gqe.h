@@ -227,6 +227,20 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
 
 /*
+ * gqe_kv_proj -- the K and V projections ahead of the path (GQA tutorial,
+ * freeguideonline, "GQA 核心原理与计算流程" step 2: the input is projected
+ * linearly to K and V, split into H_kv heads as wide as a query head):
+ *   k[b, h, t, :] = W_k[h] x[b*T + t],   v[b, h, t, :] = W_v[h] x[b*T + t]
+ * In:  x [B*T, d_model], w_k, w_v [H_kv, d_head, d_model] (dtype).
+ * Out: k, v [B, H_kv, T, d_head] (dtype; bf16 results are fp32 sums rounded
+ *      to nearest even), the layout gqe_attn_prefill reads.
+ * Only B, T, d_model, H_kv, d_head and dtype of desc are used (plus its
+ * validity checks).
+ */
+int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void* w_v, void* k, void* v,
+                void* stream);
+
+/*
  * gqe_out_proj -- the attention output projection, fused with slot assembly.
  * The S slots of a token are concatenated in slot order into h_t (width
  * S*d_head) and passed through one linear map, y_t = W_o h_t, no bias (GQA

@@ -216,6 +216,22 @@ int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* s
     return launch_status(gqe::launch_assemble(p_tilde, out, s.BT, s.G, s.k, s.D, s.S, s.mode, (hipStream_t)stream));
 }
 
+int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void* w_v, void* k, void* v,
+                void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.BT * s.G >= (1ll << 31)) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(x));
+    GQE_TRY(need(w_k));
+    GQE_TRY(need(w_v));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    gqe::KvProjArgs a{x, w_k, w_v, k, v, s.B, s.T, s.dm, s.G, s.D, s.bf16};
+    return launch_status(gqe::launch_kv_proj(a, (hipStream_t)stream));
+}
+
 int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
                  int32_t write_weighted, void* stream)
 {

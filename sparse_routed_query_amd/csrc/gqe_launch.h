@@ -39,6 +39,17 @@ struct QprojArgs {
 };
 int launch_qproj(const QprojArgs& a, hipStream_t st);
 
+struct KvProjArgs {
+    const void* x;     // [B*T, d_model]
+    const void* w_k;   // [H_kv, d_head, d_model]
+    const void* w_v;
+    void* k;           // [B, H_kv, T, d_head]
+    void* v;
+    int B, T, d_model, H_kv, d_head;
+    bool bf16;
+};
+int launch_kv_proj(const KvProjArgs& a, hipStream_t st);
+
 struct PrefillArgs {
     const void* q_routed;   // NULL: the routed heads are not computed by this call
     const void* q_shared;   // NULL: the shared head is not computed by this call

@@ -23,12 +23,15 @@ namespace gqe {
 constexpr int kQpBM = 128;   // rows per tile of the fp32 kernel
 constexpr int kQpPad = 8;    // bf16 elements of row padding in LDS (16 bytes)
 
-// Destination element offset of row r of expert n's bucket.
-__device__ __forceinline__ size_t qp_dst(int n, int N, int tok, const int32_t* __restrict__ sel, int T, int G,
-                                         int E, int k, int d_head)
+// Destination element offset of row r of expert n's bucket.  Experts n >= N
+// are dense heads over every token, written as [B, H, T, d_head] with H = the
+// number of dense heads (1: the shared head, [B, T, d_head]; H_kv: the K or V
+// projection).
+__device__ __forceinline__ size_t qp_dst(int n, int N, int n_dense, int tok, const int32_t* __restrict__ sel,
+                                         int T, int G, int E, int k, int d_head)
 {
     const int b = tok / T, t = tok - b * T;
-    if (n == N) return (size_t)tok * d_head;  // shared head [B, T, d_head]
+    if (n >= N) return (((size_t)b * n_dense + (n - N)) * T + t) * d_head;
     const int g = n / E, e = n - g * E;
     const int32_t* s = sel + ((size_t)tok * G + g) * k;
     int j = 0;
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(
     if (lane < 32) {
         const int r = row0 + m;
         size_t o = ~(size_t)0;
-        if (r < M) o = qp_dst(n, N, n < N ? rows[base + r] : r, sel, T, G, E, k, D);
+        if (r < M) o = qp_dst(n, N, n_shared, n < N ? rows[base + r] : r, sel, T, G, E, k, D);
         s_dst[m] = o;
     }
     __syncthreads();
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(
         float s = 0.f;
         for (int i = 0; i < d_model; ++i) s = fmaf(xr[i], wr[i], s);
         float* dst = n < N ? q_routed : q_shared;
-        dst[qp_dst(n, N, tok, sel, T, G, E, k, d_head) + d] = s;
+        dst[qp_dst(n, N, n_shared, tok, sel, T, G, E, k, d_head) + d] = s;
     }
 }
 
@@ -315,6 +318,26 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
                                                a.G, a.E, a.k, a.d_head, ns);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// K and V projections (GQA tutorial, freeguideonline, "GQA 核心原理与计算流程"
+// step 2): the same kernel with no routed experts and H_kv dense heads over
+// every token, once for K and once for V, written as [B, H_kv, T, d_head].
+int launch_kv_proj(const KvProjArgs& a, hipStream_t st)
+{
+    for (int which = 0; which < 2; ++which) {
+        QprojArgs q{};
+        q.x = a.x;
+        q.w_q = which ? a.w_v : a.w_k;
+        q.q_routed = nullptr;
+        q.q_shared = which ? a.v : a.k;
+        q.B = a.B; q.T = a.T; q.d_model = a.d_model; q.G = 0; q.E = 1; q.k = 1; q.d_head = a.d_head;
+        q.n_shared = a.H_kv;
+        q.bf16 = a.bf16;
+        const int rc = launch_qproj(q, st);
+        if (rc) return rc;
+    }
+    return 0;
 }
 
 }  // namespace gqe

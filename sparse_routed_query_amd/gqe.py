@@ -28,7 +28,7 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
-           "gqe_attn_decode_paged")
+           "gqe_attn_decode_paged", "gqe_kv_proj")
 
 
 class GqeError(RuntimeError):
@@ -104,6 +104,8 @@ def load():
         lib.gqe_attn_prefill_heads.restype = I
         lib.gqe_assemble.argtypes = [D, P, P, P]
         lib.gqe_assemble.restype = I
+        lib.gqe_kv_proj.argtypes = [D, P, P, P, P, P, P]
+        lib.gqe_kv_proj.restype = I
         lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
         lib.gqe_out_proj.restype = I
         lib.gqe_decode_workspace_bytes.argtypes = [D, ctypes.c_int32]
@@ -219,6 +221,22 @@ def gqe_assemble(desc, p_tilde, out, stream=None):
     rc = load().gqe_assemble(ctypes.byref(desc), _ptr(p_tilde, torch.float32, "p_tilde"),
                              _ptr(out, torch.float32, "out"), _stream(stream))
     _check("gqe_assemble", rc)
+
+
+def gqe_kv_proj(desc, x, w_k, w_v, k, v, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_kv_proj(ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_k, dt, "w_k"), _ptr(w_v, dt, "w_v"),
+                            _ptr(k, dt, "k"), _ptr(v, dt, "v"), _stream(stream))
+    _check("gqe_kv_proj", rc)
+
+
+def kv_proj(desc, x, w_k, w_v, stream=None):
+    """K and V [B, H_kv, T, d_head] from x [B*T, d_model]."""
+    shape = (desc.B, desc.H_kv, desc.T, desc.d_head)
+    k = torch.empty(shape, dtype=desc.torch_dtype, device=x.device)
+    v = torch.empty(shape, dtype=desc.torch_dtype, device=x.device)
+    gqe_kv_proj(desc, x, w_k, w_v, k, v, stream)
+    return k, v
 
 
 def gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted=False, stream=None):

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -123,6 +123,12 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert lib.gqe_assemble(by(d), None, A16, None) == INVALID
     assert lib.gqe_assemble(by(d), A16, MIS, None) == ALIGN
     assert lib.gqe_assemble(by(main(H_q=15)), A16, A16, None) == INVALID
+    kv = lambda desc, x=A16, wk=A16, wv=A16, k=A16, v=A16: lib.gqe_kv_proj(by(desc), x, wk, wv, k, v, None)  # noqa
+    assert kv(d, x=None) == INVALID
+    assert kv(d, wv=None) == INVALID
+    assert kv(d, k=MIS) == ALIGN
+    assert kv(main(d_head=48)) == UNSUPPORTED
+    assert kv(main(B=0), x=None, wk=None, wv=None, k=None, v=None) == OK
     op = lambda desc, out=A16, pt=A16, wo=A16, y=A16, ww=0: lib.gqe_out_proj(  # noqa: E731
         by(desc), out, pt, wo, y, ww, None)
     assert op(d, out=None) == INVALID

@@ -451,3 +451,46 @@ def test_decode_and_out_proj_graph_replay_and_repeat():
         torch.cuda.synchronize()
         assert torch.equal(out, ref["out"]), f"replay {rep}: out differs from the eager run"
         assert torch.equal(y, ref["y"]), f"replay {rep}: y differs from the eager run"
+
+
+# ---------------------------------------------------------------- K / V projection ahead of the path
+
+@pytest.mark.parametrize("w", [small(), small(d_head=32, name="d32"), small(d_head=128, T=100, name="d128"),
+                               small(B=1, T=1, name="T1"), small(dtype="f32", T=100, d_model=96, name="f32"),
+                               W.WORKLOADS["main_250m"]], ids=lambda w: f"{w.name}-{w.dtype}")
+def test_kv_projection(w):
+    """K and V against the oracle element by element: bf16 output rounding (relative 2^-8 of the value)
+    plus fp32 accumulation over d_model terms (d_model 2^-24 of sum |x| |w|)."""
+    inp = W.make_inputs(w)
+    wk, wv = W.make_w_kv(w)
+    d = G.desc_from(w)
+    x = inp["x"].reshape(-1, w.d_model)
+    k, v = G.kv_proj(d, x.cuda(), wk.cuda(), wv.cuda())
+    torch.cuda.synchronize()
+    od = oracle.desc(w)
+    xa = np.abs(x.double().numpy())
+    for name, got, wt in (("k", k, wk), ("v", v, wv)):
+        ref = oracle.kv_proj(od, x, wt)
+        mag = np.einsum("tm,hdm->htd", xa, np.abs(wt.double().numpy())).reshape(w.H_kv, w.B, w.T, w.d_head)
+        mag = mag.transpose(1, 0, 2, 3)
+        eps_out = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+        bound = eps_out * np.abs(ref) + (w.d_model + 2) * 2.0 ** -24 * mag * 1.01 + 1e-30
+        err = np.abs(got.cpu().double().numpy() - ref)
+        say(f"[{w.name}] kv_proj {name}: max-abs={err.max():.3e} max err/bound={(err / bound).max():.3f}")
+        assert (err <= bound).all()
+
+
+def test_layer_from_x_kv_projection_feeds_attention():
+    """K/V projected on the GPU feed the prefill path; the attention matches the oracle's on those K/V."""
+    w = small(B=2, T=300, name="layer")
+    inp = W.make_inputs(w)
+    wk, wv = W.make_w_kv(w)
+    d = G.desc_from(w)
+    k, v = G.kv_proj(d, inp["x"].reshape(-1, w.d_model).cuda(), wk.cuda(), wv.cuda())
+    torch.cuda.synchronize()
+    inp = dict(inp, k=k.cpu(), v=v.cpu())
+    gpu = gpu_prefill(w, inp)
+    agreed = check_route(w, inp, gpu)
+    tok = np.arange(w.B * w.T)
+    check_qproj(w, inp, gpu, agreed, tok)
+    check_prefill_given_q(w, inp, gpu, agreed, tok)

@@ -183,6 +183,15 @@ def make_paged_cache(w: Workload, inp: dict, page_size: int, spare: int = 3, see
     return dict(k_pages=kp, v_pages=vp, block_table=table)
 
 
+def make_w_kv(w: Workload, seed: Optional[int] = None):
+    """Draw the K and V projection weights [H_kv, d_head, d_model] of workload ``w``, N(0, w_std^2) in the
+    workload dtype, from a generator of their own (seed + 3000017)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((w.seed if seed is None else seed) + 3000017)
+    shape = (w.H_kv, w.d_head, w.d_model)
+    return _randn(gen, shape, w.w_std).to(torch_dtype(w)), _randn(gen, shape, w.w_std).to(torch_dtype(w))
+
+
 def make_w_o(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
     """Draw the output-projection weight [d_model, S * d_head] of workload ``w``,
     N(0, w_std^2) in the workload dtype, from a generator of its own (seed +
