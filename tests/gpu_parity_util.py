@@ -195,7 +195,7 @@ def check_out_proj(w: W.Workload, slots: torch.Tensor, p_tilde: torch.Tensor, w_
                    y: torch.Tensor, tok: np.ndarray):
     """y of tokens ``tok`` against the oracle's projection of the same hard and shared slots (its own
     fp64 weighted sum), element by element within the bound the arithmetic gives: bf16 rounding of each
-    slot value (relative 2^-9), fp32 accumulation over the K = S*d_head terms and the fp32 weighted sum
+    slot value (relative 2^-8: bf16 keeps 8 significand bits), fp32 accumulation over the K = S*d_head terms and the fp32 weighted sum
     (K + kG + 1 roundings of 2^-24), each relative to sum_i |h_i| |W_o[c, i]|."""
     d = oracle.desc(w)
     S = oracle.num_slots(d)
@@ -206,7 +206,7 @@ def check_out_proj(w: W.Workload, slots: torch.Tensor, p_tilde: torch.Tensor, w_
     h_abs = oracle.assemble_rows(d, np.abs(h_gpu), pt)        # weighted part: sum p~ |hard| bounds its error too
     mag = h_abs.reshape(len(tok), -1) @ np.abs(w_o.double().numpy()).T
     K = S * w.d_head
-    eps = (2.0 ** -9 if w.dtype == "bf16" else 0.0) + (K + w.k * w.G + 1) * 2.0 ** -24
+    eps = (2.0 ** -8 if w.dtype == "bf16" else 0.0) + (K + w.k * w.G + 1) * 2.0 ** -24
     got = y.reshape(-1, w.d_model)[tok].double().numpy()
     err = np.abs(got - y_ref)
     ratio = float((err / (eps * mag + 1e-30)).max())
