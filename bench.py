@@ -20,7 +20,9 @@ divided by the whole step's time).  The same JSON line carries:
   long_context  T=32768 GQE vs all-active GQA on the same inputs;
   out_proj      the next step after the path, outside the timed step: the
                 output projection over the kG+2 slots fused with slot assembly
-                (gqe_out_proj) on the step's own slots, against the bf16 peak.
+                (gqe_out_proj) on the step's own slots, against the bf16 peak;
+  kv_proj       the step before it, also outside: the K and V projections
+                (gqe_kv_proj) of the step's x, against the bf16 peak.
 
 --graph also times the step replayed from one HIP graph of the four calls
 (on this stack replaying is not faster than launching them one by one).
@@ -275,6 +277,26 @@ def out_proj_leg(p, torch, steps):
             "context_torch_mm_bf16_us": t_lib * 1e3}
 
 
+def kv_proj_leg(p, torch, steps):
+    """The K and V projections ahead of the path (gqe_kv_proj) on the step's x: 2 * B*T * d_model * 2 *
+    H_kv * d_head FLOPs, bf16 MFMA with fp32 accumulation, outside the timed step."""
+    import workloads as W
+    w, G = p.w, p.G
+    wk, wv = (t.to(p.x.device) for t in W.make_w_kv(w))
+    k = torch.empty_like(p.k)
+    v = torch.empty_like(p.v)
+
+    def kv():
+        G.gqe_kv_proj(p.d, p.x, wk, wv, k, v)
+
+    warm([kv], torch)
+    (t,) = time_calls([kv], steps, torch)
+    fl = 2.0 * w.B * w.T * w.d_model * 2 * w.H_kv * w.d_head
+    tf = fl / (t * 1e-3) / 1e12
+    return {"workload": w.name, "kernel": f"qproj_bf16_kernel<{w.d_head}, 64> as dense heads (gqe_kv_proj)",
+            "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
@@ -414,6 +436,7 @@ def main():
                      "algorithmic_flops_per_launch": fl},
     }
     line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
+    line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
     del p
     torch.cuda.empty_cache()
     if not args.no_decode:
