@@ -286,6 +286,21 @@ int gqe_attn_decode_paged(const gqe_desc* desc, const void* q_routed, const void
                           const float* p_tilde, float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * gqe_check_decode_inputs -- audit of the decode preconditions the host cannot
+ * see, for callers that want them checked (the decode calls clamp such values
+ * instead of faulting, so a violation gives wrong results, not an error).
+ * Counts, on the device, the sequences with lens[b] outside 1 .. L_max into
+ * bad[0] and, when block_table is given, the block-table entries a sequence
+ * uses (its first ceil(lens[b] / page_size) columns) whose page id is outside
+ * 0 .. num_pages-1 into bad[1].  bad [2] int32 (device) is written, not added
+ * to; synchronise the stream before reading it.  For a paged cache pass
+ * L_max = max_pages * page_size; block_table NULL audits lens only.
+ */
+int gqe_check_decode_inputs(const gqe_desc* desc, const int32_t* lens, int32_t L_max,
+                            const int32_t* block_table, int32_t num_pages, int32_t page_size,
+                            int32_t max_pages, int32_t* bad, void* stream);
+
 /* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
 

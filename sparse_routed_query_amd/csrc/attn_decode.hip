@@ -415,4 +415,41 @@ int launch_decode(const DecodeArgs& a, hipStream_t st)
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// Precondition audit for decode inputs: counts lens[b] outside 1 .. L_max
+// into bad[0] and, for a paged cache, the block-table entries a sequence uses
+// (its first ceil(lens[b] / page_size) columns) whose page id is outside
+// 0 .. num_pages-1 into bad[1].  One workgroup; bad is written, not added to.
+__global__ __launch_bounds__(256) void decode_check_kernel(const int32_t* __restrict__ lens, int B, int L_max,
+                                                           const int32_t* __restrict__ block_table, int page_size,
+                                                           int max_pages, int num_pages, int32_t* __restrict__ bad)
+{
+    __shared__ int s_bad[2];
+    if (threadIdx.x < 2) s_bad[threadIdx.x] = 0;
+    __syncthreads();
+    int nl = 0, np = 0;
+    for (int b = threadIdx.x; b < B; b += 256) {
+        const int L = lens[b];
+        nl += (L < 1 || L > L_max) ? 1 : 0;
+        if (block_table) {
+            const int used = min(max(L, 0), max_pages * page_size);
+            const int cols = (used + page_size - 1) / page_size;
+            for (int j = 0; j < cols; ++j) {
+                const int id = block_table[(size_t)b * max_pages + j];
+                np += (id < 0 || id >= num_pages) ? 1 : 0;
+            }
+        }
+    }
+    atomicAdd(&s_bad[0], nl);
+    atomicAdd(&s_bad[1], np);
+    __syncthreads();
+    if (threadIdx.x < 2) bad[threadIdx.x] = s_bad[threadIdx.x];
+}
+
+int launch_decode_check(const int32_t* lens, int B, int L_max, const int32_t* block_table, int page_size,
+                        int max_pages, int num_pages, int32_t* bad, hipStream_t st)
+{
+    decode_check_kernel<<<1, 256, 0, st>>>(lens, B, L_max, block_table, page_size, max_pages, num_pages, bad);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace gqe

@@ -283,6 +283,23 @@ int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_sh
     return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
 }
 
+int gqe_check_decode_inputs(const gqe_desc* desc, const int32_t* lens, int32_t L_max, const int32_t* block_table,
+                            int32_t num_pages, int32_t page_size, int32_t max_pages, int32_t* bad, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (L_max < 1) return GQE_ERR_INVALID;
+    GQE_TRY(need(lens));
+    GQE_TRY(need(bad));
+    GQE_TRY(maybe(block_table));
+    if (block_table) {
+        if (num_pages < 1 || max_pages < 1 || page_size < 1) return GQE_ERR_INVALID;
+        if ((long long)max_pages * page_size < L_max) return GQE_ERR_INVALID;
+    }
+    return launch_status(gqe::launch_decode_check(lens, s.B, L_max, block_table, page_size, max_pages, num_pages,
+                                                  bad, (hipStream_t)stream));
+}
+
 int gqe_attn_decode_paged(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k_pages,
                           const void* v_pages, int32_t num_pages, int32_t page_size, int32_t max_pages,
                           const int32_t* block_table, const int32_t* lens, const float* p_tilde, float* out,

@@ -103,6 +103,8 @@ struct DecodeArgs {
     int page_shift = 0, max_pages = 0, num_pages = 0;
 };
 size_t decode_workspace_bytes(int B, int G, int k, int n_shared, int d_head, int L_max, bool bf16);
+int launch_decode_check(const int32_t* lens, int B, int L_max, const int32_t* block_table, int page_size,
+                        int max_pages, int num_pages, int32_t* bad, hipStream_t st);
 int launch_decode(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace gqe

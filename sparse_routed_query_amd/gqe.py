@@ -28,7 +28,7 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
-           "gqe_attn_decode_paged", "gqe_kv_proj")
+           "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs")
 
 
 class GqeError(RuntimeError):
@@ -104,6 +104,9 @@ def load():
         lib.gqe_attn_prefill_heads.restype = I
         lib.gqe_assemble.argtypes = [D, P, P, P]
         lib.gqe_assemble.restype = I
+        lib.gqe_check_decode_inputs.argtypes = [D, P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, P, P]
+        lib.gqe_check_decode_inputs.restype = I
         lib.gqe_kv_proj.argtypes = [D, P, P, P, P, P, P]
         lib.gqe_kv_proj.restype = I
         lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
@@ -221,6 +224,18 @@ def gqe_assemble(desc, p_tilde, out, stream=None):
     rc = load().gqe_assemble(ctypes.byref(desc), _ptr(p_tilde, torch.float32, "p_tilde"),
                              _ptr(out, torch.float32, "out"), _stream(stream))
     _check("gqe_assemble", rc)
+
+
+def check_decode_inputs(desc, lens, L_max, block_table=None, num_pages=0, page_size=0, stream=None):
+    """Device-side audit of decode inputs: returns (bad lengths, bad page ids) after a synchronise."""
+    bad = torch.zeros(2, dtype=torch.int32, device=lens.device)
+    max_pages = block_table.shape[1] if block_table is not None else 0
+    rc = load().gqe_check_decode_inputs(ctypes.byref(desc), _ptr(lens, torch.int32, "lens"), int(L_max),
+                                        _ptr(block_table, torch.int32, "block_table"), int(num_pages),
+                                        int(page_size), int(max_pages), _ptr(bad, None, "bad"), _stream(stream))
+    _check("gqe_check_decode_inputs", rc)
+    torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+    return int(bad[0]), int(bad[1])
 
 
 def gqe_kv_proj(desc, x, w_k, w_v, k, v, stream=None):

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -160,6 +160,14 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert pg(dd, bt=MIS) == ALIGN
     assert pg(dd, wb=pws_ - 1) == WORKSPACE     # sized for max_pages * page_size positions
     assert pg(main(B=0, T=1), bt=None, w=None) == OK
+    ck = lambda desc, lens=A16, L=64, bt=None, npg=4, P=16, mp=4, bad=A16: lib.gqe_check_decode_inputs(  # noqa: E731
+        by(desc), lens, L, bt, npg, P, mp, bad, None)
+    assert ck(dd, lens=None) == INVALID
+    assert ck(dd, bad=None) == INVALID
+    assert ck(dd, L=0) == INVALID
+    assert ck(dd, bt=MIS) == ALIGN
+    assert ck(dd, bt=A16, mp=2) == INVALID      # the table must cover L_max positions
+    assert ck(dd, bt=A16, npg=0) == INVALID
 
 
 def test_python_binding_refuses_host_tensors():

@@ -494,3 +494,23 @@ def test_layer_from_x_kv_projection_feeds_attention():
     tok = np.arange(w.B * w.T)
     check_qproj(w, inp, gpu, agreed, tok)
     check_prefill_given_q(w, inp, gpu, agreed, tok)
+
+
+def test_decode_input_audit_counts_bad_lengths_and_page_ids():
+    """gqe_check_decode_inputs counts what the decode calls would clamp: lengths outside 1..L_max and
+    page ids outside the pool in the table columns a sequence uses (unused columns are not counted)."""
+    w = decode_case(B=8, name="audit")
+    d = G.desc_from(w)
+    lens = torch.tensor([1, 700, 0, 701, -3, 350, 64, 65], dtype=torch.int32)
+    assert G.check_decode_inputs(d, lens.cuda(), 700) == (3, 0)
+    assert G.check_decode_inputs(d, torch.tensor([5] * 8, dtype=torch.int32).cuda(), 700) == (0, 0)
+    P, max_pages, num_pages = 64, 11, 40
+    table = torch.randint(0, num_pages, (8, max_pages), dtype=torch.int32, generator=torch.Generator().manual_seed(1))
+    good = lens.clamp(1, 700)
+    assert G.check_decode_inputs(d, good.cuda(), max_pages * P, table.cuda(), num_pages, P) == (0, 0)
+    table[0, 0] = -1          # used (length 1)
+    table[1, 10] = num_pages  # used (length 700 reaches column 10)
+    table[6, 0] = 10 ** 6     # used (length 64 fills column 0 only)
+    table[6, 1] = -5          # not used by a length of 64
+    table[7, 1] = num_pages + 3   # used (length 65 reaches column 1)
+    assert G.check_decode_inputs(d, good.cuda(), max_pages * P, table.cuda(), num_pages, P) == (0, 4)
