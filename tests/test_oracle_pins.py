@@ -430,3 +430,86 @@ def test_main_setting_counts_from_the_study_note():
     assert small.G * small.E == g["routed_pool"] and small.G == g["groups"] and small.E == g["experts_per_group"]
     c = oracle.compact(d, r["sel"])
     assert c["counts"].sum() == small.T * g["routed_active"]
+
+# ---------------------------------------------------------------- backward through assembly and routing
+
+from oracle.backward import route_assemble_backward  # noqa: E402
+
+
+def _bwd_case(k, E=3, G=2, route_mode=0, seed=3):
+    w = wl(B=1, T=4, d_model=5, H_q=G * E, H_kv=G, k=k, d_head=3, route_mode=route_mode, seed=seed)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"])
+    rng = np.random.default_rng(seed)
+    S = oracle.num_slots(d)
+    hard = rng.standard_normal((w.B * w.T, G * k, w.d_head))
+    dout = rng.standard_normal((w.B * w.T, S, w.d_head))
+    return w, inp, r, hard, dout
+
+
+def _loss(w, x, w_router, sel, hard, dout):
+    """L = sum(dout * slots) with the slots assembled from p~ of the given selection (numpy, float64)."""
+    G, k, E = w.H_kv, w.k, w.H_q // w.H_kv
+    logits = x @ w_router.T
+    p = np.exp(logits.reshape(-1, G, E) - logits.reshape(-1, G, E).max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    q = np.take_along_axis(p, sel.astype(np.int64), -1)
+    pt = q / q.sum(-1, keepdims=True)
+    kG = G * k
+    L = (dout[:, :kG] * hard).sum()
+    hg = hard.reshape(-1, G, k, hard.shape[-1])
+    if w.route_mode == 0:
+        L += (dout[:, kG] * (pt[..., None] * hg).sum((1, 2))).sum()
+    elif w.route_mode == 1:
+        L += (dout[:, kG:kG + G] * (pt[..., None] * hg).sum(2)).sum()
+    return L
+
+
+@pytest.mark.parametrize("route_mode", [0, 1])
+def test_router_backward_matches_finite_differences(route_mode):
+    w, inp, r, hard, dout = _bwd_case(k=2, route_mode=route_mode)
+    x = inp["x"].double().numpy().reshape(-1, w.d_model)
+    wr = inp["w_router"].double().numpy()
+    g = route_assemble_backward(w, x, wr, None, r["sel"], hard, dout)
+    h = 1e-6
+    for n in range(wr.shape[0]):
+        for c in range(wr.shape[1]):
+            a, b = wr.copy(), wr.copy()
+            a[n, c] += h; b[n, c] -= h
+            fd = (_loss(w, x, a, r["sel"], hard, dout) - _loss(w, x, b, r["sel"], hard, dout)) / (2 * h)
+            assert abs(fd - g["dw_router"][n, c]) <= 1e-6 * max(1.0, abs(fd))
+    for t in range(x.shape[0]):
+        for c in range(x.shape[1]):
+            a, b = x.copy(), x.copy()
+            a[t, c] += h; b[t, c] -= h
+            fd = (_loss(w, a, wr, r["sel"], hard, dout) - _loss(w, b, wr, r["sel"], hard, dout)) / (2 * h)
+            assert abs(fd - g["dx"][t, c]) <= 1e-6 * max(1.0, abs(fd))
+    # the loss is linear in the hard slots: one probe per slot entry gives its gradient exactly
+    e = np.zeros_like(hard); e[1, 2, 1] = 1.0
+    assert np.isclose(_loss(w, x, wr, r["sel"], hard + e, dout) - _loss(w, x, wr, r["sel"], hard, dout),
+                      g["d_hard"][1, 2, 1], rtol=1e-12, atol=1e-12)
+    # p~ depends on a group's scores only through their differences: the score gradient sums to zero
+    assert np.allclose(g["d_logits"].reshape(-1, w.G, w.E).sum(-1), 0.0, atol=1e-13)
+
+
+def test_router_backward_closed_forms():
+    # top-1: p~ = 1 whatever the scores, so the router gets no gradient and the hard slots get dout + dout_w
+    w, inp, r, hard, dout = _bwd_case(k=1)
+    x = inp["x"].double().numpy().reshape(-1, w.d_model)
+    g = route_assemble_backward(w, x, inp["w_router"], None, r["sel"], hard, dout)
+    assert not g["d_logits"].any() and not g["dw_router"].any() and not g["dx"].any()
+    kG = w.G * w.k
+    assert np.array_equal(g["d_hard"], dout[:, :kG] + dout[:, kG:kG + 1])
+    # no weighted slot (route mode 2): no learning signal reaches the router ([note] §3-2 (4))
+    w2, inp2, r2, hard2, dout2 = _bwd_case(k=2, route_mode=2)
+    g2 = route_assemble_backward(w2, inp2["x"], inp2["w_router"], None, r2["sel"], hard2, dout2)
+    assert not g2["d_logits"].any() and np.array_equal(g2["d_hard"], dout2[:, :w2.G * w2.k])
+    # all experts kept: p~ = p, so d s_e = p_e (g_e - sum_e' p_e' g_e') with g_e = <dout_w, o_e>
+    w3, inp3, r3, hard3, dout3 = _bwd_case(k=3, E=3)
+    g3 = route_assemble_backward(w3, inp3["x"], inp3["w_router"], None, r3["sel"], hard3, dout3)
+    kG3 = w3.G * w3.k
+    ge = np.einsum("td,thd->th", dout3[:, kG3], hard3).reshape(-1, w3.G, 3)
+    p = r3["probs"].reshape(-1, w3.G, 3)
+    want = p * (ge - (p * ge).sum(-1, keepdims=True))
+    np.testing.assert_allclose(g3["d_logits"].reshape(-1, w3.G, 3), want, rtol=1e-10, atol=1e-13)
