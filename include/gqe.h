@@ -226,6 +226,37 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
  */
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
 
+/* Bytes of device workspace gqe_route_backward needs when it computes dw_router. */
+size_t gqe_route_backward_workspace_bytes(const gqe_desc* desc);
+
+/*
+ * gqe_route_backward -- gradients through slot assembly and routing: what
+ * the weighted slot carries back to the router, its differentiable learning
+ * path (GQE study note §3-2 (4)), and the hard slots' share of dout.  With the
+ * kept sets held fixed, p~ is the softmax of the kept scores alone, so
+ *   d_hard[t, h]  = dout[t, h] + p~[t, h] dout[t, w(h)]   (w(h): the weighted
+ *                   slot that sums hard slot h; none in route mode 2)
+ *   dp~[t, h]     = <dout[t, w(h)], out[t, h]>
+ *   d_logits[t, g*E + S_j] = p~_j (dp~_j - sum_i p~_i dp~_i), 0 for experts not kept
+ *   dw_router     = sum_t d_logits[t]^T x[t],   db_router = sum_t d_logits[t]
+ *   dx            = d_logits W_router  (the router's part of dx only)
+ * In:  dout [B*T, S, d_head] fp32 (gradient of every slot; the shared slot's
+ *      is not used here), out [B*T, S, d_head] fp32 (its hard slots are read),
+ *      sel, p_tilde [B*T, G, k] as gqe_route gives them, x [B*T, d_model] and
+ *      w_router [N, d_model] (dtype).
+ * Out: d_hard [B*T, G*k, d_head] fp32, d_logits [B*T, N] fp32; optional (NULL
+ *      skips): dw_router [N, d_model] fp32, db_router [N] fp32 (only with
+ *      dw_router), dx [B*T, d_model] fp32.
+ * Sums run in fixed order (dw_router: partial sums over blocks of 256 tokens,
+ * then the blocks in order), so results do not depend on timing.
+ * Workspace: gqe_route_backward_workspace_bytes(desc) bytes when dw_router is
+ * given (else may be NULL); no initialisation needed.
+ */
+int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out, const int32_t* sel,
+                       const float* p_tilde, const void* x, const void* w_router, float* d_hard,
+                       float* d_logits, float* dw_router, float* db_router, float* dx, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /*
  * gqe_kv_proj -- the K and V projections ahead of the path (GQA tutorial,
  * freeguideonline, "GQA 核心原理与计算流程" step 2: the input is projected

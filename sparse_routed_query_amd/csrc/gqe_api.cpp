@@ -216,6 +216,44 @@ int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* s
     return launch_status(gqe::launch_assemble(p_tilde, out, s.BT, s.G, s.k, s.D, s.S, s.mode, (hipStream_t)stream));
 }
 
+size_t gqe_route_backward_workspace_bytes(const gqe_desc* desc)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK) return 0;
+    return gqe::route_bwd_workspace_bytes(s.BT, s.Hq, s.dm);
+}
+
+int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out, const int32_t* sel,
+                       const float* p_tilde, const void* x, const void* w_router, float* d_hard, float* d_logits,
+                       float* dw_router, float* db_router, float* dx, void* workspace, size_t workspace_bytes,
+                       void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.BT * s.dm >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(dout));
+    GQE_TRY(need(out));
+    GQE_TRY(need(sel));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(d_hard));
+    GQE_TRY(need(d_logits));
+    GQE_TRY(maybe(dw_router));
+    GQE_TRY(maybe(db_router));
+    GQE_TRY(maybe(dx));
+    if (db_router && !dw_router) return GQE_ERR_INVALID;
+    if (dw_router) GQE_TRY(need(x));
+    if (dx) GQE_TRY(need(w_router));
+    if (dw_router) {
+        if (!workspace) return GQE_ERR_WORKSPACE;
+        GQE_TRY(need(workspace));
+        if (workspace_bytes < gqe::route_bwd_workspace_bytes(s.BT, s.Hq, s.dm)) return GQE_ERR_WORKSPACE;
+    }
+    gqe::RouteBwdArgs a{dout, out, sel, p_tilde, x, w_router, d_hard, d_logits, dw_router, db_router, dx,
+                        workspace, s.BT, s.G, s.E, s.k, s.D, s.dm, s.S, s.mode, s.bf16};
+    return launch_status(gqe::launch_route_bwd(a, (hipStream_t)stream));
+}
+
 int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void* w_v, void* k, void* v,
                 void* stream)
 {

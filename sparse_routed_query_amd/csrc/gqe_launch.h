@@ -39,6 +39,26 @@ struct QprojArgs {
 };
 int launch_qproj(const QprojArgs& a, hipStream_t st);
 
+struct RouteBwdArgs {
+    const float* dout;      // [BT, S, d_head]
+    const float* out;       // [BT, S, d_head]: the hard slots are read
+    const int32_t* sel;     // [BT, G, k]
+    const float* p_tilde;   // [BT, G, k]
+    const void* x;          // [BT, d_model]
+    const void* w_router;   // [N, d_model]
+    float* d_hard;          // [BT, G*k, d_head]
+    float* d_logits;        // [BT, N]
+    float* dw_router;       // [N, d_model] or NULL (then db_router is NULL too)
+    float* db_router;       // [N] or NULL
+    float* dx;              // [BT, d_model] or NULL
+    void* workspace;        // route_bwd_workspace_bytes(), needed when dw_router is set
+    long long BT;
+    int G, E, k, d_head, d_model, S, route_mode;
+    bool bf16;
+};
+size_t route_bwd_workspace_bytes(long long BT, int N, int C);
+int launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
+
 struct KvProjArgs {
     const void* x;     // [B*T, d_model]
     const void* w_k;   // [H_kv, d_head, d_model]

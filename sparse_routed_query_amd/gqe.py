@@ -28,7 +28,8 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
-           "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs")
+           "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
+           "gqe_route_backward")
 
 
 class GqeError(RuntimeError):
@@ -107,6 +108,10 @@ def load():
         lib.gqe_check_decode_inputs.argtypes = [D, P, ctypes.c_int32, P, ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, P, P]
         lib.gqe_check_decode_inputs.restype = I
+        lib.gqe_route_backward_workspace_bytes.argtypes = [D]
+        lib.gqe_route_backward_workspace_bytes.restype = Z
+        lib.gqe_route_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.gqe_route_backward.restype = I
         lib.gqe_kv_proj.argtypes = [D, P, P, P, P, P, P]
         lib.gqe_kv_proj.restype = I
         lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
@@ -236,6 +241,25 @@ def check_decode_inputs(desc, lens, L_max, block_table=None, num_pages=0, page_s
     _check("gqe_check_decode_inputs", rc)
     torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
     return int(bad[0]), int(bad[1])
+
+
+def route_backward(desc, dout, out, sel, p_tilde, x, w_router, want_dw=True, want_dx=True, stream=None) -> dict:
+    """Gradients through slot assembly and routing (allocates its outputs and workspace)."""
+    BT, G, k, N, D = desc.B * desc.T, desc.H_kv, desc.k, desc.H_q, desc.d_head
+    dev = dout.device
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    res = dict(d_hard=e(BT, G * k, D), d_logits=e(BT, N), dw_router=e(N, desc.d_model) if want_dw else None,
+               db_router=e(N) if want_dw else None, dx=e(BT, desc.d_model) if want_dx else None)
+    nb = load().gqe_route_backward_workspace_bytes(ctypes.byref(desc)) if want_dw else 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if want_dw else None
+    dt = desc.torch_dtype
+    rc = load().gqe_route_backward(ctypes.byref(desc), _ptr(dout, torch.float32, "dout"), _ptr(out, torch.float32, "out"),
+                                   _ptr(sel, torch.int32, "sel"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                   _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"), _ptr(res["d_hard"]),
+                                   _ptr(res["d_logits"]), _ptr(res["dw_router"]), _ptr(res["db_router"]),
+                                   _ptr(res["dx"]), _ptr(ws), nb, _stream(stream))
+    _check("gqe_route_backward", rc)
+    return res
 
 
 def gqe_kv_proj(desc, x, w_k, w_v, k, v, stream=None):

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -123,6 +123,16 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert lib.gqe_assemble(by(d), None, A16, None) == INVALID
     assert lib.gqe_assemble(by(d), A16, MIS, None) == ALIGN
     assert lib.gqe_assemble(by(main(H_q=15)), A16, A16, None) == INVALID
+    rws = G.load().gqe_route_backward_workspace_bytes(by(d))
+    assert rws >= 64 * 16 * 1025 * 4                       # 64 blocks of 256 tokens x N x (d_model + 1)
+    rb = lambda desc, dout=A16, dw=A16, db=A16, dx=A16, w=A16, wb=rws: lib.gqe_route_backward(  # noqa: E731
+        by(desc), dout, A16, A16, A16, A16, A16, A16, A16, dw, db, dx, w, wb, None)
+    assert rb(d, dout=None) == INVALID
+    assert rb(d, dw=None, db=A16) == INVALID     # db only with dw
+    assert rb(d, wb=rws - 1) == WORKSPACE
+    assert rb(d, w=None) == WORKSPACE
+    assert rb(d, dx=MIS) == ALIGN
+    assert rb(main(B=0), dout=None, dw=None, db=None, dx=None, w=None) == OK
     kv = lambda desc, x=A16, wk=A16, wv=A16, k=A16, v=A16: lib.gqe_kv_proj(by(desc), x, wk, wv, k, v, None)  # noqa
     assert kv(d, x=None) == INVALID
     assert kv(d, wv=None) == INVALID
