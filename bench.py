@@ -22,7 +22,9 @@ divided by the whole step's time).  The same JSON line carries:
                 output projection over the kG+2 slots fused with slot assembly
                 (gqe_out_proj) on the step's own slots, against the bf16 peak;
   kv_proj       the step before it, also outside: the K and V projections
-                (gqe_kv_proj) of the step's x, against the bf16 peak.
+                (gqe_kv_proj) of the step's x, against the bf16 peak;
+  route_backward  the backward through slot assembly and routing
+                (gqe_route_backward) on the step's outputs, GB/s against HBM.
 
 --graph also times the step replayed from one HIP graph of the four calls
 (on this stack replaying is not faster than launching them one by one).
@@ -297,6 +299,31 @@ def kv_proj_leg(p, torch, steps):
             "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
 
 
+def route_backward_leg(p, torch, steps):
+    """The backward through slot assembly and routing (gqe_route_backward) on the step's own slots and
+    routing with a seeded upstream gradient: memory-bound, so bytes it must move over its time against the
+    HBM peak (reads dout, the hard slots and x; writes d_hard, the score gradient and dx; W_router and
+    dW_router are small)."""
+    w, G = p.w, p.G
+    BT, S, D, kG, N = w.B * w.T, p.d.S, w.d_head, w.k * w.G, w.H_q
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    dout = torch.randn((BT, S, D), generator=gen).to(p.x.device)
+    out = p.out.view(BT, S, D)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=p.x.device)  # noqa: E731
+    d_hard, d_logits, dw, db, dx = f32(BT, kG, D), f32(BT, N), f32(N, w.d_model), f32(N), f32(BT, w.d_model)
+    ws = torch.empty(G.gqe_route_backward_workspace_bytes(p.d), dtype=torch.uint8, device=p.x.device)
+
+    def bwd():
+        G.gqe_route_backward(p.d, dout, out, p.r["sel"], p.r["p_tilde"], p.x, p.wr, d_hard, d_logits, dw, db, dx, ws)
+
+    warm([bwd], torch)
+    (t,) = time_calls([bwd], steps, torch)
+    nbytes = 4.0 * BT * (S * D + kG * D) + 2.0 * BT * w.d_model + 4.0 * BT * (kG * D + N + w.d_model)
+    gbs = nbytes / (t * 1e-3) / 1e9
+    return {"workload": w.name, "kernel": "route_bwd token, dW partial + final, dx kernels (gqe_route_backward)",
+            "us": t * 1e3, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS, "bytes": nbytes}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
@@ -437,6 +464,7 @@ def main():
     }
     line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
     line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
+    line["route_backward"] = route_backward_leg(p, torch, max(10, args.steps))
     del p
     torch.cuda.empty_cache()
     if not args.no_decode:

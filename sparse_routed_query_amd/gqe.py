@@ -243,6 +243,24 @@ def check_decode_inputs(desc, lens, L_max, block_table=None, num_pages=0, page_s
     return int(bad[0]), int(bad[1])
 
 
+def gqe_route_backward_workspace_bytes(desc: GqeDesc) -> int:
+    return load().gqe_route_backward_workspace_bytes(ctypes.byref(desc))
+
+
+def gqe_route_backward(desc, dout, out, sel, p_tilde, x, w_router, d_hard, d_logits, dw_router, db_router, dx,
+                       workspace, stream=None):
+    dt = desc.torch_dtype
+    nb = workspace.numel() if workspace is not None else 0
+    rc = load().gqe_route_backward(ctypes.byref(desc), _ptr(dout, torch.float32, "dout"), _ptr(out, torch.float32, "out"),
+                                   _ptr(sel, torch.int32, "sel"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                   _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+                                   _ptr(d_hard, torch.float32, "d_hard"), _ptr(d_logits, torch.float32, "d_logits"),
+                                   _ptr(dw_router, torch.float32, "dw_router"), _ptr(db_router, torch.float32, "db_router"),
+                                   _ptr(dx, torch.float32, "dx"), _ptr(workspace, torch.uint8, "workspace"), nb,
+                                   _stream(stream))
+    _check("gqe_route_backward", rc)
+
+
 def route_backward(desc, dout, out, sel, p_tilde, x, w_router, want_dw=True, want_dx=True, stream=None) -> dict:
     """Gradients through slot assembly and routing (allocates its outputs and workspace)."""
     BT, G, k, N, D = desc.B * desc.T, desc.H_kv, desc.k, desc.H_q, desc.d_head
@@ -250,15 +268,10 @@ def route_backward(desc, dout, out, sel, p_tilde, x, w_router, want_dw=True, wan
     e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
     res = dict(d_hard=e(BT, G * k, D), d_logits=e(BT, N), dw_router=e(N, desc.d_model) if want_dw else None,
                db_router=e(N) if want_dw else None, dx=e(BT, desc.d_model) if want_dx else None)
-    nb = load().gqe_route_backward_workspace_bytes(ctypes.byref(desc)) if want_dw else 0
+    nb = gqe_route_backward_workspace_bytes(desc) if want_dw else 0
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if want_dw else None
-    dt = desc.torch_dtype
-    rc = load().gqe_route_backward(ctypes.byref(desc), _ptr(dout, torch.float32, "dout"), _ptr(out, torch.float32, "out"),
-                                   _ptr(sel, torch.int32, "sel"), _ptr(p_tilde, torch.float32, "p_tilde"),
-                                   _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"), _ptr(res["d_hard"]),
-                                   _ptr(res["d_logits"]), _ptr(res["dw_router"]), _ptr(res["db_router"]),
-                                   _ptr(res["dx"]), _ptr(ws), nb, _stream(stream))
-    _check("gqe_route_backward", rc)
+    gqe_route_backward(desc, dout, out, sel, p_tilde, x, w_router, res["d_hard"], res["d_logits"], res["dw_router"],
+                       res["db_router"], res["dx"], ws, stream)
     return res
 
 

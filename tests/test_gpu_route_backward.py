@@ -9,7 +9,7 @@ when a group's kept experts produce equal outputs, are judged on the scale of wh
   d_hard    dout_h + p~ dout_w: 3 roundings, plus the GPU's fp32 p~ (2e-6 relative)
   d_logits  p~_j (dp~_j - sum_i p~_i dp~_i): the d_head-term dot products and the k-term sum, plus p~;
             experts that were not kept are exactly 0
-  dw, db    256-token block sums then up to 64 blocks in order, plus the d_logits bounds carried through
+  dw, db    sums over 256-token blocks, then the blocks added, plus the d_logits bounds carried through
   dx        N-term sums, plus the d_logits bounds carried through
 """
 import numpy as np
@@ -96,7 +96,9 @@ def run_case(w):
     small(), small(route_mode=1, name="per_group"), small(route_mode=2, name="hard_only"),
     small(H_q=16, H_kv=4, k=3, zipf_s=1.2, name="E4k3_bias"), small(k=1, H_q=4, H_kv=2, name="top1"),
     small(d_head=32, name="d32"), small(d_head=128, name="d128"), small(dtype="f32", T=100, d_model=96, name="f32"),
-    small(B=1, T=1, name="T1"), W.WORKLOADS["main_250m"],
+    small(B=1, T=1, name="T1"), small(d_model=192, H_q=48, H_kv=4, k=3, name="N48_C192"),
+    small(dtype="f32", T=50, d_model=100, H_q=48, H_kv=4, k=2, name="f32_N48"), small(d_head=32, H_q=32, H_kv=2, k=4, T=513, name="N32_d32"),
+    W.WORKLOADS["main_250m"],
     W.WORKLOADS["main_250m"].replace(k=2, name="main_250m_k2"),   # full size with a router gradient
 ], ids=lambda w: f"{w.name}-{w.dtype}")
 def test_route_backward(w):
