@@ -305,10 +305,11 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restri
                 for (int e = 0; e < CPT; ++e) acc[e] = fmaf(a[m], w[n4 + m][e], acc[e]);
         }
         float* o = dx + (size_t)(t0 + tt) * C + c0;
-        if (vec) {
-            if constexpr (CPT == 4) *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            else if constexpr (CPT == 2) *(float2*)o = make_float2(acc[0], acc[1]);
-            else o[0] = acc[0];
+        if (vec) {   // (streamed out: nothing reads dx back here)
+            if constexpr (CPT == 4) __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)o);
+            else if constexpr (CPT == 2)
+                __builtin_nontemporal_store(__builtin_bit_cast(double, make_float2(acc[0], acc[1])), (double*)o);
+            else __builtin_nontemporal_store(acc[0], o);
         } else {
 #pragma unroll
             for (int e = 0; e < CPT; ++e)
