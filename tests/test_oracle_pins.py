@@ -513,3 +513,118 @@ def test_router_backward_closed_forms():
     p = r3["probs"].reshape(-1, w3.G, 3)
     want = p * (ge - (p * ge).sum(-1, keepdims=True))
     np.testing.assert_allclose(g3["d_logits"].reshape(-1, w3.G, 3), want, rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------- attention backward (oracle/attn_backward.py)
+
+from oracle.attn_backward import attention_backward, head_backward  # noqa: E402
+
+
+def _attn_bwd_case(k=2, E=2, G=2, T=5, d=3, seed=11, causal=1):
+    w = wl(B=1, T=T, d_model=4, H_q=G * E, H_kv=G, k=k, d_head=d, seed=seed, causal=causal)
+    rng = np.random.default_rng(seed)
+    n = w.B * w.T
+    q_tok = rng.standard_normal((n, G, k, d))              # token-major, as attend_rows takes them
+    q_sh = rng.standard_normal((n, d))
+    K = rng.standard_normal((w.B, G, T, d))
+    V = rng.standard_normal((w.B, G, T, d))
+    S = G * k + 2
+    dout = rng.standard_normal((n, S, d))
+    return w, q_tok, q_sh, K, V, dout
+
+
+def _q_routed(w, q_tok):
+    """[B*T, G, k, d] token-major -> [B, G, T*k, d], row t*k + j."""
+    G, k, d = q_tok.shape[1:]
+    return q_tok.reshape(w.B, w.T, G, k, d).transpose(0, 2, 1, 3, 4).reshape(w.B, G, w.T * k, d)
+
+
+def _attn_loss(w, q_tok, q_sh, K, V, dout):
+    """sum over the hard and shared slots of dout * slot, the slots from the C oracle's forward."""
+    d = oracle.desc(w)
+    G, k = w.H_kv, w.k
+    pt = np.full((w.B * w.T, G, k), 1.0 / k)
+    out = oracle.attend_rows(d, q_tok, q_sh, K, V, pt)
+    kG = G * k
+    return float((dout[:, :kG] * out[:, :kG]).sum() + (dout[:, -1] * out[:, -1]).sum())
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_attention_backward_matches_finite_differences_of_the_forward(causal):
+    # the forward here is the C oracle's attention (pinned against SDPA above), the gradient is autograd
+    w, q_tok, q_sh, K, V, dout = _attn_bwd_case(causal=causal)
+    G, k = w.H_kv, w.k
+    g = attention_backward(w, _q_routed(w, q_tok), q_sh.reshape(w.B, w.T, -1), K, V, dout[:, :G * k], dout)
+    h = 1e-6
+
+    def fd(arr, idx):
+        a, b = arr.copy(), arr.copy()
+        a[idx] += h
+        b[idx] -= h
+        args_a = [a if x is arr else x for x in (q_tok, q_sh, K, V)]
+        args_b = [b if x is arr else x for x in (q_tok, q_sh, K, V)]
+        return (_attn_loss(w, *args_a, dout) - _attn_loss(w, *args_b, dout)) / (2 * h)
+
+    dq_tok = g["dq_routed"].reshape(w.B, G, w.T, k, -1).transpose(0, 2, 1, 3, 4).reshape(q_tok.shape)
+    for arr, grad in ((q_tok, dq_tok), (q_sh, g["dq_shared"].reshape(q_sh.shape)), (K, g["dk"]), (V, g["dv"])):
+        for idx in itertools.product(*[range(s) for s in arr.shape]):
+            f = fd(arr, idx)
+            assert abs(f - grad[idx]) <= 1e-6 * max(1.0, abs(f)), (idx, f, grad[idx])
+
+
+def test_attention_backward_single_key():
+    # one key: P = 1 whatever the scores, so no gradient reaches q or K, and V gets the sum of the rows' dO
+    rng = np.random.default_rng(1)
+    q, K, V, dO = rng.standard_normal((3, 4)), rng.standard_normal((1, 4)), rng.standard_normal((1, 4)), \
+        rng.standard_normal((3, 4))
+    r = head_backward(q, K, V, dO, kk=3)
+    assert not r["dq"].any() and not r["dk"].any()
+    np.testing.assert_allclose(r["dv"][0], dO.sum(0), rtol=1e-14)
+
+
+@pytest.mark.parametrize("kk", [1, 2])
+def test_attention_backward_uniform_scores_closed_form(kk):
+    # q = 0: row r (position t = r // kk) weights keys 0..t equally, so
+    #   dv_s = sum over rows with t >= s of dO_r / (t + 1),
+    #   dq_r = (1/sqrt(d)) (1/(t+1)) sum_s (g_rs - mean_s g_rs) k_s,  g_rs = dO_r . v_s,   dk = 0
+    rng = np.random.default_rng(2)
+    T, d = 6, 5
+    R = T * kk
+    q = np.zeros((R, d))
+    K, V, dO = rng.standard_normal((T, d)), rng.standard_normal((T, d)), rng.standard_normal((R, d))
+    r = head_backward(q, K, V, dO, kk)
+    dv = np.zeros((T, d))
+    dq = np.zeros((R, d))
+    for row in range(R):
+        t = row // kk
+        for s in range(t + 1):
+            dv[s] += dO[row] / (t + 1)
+        gr = np.array([dO[row] @ V[s] for s in range(t + 1)])
+        for s in range(t + 1):
+            dq[row] += (gr[s] - gr.mean()) * K[s] / (t + 1) / np.sqrt(d)
+    np.testing.assert_allclose(r["dv"], dv, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(r["dq"], dq, rtol=1e-12, atol=1e-14)
+    assert np.abs(r["dk"]).max() < 1e-14
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_attention_backward_all_experts_equals_dense_gqa(causal):
+    # k = E: the routed rows are every query head of the group, so the gradients are those of dense GQA,
+    # here by torch's SDPA autograd on K/V repeated over each group's heads (GQA tutorial code listing)
+    w, q_tok, q_sh, K, V, dout = _attn_bwd_case(k=3, E=3, G=2, T=7, d=4, causal=causal)
+    G, E, T, d = w.H_kv, 3, w.T, w.d_head
+    g = attention_backward(w, _q_routed(w, q_tok), q_sh.reshape(1, T, d), K, V, dout[:, :G * E], dout)
+    qd = torch.tensor(q_tok.reshape(T, G * E, d).transpose(1, 0, 2)[None], requires_grad=True)   # [1, H, T, d]
+    qs = torch.tensor(q_sh[None, None], requires_grad=True)
+    Kt = torch.tensor(K, requires_grad=True)
+    Vt = torch.tensor(V, requires_grad=True)
+    o = torch_sdpa(qd, Kt.repeat_interleave(E, dim=1), Vt.repeat_interleave(E, dim=1), causal)
+    os_ = torch_sdpa(qs, Kt[:, :1], Vt[:, :1], causal)
+    dO = torch.tensor(dout[:, :G * E].reshape(T, G * E, d).transpose(1, 0, 2)[None])
+    ((o * dO).sum() + (os_ * torch.tensor(dout[:, -1][None, None])).sum()).backward()
+    dq_dense = qd.grad.numpy()[0].transpose(1, 0, 2).reshape(T, G, E, d)     # [T, G, E, d]
+    want_routed = dq_dense.transpose(1, 0, 2, 3).reshape(1, G, T * E, d)
+    np.testing.assert_allclose(g["dq_routed"], want_routed, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dq_shared"], qs.grad.numpy()[0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], Kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], Vt.grad.numpy(), rtol=1e-10, atol=1e-12)
