@@ -226,6 +226,37 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
  */
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
 
+/* Bytes of device workspace gqe_attn_backward needs (two floats per query row). */
+size_t gqe_attn_backward_workspace_bytes(const gqe_desc* desc);
+
+/*
+ * gqe_attn_backward -- gradients of the routed and shared attention (GQE
+ * study note §3-2 (3); GQA tutorial, step 4 of the GQA computation) given the
+ * gradient of the hard and shared slots.  Per head, S = q K^T / sqrt(d_head)
+ * with the forward's masking, P = softmax(S), O = P V, and
+ *   dV = P^T dO,  dS = P o (dO V^T - rowsum(dO o O)),
+ *   dq = dS K / sqrt(d_head),  dK = dS^T q / sqrt(d_head),
+ * dK and dV of KV head 0 also summing the shared rows' terms.  Routed row
+ * t*k + j of group g has dO = d_hard[t, g*k + j] and O = out[t, g*k + j]; a
+ * shared row has dout[t, S-1] and out[t, S-1].
+ * bf16 only (GQE_ERR_UNSUPPORTED for fp32): q, K, V as the forward reads them;
+ * dO, P and dS are rounded to bf16 for the matrix products, which accumulate
+ * in fp32.  Deterministic (no atomics; every sum in a fixed order).
+ * In:  q_routed [B, G, T*k, d_head], q_shared [B, T, d_head] (n_shared = 1),
+ *      k, v [B, H_kv, T, d_head]; out [B*T, S, d_head] fp32 (the forward's
+ *      slots), d_hard [B*T, G*k, d_head] fp32 (as gqe_route_backward gives
+ *      it: the weighted slot's share already added), dout [B*T, S, d_head] fp32
+ *      (only the shared slot is read; n_shared = 1).
+ * Out: dq_routed [B, G, T*k, d_head], dq_shared [B, T, d_head] (n_shared = 1),
+ *      dk, dv [B, H_kv, T, d_head], all fp32, every element written.
+ * Workspace: gqe_attn_backward_workspace_bytes(desc) bytes; no initialisation.
+ * q_shared, dout and dq_shared are ignored when n_shared = 0.
+ */
+int gqe_attn_backward(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                      const void* v, const float* out, const float* d_hard, const float* dout,
+                      float* dq_routed, float* dq_shared, float* dk, float* dv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace gqe_route_backward needs when it computes dw_router. */
 size_t gqe_route_backward_workspace_bytes(const gqe_desc* desc);
 

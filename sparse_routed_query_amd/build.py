@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgqe.so")
 SOURCES = ["gqe_api.cpp", "route.hip", "qproj.hip", "attn_prefill.hip", "attn_decode.hip", "outproj.hip",
-           "route_bwd.hip"]
+           "route_bwd.hip", "attn_bwd.hip"]
 ARCH = os.environ.get("GQE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

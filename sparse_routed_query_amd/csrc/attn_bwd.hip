@@ -1,0 +1,457 @@
+// Backward of the routed and shared causal attention (gfx950; bf16 operands,
+// fp32 accumulation): gradients of the query rows, K and V given the gradient
+// of the hard and shared slots (GQE study note §3-2 (3); GQA tutorial, step 4
+// of the GQA computation).
+//
+// Per head, with S = q K^T / sqrt(d), P = softmax(S) (masked), O = P V:
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Delta),  Delta_r = <dO_r, O_r>,
+//   dq = dS K / sqrt(d),   dK = dS^T q / sqrt(d).
+// The forward keeps no row statistics, so the dq kernel first recomputes each
+// row's log-sum-exp (base 2) and Delta, writes them to the workspace for the
+// dK/dV kernel, then forms dq.  No atomics: every output element is written by
+// one workgroup, with its sums in a fixed order.
+//
+// Both kernels: 256 threads = 4 waves, tiles of 64 query rows x 64 keys,
+// 32x32x16 bf16 MFMA.  Score tiles are formed transposed (S^T = K q^T), so a
+// lane's accumulator column is one query row and the row statistics are one
+// value per lane; wave w computes the 32 x 32 quadrant (keys 32 (w & 1),
+// rows 32 (w >> 1)).  Operands are read from LDS: a fragment along a tile's
+// contiguous axis is one 16-byte read, one across it is 8 strided reads.
+//   attn_bwd_dq_kernel<D>    one 64-row tile of one head (routed or shared)
+//   attn_bwd_dkdv_kernel<D>  one 64-key tile of one KV head, over every row
+//                            tile that sees it: the group's routed rows and,
+//                            for KV head 0, the shared rows
+#include "gqe_device.h"
+#include "gqe_launch.h"
+
+namespace gqe {
+
+namespace {
+
+constexpr int kAbTile = 64;
+
+// MFMA 32x32x16 bf16 fragments, lane l: A row l%32 / B column l%32, with
+// k = 8 (l/32) .. +7; accumulator element i: column l%32, row
+// 8 (i/4) + 4 (l/32) + i%4.
+__device__ __forceinline__ bf16x8 frag_row(const uint16_t* p) { return ld_bf16x8(p); }
+__device__ __forceinline__ bf16x8 frag_col(const uint16_t* p, int pitch)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(bf16, p[i * pitch]);
+    return v;
+}
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, f2bf(f)); }
+
+// (m, l) of two partial softmax sums over disjoint keys, base 2
+__device__ __forceinline__ void ml_merge(float& m, float& l, float m2, float l2)
+{
+    const float mm = fmaxf(m, m2);
+    l = l * __builtin_amdgcn_exp2f(m - mm) + l2 * __builtin_amdgcn_exp2f(m2 - mm);
+    m = mm;
+}
+
+struct RowSet {
+    const uint16_t* q;     // row r at q + r * D
+    const float* dO;       // token t's slot at dO + t * dO_stride, then + j * D for row t*kk + j
+    const float* O;        // likewise
+    long long dO_stride, O_stride;
+    float* dq;             // row r at dq + r * D
+    float* lse;            // row r's base-2 log-sum-exp at lse[r], Delta at delta[r]
+    float* delta;
+    int R, kk;
+};
+
+__device__ __forceinline__ RowSet row_set(const AttnBwdArgs& a, int b, int h)
+{
+    const int T = a.T, D = a.d_head, G = a.G, k = a.k, S = a.S, kG = G * k;
+    RowSet rs;
+    const long long nrouted = (long long)a.B * G * T * k;
+    if (h < G) {
+        const long long base = ((long long)b * G + h) * T * k;
+        rs.q = (const uint16_t*)a.q_routed + base * D;
+        rs.dO = a.d_hard + ((size_t)b * T * kG + (size_t)h * k) * D;
+        rs.dO_stride = (long long)kG * D;
+        rs.O = a.out + ((size_t)b * T * S + (size_t)h * k) * D;
+        rs.O_stride = (long long)S * D;
+        rs.dq = a.dq_routed + base * D;
+        rs.lse = a.lse + base;
+        rs.delta = a.delta + base;
+        rs.R = T * k;
+        rs.kk = k;
+    } else {
+        const long long base = (long long)b * T;
+        rs.q = (const uint16_t*)a.q_shared + base * D;
+        rs.dO = a.dout + ((size_t)b * T * S + (S - 1)) * D;
+        rs.dO_stride = (long long)S * D;
+        rs.O = a.out + ((size_t)b * T * S + (S - 1)) * D;
+        rs.O_stride = (long long)S * D;
+        rs.dq = a.dq_shared + base * D;
+        rs.lse = a.lse + nrouted + base;
+        rs.delta = a.delta + nrouted + base;
+        rs.R = T;
+        rs.kk = 1;
+    }
+    return rs;
+}
+
+// rows r0 .. r0+63 of a row set into LDS: q (bf16) and dO (rounded to bf16);
+// rows past R are zero.  With s_dp, also the partial <dO, O> of each 8-wide chunk.
+template <int D>
+__device__ __forceinline__ void load_rows(const RowSet& rs, int r0, uint16_t* sQ, uint16_t* sdO, float* s_dp)
+{
+    constexpr int P = D + 8, CPR = D / 8;
+    for (int c = threadIdx.x; c < kAbTile * CPR; c += 256) {
+        const int row = c / CPR, d0 = (c % CPR) * 8, r = r0 + row;
+        u32x4 qv = {0u, 0u, 0u, 0u}, gv = {0u, 0u, 0u, 0u};
+        float dp = 0.f;
+        if (r < rs.R) {
+            qv = ld_u32x4(rs.q + (size_t)r * D + d0);
+            const int t = r / rs.kk, j = r - t * rs.kk;
+            const float* g = rs.dO + (size_t)t * rs.dO_stride + (size_t)j * D + d0;
+            const f32x4 g0 = *(const f32x4*)g, g1 = *(const f32x4*)(g + 4);
+            gv = u32x4{pack_bf2(g0[0], g0[1]), pack_bf2(g0[2], g0[3]), pack_bf2(g1[0], g1[1]), pack_bf2(g1[2], g1[3])};
+            if (s_dp) {
+                const float* o = rs.O + (size_t)t * rs.O_stride + (size_t)j * D + d0;
+                const f32x4 o0 = *(const f32x4*)o, o1 = *(const f32x4*)(o + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp = fmaf(g0[e], o0[e], dp);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp = fmaf(g1[e], o1[e], dp);
+            }
+        }
+        *(u32x4*)(sQ + row * P + d0) = qv;
+        *(u32x4*)(sdO + row * P + d0) = gv;
+        if (s_dp) s_dp[row * CPR + c % CPR] = dp;
+    }
+}
+
+// keys s0 .. s0+63 of one head into LDS (bf16); keys past T are zero
+template <int D>
+__device__ __forceinline__ void load_keys(const uint16_t* src, int s0, int T, uint16_t* dst)
+{
+    constexpr int P = D + 8, CPR = D / 8;
+    for (int c = threadIdx.x; c < kAbTile * CPR; c += 256) {
+        const int row = c / CPR, d0 = (c % CPR) * 8, s = s0 + row;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (s < T) v = ld_u32x4(src + (size_t)s * D + d0);
+        *(u32x4*)(dst + row * P + d0) = v;
+    }
+}
+
+// 32 x 32 quadrant of X Y^T over d: X rows x0.., Y rows y0.. (both [64][P] bf16 tiles)
+template <int D>
+__device__ __forceinline__ f32x16 quad_xyT(const uint16_t* X, int x0, const uint16_t* Y, int y0, int lane)
+{
+    constexpr int P = D + 8;
+    f32x16 c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = 0.f;
+    const uint16_t* xa = X + (x0 + (lane & 31)) * P + 8 * (lane >> 5);
+    const uint16_t* yb = Y + (y0 + (lane & 31)) * P + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) c = mfma32(frag_row(xa + 16 * s), frag_row(yb + 16 * s), c);
+    return c;
+}
+
+// C[m][n] += sum over 64 k of A[m][k] Z[k][n]: A a [64][64+8] tile (row m0 + l%32),
+// Z a [64][D+8] tile read across (columns n0 + l%32)
+template <int D>
+__device__ __forceinline__ f32x16 gemm_az(f32x16 c, const uint16_t* A, int m0, const uint16_t* Z, int n0, int lane)
+{
+    constexpr int P = D + 8, PS = kAbTile + 8;
+    const uint16_t* aa = A + (m0 + (lane & 31)) * PS + 8 * (lane >> 5);
+    const uint16_t* zb = Z + (8 * (lane >> 5)) * P + n0 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < kAbTile / 16; ++s) c = mfma32(frag_row(aa + 16 * s), frag_col(zb + 16 * s * P, P), c);
+    return c;
+}
+
+template <int D>
+constexpr int ab_lds_bytes(bool dq)
+{
+    // q, dO, K, V tiles; then dS (dq kernel) or P^T and dS^T (dK/dV kernel); then row data
+    return 4 * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 +
+           (dq ? kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 : 0) + 2 * kAbTile * 4;
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
+{
+    constexpr int P = D + 8, PS = kAbTile + 8, CPR = D / 8, NBW = (2 * (D / 32) + 3) / 4;
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
+    uint16_t* sQ = s_ab;
+    uint16_t* sdO = sQ + kAbTile * P;
+    uint16_t* sK = sdO + kAbTile * P;
+    uint16_t* sV = sK + kAbTile * P;
+    uint16_t* sS = sV + kAbTile * P;
+    float* s_dp = (float*)(sS + kAbTile * PS);
+    float* s_m = s_dp + kAbTile * CPR;            // [4][32]
+    float* s_l = s_m + 4 * 32;                    // [4][32]
+    float* s_lse = s_l + 4 * 32;                  // [64]
+    float* s_delta = s_lse + kAbTile;             // [64]
+
+    const int T = a.T, G = a.G;
+    const int ntr = (T * a.k + kAbTile - 1) / kAbTile, nts = (T + kAbTile - 1) / kAbTile;
+    long long it = blockIdx.x;
+    int b, h, tile;
+    if (it < (long long)a.B * G * ntr) {
+        b = (int)(it / ((long long)G * ntr));
+        const int rem = (int)(it - (long long)b * G * ntr);
+        h = rem / ntr;
+        tile = ntr - 1 - rem % ntr;   // longest first
+    } else {
+        it -= (long long)a.B * G * ntr;
+        b = (int)(it / nts);
+        h = G;
+        tile = nts - 1 - (int)(it % nts);
+    }
+    const RowSet rs = row_set(a, b, h);
+    const int kvh = h < G ? h : 0;
+    const uint16_t* Kh = (const uint16_t*)a.k_ + ((size_t)b * G + kvh) * T * D;
+    const uint16_t* Vh = (const uint16_t*)a.v_ + ((size_t)b * G + kvh) * T * D;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = wave & 1, wr = wave >> 1;
+    const int r0 = tile * kAbTile;
+    const int last = min(rs.R - 1, r0 + kAbTile - 1);
+    const int nkt = a.causal ? (last / rs.kk) / kAbTile + 1 : (T + kAbTile - 1) / kAbTile;
+    const int row = wr * 32 + (lane & 31);          // this lane's query row in the tile
+    const int rg = r0 + row;
+    const int tq = rg / rs.kk;
+    const float qs2 = a.qscale2;
+
+    load_rows<D>(rs, r0, sQ, sdO, s_dp);
+    __syncthreads();
+    if (tid < kAbTile) {
+        float dsum = 0.f;
+        for (int c = 0; c < CPR; ++c) dsum += s_dp[tid * CPR + c];
+        s_delta[tid] = dsum;
+    }
+
+    // pass 1: the rows' base-2 log-sum-exp
+    float m = -1e30f, l = 0.f;
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int s0 = kt * kAbTile;
+        load_keys<D>(Kh, s0, T, sK);
+        __syncthreads();
+        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        float sv[16], mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = s0 + wk * 32 + acc_row(i, lane);
+            const bool ok = key < T && (!a.causal || key <= tq);
+            sv[i] = ok ? c[i] * qs2 : -INFINITY;
+            mt = fmaxf(mt, sv[i]);
+        }
+        const float mn = fmaxf(m, mt);
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f(sv[i] - mn);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + ls;
+        m = mn;
+        __syncthreads();
+    }
+    {
+        // lanes l and l^32 hold the same row over different keys; then the two key halves (waves)
+        const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
+        if (lane < 32) ml_merge(m, l, m2, l2);
+        if (lane < 32) {
+            s_m[wave * 32 + lane] = m;
+            s_l[wave * 32 + lane] = l;
+        }
+        __syncthreads();
+        if (wk == 0 && lane < 32) {
+            float mf = s_m[(wr * 2) * 32 + lane], lf = s_l[(wr * 2) * 32 + lane];
+            ml_merge(mf, lf, s_m[(wr * 2 + 1) * 32 + lane], s_l[(wr * 2 + 1) * 32 + lane]);
+            const float lse = rg < rs.R ? mf + __log2f(lf) : INFINITY;   // (rows past R weigh nothing)
+            s_lse[row] = lse;
+            if (rg < rs.R) {
+                rs.lse[rg] = lse;
+                rs.delta[rg] = s_delta[row];
+            }
+        }
+        __syncthreads();
+    }
+
+    // pass 2: dq = dS K / sqrt(d)
+    const float lse_r = s_lse[row], dl_r = s_delta[row];
+    f32x16 acc[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int s0 = kt * kAbTile;
+        load_keys<D>(Kh, s0, T, sK);
+        load_keys<D>(Vh, s0, T, sV);
+        __syncthreads();
+        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
+        // dS[row][key] as bf16, four consecutive keys per 8-byte store
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                const int key = s0 + wk * 32 + acc_row(i, lane);
+                const bool ok = key < T && (!a.causal || key <= tq);
+                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * qs2 - lse_r) : 0.f;
+                v[e] = pv * (dp[i] - dl_r);
+            }
+            const int k0 = wk * 32 + acc_row(4 * i4, lane);
+            *(uint2*)(sS + row * PS + k0) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int blk = wave + 4 * j;
+            if (blk < 2 * (D / 32)) acc[j] = gemm_az<D>(acc[j], sS, (blk & 1) * 32, sK, (blk >> 1) * 32, lane);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + 4 * j;
+        if (blk >= 2 * (D / 32)) continue;
+        const int d = (blk >> 1) * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = r0 + (blk & 1) * 32 + acc_row(i, lane);
+            if (r < rs.R) rs.dq[(size_t)r * D + d] = acc[j][i] * a.inv_sqrt_d;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
+{
+    constexpr int P = D + 8, PS = kAbTile + 8, NBW = (2 * (D / 32) + 3) / 4;
+    extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
+    uint16_t* sQ = s_ab;
+    uint16_t* sdO = sQ + kAbTile * P;
+    uint16_t* sK = sdO + kAbTile * P;
+    uint16_t* sV = sK + kAbTile * P;
+    uint16_t* sP = sV + kAbTile * P;          // P^T [key][row]
+    uint16_t* sD = sP + kAbTile * PS;         // dS^T [key][row]
+    float* s_lse = (float*)(sD + kAbTile * PS);
+    float* s_delta = s_lse + kAbTile;
+
+    const int T = a.T, G = a.G;
+    const int nkt = (T + kAbTile - 1) / kAbTile;
+    const int kt = (int)(blockIdx.x % nkt);           // ascending: the longest first
+    const int g = (int)((blockIdx.x / nkt) % G);
+    const int b = (int)(blockIdx.x / ((long long)nkt * G));
+    const int s0 = kt * kAbTile;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = wave & 1, wr = wave >> 1;
+    const int row = wr * 32 + (lane & 31);
+
+    load_keys<D>((const uint16_t*)a.k_ + ((size_t)b * G + g) * T * D, s0, T, sK);
+    load_keys<D>((const uint16_t*)a.v_ + ((size_t)b * G + g) * T * D, s0, T, sV);
+
+    f32x16 dk[NBW], dv[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[j][r] = dv[j][r] = 0.f;
+
+    const int nsets = (g == 0 && a.n_shared) ? 2 : 1;
+    for (int set = 0; set < nsets; ++set) {
+        const RowSet rs = row_set(a, b, set == 0 ? g : G);
+        const int ntr = (rs.R + kAbTile - 1) / kAbTile;
+        const int rt0 = a.causal ? (int)(((long long)s0 * rs.kk) / kAbTile) : 0;
+        for (int rt = rt0; rt < ntr; ++rt) {
+            const int r0 = rt * kAbTile;
+            __syncthreads();   // (the previous tile's reads of sQ, sdO, sP, sD are done)
+            load_rows<D>(rs, r0, sQ, sdO, nullptr);
+            if (tid < kAbTile) {
+                const int r = r0 + tid;
+                s_lse[tid] = r < rs.R ? rs.lse[r] : INFINITY;
+                s_delta[tid] = r < rs.R ? rs.delta[r] : 0.f;
+            }
+            __syncthreads();
+            const int tq = (r0 + row) / rs.kk;
+            const float lse_r = s_lse[row], dl_r = s_delta[row];
+            const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+            const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kl = wk * 32 + acc_row(i, lane);
+                const int key = s0 + kl;
+                const bool ok = key < T && (!a.causal || key <= tq);
+                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
+                sP[kl * PS + row] = bf16_bits(pv);
+                sD[kl * PS + row] = bf16_bits(pv * (dp[i] - dl_r));
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const int blk = wave + 4 * j;
+                if (blk < 2 * (D / 32)) {
+                    dv[j] = gemm_az<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
+                    dk[j] = gemm_az<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
+                }
+            }
+        }
+    }
+    float* dkh = a.dk + ((size_t)b * G + g) * T * D;
+    float* dvh = a.dv + ((size_t)b * G + g) * T * D;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int blk = wave + 4 * j;
+        if (blk >= 2 * (D / 32)) continue;
+        const int d = (blk >> 1) * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = s0 + (blk & 1) * 32 + acc_row(i, lane);
+            if (key < T) {
+                dkh[(size_t)key * D + d] = dk[j][i] * a.inv_sqrt_d;
+                dvh[(size_t)key * D + d] = dv[j][i];
+            }
+        }
+    }
+}
+
+size_t attn_bwd_workspace_bytes(int B, int T, int G, int k, int n_shared)
+{
+    const long long rows = (long long)B * G * T * k + (n_shared ? (long long)B * T : 0);
+    return (size_t)rows * 2 * sizeof(float) + 256;
+}
+
+template <int D>
+static int launch_attn_bwd_d(AttnBwdArgs a, hipStream_t st)
+{
+    const int ntr = (a.T * a.k + kAbTile - 1) / kAbTile, nts = (a.T + kAbTile - 1) / kAbTile;
+    const long long nq = (long long)a.B * a.G * ntr + (a.n_shared ? (long long)a.B * nts : 0);
+    const long long nkv = (long long)a.B * a.G * nts;
+    const int lq = ab_lds_bytes<D>(true), lkv = ab_lds_bytes<D>(false);
+    if (lq > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dq_kernel<D>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, lq) != hipSuccess)
+        return -1;
+    if (lkv > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dkdv_kernel<D>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lkv) != hipSuccess)
+        return -1;
+    attn_bwd_dq_kernel<D><<<(unsigned)nq, 256, lq, st>>>(a);
+    attn_bwd_dkdv_kernel<D><<<(unsigned)nkv, 256, lkv, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st)
+{
+    if (a.B == 0 || a.T == 0) return 0;
+    switch (a.d_head) {
+    case 32: return launch_attn_bwd_d<32>(a, st);
+    case 64: return launch_attn_bwd_d<64>(a, st);
+    case 128: return launch_attn_bwd_d<128>(a, st);
+    default: return -2;
+    }
+}
+
+}  // namespace gqe

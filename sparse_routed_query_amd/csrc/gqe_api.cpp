@@ -254,6 +254,45 @@ int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out
     return launch_status(gqe::launch_route_bwd(a, (hipStream_t)stream));
 }
 
+size_t gqe_attn_backward_workspace_bytes(const gqe_desc* desc)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK) return 0;
+    return gqe::attn_bwd_workspace_bytes(s.B, s.T, s.G, s.k, s.ns);
+}
+
+int gqe_attn_backward(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                      const void* v, const float* out, const float* d_hard, const float* dout, float* dq_routed,
+                      float* dq_shared, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!s.bf16) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    GQE_TRY(need(out));
+    GQE_TRY(need(d_hard));
+    GQE_TRY(need(dq_routed));
+    GQE_TRY(need(dk));
+    GQE_TRY(need(dv));
+    if (s.ns) {
+        GQE_TRY(need(q_shared));
+        GQE_TRY(need(dout));
+        GQE_TRY(need(dq_shared));
+    }
+    if (!workspace) return GQE_ERR_WORKSPACE;
+    GQE_TRY(need(workspace));
+    if (workspace_bytes < gqe::attn_bwd_workspace_bytes(s.B, s.T, s.G, s.k, s.ns)) return GQE_ERR_WORKSPACE;
+    const long long rows = (long long)s.B * s.G * s.T * s.k + (s.ns ? s.BT : 0);
+    gqe::AttnBwdArgs a{q_routed, s.ns ? q_shared : nullptr, k, v, out, d_hard, s.ns ? dout : nullptr, dq_routed,
+                       s.ns ? dq_shared : nullptr, dk, dv, (float*)workspace, (float*)workspace + rows,
+                       s.B, s.T, s.G, s.k, s.S, s.D, s.causal, s.ns,
+                       1.4426950408889634f / sqrtf((float)s.D), 1.f / sqrtf((float)s.D)};
+    return launch_status(gqe::launch_attn_bwd(a, (hipStream_t)stream));
+}
+
 int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void* w_v, void* k, void* v,
                 void* stream)
 {

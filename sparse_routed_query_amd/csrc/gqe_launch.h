@@ -59,6 +59,26 @@ struct RouteBwdArgs {
 size_t route_bwd_workspace_bytes(long long BT, int N, int C);
 int launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
 
+struct AttnBwdArgs {
+    const void* q_routed;   // [B, G, T*k, d_head] bf16, row t*k + j
+    const void* q_shared;   // [B, T, d_head] bf16 (n_shared = 1)
+    const void* k_;         // [B, G, T, d_head] bf16
+    const void* v_;         // [B, G, T, d_head] bf16
+    const float* out;       // [B*T, S, d_head]: the hard and shared slots are read
+    const float* d_hard;    // [B*T, G*k, d_head]
+    const float* dout;      // [B*T, S, d_head]: the shared slot is read (n_shared = 1)
+    float* dq_routed;       // [B, G, T*k, d_head]
+    float* dq_shared;       // [B, T, d_head] (n_shared = 1)
+    float* dk;              // [B, G, T, d_head]
+    float* dv;              // [B, G, T, d_head]
+    float* lse;             // workspace: one base-2 log-sum-exp per row (routed rows, then shared)
+    float* delta;           // workspace: one <dO, O> per row
+    int B, T, G, k, S, d_head, causal, n_shared;
+    float qscale2, inv_sqrt_d;
+};
+size_t attn_bwd_workspace_bytes(int B, int T, int G, int k, int n_shared);
+int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
+
 struct KvProjArgs {
     const void* x;     // [B*T, d_model]
     const void* w_k;   // [H_kv, d_head, d_model]

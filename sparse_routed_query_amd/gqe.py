@@ -29,7 +29,7 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
-           "gqe_route_backward")
+           "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward")
 
 
 class GqeError(RuntimeError):
@@ -112,6 +112,10 @@ def load():
         lib.gqe_route_backward_workspace_bytes.restype = Z
         lib.gqe_route_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.gqe_route_backward.restype = I
+        lib.gqe_attn_backward_workspace_bytes.argtypes = [D]
+        lib.gqe_attn_backward_workspace_bytes.restype = Z
+        lib.gqe_attn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.gqe_attn_backward.restype = I
         lib.gqe_kv_proj.argtypes = [D, P, P, P, P, P, P]
         lib.gqe_kv_proj.restype = I
         lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
@@ -272,6 +276,38 @@ def route_backward(desc, dout, out, sel, p_tilde, x, w_router, want_dw=True, wan
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if want_dw else None
     gqe_route_backward(desc, dout, out, sel, p_tilde, x, w_router, res["d_hard"], res["d_logits"], res["dw_router"],
                        res["db_router"], res["dx"], ws, stream)
+    return res
+
+
+def gqe_attn_backward_workspace_bytes(desc: GqeDesc) -> int:
+    return load().gqe_attn_backward_workspace_bytes(ctypes.byref(desc))
+
+
+def gqe_attn_backward(desc, q_routed, q_shared, k, v, out, d_hard, dout, dq_routed, dq_shared, dk, dv, workspace,
+                      stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_attn_backward(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
+                                  _ptr(k, dt, "k"), _ptr(v, dt, "v"), _ptr(out, torch.float32, "out"),
+                                  _ptr(d_hard, torch.float32, "d_hard"), _ptr(dout, torch.float32, "dout"),
+                                  _ptr(dq_routed, torch.float32, "dq_routed"),
+                                  _ptr(dq_shared, torch.float32, "dq_shared"), _ptr(dk, torch.float32, "dk"),
+                                  _ptr(dv, torch.float32, "dv"), _ptr(workspace, torch.uint8, "workspace"),
+                                  workspace.numel(), _stream(stream))
+    _check("gqe_attn_backward", rc)
+
+
+def attn_backward(desc, q_routed, q_shared, k, v, out, d_hard, dout, stream=None) -> dict:
+    """Gradients of the attention: dq_routed [B, G, T*k, d], dq_shared [B, T, d] or None, dk, dv [B, H_kv, T, d]
+    (fp32; allocates its outputs and workspace)."""
+    B, T, G, k_, D = desc.B, desc.T, desc.H_kv, desc.k, desc.d_head
+    dev = d_hard.device
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    res = dict(dq_routed=e(B, G, T * k_, D), dq_shared=e(B, T, D) if desc.n_shared else None, dk=e(B, G, T, D),
+               dv=e(B, G, T, D))
+    ws = torch.empty(gqe_attn_backward_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    gqe_attn_backward(desc, q_routed, q_shared if desc.n_shared else None, k, v, out, d_hard,
+                      dout if desc.n_shared else None, res["dq_routed"], res["dq_shared"], res["dk"], res["dv"], ws,
+                      stream)
     return res
 
 

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -133,6 +133,19 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert rb(d, w=None) == WORKSPACE
     assert rb(d, dx=MIS) == ALIGN
     assert rb(main(B=0), dout=None, dw=None, db=None, dx=None, w=None) == OK
+    aws = G.load().gqe_attn_backward_workspace_bytes(by(d))
+    assert aws == (4 * 8 * 4096 + 4 * 4096) * 8 + 256          # two floats per routed and shared row
+    assert G.load().gqe_attn_backward_workspace_bytes(by(main(n_shared=0))) == 4 * 8 * 4096 * 8 + 256
+    ab = lambda desc, q=A16, qs=A16, dh=A16, dq=A16, w=A16, wb=aws: lib.gqe_attn_backward(  # noqa: E731
+        by(desc), q, qs, A16, A16, A16, dh, A16, dq, A16, A16, A16, w, wb, None)
+    assert ab(d, q=None) == INVALID
+    assert ab(d, qs=None) == INVALID             # the shared head's rows are needed with n_shared = 1
+    assert ab(d, dh=MIS) == ALIGN
+    assert ab(d, w=None) == WORKSPACE
+    assert ab(d, wb=aws - 1) == WORKSPACE
+    assert ab(main(dtype="f32")) == UNSUPPORTED  # bf16 only
+    assert ab(main(d_head=48)) == UNSUPPORTED
+    assert ab(main(B=0), q=None, qs=None, dh=None, dq=None, w=None) == OK
     kv = lambda desc, x=A16, wk=A16, wv=A16, k=A16, v=A16: lib.gqe_kv_proj(by(desc), x, wk, wv, k, v, None)  # noqa
     assert kv(d, x=None) == INVALID
     assert kv(d, wv=None) == INVALID
