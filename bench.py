@@ -24,7 +24,9 @@ divided by the whole step's time).  The same JSON line carries:
   kv_proj       the step before it, also outside: the K and V projections
                 (gqe_kv_proj) of the step's x, against the bf16 peak;
   route_backward  the backward through slot assembly and routing
-                (gqe_route_backward) on the step's outputs, GB/s against HBM.
+                (gqe_route_backward) on the step's outputs, GB/s against HBM;
+  attn_backward the attention backward (gqe_attn_backward) on the step's
+                query rows and slots, TFLOP/s against the bf16 peak.
 
 --graph also times the step replayed from one HIP graph of the four calls
 (on this stack replaying is not faster than launching them one by one).
@@ -324,6 +326,34 @@ def route_backward_leg(p, torch, steps):
             "us": t * 1e3, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS, "bytes": nbytes}
 
 
+def attn_backward_leg(p, torch, steps):
+    """The attention backward (gqe_attn_backward) on the step's own query rows, K, V and slots with seeded slot
+    gradients.  Algorithmic work: the four products dV = P^T dO, dP = dO V^T, dq = dS K, dK = dS^T q over the
+    causal scores, twice the forward's attention FLOPs (recomputing S, which the implementation does twice,
+    is not counted); against the bf16 peak."""
+    import workloads as W
+    w, G = p.w, p.G
+    BT, S, D, kG = w.B * w.T, p.d.S, w.d_head, w.k * w.G
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    d_hard = torch.randn((BT, kG, D), generator=gen).to(p.x.device)
+    dout = torch.randn((BT, S, D), generator=gen).to(p.x.device)
+    out = p.out.view(BT, S, D)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=p.x.device)  # noqa: E731
+    dqr, dqs = f32(w.B, w.G, w.T * w.k, D), f32(w.B, w.T, D)
+    dk, dv = f32(w.B, w.G, w.T, D), f32(w.B, w.G, w.T, D)
+    ws = torch.empty(G.gqe_attn_backward_workspace_bytes(p.d), dtype=torch.uint8, device=p.x.device)
+
+    def bwd():
+        G.gqe_attn_backward(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, out, d_hard, dout, dqr, dqs, dk, dv, ws)
+
+    warm([bwd], torch)
+    (t,) = time_calls([bwd], steps, torch)
+    fl = 2.0 * W.attention_flops(w)
+    tf = fl / (t * 1e-3) / 1e12
+    return {"workload": w.name, "kernel": "attn_bwd_dq_kernel<%d> + attn_bwd_dkdv_kernel<%d> (gqe_attn_backward)" % (D, D),
+            "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
@@ -465,6 +495,7 @@ def main():
     line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
     line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
     line["route_backward"] = route_backward_leg(p, torch, max(10, args.steps))
+    line["attn_backward"] = attn_backward_leg(p, torch, max(10, args.steps))
     del p
     torch.cuda.empty_cache()
     if not args.no_decode:

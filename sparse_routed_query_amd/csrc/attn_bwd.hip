@@ -141,6 +141,87 @@ __device__ __forceinline__ void load_keys(const uint16_t* src, int s0, int T, ui
     }
 }
 
+// Register stages: the next tile's global loads are issued before the
+// current tile's products, and stored to LDS after them, so the loads' latency
+// is hidden by the math.  Thread tid moves 16-byte chunks tid + 256 i.
+template <int D>
+struct KeyRegs {
+    static constexpr int N = kAbTile * D / 8 / 256;
+    u32x4 v[N];
+};
+template <int D>
+__device__ __forceinline__ void keys_load(const uint16_t* src, int s0, int T, KeyRegs<D>& r)
+{
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < KeyRegs<D>::N; ++i) {
+        const int c = threadIdx.x + 256 * i, row = c / CPR, d0 = (c % CPR) * 8, s = s0 + row;
+        r.v[i] = s < T ? ld_u32x4(src + (size_t)s * D + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+template <int D>
+__device__ __forceinline__ void keys_store(const KeyRegs<D>& r, uint16_t* dst)
+{
+    constexpr int P = D + 8, CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < KeyRegs<D>::N; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        *(u32x4*)(dst + (c / CPR) * P + (c % CPR) * 8) = r.v[i];
+    }
+}
+// a row tile's q (bf16), dO (fp32, rounded to bf16 when stored), log-sum-exp and Delta
+template <int D>
+struct RowRegs {
+    static constexpr int N = kAbTile * D / 8 / 256;
+    u32x4 q[N];
+    f32x4 g[2 * N];
+    float lse, delta;
+};
+template <int D>
+__device__ __forceinline__ void rows_load(const RowSet& rs, int r0, RowRegs<D>& r)
+{
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < RowRegs<D>::N; ++i) {
+        const int c = threadIdx.x + 256 * i, row = c / CPR, d0 = (c % CPR) * 8, rr = r0 + row;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        r.q[i] = u32x4{0u, 0u, 0u, 0u};
+        r.g[2 * i] = r.g[2 * i + 1] = z;
+        if (rr < rs.R) {
+            r.q[i] = ld_u32x4(rs.q + (size_t)rr * D + d0);
+            const int t = rr / rs.kk, j = rr - t * rs.kk;
+            const float* g = rs.dO + (size_t)t * rs.dO_stride + (size_t)j * D + d0;
+            r.g[2 * i] = *(const f32x4*)g;
+            r.g[2 * i + 1] = *(const f32x4*)(g + 4);
+        }
+    }
+    const int rr = r0 + (int)threadIdx.x;
+    r.lse = INFINITY;   // (rows past R weigh nothing)
+    r.delta = 0.f;
+    if (threadIdx.x < kAbTile && rr < rs.R) {
+        r.lse = rs.lse[rr];
+        r.delta = rs.delta[rr];
+    }
+}
+template <int D>
+__device__ __forceinline__ void rows_store(const RowRegs<D>& r, uint16_t* sQ, uint16_t* sdO, float* s_lse,
+                                           float* s_delta)
+{
+    constexpr int P = D + 8, CPR = D / 8;
+#pragma unroll
+    for (int i = 0; i < RowRegs<D>::N; ++i) {
+        const int c = threadIdx.x + 256 * i, off = (c / CPR) * P + (c % CPR) * 8;
+        const f32x4 g0 = r.g[2 * i], g1 = r.g[2 * i + 1];
+        *(u32x4*)(sQ + off) = r.q[i];
+        *(u32x4*)(sdO + off) =
+            u32x4{pack_bf2(g0[0], g0[1]), pack_bf2(g0[2], g0[3]), pack_bf2(g1[0], g1[1]), pack_bf2(g1[2], g1[3])};
+    }
+    if (threadIdx.x < kAbTile) {
+        s_lse[threadIdx.x] = r.lse;
+        s_delta[threadIdx.x] = r.delta;
+    }
+}
+
 // 32 x 32 quadrant of X Y^T over d: X rows x0.., Y rows y0.. (both [64][P] bf16 tiles)
 template <int D>
 __device__ __forceinline__ f32x16 quad_xyT(const uint16_t* X, int x0, const uint16_t* Y, int y0, int lane)
@@ -225,6 +306,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
     const int tq = rg / rs.kk;
     const float qs2 = a.qscale2;
 
+    KeyRegs<D> rk, rv;
+    keys_load<D>(Kh, 0, T, rk);
     load_rows<D>(rs, r0, sQ, sdO, s_dp);
     __syncthreads();
     if (tid < kAbTile) {
@@ -232,13 +315,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         for (int c = 0; c < CPR; ++c) dsum += s_dp[tid * CPR + c];
         s_delta[tid] = dsum;
     }
+    keys_store<D>(rk, sK);
+    __syncthreads();
 
-    // pass 1: the rows' base-2 log-sum-exp
+    // pass 1: the rows' base-2 log-sum-exp.  Its last step fetches pass 2's first K and V tiles.
     float m = -1e30f, l = 0.f;
     for (int kt = 0; kt < nkt; ++kt) {
         const int s0 = kt * kAbTile;
-        load_keys<D>(Kh, s0, T, sK);
-        __syncthreads();
+        const bool more = kt + 1 < nkt;
+        keys_load<D>(Kh, more ? s0 + kAbTile : 0, T, rk);
+        if (!more) keys_load<D>(Vh, 0, T, rv);
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         float sv[16], mt = -INFINITY;
 #pragma unroll
@@ -254,6 +340,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         for (int i = 0; i < 16; ++i) ls += __builtin_amdgcn_exp2f(sv[i] - mn);
         l = l * __builtin_amdgcn_exp2f(m - mn) + ls;
         m = mn;
+        __syncthreads();
+        keys_store<D>(rk, sK);
+        if (!more) keys_store<D>(rv, sV);
         __syncthreads();
     }
     {
@@ -287,9 +376,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
     for (int kt = 0; kt < nkt; ++kt) {
         const int s0 = kt * kAbTile;
-        load_keys<D>(Kh, s0, T, sK);
-        load_keys<D>(Vh, s0, T, sV);
-        __syncthreads();
+        const bool more = kt + 1 < nkt;
+        if (more) {
+            keys_load<D>(Kh, s0 + kAbTile, T, rk);
+            keys_load<D>(Vh, s0 + kAbTile, T, rv);
+        }
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
         // dS[row][key] as bf16, four consecutive keys per 8-byte store
@@ -314,6 +405,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
             if (blk < 2 * (D / 32)) acc[j] = gemm_az<D>(acc[j], sS, (blk & 1) * 32, sK, (blk >> 1) * 32, lane);
         }
         __syncthreads();
+        if (more) {
+            keys_store<D>(rk, sK);
+            keys_store<D>(rv, sV);
+            __syncthreads();
+        }
     }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
@@ -362,43 +458,54 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dk[j][r] = dv[j][r] = 0.f;
 
-    const int nsets = (g == 0 && a.n_shared) ? 2 : 1;
-    for (int set = 0; set < nsets; ++set) {
-        const RowSet rs = row_set(a, b, set == 0 ? g : G);
-        const int ntr = (rs.R + kAbTile - 1) / kAbTile;
-        const int rt0 = a.causal ? (int)(((long long)s0 * rs.kk) / kAbTile) : 0;
-        for (int rt = rt0; rt < ntr; ++rt) {
-            const int r0 = rt * kAbTile;
-            __syncthreads();   // (the previous tile's reads of sQ, sdO, sP, sD are done)
-            load_rows<D>(rs, r0, sQ, sdO, nullptr);
-            if (tid < kAbTile) {
-                const int r = r0 + tid;
-                s_lse[tid] = r < rs.R ? rs.lse[r] : INFINITY;
-                s_delta[tid] = r < rs.R ? rs.delta[r] : 0.f;
-            }
-            __syncthreads();
-            const int tq = (r0 + row) / rs.kk;
-            const float lse_r = s_lse[row], dl_r = s_delta[row];
-            const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
-            const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
+    // the row tiles that see this key tile: the group's routed rows, then (KV head 0) the shared rows
+    const RowSet rs0 = row_set(a, b, g);
+    const bool two = g == 0 && a.n_shared;
+    const RowSet rs1 = two ? row_set(a, b, G) : rs0;
+    const int n0 = (rs0.R + kAbTile - 1) / kAbTile, n1 = (rs1.R + kAbTile - 1) / kAbTile;
+    const int a0 = a.causal ? (int)(((long long)s0 * rs0.kk) / kAbTile) : 0;
+    const int a1 = a.causal ? (int)(((long long)s0 * rs1.kk) / kAbTile) : 0;
+    const int c0 = n0 - a0, nit = c0 + (two ? n1 - a1 : 0);
+    RowRegs<D> rr;
+    if (nit > 0) rows_load<D>(rs0, a0 * kAbTile, rr);
+    __syncthreads();
+    if (nit > 0) rows_store<D>(rr, sQ, sdO, s_lse, s_delta);
+    __syncthreads();
+    for (int it = 0; it < nit; ++it) {
+        const bool in0 = it < c0;
+        const RowSet& rs = in0 ? rs0 : rs1;
+        const int r0 = (in0 ? a0 + it : a1 + it - c0) * kAbTile;
+        const bool more = it + 1 < nit;
+        if (more) {
+            const bool nx0 = it + 1 < c0;
+            rows_load<D>(nx0 ? rs0 : rs1, (nx0 ? a0 + it + 1 : a1 + it + 1 - c0) * kAbTile, rr);
+        }
+        const int tq = (r0 + row) / rs.kk;
+        const float lse_r = s_lse[row], dl_r = s_delta[row];
+        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kl = wk * 32 + acc_row(i, lane);
-                const int key = s0 + kl;
-                const bool ok = key < T && (!a.causal || key <= tq);
-                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
-                sP[kl * PS + row] = bf16_bits(pv);
-                sD[kl * PS + row] = bf16_bits(pv * (dp[i] - dl_r));
-            }
-            __syncthreads();
+        for (int i = 0; i < 16; ++i) {
+            const int kl = wk * 32 + acc_row(i, lane);
+            const int key = s0 + kl;
+            const bool ok = key < T && (!a.causal || key <= tq);
+            const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
+            sP[kl * PS + row] = bf16_bits(pv);
+            sD[kl * PS + row] = bf16_bits(pv * (dp[i] - dl_r));
+        }
+        __syncthreads();
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                const int blk = wave + 4 * j;
-                if (blk < 2 * (D / 32)) {
-                    dv[j] = gemm_az<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
-                    dk[j] = gemm_az<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
-                }
+        for (int j = 0; j < NBW; ++j) {
+            const int blk = wave + 4 * j;
+            if (blk < 2 * (D / 32)) {
+                dv[j] = gemm_az<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
+                dk[j] = gemm_az<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
             }
+        }
+        __syncthreads();
+        if (more) {
+            rows_store<D>(rr, sQ, sdO, s_lse, s_delta);
+            __syncthreads();
         }
     }
     float* dkh = a.dk + ((size_t)b * G + g) * T * D;
