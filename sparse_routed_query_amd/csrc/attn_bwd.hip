@@ -16,7 +16,7 @@
 // lane's accumulator column is one query row and the row statistics are one
 // value per lane; wave w computes the 32 x 32 quadrant (keys 32 (w & 1),
 // rows 32 (w >> 1)).  Operands are read from LDS: a fragment along a tile's
-// contiguous axis is one 16-byte read, one across it is 8 strided reads.
+// contiguous axis is one 16-byte read, one across it two transposing reads.
 //   attn_bwd_dq_kernel<D>    one 64-row tile of one head (routed or shared)
 //   attn_bwd_dkdv_kernel<D>  one 64-key tile of one KV head, over every row
 //                            tile that sees it: the group's routed rows and,
@@ -34,14 +34,34 @@ constexpr int kAbTile = 64;
 // k = 8 (l/32) .. +7; accumulator element i: column l%32, row
 // 8 (i/4) + 4 (l/32) + i%4.
 __device__ __forceinline__ bf16x8 frag_row(const uint16_t* p) { return ld_bf16x8(p); }
-__device__ __forceinline__ bf16x8 frag_col(const uint16_t* p, int pitch)
-{
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(bf16, p[i * pitch]);
-    return v;
-}
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// B fragment read across a row-major LDS tile M[k][n] (pitch in elements) with
+// two transposing reads.  Within each 16-lane group, lane i of
+// ds_read_b64_tr_b16 receives, as its element j, element i % 4 of the 8 bytes
+// that lane 4 j + i / 4 addresses; pointing lane 4 j + q at
+// M[k0 + 4 (l/32) + j][n + 4 q .. +3] gives lane l column n0 + l%32 and rows
+// k0 + 4 (l/32) + 0..3, then (second read) 8 rows further.  In the MFMA's k
+// order, rows 4-7 and 8-11 of each 16-row block are therefore swapped; the A
+// operand is stored with the same swap (kpos), so the products are unchanged.
+typedef short ab_s16x4 __attribute__((ext_vector_type(4)));
+typedef short ab_s16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* M, int pitch, int k0, int n0, int lane)
+{
+    typedef __attribute__((address_space(3))) ab_s16x4 lds_s16x4;
+    const int s16 = lane & 15;
+    const uint16_t* p = M + (k0 + 4 * (lane >> 5) + (s16 >> 2)) * pitch + n0 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
+    const ab_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const ab_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * pitch));
+    const ab_s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+// storage position of contraction index k (0..63) in an A-operand tile read by frag_row
+__device__ __forceinline__ int kpos(int k)
+{
+    const int b = k & 12;
+    return b == 4 ? k + 4 : b == 8 ? k - 4 : k;
+}
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, f2bf(f)); }
 
@@ -237,16 +257,15 @@ __device__ __forceinline__ f32x16 quad_xyT(const uint16_t* X, int x0, const uint
     return c;
 }
 
-// C[m][n] += sum over 64 k of A[m][k] Z[k][n]: A a [64][64+8] tile (row m0 + l%32),
-// Z a [64][D+8] tile read across (columns n0 + l%32)
+// C[m][n] += sum over 64 k of A[m][k] Z[k][n]: A a [64][64+8] tile (row m0 + l%32)
+// holding k at position kpos(k), Z a row-major [64][D+8] tile read across (columns n0 + l%32)
 template <int D>
 __device__ __forceinline__ f32x16 gemm_az(f32x16 c, const uint16_t* A, int m0, const uint16_t* Z, int n0, int lane)
 {
     constexpr int P = D + 8, PS = kAbTile + 8;
     const uint16_t* aa = A + (m0 + (lane & 31)) * PS + 8 * (lane >> 5);
-    const uint16_t* zb = Z + (8 * (lane >> 5)) * P + n0 + (lane & 31);
 #pragma unroll
-    for (int s = 0; s < kAbTile / 16; ++s) c = mfma32(frag_row(aa + 16 * s), frag_col(zb + 16 * s * P, P), c);
+    for (int s = 0; s < kAbTile / 16; ++s) c = mfma32(frag_row(aa + 16 * s), frag_tr(Z, P, 16 * s, n0, lane), c);
     return c;
 }
 
@@ -395,8 +414,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
                 const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * qs2 - lse_r) : 0.f;
                 v[e] = pv * (dp[i] - dl_r);
             }
-            const int k0 = wk * 32 + acc_row(4 * i4, lane);
-            *(uint2*)(sS + row * PS + k0) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+            const int k0 = wk * 32 + acc_row(4 * i4, lane);   // (kpos moves whole 4-key blocks)
+            *(uint2*)(sS + row * PS + kpos(k0)) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
         }
         __syncthreads();
 #pragma unroll
@@ -490,8 +509,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
             const int key = s0 + kl;
             const bool ok = key < T && (!a.causal || key <= tq);
             const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
-            sP[kl * PS + row] = bf16_bits(pv);
-            sD[kl * PS + row] = bf16_bits(pv * (dp[i] - dl_r));
+            sP[kl * PS + kpos(row)] = bf16_bits(pv);
+            sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
         }
         __syncthreads();
 #pragma unroll
