@@ -124,6 +124,14 @@ def route(d: _Desc, x, w_router, b_router=None):
     return dict(logits=logits, probs=probs, sel=sel, ptilde=pt, tie=tie.astype(bool))
 
 
+def expert_importance(d: _Desc, probs):
+    """Per-expert router importance, the probability mass each expert receives summed over tokens:
+    importance[n] = sum_t p[t, n] with p the in-group softmax (study note §3-2 (2)).  With the per-expert
+    counts of kept tokens (compact's counts) these are the load statistics a balance loss is formed from
+    (§4 names the loss but not its exact form).  probs [BT, N] as route() returns them."""
+    return np.asarray(probs, dtype=np.float64).reshape(-1, d.H_q).sum(axis=0)
+
+
 def compact(d: _Desc, sel):
     """Counting sort of kept (token, expert) pairs: counts [N], offsets [N+1], rows [BT*G*k]."""
     lib = _load()

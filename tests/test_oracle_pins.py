@@ -628,3 +628,24 @@ def test_attention_backward_all_experts_equals_dense_gqa(causal):
     np.testing.assert_allclose(g["dq_shared"], qs.grad.numpy()[0], rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dk"], Kt.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dv"], Vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- expert load statistics
+
+
+@pytest.mark.parametrize("zipf", [0.0, 1.2])
+def test_expert_importance(zipf):
+    w = wl(H_q=12, H_kv=3, k=2, zipf_s=zipf)
+    inp = W.make_inputs(w)
+    d = oracle.desc(w)
+    r = oracle.route(d, inp["x"], inp["w_router"], inp["b_router"])
+    imp = oracle.expert_importance(d, r["probs"])
+    BT, G, E = w.B * w.T, w.H_kv, w.H_q // w.H_kv
+    # every token spreads probability 1 over each group's experts
+    np.testing.assert_allclose(imp.reshape(G, E).sum(-1), BT, rtol=1e-12)
+    # torch: softmax of the oracle's scores within each group, summed over tokens
+    lg = torch.tensor(r["logits"]).reshape(BT, G, E)
+    np.testing.assert_allclose(imp, torch.softmax(lg, -1).reshape(BT, -1).sum(0).numpy(), rtol=1e-12)
+    # a zero router spreads it evenly
+    r0 = oracle.route(d, inp["x"], np.zeros_like(inp["w_router"].double().numpy()))
+    np.testing.assert_allclose(oracle.expert_importance(d, r0["probs"]), BT / E, rtol=1e-12)
