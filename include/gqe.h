@@ -226,6 +226,17 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
  */
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream);
 
+/*
+ * gqe_route_stats -- per-expert router importance, the load statistic a
+ * balance loss is formed from together with the per-expert counts gqe_route
+ * returns (GQE study note §4 names the loss without its exact form):
+ *   importance[g*E + e] = sum over tokens t of softmax_e(logits[t, g, :])
+ * (study note §3-2 (2)), accumulated in fp64 in a fixed order, stored fp32.
+ * In:  logits [B*T, N] fp64 as gqe_route writes them (may be NULL when
+ *      B*T = 0).  Out: importance [N] fp32 (all 0 when B*T = 0).
+ */
+int gqe_route_stats(const gqe_desc* desc, const double* logits, float* importance, void* stream);
+
 /* Bytes of device workspace gqe_attn_backward needs (two floats per query row). */
 size_t gqe_attn_backward_workspace_bytes(const gqe_desc* desc);
 

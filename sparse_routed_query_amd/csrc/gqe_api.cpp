@@ -254,6 +254,15 @@ int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out
     return launch_status(gqe::launch_route_bwd(a, (hipStream_t)stream));
 }
 
+int gqe_route_stats(const gqe_desc* desc, const double* logits, float* importance, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    GQE_TRY(need(importance));
+    if (s.BT > 0) GQE_TRY(need(logits));   // (with no tokens every importance is 0)
+    return launch_status(gqe::launch_route_stats(logits, s.BT, s.G, s.E, importance, (hipStream_t)stream));
+}
+
 size_t gqe_attn_backward_workspace_bytes(const gqe_desc* desc)
 {
     Shape s;

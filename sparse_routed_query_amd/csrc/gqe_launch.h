@@ -58,6 +58,7 @@ struct RouteBwdArgs {
 };
 size_t route_bwd_workspace_bytes(long long BT, int N, int C);
 int launch_route_bwd(const RouteBwdArgs& a, hipStream_t st);
+int launch_route_stats(const double* logits, long long BT, int G, int E, float* importance, hipStream_t st);
 
 struct AttnBwdArgs {
     const void* q_routed;   // [B, G, T*k, d_head] bf16, row t*k + j

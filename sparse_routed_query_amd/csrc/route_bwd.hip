@@ -318,6 +318,39 @@ __global__ __launch_bounds__(256) void route_bwd_dx_kernel(const float* __restri
     }
 }
 
+// Router importance of expert n = g*E + e: sum over tokens of its in-group
+// softmax probability, from the router's fp64 scores.  One workgroup per
+// expert; thread i takes tokens i, i + 256, ..., in fp64, then the 256 partial
+// sums are added in a fixed tree order.
+__global__ __launch_bounds__(256) void route_stats_kernel(const double* __restrict__ logits, long long BT, int G,
+                                                          int E, float* __restrict__ importance)
+{
+    __shared__ double s_red[256];
+    const int n = blockIdx.x, g = n / E, e = n - g * E, N = G * E;
+    double acc = 0.0;
+    for (long long t = threadIdx.x; t < BT; t += 256) {
+        const double* lg = logits + (size_t)t * N + (size_t)g * E;
+        double m = lg[0];
+        for (int i = 1; i < E; ++i) m = fmax(m, lg[i]);
+        double den = 0.0;
+        for (int i = 0; i < E; ++i) den += exp(lg[i] - m);
+        acc += exp(lg[e] - m) / den;
+    }
+    s_red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) s_red[threadIdx.x] += s_red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) importance[n] = (float)s_red[0];
+}
+
+int launch_route_stats(const double* logits, long long BT, int G, int E, float* importance, hipStream_t st)
+{
+    route_stats_kernel<<<(unsigned)(G * E), 256, 0, st>>>(logits, BT, G, E, importance);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 size_t route_bwd_workspace_bytes(long long BT, int N, int C)
 {
     const long long nblk = (BT + kRbTokBlock - 1) / kRbTokBlock;

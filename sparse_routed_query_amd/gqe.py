@@ -29,7 +29,7 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
-           "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward")
+           "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats")
 
 
 class GqeError(RuntimeError):
@@ -112,6 +112,8 @@ def load():
         lib.gqe_route_backward_workspace_bytes.restype = Z
         lib.gqe_route_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.gqe_route_backward.restype = I
+        lib.gqe_route_stats.argtypes = [D, P, P, P]
+        lib.gqe_route_stats.restype = I
         lib.gqe_attn_backward_workspace_bytes.argtypes = [D]
         lib.gqe_attn_backward_workspace_bytes.restype = Z
         lib.gqe_attn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
@@ -277,6 +279,19 @@ def route_backward(desc, dout, out, sel, p_tilde, x, w_router, want_dw=True, wan
     gqe_route_backward(desc, dout, out, sel, p_tilde, x, w_router, res["d_hard"], res["d_logits"], res["dw_router"],
                        res["db_router"], res["dx"], ws, stream)
     return res
+
+
+def gqe_route_stats(desc, logits, importance, stream=None):
+    rc = load().gqe_route_stats(ctypes.byref(desc), _ptr(logits, torch.float64, "logits"),
+                                _ptr(importance, torch.float32, "importance"), _stream(stream))
+    _check("gqe_route_stats", rc)
+
+
+def route_stats(desc, logits, stream=None) -> torch.Tensor:
+    """Per-expert router importance [N] (fp32) from gqe_route's fp64 scores."""
+    imp = torch.empty(desc.H_q, dtype=torch.float32, device=logits.device)
+    gqe_route_stats(desc, logits, imp, stream)
+    return imp
 
 
 def gqe_attn_backward_workspace_bytes(desc: GqeDesc) -> int:

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -133,6 +133,11 @@ def test_qproj_prefill_decode_reject_bad_arguments():
     assert rb(d, w=None) == WORKSPACE
     assert rb(d, dx=MIS) == ALIGN
     assert rb(main(B=0), dout=None, dw=None, db=None, dx=None, w=None) == OK
+    rs = lambda desc, lg=A16, imp=A16: lib.gqe_route_stats(by(desc), lg, imp, None)  # noqa: E731
+    assert rs(d, lg=None) == INVALID
+    assert rs(d, imp=None) == INVALID
+    assert rs(d, imp=MIS) == ALIGN
+    assert rs(main(H_q=15)) == INVALID
     aws = G.load().gqe_attn_backward_workspace_bytes(by(d))
     assert aws == (4 * 8 * 4096 + 4 * 4096) * 8 + 256          # two floats per routed and shared row
     assert G.load().gqe_attn_backward_workspace_bytes(by(main(n_shared=0))) == 4 * 8 * 4096 * 8 + 256

@@ -121,3 +121,27 @@ def test_route_backward_is_deterministic():
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("w", [
+    small(), small(H_q=16, H_kv=4, k=3, zipf_s=1.2, name="E4k3_bias"), small(H_q=64, H_kv=2, k=4, name="N64"),
+    small(B=1, T=1, name="T1"), W.WORKLOADS["main_250m"],
+], ids=lambda w: w.name)
+def test_route_stats_importance(w):
+    # per-expert importance (sum over tokens of the in-group softmax) from the GPU router's fp64 scores, against
+    # the oracle end to end.  The router's scores are within 5e-7 of the oracle's, which moves each token's
+    # probability by at most ~2.5e-7: the sums stay within 1e-6 BT, plus fp32 rounding of the result.
+    import oracle
+    inp = W.make_inputs(w)
+    gpu = gpu_prefill(w, inp)
+    d = G.desc_from(w)
+    BT, Gn, E = w.B * w.T, w.H_kv, w.H_q // w.H_kv
+    imp = G.route_stats(d, gpu["logits"].cuda()).cpu().double().numpy()
+    od = oracle.desc(w)
+    ref = oracle.expert_importance(od, oracle.route(od, inp["x"], inp["w_router"], inp["b_router"])["probs"])
+    err = np.abs(imp - ref).max()
+    say(f"[{w.name}] importance max err {err:.3e} (BT = {BT})")
+    assert err <= 1e-6 * BT + 2.0 ** -24 * np.abs(ref).max()
+    np.testing.assert_allclose(imp.reshape(Gn, E).sum(-1), BT, rtol=E * 2.0 ** -23)
+    again = G.route_stats(d, gpu["logits"].cuda()).cpu().double().numpy()
+    assert np.array_equal(imp, again)
