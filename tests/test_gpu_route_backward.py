@@ -100,6 +100,7 @@ def run_case(w):
     small(dtype="f32", T=50, d_model=100, H_q=48, H_kv=4, k=2, name="f32_N48"), small(d_head=32, H_q=32, H_kv=2, k=4, T=513, name="N32_d32"),
     W.WORKLOADS["main_250m"],
     W.WORKLOADS["main_250m"].replace(k=2, name="main_250m_k2"),   # full size with a router gradient
+    W.WORKLOADS["wide_zipf"],   # full size: 32 experts (two MFMA row tiles), d_model 4096, k = 2, d_head 128
 ], ids=lambda w: f"{w.name}-{w.dtype}")
 def test_route_backward(w):
     res, ref = run_case(w)
@@ -125,7 +126,7 @@ def test_route_backward_is_deterministic():
 
 @pytest.mark.parametrize("w", [
     small(), small(H_q=16, H_kv=4, k=3, zipf_s=1.2, name="E4k3_bias"), small(H_q=64, H_kv=2, k=4, name="N64"),
-    small(B=1, T=1, name="T1"), W.WORKLOADS["main_250m"],
+    small(B=1, T=1, name="T1"), W.WORKLOADS["main_250m"], W.WORKLOADS["wide_zipf"],
 ], ids=lambda w: w.name)
 def test_route_stats_importance(w):
     # per-expert importance (sum over tokens of the in-group softmax) from the GPU router's fp64 scores, against
