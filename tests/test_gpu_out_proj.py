@@ -81,3 +81,35 @@ def test_out_proj_after_decode_and_without_write_back():
     assert torch.isnan(after2[:, kG]).all()
     assert torch.equal(after2[:, :kG], slots[:, :kG]) and torch.equal(after2[:, kG + 1:], slots[:, kG + 1:])
     say(f"[{w.name}] out_proj after decode ok")
+
+
+@pytest.mark.parametrize("w", [small(route_mode=1, name="combination_only"),
+                               small(route_mode=1, n_shared=0, H_q=16, H_kv=4, k=2, name="combination_only_noshared")],
+                         ids=lambda w: w.name)
+def test_weighted_combination_only_output(w):
+    # The ai-feeds summary's output: per group the router-weighted combination of its kept experts' outputs
+    # (route mode 1's weighted slots), with no hard slots.  gqe_out_proj gives it when W_o's hard-slot
+    # columns are zero.  Reference: that definition written out in fp64 from the GPU's hard and shared slots.
+    inp = W.make_inputs(w)
+    gpu = gpu_prefill(w, inp)
+    wo = W.make_w_o(w).clone()
+    kG, D, Gn, k = w.k * w.G, w.d_head, w.G, w.k
+    wo[:, :kG * D] = 0
+    y, _ = gpu_out_proj(w, gpu["out"], gpu["p_tilde"], wo)
+    BT = w.B * w.T
+    S = kG + Gn + w.n_shared
+    h = gpu["out"].reshape(BT, S, D).double().numpy()
+    pt = gpu["p_tilde"].reshape(BT, Gn, k).double().numpy()
+    comb = (pt[..., None] * h[:, :kG].reshape(BT, Gn, k, D)).sum(2)            # [BT, G, d]
+    wod = wo.double().numpy()
+    ref = comb.reshape(BT, Gn * D) @ wod[:, kG * D:(kG + Gn) * D].T
+    mag = (np.abs(pt[..., None]) * np.abs(h[:, :kG].reshape(BT, Gn, k, D))).sum(2).reshape(BT, -1) \
+        @ np.abs(wod[:, kG * D:(kG + Gn) * D]).T
+    if w.n_shared:
+        ref = ref + h[:, S - 1] @ wod[:, (S - 1) * D:].T
+        mag = mag + np.abs(h[:, S - 1]) @ np.abs(wod[:, (S - 1) * D:]).T
+    eps = 2.0 ** -8 + (S * D + kG + 1) * 2.0 ** -24
+    err = np.abs(y.double().numpy() - ref)
+    r = float((err / (eps * mag + 1e-30)).max())
+    say(f"[{w.name}] combination-only projection: max err/bound {r:.3f}")
+    assert np.isfinite(y.numpy()).all() and r <= 1.0
