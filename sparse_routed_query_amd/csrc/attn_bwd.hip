@@ -346,12 +346,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         if (!more) keys_load<D>(Vh, 0, T, rv);
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         float sv[16], mt = -INFINITY;
+        if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = s0 + wk * 32 + acc_row(i, lane);
-            const bool ok = key < T && (!a.causal || key <= tq);
-            sv[i] = ok ? c[i] * qs2 : -INFINITY;
-            mt = fmaxf(mt, sv[i]);
+            for (int i = 0; i < 16; ++i) {
+                const int key = s0 + wk * 32 + acc_row(i, lane);
+                const bool ok = key < T && (!a.causal || key <= tq);
+                sv[i] = ok ? c[i] * qs2 : -INFINITY;
+                mt = fmaxf(mt, sv[i]);
+            }
+        } else {   // every key of the tile is inside T and before the tile's first row's position
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sv[i] = c[i] * qs2;
+                mt = fmaxf(mt, sv[i]);
+            }
         }
         const float mn = fmaxf(m, mt);
         float ls = 0.f;
@@ -403,6 +411,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
         // dS[row][key] as bf16, four consecutive keys per 8-byte store
+        const bool need_mask = s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk);
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             float v[4];
@@ -410,7 +419,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * i4 + e;
                 const int key = s0 + wk * 32 + acc_row(i, lane);
-                const bool ok = key < T && (!a.causal || key <= tq);
+                const bool ok = !need_mask || (key < T && (!a.causal || key <= tq));
                 const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * qs2 - lse_r) : 0.f;
                 v[e] = pv * (dp[i] - dl_r);
             }
@@ -503,14 +512,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
         const float lse_r = s_lse[row], dl_r = s_delta[row];
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
+        // a tile whose keys all lie inside T and before its first row's position needs no mask
+        if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kl = wk * 32 + acc_row(i, lane);
-            const int key = s0 + kl;
-            const bool ok = key < T && (!a.causal || key <= tq);
-            const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
-            sP[kl * PS + kpos(row)] = bf16_bits(pv);
-            sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
+            for (int i = 0; i < 16; ++i) {
+                const int kl = wk * 32 + acc_row(i, lane);
+                const int key = s0 + kl;
+                const bool ok = key < T && (!a.causal || key <= tq);
+                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
+                sP[kl * PS + kpos(row)] = bf16_bits(pv);
+                sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kl = wk * 32 + acc_row(i, lane);
+                const float pv = __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r);
+                sP[kl * PS + kpos(row)] = bf16_bits(pv);
+                sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
+            }
         }
         __syncthreads();
 #pragma unroll
