@@ -17,7 +17,10 @@ divided by the whole step's time).  The same JSON line carries:
                 lengths in [4096, 8192]): gqe_attn_decode timed alone, bytes of
                 K/V it must read over its time, against the HBM peak;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload;
-  long_context  T=32768 GQE vs all-active GQA on the same inputs;
+  long_context  T=32768 GQE vs all-active GQA on the same inputs, every call
+                timed, attention and projection as fractions of the bf16 peak;
+  wide_zipf     the wider expert pool with skewed routing (B=2, T=16384,
+                d_model=4096, H_q=32, H_kv=8, k=2, d_head=128), the same;
   out_proj      the next step after the path, outside the timed step: the
                 output projection over the kG+2 slots fused with slot assembly
                 (gqe_out_proj) on the step's own slots, against the bf16 peak;
@@ -32,7 +35,8 @@ divided by the whole step's time).  The same JSON line carries:
 (on this stack replaying is not faster than launching them one by one).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu] [--no-context] [--no-decode]
-       python bench.py --only {step,prefill,outproj,decode,copy} --steps K   (profiler runs)
+       python bench.py --only {step,prefill,prefill_wide,prefill_long,qproj,qproj_wide,outproj,decode,copy}
+                       --steps K   (profiler runs)
 """
 from __future__ import annotations
 
@@ -63,7 +67,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="also time the step replayed from one HIP graph")
-    ap.add_argument("--only", choices=["step", "prefill", "outproj", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["step", "prefill", "outproj", "decode", "copy", "qproj", "prefill_wide",
+                                       "qproj_wide", "prefill_long"], default=None,
                     help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
 
@@ -115,7 +120,8 @@ class Prefill:
 
 def warm(fns, torch, ms=30.0, min_calls=3):
     """Run the calls until at least `ms` of wall time has passed: the first
-    tens of milliseconds of load run at a lower clock than the steady state."""
+    tens of milliseconds of load run at a lower clock than the steady state.
+    Returns (rounds of the calls, milliseconds)."""
     t0 = time.perf_counter()
     i = 0
     while i < min_calls or (time.perf_counter() - t0) * 1e3 < ms:
@@ -125,6 +131,38 @@ def warm(fns, torch, ms=30.0, min_calls=3):
         if i % 8 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return i, (time.perf_counter() - t0) * 1e3
+
+
+def sclk_under_load(fn, torch, n=64):
+    """The GPU's current shader clock (MHz) read from sysfs while `n` calls of `fn` are in flight, or
+    None where the driver does not expose it."""
+    import glob
+    for _ in range(n):
+        fn()
+    mhz = None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for ln in open(path):
+                if ln.strip().endswith("*"):
+                    mhz = float(ln.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+        if mhz is not None:
+            break
+    torch.cuda.synchronize()
+    return mhz
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def time_calls(fn_list, n, torch):
@@ -164,7 +202,9 @@ def traffic_for(kernel_key: str):
 
 
 def cpu_baseline(w, inp, target_s: float):
-    """The oracle as it stands on a stratified sample of the workload's tokens."""
+    """The oracle as it stands on a stratified sample of the workload's tokens: the attention and slots of
+    those tokens (oracle.attend_rows) timed alone, over the same attention FLOPs as the GPU's figure; the
+    routing and query projection of the sample run first, untimed, and their time is reported beside it."""
     import numpy as np
     import oracle
     import workloads as W
@@ -177,22 +217,26 @@ def cpu_baseline(w, inp, target_s: float):
         sel_full = np.zeros((w.B * w.T, w.G, w.k), dtype=np.int32)
         pt_full = np.zeros((w.B * w.T, w.G, w.k))
         sel_full[tok], pt_full[tok] = r["sel"], r["ptilde"]
-        oracle.prefill_rows(d, inp["x"], inp["w_q"], inp["k"], inp["v"], sel_full, pt_full, tok)
-        return time.perf_counter() - t0
+        qr, qs = oracle.qproj_rows(d, inp["x"], inp["w_q"], sel_full, tok)
+        t1 = time.perf_counter()
+        oracle.attend_rows(d, qr, qs, inp["k"], inp["v"], pt_full[tok], tok)
+        return time.perf_counter() - t1, t1 - t0
 
     def flops(tok):
         t = tok % w.T
         return float(np.sum(4.0 * w.d_head * w.h_active * (t + 1)))
 
     probe = W.stratified_rows(w, 128, seed=7).numpy()
-    tp = run(probe)
+    tp, _ = run(probe)
     n = int(min(w.B * w.T, max(128, 128 * target_s / max(tp, 1e-3))))
     tok = W.stratified_rows(w, n, seed=8).numpy()
-    dt = run(tok)
+    dt, dt_pre = run(tok)
     return {"value": flops(tok) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{len(tok)} of {w.B * w.T} tokens of {w.name}, stratified over position; routing of those "
-                      f"tokens plus their projections, causal attention and slots; {dt:.1f} s wall",
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "sample": f"{len(tok)} of {w.B * w.T} tokens of {w.name}, stratified over position: the causal attention "
+                      f"and slots of those tokens (oracle.attend_rows), {dt:.1f} s wall; their routing and query "
+                      f"projection ran before, untimed ({dt_pre:.2f} s)",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "routing_and_projection_s": dt_pre, "attention_s": dt}
 
 
 def decode_leg(torch, dev, steps):
@@ -354,23 +398,50 @@ def attn_backward_leg(p, torch, steps):
             "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
 
 
+def prefill_leg(w, inp, torch, dev, steps):
+    """Every call of the step on one workload, each timed alone with events (after warming the clock),
+    and the step as a whole: attention TFLOP/s and projection TFLOP/s against the bf16 peak."""
+    import workloads as W
+    p = Prefill(w, inp, dev)
+    warm([p.step], torch)
+    t_route, t_qp, t_attn, t_asm = time_calls([p.route, p.qproj, p.attn, p.assemble], steps, torch)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        p.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_step = ev0.elapsed_time(ev1) / steps
+    fl, fq = W.attention_flops(w), W.qproj_flops(w)
+    at, qt = fl / (t_attn * 1e-3) / 1e12, fq / (t_qp * 1e-3) / 1e12
+    counts = p.r["counts"].cpu().tolist()
+    del p
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "B": w.B, "T": w.T, "d_model": w.d_model, "H_q": w.H_q, "H_kv": w.H_kv, "k": w.k,
+            "d_head": w.d_head, "active_heads": w.h_active,
+            "route_us": t_route * 1e3, "qproj_us": t_qp * 1e3, "attn_us": t_attn * 1e3, "assemble_us": t_asm * 1e3,
+            "step_us": t_step * 1e3, "attn_flops": fl, "attn_tflops": at, "attn_frac": at / MFMA_BF16_PEAK_TFLOPS,
+            "qproj_flops": fq, "qproj_tflops": qt, "qproj_frac": qt / MFMA_BF16_PEAK_TFLOPS,
+            "step_attn_tflops": fl / (t_step * 1e-3) / 1e12,
+            "attn_kernel": f"prefill_bf16_kernel<{w.d_head}>", "qproj_kernel": f"qproj_bf16_kernel<{w.d_head}, 64>",
+            "expert_rows": counts}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
     inp = W.make_inputs(w)
-    res = {}
-    for name, ww in (("gqe", w), ("dense", W.dense_variant(w))):
-        p = Prefill(ww, inp, dev)
-        warm([p.step], torch)
-        t_route, t_qp, t_attn, t_asm = time_calls([p.route, p.qproj, p.attn, p.assemble], steps, torch)
-        fl = W.attention_flops(ww)
-        res[name] = {"attn_ms": t_attn, "step_ms": t_route + t_qp + t_attn + t_asm,
-                     "attn_tflops": fl / (t_attn * 1e-3) / 1e12, "active_heads": ww.h_active}
-        del p
-    res["speedup_attn"] = res["dense"]["attn_ms"] / res["gqe"]["attn_ms"]
-    res["speedup_step"] = res["dense"]["step_ms"] / res["gqe"]["step_ms"]
+    res = {"gqe": prefill_leg(w, inp, torch, dev, steps), "dense": prefill_leg(W.dense_variant(w), inp, torch, dev, steps)}
+    res["speedup_attn"] = res["dense"]["attn_us"] / res["gqe"]["attn_us"]
+    res["speedup_step"] = res["dense"]["step_us"] / res["gqe"]["step_us"]
     res["ideal_flop_ratio"] = 16 / 9
     return res
+
+
+def wide_leg(torch, dev, steps):
+    import workloads as W
+    w = W.WORKLOADS["wide_zipf"]
+    return prefill_leg(w, W.make_inputs(w), torch, dev, steps)
 
 
 def only(args, torch):
@@ -391,14 +462,20 @@ def only(args, torch):
         p = Prefill(w, W.make_inputs(w), dev)
         for _ in range(args.steps):
             p.step()
-    elif args.only == "prefill":
-        w = W.WORKLOADS["main_250m"]
+    elif args.only in ("prefill", "prefill_wide", "prefill_long"):
+        w = W.WORKLOADS[{"prefill": "main_250m", "prefill_wide": "wide_zipf", "prefill_long": "long_32k"}[args.only]]
         p = Prefill(w, W.make_inputs(w), dev)
         p.route()
         p.qproj()
         for _ in range(args.steps):
             p.attn()
             p.assemble()
+    elif args.only in ("qproj", "qproj_wide"):
+        w = W.WORKLOADS["main_250m" if args.only == "qproj" else "wide_zipf"]
+        p = Prefill(w, W.make_inputs(w), dev)
+        p.route()
+        for _ in range(args.steps):
+            p.qproj()
     elif args.only == "outproj":
         w = W.WORKLOADS["main_250m"]
         p = Prefill(w, W.make_inputs(w), dev)
@@ -441,6 +518,9 @@ def main():
     for _ in range(args.warmup):
         p.step()
     torch.cuda.synchronize()
+    # then at least 30 ms more of the same step, so the timed steps run at the steady clock (the first
+    # tens of milliseconds of load run slower whatever the step count)
+    clock_warm_steps, clock_warm_ms = warm([p.step], torch)
 
     def timed(fn, n):
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -486,12 +566,15 @@ def main():
         "step_split_us": {"route": t_route * 1e3, "qproj": t_qp * 1e3, "attn_prefill_heads": t_attn * 1e3,
                           "assemble": t_asm * 1e3},
         "wall_s_timed": wall,
+        "clock_warm": {"steps": clock_warm_steps, "ms": clock_warm_ms,
+                       "note": "untimed steps run after the --warmup steps and before the timed ones"},
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic_for("prefill"),
                      "kernel": f"prefill_bf16_kernel<{w.d_head}> (the one kernel of gqe_attn_prefill_heads)",
                      "algorithmic_flops_per_launch": fl},
     }
+    line["sclk_mhz_under_load"] = sclk_under_load(p.step, torch)
     line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
     line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
     line["route_backward"] = route_backward_leg(p, torch, max(10, args.steps))
@@ -502,7 +585,9 @@ def main():
         line["decode"] = decode_leg(torch, dev, max(10, args.steps // 2))
         torch.cuda.empty_cache()
     if not args.no_context:
-        line["long_context"] = long_context_leg(torch, dev, 5)
+        line["long_context"] = long_context_leg(torch, dev, 10)
+        torch.cuda.empty_cache()
+        line["wide_zipf"] = wide_leg(torch, dev, 10)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

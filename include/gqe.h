@@ -345,7 +345,8 @@ int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const v
  *      holds page_size consecutive positions of every KV head;
  *      block_table [B, max_pages] int32: position p of sequence b is row
  *      p % page_size of page block_table[b, p / page_size];
- *      lens [B] int32 with 1 <= lens[b] <= max_pages * page_size;
+ *      lens [B] int32 with 1 <= lens[b] <= max_pages * page_size (out-of-range
+ *      lengths behave as for gqe_attn_decode);
  *      q_routed, q_shared, p_tilde as for gqe_attn_decode.
  * page_size is a power of two from 8 to 4096.  Page ids outside
  * 0 .. num_pages-1 are clamped into that range (a bad table gives wrong
@@ -384,7 +385,9 @@ size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
  *
  * In:  q_routed [B, G, 1, k, d_head], q_shared [B, 1, d_head] or NULL,
  *      k_cache, v_cache [B, H_kv, L_max, d_head] (dtype), lens [B] int32 with
- *      1 <= lens[b] <= L_max (positions >= lens[b] are never read),
+ *      1 <= lens[b] <= L_max (positions >= lens[b] are never read; a length
+ *      above L_max is read as L_max and one below 1 makes that sequence's
+ *      slots NaN, with no access outside the cache or the workspace),
  *      p_tilde [B, G, k] fp32.
  * Out: out [B, S, d_head] fp32, slots as in gqe_attn_prefill.
  * Workspace: gqe_decode_workspace_bytes(desc, L_max) bytes of device memory

@@ -65,6 +65,8 @@ def _load():
         lib.ora_out_proj_rows.restype = None
         lib.ora_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
         lib.ora_decode.restype = ctypes.c_int
+        lib.ora_decode_given.argtypes = [P, P, P, P, P, ctypes.c_int32, P, P, P, P]
+        lib.ora_decode_given.restype = ctypes.c_int
         lib.ora_num_slots.argtypes = [P]
         lib.ora_num_slots.restype = ctypes.c_int
         lib.ora_num_threads.argtypes = []
@@ -247,9 +249,11 @@ def prefill(d: _Desc, inputs: dict, tok=None, routing=None):
     return dict(r, **c, out=out)
 
 
-def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens):
+def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens, routing=None):
     """One decode step per sequence.  x [B, d_model] (or [B, 1, d_model]).
 
+    ``routing`` may carry an agreed selection (sel [B, G, k], ptilde [B, G, k]) to attend with, in place of
+    the oracle's own; sel, ptilde and tie in the result are then still the oracle's own routing.
     Returns dict(out [B, S, d_head], sel [B, G, k], ptilde [B, G, k], tie [B, G]).
     """
     lib = _load()
@@ -265,6 +269,13 @@ def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens):
                         _ptr(kc), _ptr(vc), L_max, _ptr(lens), _ptr(out), _ptr(sel), _ptr(pt), _ptr(tie))
     if rc != 0:
         raise ValueError("oracle decode: invalid shape or cache length")
+    if routing is not None:
+        rs = np.ascontiguousarray(np.asarray(routing["sel"], dtype=np.int32).reshape(d.B, d.H_kv, d.k))
+        rp = np.ascontiguousarray(np.asarray(routing["ptilde"], dtype=np.float64).reshape(d.B, d.H_kv, d.k))
+        rc = lib.ora_decode_given(ctypes.byref(d), _ptr(x), _ptr(_f64(w_q)), _ptr(kc), _ptr(vc), L_max, _ptr(lens),
+                                  _ptr(rs), _ptr(rp), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle decode: invalid cache length")
     return dict(out=out, sel=sel, ptilde=pt, tie=tie.astype(bool))
 
 

@@ -390,16 +390,15 @@ void ora_out_proj_rows(const ora_desc* D, const double* slots, const double* w_o
  * out [B, S, d_head]; sel [B, G, k], ptilde [B, G, k] and tie [B, G] are
  * filled as by ora_route (tie and ptilde may be NULL).
  */
-int ora_decode(const ora_desc* D, const double* x, const double* w_router, const double* b_router,
-               const double* w_q, const double* k_cache, const double* v_cache, int32_t L_max,
-               const int32_t* lens, double* out, int32_t* sel, double* ptilde, uint8_t* tie)
+/* Decode steps 6-8 for a given selection and p~ (the caller's routing): each
+ * sequence's one new token at position lens[b]-1 attends its cache prefix. */
+int ora_decode_given(const ora_desc* D, const double* x, const double* w_q, const double* k_cache,
+                     const double* v_cache, int32_t L_max, const int32_t* lens, const int32_t* sel,
+                     const double* pt, double* out)
 {
     const int G = D->H_kv, E = D->H_q / D->H_kv, k = D->k, dh = D->d_head, B = D->B;
     const int S = ora_nslots(D);
-    double* pt = ptilde ? ptilde : (double*)malloc(sizeof(double) * (size_t)B * G * k);
-    int rc = ora_route(D, B, x, w_router, b_router, NULL, NULL, sel, pt, tie);
-    if (rc) { if (!ptilde) free(pt); return rc; }
-    for (int b = 0; b < B; ++b) if (lens[b] < 1 || lens[b] > L_max) { if (!ptilde) free(pt); return -1; }
+    for (int b = 0; b < B; ++b) if (lens[b] < 1 || lens[b] > L_max) return -1;
 #pragma omp parallel
     {
         double* q = (double*)malloc(sizeof(double) * dh);
@@ -426,6 +425,17 @@ int ora_decode(const ora_desc* D, const double* x, const double* w_router, const
         }
         free(q); free(o_r); free(o_sh); free(w);
     }
-    if (!ptilde) free(pt);
     return 0;
+}
+
+int ora_decode(const ora_desc* D, const double* x, const double* w_router, const double* b_router,
+               const double* w_q, const double* k_cache, const double* v_cache, int32_t L_max,
+               const int32_t* lens, double* out, int32_t* sel, double* ptilde, uint8_t* tie)
+{
+    const int G = D->H_kv, k = D->k, B = D->B;
+    double* pt = ptilde ? ptilde : (double*)malloc(sizeof(double) * (size_t)B * G * k);
+    int rc = ora_route(D, B, x, w_router, b_router, NULL, NULL, sel, pt, tie);
+    if (rc == 0) rc = ora_decode_given(D, x, w_q, k_cache, v_cache, L_max, lens, sel, pt, out);
+    if (!ptilde) free(pt);
+    return rc;
 }

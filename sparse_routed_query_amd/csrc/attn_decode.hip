@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
 #pragma unroll
                 for (int i = 0; i < ND; ++i) {
                     const int d = min(64 * i + lane, D - 1);
-                    ov[c][i] = pp[(size_t)min(c, nc - 1) * (D + 2) + 2 + d];
+                    ov[c][i] = pp[(size_t)min(c, max(nc - 1, 0)) * (D + 2) + 2 + d];
                 }
             const float M = wave_max(m);
             const float wgt = lane < nc ? __builtin_amdgcn_exp2f(m - M) : 0.f;
@@ -318,7 +318,8 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
             }
         }
         Ls = wave_sum(Ls);
-        const float inv = 1.f / Ls;
+        // a length below 1 (outside the documented range) has no chunk: its slots are NaN
+        const float inv = nc > 0 ? 1.f / Ls : __builtin_nanf("");
         float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
 #pragma unroll
         for (int d0 = 0; d0 < D; d0 += 64) {

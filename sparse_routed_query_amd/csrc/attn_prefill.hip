@@ -14,8 +14,10 @@
 //     K/V tile staged in LDS -- each K/V tile is loaded once per 128 rows.
 //   * The wave computes S^T = K Q^T (32 keys x 32 queries per MFMA block), so a
 //     lane owns one query column: the row max and row sum need one exchange
-//     with lane l^32 and no LDS.  Q is pre-scaled by log2(e)/sqrt(d), so the
-//     softmax is a bare exp2.
+//     with lane l^32 and no LDS.  Q enters the product exactly as the
+//     projection stored it; the scale log2(e)/sqrt(d) is applied in fp32 to
+//     the scores, fused with the subtraction of the row's reference, so the
+//     softmax is one fma and one exp2 per score and q is rounded only once.
 //   * P^T feeds O^T = V^T P^T straight from the S^T accumulators.  The order
 //     of keys inside a 16-key MFMA step is permuted to match the accumulator
 //     layout; V^T is written to LDS in that permuted order, so no shuffle of P
@@ -331,21 +333,17 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
     float m_ref = 0.f, l_half = 0.f;
-    f32x16 cneg;
+    float negm = 0.f;   // -m_ref, the fma addend of every exponent
+    f32x16 zero16;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cneg[r] = 0.f;
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
 
     load(kt0);
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-        bf16x8 v = {};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = f2bf(bf2f((uint16_t)(qraw[c][i] & 0xffff)) * qscale);
-            v[2 * i + 1] = f2bf(bf2f((uint16_t)(qraw[c][i] >> 16)) * qscale);
-        }
-        qf[c] = qvalid ? v : bf16x8{};
+        const u32x4 v = qvalid ? qraw[c] : u32x4{0, 0, 0, 0};
+        qf[c] = __builtin_bit_cast(bf16x8, v);
         // pin the Q fragments here, ahead of the first tile's store: the Q loads
         // are then in flight together with the tile loads, not issued after them
         asm volatile("" ::"v"(qf[c]));
@@ -369,10 +367,10 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                 // accumulated yet), block 1 to moving the reference on its own
                 // (which rescales what block 0 already added).
                 f32x16 sb0, sb1;
-                sb0 = mfma32(ld_bf16x8(bK + k_off), qf[0], cneg);
+                sb0 = mfma32(ld_bf16x8(bK + k_off), qf[0], zero16);
 #pragma unroll
                 for (int c = 1; c < D / 16; ++c) sb0 = mfma32(ld_bf16x8(bK + k_off + 16 * c), qf[c], sb0);
-                sb1 = mfma32(ld_bf16x8(bK + k_off + 32 * P), qf[0], cneg);
+                sb1 = mfma32(ld_bf16x8(bK + k_off + 32 * P), qf[0], zero16);
 #pragma unroll
                 for (int c = 1; c < D / 16; ++c) sb1 = mfma32(ld_bf16x8(bK + k_off + 32 * P + 16 * c), qf[c], sb1);
                 uint32_t pb0[8], pb1[8];
@@ -380,7 +378,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                     float la = 0.f, lb = 0.f;
 #pragma unroll
                     for (int r = 0; r < 16; r += 2) {
-                        const float e0 = __builtin_amdgcn_exp2f(sv[r]), e1 = __builtin_amdgcn_exp2f(sv[r + 1]);
+                        const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[r], qscale, negm));
+                        const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], qscale, negm));
                         pw8[r / 2] = pk_bf16(e0, e1);
                         la += e0;
                         lb += e1;
@@ -407,19 +406,18 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                         float mt = sb1[0];
 #pragma unroll
                         for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, sb1[r]), sb1[r + 1]);
-                        mt = half_max(fmaxf(mt, sb1[15]));
+                        // (fma by a positive scale is monotone: the scaled maximum is the
+                        // maximum of the scaled scores)
+                        mt = half_max(fmaf(fmaxf(mt, sb1[15]), qscale, negm));
                         const float shift = mt > kPfRescale ? mt : 0.f;
                         const float alpha = __builtin_amdgcn_exp2f(-shift);
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) sb1[r] -= shift;
 #pragma unroll
                         for (int j = 0; j < NDB; ++j)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
                         l_half *= alpha;
                         m_ref += shift;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                        negm = -m_ref;
                         ls1 = probs_block(sb1, pb1);
                     }
                     l_half += ls1;
@@ -430,11 +428,11 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
             if (!done) {
                 // General path: the first tile of the item, tiles that need a
                 // mask, and tiles whose first block failed the check above.
-                // S^T - m_ref = K Q^T + cneg for two 32-key blocks
+                // S^T = K Q^T for two 32-key blocks (unscaled)
                 f32x16 s[2];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P), qf[0], cneg);
+                    s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P), qf[0], zero16);
 #pragma unroll
                     for (int c = 1; c < D / 16; ++c) s[kb] = mfma32(ld_bf16x8(bK + k_off + kb * 32 * P + 16 * c), qf[c], s[kb]);
                 }
@@ -447,7 +445,7 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                         for (int r = 0; r < 16; ++r)
                             s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) > lim ? -INFINITY : s[kb][r];
                 }
-                // P = exp2(S - m_ref), packed to bf16 for the PV product.  The row sum
+                // P = exp2(S * log2(e)/sqrt(d) - m_ref), packed to bf16 for the PV product.  The row sum
                 // adds the fp32 values with plain adds (v_dot2 on the packed values
                 // does not run alongside other waves' MFMAs; adds do).
                 // If no lane's partial row sum exceeds 2^8, no probability does, so the
@@ -461,7 +459,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; r += 2) {
-                            const float e0 = __builtin_amdgcn_exp2f(s[kb][r]), e1 = __builtin_amdgcn_exp2f(s[kb][r + 1]);
+                            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], qscale, negm));
+                            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], qscale, negm));
                             pw[kb * 8 + r / 2] = pk_bf16(e0, e1);
                             la += e0;
                             lb += e1;
@@ -483,24 +482,19 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 #pragma unroll
                     for (int r = 1; r < 15; r += 2) mt = fmaxf(fmaxf(mt, s[1][r]), s[1][r + 1]);
                     mt = fmaxf(mt, s[1][15]);
-                    mt = half_max(mt);
+                    mt = half_max(fmaf(mt, qscale, negm));
                     // first tile: set the reference; later tiles: move it only on a large jump
                     const bool move = kt == kt0 ? true : mt > kPfRescale;
                     if (__ballot(move)) {
                         const float shift = move ? mt : 0.f;
                         const float alpha = kt == kt0 ? 0.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) s[kb][r] -= shift;
-#pragma unroll
                         for (int j = 0; j < NDB; ++j)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
                         l_half *= alpha;
                         m_ref += shift;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) cneg[r] = -m_ref;
+                        negm = -m_ref;
                     }
                     l_half += probs();
                 }

@@ -286,6 +286,31 @@ def test_decode_shapes(w):
     full_decode_check(w, W.make_inputs(w, lens=lens))
 
 
+def test_decode_lengths_outside_the_range_stay_in_bounds():
+    """A sequence whose length is 0 or negative gets NaN slots and one longer than L_max is read as L_max;
+    the other sequences are unaffected: their slots equal, bit for bit, those of the same call with every
+    length in range (the workspace and the cache past each length hold NaN, so a stray read would show)."""
+    w = decode_case(B=6, name="dec_bad_lens")
+    good = torch.tensor([5, 700, 300, 1, 700, 64], dtype=torch.int32)
+    bad = torch.tensor([0, 700, -4, 1, 900, 64], dtype=torch.int32)
+    inp = W.make_inputs(w, lens=good)            # cache positions >= good[b] hold NaN
+    d = G.desc_from(w)
+    dev = "cuda"
+    x = inp["x"].reshape(w.B, w.d_model).to(dev)
+    r = G.route(d, x, inp["w_router"].to(dev))
+    q = G.qproj(d, x, inp["w_q"].to(dev), r)
+    kc, vc = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    ws = torch.full((G.gqe_decode_workspace_bytes(d, w.L_max) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    ref = G.attn_decode(d, q, kc, vc, good.to(dev), r["p_tilde"], workspace=ws).cpu()
+    ws.fill_(float("nan"))
+    got = G.attn_decode(d, q, kc, vc, bad.to(dev), r["p_tilde"], workspace=ws).cpu()
+    torch.cuda.synchronize()
+    say(f"[{w.name}] lengths {bad.tolist()}: NaN rows {torch.isnan(got).all(-1).all(-1).tolist()}")
+    assert torch.isnan(got[0]).all() and torch.isnan(got[2]).all()
+    for b in (1, 3, 4, 5):                      # 900 > L_max = 700 reads as 700
+        assert torch.equal(got[b], ref[b]), f"sequence {b} changed"
+
+
 def test_decode_matches_last_prefill_row():
     """Decode of position L-1 equals prefill row L-1 computed by the GPU."""
     w = small(B=3, T=200, k=1, H_q=8, H_kv=4)
@@ -340,9 +365,10 @@ def test_large_scores_move_the_softmax_reference():
     """Scores spread over tens of log2 units and growing along the keys, so new row maxima keep arriving:
     the lazy softmax reference moves on the first tile, on the first and on the second 32-key block of
     later tiles, and across the two halves of split query tiles (T = 2500), on every token.  With scores
-    this large (|s| up to ~40 log2 units) the bf16 roundings of the query -- by the projection, and of the
-    query pre-scaled by log2(e)/sqrt(d) that the kernel multiplies with -- move outputs by up to ~0.1, so
-    the attention is compared with the oracle's attention of exactly that query (kernel_query)."""
+    this large (|s| up to ~40 log2 units) the projection's bf16 rounding of the query alone moves outputs
+    by up to ~0.1, so the attention is compared with the oracle's attention of the query rows the
+    projection returned (their exact bf16 values), at the same 2e-2 / 2e-3 bar; the rows themselves are
+    checked against the oracle's projection first."""
     w = small(B=1, T=2500, k=1, w_std=0.35, name="large_scores")
     inp = W.make_inputs(w)
     ramp = 1.0 + 3.0 * torch.arange(w.T, dtype=torch.float32) / w.T

@@ -411,6 +411,32 @@ def test_decode_equals_last_prefill_row():
     # a one-entry cache returns v_0
     assert np.array_equal(dec["out"][1, 0], inp["v"][1, 0, 0].double().numpy())
 
+
+def test_decode_with_a_given_selection_equals_that_prefill_row():
+    """decode(routing=...) attends with the selection it is given: with another valid selection (the
+    next expert after the one the oracle kept, k = 1 of E = 4) it equals the prefill rows of that selection at each
+    sequence's last position, and with its own routing it repeats its plain result bit for bit."""
+    w = wl(H_q=8, H_kv=2, k=1, B=3, T=20)
+    inp = W.make_inputs(w)
+    lens = np.array([20, 1, 13], dtype=np.int32)
+    d = oracle.desc(w)
+    full = oracle.route(d, inp["x"], inp["w_router"])
+    tok = np.array([b * w.T + lens[b] - 1 for b in range(w.B)])
+    other = ((full["sel"] + 1) % w.E).astype(np.int32)           # an expert not kept, in each group
+    pt_other = np.ones_like(full["ptilde"])
+    ref = oracle.prefill_rows(d, inp["x"], inp["w_q"], inp["k"], inp["v"], other, pt_other, tok)
+    xs = inp["x"][torch.arange(w.B), torch.as_tensor(lens - 1).long()]
+    dd = oracle.desc(w, T=1)
+    dec = oracle.decode(dd, xs, inp["w_router"], None, inp["w_q"], inp["k"], inp["v"], lens,
+                        routing=dict(sel=other[tok], ptilde=pt_other[tok]))
+    assert np.array_equal(dec["out"], ref)
+    assert np.array_equal(dec["sel"], full["sel"][tok])          # the reported routing is still its own
+    plain = oracle.decode(dd, xs, inp["w_router"], None, inp["w_q"], inp["k"], inp["v"], lens)
+    own = oracle.decode(dd, xs, inp["w_router"], None, inp["w_q"], inp["k"], inp["v"], lens,
+                        routing=dict(sel=plain["sel"], ptilde=plain["ptilde"]))
+    assert np.array_equal(own["out"], plain["out"])
+    assert not np.allclose(dec["out"][:, :w.k * w.G], plain["out"][:, :w.k * w.G])
+
 # ---------------------------------------------------------------- printed counts
 
 def test_main_setting_counts_from_the_study_note():
