@@ -50,7 +50,8 @@ typedef enum {
     GQE_ERR_UNSUPPORTED = -2,  /* valid but not built: d_head, dtype, too many experts */
     GQE_ERR_ALIGN = -3,        /* a pointer is not 16-byte aligned */
     GQE_ERR_LAUNCH = -4,       /* the HIP runtime rejected a launch */
-    GQE_ERR_WORKSPACE = -5     /* workspace missing or smaller than required */
+    GQE_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+    GQE_ERR_SCRATCH = -6       /* gqe_attn_decode_noalloc: more than GQE_DECODE_SCRATCH_BYTES needed */
 } gqe_status;
 
 typedef enum { GQE_F32 = 0, GQE_BF16 = 1 } gqe_dtype;
@@ -399,6 +400,29 @@ int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_sh
                     const void* k_cache, const void* v_cache, int32_t L_max, const int32_t* lens,
                     const float* p_tilde, float* out, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Bytes of the static device scratch gqe_attn_decode_noalloc uses (16 MiB). */
+#define GQE_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * gqe_attn_decode_noalloc -- gqe_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, bit for bit,
+ * with the split-KV partials kept in a static device array of the library
+ * (GQE_DECODE_SCRATCH_BYTES, one copy per GPU, held until the process ends)
+ * instead of a caller's workspace.  Nothing is allocated or freed; the
+ * array's device address is looked up on the first call on each device.
+ * In/Out: as gqe_attn_decode, without the workspace arguments.
+ * Returns GQE_ERR_SCRATCH, with nothing enqueued, when
+ * gqe_decode_workspace_bytes(desc, L_max) exceeds GQE_DECODE_SCRATCH_BYTES
+ * (e.g. B = 64, L_max = 8192, H_kv = 8, k = 1, d_head = 64 needs 5.9 MB).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (two streams, two host threads) race and must be ordered by the caller.
+ * The partials need no initialisation (every chunk a call reads it writes).
+ */
+int gqe_attn_decode_noalloc(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                            const void* k_cache, const void* v_cache, int32_t L_max, const int32_t* lens,
+                            const float* p_tilde, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,14 @@
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
+#include <mutex>
+
+// Split-KV partials of gqe_attn_decode_noalloc: a fixed device array instead
+// of a caller's workspace, for callers that cannot allocate.  Each GPU holds
+// its own copy for the life of the process.  In host code the name is only a
+// symbol: kernels get the device address hipGetSymbolAddress returns for it.
+static __device__ __align__(256) unsigned char scratch[gqe::kDecodeScratchBytes];
+
 namespace gqe {
 
 constexpr int kDcPasses = 12;  // 16-byte loads per thread for each of K and V
@@ -393,6 +401,28 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t st)
     const size_t lds = (size_t)a.G * a.k * D * sizeof(float);
     decode_merge_kernel<D><<<a.B, 64 * kDcMergeWaves, lds, st>>>((const float*)a.workspace, a.lens, a.p_tilde, a.out,
                                                                  a.G, a.k, a.n_shared, a.S, a.route_mode, nch, CH);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+int decode_scratch(void** ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return -1;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return 0;
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t st)

@@ -117,6 +117,7 @@ const char* gqe_status_string(int status)
     case GQE_ERR_ALIGN: return "pointer not 16-byte aligned";
     case GQE_ERR_LAUNCH: return "kernel launch failed";
     case GQE_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQE_ERR_SCRATCH: return "call needs more than the static scratch holds";
     default: return "unknown status";
     }
 }
@@ -365,6 +366,32 @@ int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_sh
     if (workspace_bytes < gqe::decode_workspace_bytes(s.B, s.G, s.k, s.ns, s.D, L_max, s.bf16))
         return GQE_ERR_WORKSPACE;
     gqe::DecodeArgs a{q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace,
+                      s.B, s.G, s.k, s.D, s.ns, s.mode, s.S, L_max, s.bf16};
+    return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
+}
+
+int gqe_attn_decode_noalloc(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k_cache,
+                            const void* v_cache, int32_t L_max, const int32_t* lens, const float* p_tilde, float* out,
+                            void* stream)
+{
+    static_assert(GQE_DECODE_SCRATCH_BYTES == gqe::kDecodeScratchBytes, "scratch size in gqe.h");
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.T != 1 || L_max < 1) return GQE_ERR_INVALID;
+    if ((long long)s.B * s.G * L_max * s.D >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    if (s.B == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k_cache));
+    GQE_TRY(need(v_cache));
+    GQE_TRY(need(lens));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(out));
+    if (gqe::decode_workspace_bytes(s.B, s.G, s.k, s.ns, s.D, L_max, s.bf16) > gqe::kDecodeScratchBytes)
+        return GQE_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (gqe::decode_scratch(&scratch) != 0) return GQE_ERR_LAUNCH;
+    gqe::DecodeArgs a{q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, scratch,
                       s.B, s.G, s.k, s.D, s.ns, s.mode, s.S, L_max, s.bf16};
     return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
 }

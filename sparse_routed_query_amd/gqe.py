@@ -22,14 +22,17 @@ _lib = None
 
 GQE_F32, GQE_BF16 = 0, 1
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype", -3: "pointer not 16-byte aligned",
-           -4: "kernel launch failed", -5: "workspace missing or too small"}
+           -4: "kernel launch failed", -5: "workspace missing or too small",
+           -6: "call needs more than the static scratch holds"}
+DECODE_SCRATCH_BYTES = 16 << 20   # GQE_DECODE_SCRATCH_BYTES
 
 # Every symbol the C header declares (checked by the host tests).
 EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "gqe_route", "gqe_qproj",
            "gqe_attn_prefill_workspace_bytes", "gqe_attn_prefill_plan", "gqe_attn_prefill",
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
-           "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats")
+           "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
+           "gqe_attn_decode_noalloc")
 
 
 class GqeError(RuntimeError):
@@ -126,6 +129,8 @@ def load():
         lib.gqe_decode_workspace_bytes.restype = Z
         lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
         lib.gqe_attn_decode.restype = I
+        lib.gqe_attn_decode_noalloc.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P]
+        lib.gqe_attn_decode_noalloc.restype = I
         i32 = ctypes.c_int32
         lib.gqe_attn_decode_paged.argtypes = [D, P, P, P, P, i32, i32, i32, P, P, P, P, P, Z, P]
         lib.gqe_attn_decode_paged.restype = I
@@ -358,6 +363,18 @@ def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, o
                                 _ptr(out, torch.float32, "out"), _ptr(workspace, None, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check("gqe_attn_decode", rc)
+
+
+def gqe_attn_decode_noalloc(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, stream=None):
+    """gqe_attn_decode with its partials in the library's static device scratch (no workspace)."""
+    dt = desc.torch_dtype
+    L_max = k_cache.shape[2]
+    rc = load().gqe_attn_decode_noalloc(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"),
+                                        _ptr(q_shared, dt, "q_shared"), _ptr(k_cache, dt, "k_cache"),
+                                        _ptr(v_cache, dt, "v_cache"), L_max, _ptr(lens, torch.int32, "lens"),
+                                        _ptr(p_tilde, torch.float32, "p_tilde"), _ptr(out, torch.float32, "out"),
+                                        _stream(stream))
+    _check("gqe_attn_decode_noalloc", rc)
 
 
 def gqe_attn_decode_paged(desc, q_routed, q_shared, k_pages, v_pages, block_table, lens, p_tilde, out, workspace,

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -283,3 +283,23 @@ def test_prefill_workspace_only_for_split_shapes():
     assert G.gqe_attn_prefill_workspace_bytes(main(B=1, T=32768)) == 0     # balanced without splitting
     assert G.gqe_attn_prefill_workspace_bytes(main(dtype="f32")) == 0
     assert G.load().gqe_attn_prefill_plan(ctypes.byref(main(dtype="f32")), 1, None, 0) == UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_more_than_its_static_scratch():
+    """A call whose split partials exceed GQE_DECODE_SCRATCH_BYTES returns GQE_ERR_SCRATCH on the host, before
+    the scratch is looked up or anything is enqueued; bad descriptors and pointers fail as in gqe_attn_decode."""
+    SCRATCH = -6
+    lib = G.load()
+
+    def rc(desc, L_max=8192, lens=A16):
+        return lib.gqe_attn_decode_noalloc(ctypes.byref(desc), A16, A16, A16, A16, L_max, lens, A16, A16, None)
+
+    big = main(B=256, T=1)                                     # 256 * 8 * 2 * 22 * 66 * 4 B = 23.8 MB
+    assert G.gqe_decode_workspace_bytes(big, 8192) > G.DECODE_SCRATCH_BYTES
+    assert rc(big) == SCRATCH
+    assert G.gqe_decode_workspace_bytes(main(B=64, T=1), 8192) <= G.DECODE_SCRATCH_BYTES
+    assert rc(main(B=64, T=2)) == INVALID                      # decode is one token per sequence
+    assert rc(main(B=64, T=1), L_max=0) == INVALID
+    assert rc(big, lens=None) == INVALID
+    assert rc(big, lens=MIS) == ALIGN
+    assert lib.gqe_status_string(SCRATCH) == b"call needs more than the static scratch holds"
