@@ -21,6 +21,8 @@ divided by the whole step's time).  The same JSON line carries:
                 timed, attention and projection as fractions of the bf16 peak;
   wide_zipf     the wider expert pool with skewed routing (B=2, T=16384,
                 d_model=4096, H_q=32, H_kv=8, k=2, d_head=128), the same;
+  ceilings      a sustained dense bf16 MFMA loop with the clock it ran at,
+                and a streaming HBM read: measured ceilings of this chip;
   out_proj      the next step after the path, outside the timed step: the
                 output projection over the kG+2 slots fused with slot assembly
                 (gqe_out_proj) on the step's own slots, against the bf16 peak;
@@ -132,26 +134,6 @@ def warm(fns, torch, ms=30.0, min_calls=3):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     return i, (time.perf_counter() - t0) * 1e3
-
-
-def sclk_under_load(fn, torch, n=64):
-    """The GPU's current shader clock (MHz) read from sysfs while `n` calls of `fn` are in flight, or
-    None where the driver does not expose it."""
-    import glob
-    for _ in range(n):
-        fn()
-    mhz = None
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for ln in open(path):
-                if ln.strip().endswith("*"):
-                    mhz = float(ln.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
-        except (OSError, ValueError, IndexError):
-            continue
-        if mhz is not None:
-            break
-    torch.cuda.synchronize()
-    return mhz
 
 
 def cpu_model() -> str:
@@ -398,7 +380,42 @@ def attn_backward_leg(p, torch, steps):
             "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
 
 
-def prefill_leg(w, inp, torch, dev, steps):
+def ceilings_leg(torch, dev):
+    """What this chip reaches under sustained load with nothing but dense bf16 MFMAs (every SIMD two waves,
+    each four independent chains of v_mfma_f32_32x32x16_bf16), the shader clock that loop ran at (from the
+    s_memtime and s_memrealtime counters of one wave), and a streaming read of 2 GiB with non-temporal
+    16-byte loads: measured ceilings beside the published peaks the fractions are quoted against."""
+    import sparse_routed_query_amd.calib as C
+    blocks, iters = 512, 40000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def mf():
+        C.mfma(sink, clk, blocks, iters)
+
+    warm([mf], torch, ms=60.0)
+    (t_mfma,) = time_calls([mf], 10, torch)
+    ticks = clk.cpu().tolist()
+    fl = blocks * 4.0 * 4 * iters * 32768
+    src = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    rsink = torch.empty(256 * 8, dtype=torch.int32, device=dev)
+
+    def rd():
+        C.read(src, rsink, 256 * 8)
+
+    warm([rd], torch)
+    (t_read,) = time_calls([rd], 10, torch)
+    del src
+    torch.cuda.empty_cache()
+    tf = fl / (t_mfma * 1e-3) / 1e12
+    gbs = (2 << 30) / (t_read * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": tf, "mfma_frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_loop_clock_ghz": ticks[0] / ticks[1] * 0.1 if ticks[1] > 0 else None,
+            "mfma_loop_ms": t_mfma, "stream_read_gbs": gbs, "stream_read_frac_of_peak": gbs / HBM_PEAK_GBS,
+            "kernels": "calib_mfma_kernel, calib_read_kernel (libgqe_calib.so)"}
+
+
+def prefill_leg(w, inp, torch, dev, steps, traffic_key=None):
     """Every call of the step on one workload, each timed alone with events (after warming the clock),
     and the step as a whole: attention TFLOP/s and projection TFLOP/s against the bf16 peak."""
     import workloads as W
@@ -424,6 +441,7 @@ def prefill_leg(w, inp, torch, dev, steps):
             "qproj_flops": fq, "qproj_tflops": qt, "qproj_frac": qt / MFMA_BF16_PEAK_TFLOPS,
             "step_attn_tflops": fl / (t_step * 1e-3) / 1e12,
             "attn_kernel": f"prefill_bf16_kernel<{w.d_head}>", "qproj_kernel": f"qproj_bf16_kernel<{w.d_head}, 64>",
+            "attn_traffic": traffic_for(traffic_key) if traffic_key else None,
             "expert_rows": counts}
 
 
@@ -431,7 +449,8 @@ def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
     inp = W.make_inputs(w)
-    res = {"gqe": prefill_leg(w, inp, torch, dev, steps), "dense": prefill_leg(W.dense_variant(w), inp, torch, dev, steps)}
+    res = {"gqe": prefill_leg(w, inp, torch, dev, steps, "prefill_long"),
+           "dense": prefill_leg(W.dense_variant(w), inp, torch, dev, steps)}
     res["speedup_attn"] = res["dense"]["attn_us"] / res["gqe"]["attn_us"]
     res["speedup_step"] = res["dense"]["step_us"] / res["gqe"]["step_us"]
     res["ideal_flop_ratio"] = 16 / 9
@@ -441,7 +460,7 @@ def long_context_leg(torch, dev, steps):
 def wide_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["wide_zipf"]
-    return prefill_leg(w, W.make_inputs(w), torch, dev, steps)
+    return prefill_leg(w, W.make_inputs(w), torch, dev, steps, "prefill_wide")
 
 
 def only(args, torch):
@@ -574,7 +593,6 @@ def main():
                      "kernel": f"prefill_bf16_kernel<{w.d_head}> (the one kernel of gqe_attn_prefill_heads)",
                      "algorithmic_flops_per_launch": fl},
     }
-    line["sclk_mhz_under_load"] = sclk_under_load(p.step, torch)
     line["out_proj"] = out_proj_leg(p, torch, max(10, args.steps))
     line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
     line["route_backward"] = route_backward_leg(p, torch, max(10, args.steps))
@@ -588,6 +606,9 @@ def main():
         line["long_context"] = long_context_leg(torch, dev, 10)
         torch.cuda.empty_cache()
         line["wide_zipf"] = wide_leg(torch, dev, 10)
+        torch.cuda.empty_cache()
+    if not args.no_context:
+        line["ceilings"] = ceilings_leg(torch, dev)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

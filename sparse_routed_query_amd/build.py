@@ -1,7 +1,8 @@
 """Build libgqe.so (HIP, gfx950) in-tree with hipcc.
 
 Each source compiles to an object in ``_build/`` in parallel, then one link
-step writes ``sparse_routed_query_amd/libgqe.so``.  Run as a module
+step writes ``sparse_routed_query_amd/libgqe.so``; the benchmark's calibration
+kernels (``csrc/calib.hip``) link separately into ``libgqe_calib.so``.  Run as a module
 (``python -m sparse_routed_query_amd.build``) or call ``build()``.
 """
 from __future__ import annotations
@@ -16,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgqe.so")
+# calibration kernels for the benchmark's measured ceilings (not part of the path)
+CALIB_SRC = "calib.hip"
+CALIB_LIB = os.path.join(HERE, "libgqe_calib.so")
 SOURCES = ["gqe_api.cpp", "route.hip", "qproj.hip", "attn_prefill.hip", "attn_decode.hip", "outproj.hip",
            "route_bwd.hip", "attn_bwd.hip"]
 ARCH = os.environ.get("GQE_OFFLOAD_ARCH", "gfx950")
@@ -41,16 +45,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES) + 1, os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [CALIB_SRC]))
+    calib_obj = objs.pop()
+    _link([calib_obj], CALIB_LIB)
+    _link(objs, LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
