@@ -15,8 +15,8 @@
  *   G = H_kv, E = H_q / H_kv, N = G * E (routed experts), global expert index
  *   n = g * E + e (the GQA query-head index of the GQA tutorial, freeguideonline,
  *   "GQA 核心原理与计算流程" step 3).  BT = B * T.
- *   S = k*G + R + n_shared output slots per token, R = 1, G or 0 weighted
- *   slots for route_mode 0, 1 or 2.
+ *   S = k*G + R + n_shared output slots per token, R = 1, G, 0 or 0 weighted
+ *   slots for route_mode 0, 1, 2 or 3.
  *   Slot order: hard slots g-major then ascending expert index, weighted
  *   slot(s), shared slot.  The shared head's projection is W_q row block N
  *   and it attends KV head 0.  Attention scale is 1/sqrt(d_head).
@@ -72,7 +72,11 @@ typedef struct {
     int32_t route_mode; /* 0: one weighted slot summed over groups (study note
                            §3-2 (4)); 1: one weighted slot per group; 2: no
                            weighted slot (the "hard concat only" row of the
-                           study note's §5-1 ablation table) */
+                           study note's §5-1 ablation table); 3: no weighted
+                           slot, each hard slot scaled by its kept expert's
+                           group softmax probability, not renormalised (the
+                           table's "weighted concat, no renormalized slot"
+                           row) */
     int32_t dtype;      /* gqe_dtype of x, W_router, W_q, q, K, V; outputs are fp32 */
 } gqe_desc;
 
@@ -94,7 +98,7 @@ size_t gqe_route_workspace_bytes(const gqe_desc* desc);
  *   p[t,g,e] = softmax over the E experts of group g
  *   S[t,g]  = the k largest scores of the group (ties: lower e first),
  *             written in ascending expert index
- *   p~[t,g,j] = p[t,g,S_j] / sum_j' p[t,g,S_j']
+ *   p~[t,g,j] = p[t,g,S_j] / sum_j' p[t,g,S_j']   (route mode 3: p[t,g,S_j])
  *   counts[n] = tokens that kept expert n;  offsets = exclusive prefix sum,
  *   offsets[N] = BT*G*k;  rows[offsets[n] + r] = the r-th smallest token id
  *   (b*T + t) that kept n.
@@ -184,6 +188,8 @@ int64_t gqe_attn_prefill_plan(const gqe_desc* desc, int split, int32_t* items, i
  *   out[b,t, g*k+j]  = o of routed row (g, j)                 (hard slots, §3-2 (3))
  *   mode 0: out[b,t,kG] = sum_g sum_j p~[t,g,j] o(g,j)         (§3-2 (4))
  *   mode 1: out[b,t,kG+g] = sum_j p~[t,g,j] o(g,j)
+ *   mode 3: out[b,t,g*k+j] = p~[t,g,j] o(g,j), p~ then being the group softmax
+ *           of the kept expert (study note §5-1 ablation table), no weighted slot
  *   out[b,t,S-1] = o of the shared row against KV head 0       (§3-2 (5))
  *
  * In:  q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] or NULL (the
@@ -222,6 +228,8 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
  *   mode 0: out[t, kG]   = sum_g sum_j p~[t,g,j] out[t, g*k+j]
  *   mode 1: out[t, kG+g] = sum_j p~[t,g,j] out[t, g*k+j]
  * summed in fp32 in that fixed order (g, then j).  Reads only the hard slots.
+ * mode 3: out[t, g*k+j] *= p~[t,g,j] in place (so a second call scales again).
+ * mode 2: nothing to do.
  * In:  p_tilde [B*T, G, k] fp32.  In/Out: out [B*T, S, d_head] fp32.
  * Works for decode outputs too (T = 1).
  */
@@ -294,6 +302,8 @@ size_t gqe_route_backward_workspace_bytes(const gqe_desc* desc);
  * then the blocks in order), so results do not depend on timing.
  * Workspace: gqe_route_backward_workspace_bytes(desc) bytes when dw_router is
  * given (else may be NULL); no initialisation needed.
+ * Route mode 3 returns GQE_ERR_UNSUPPORTED (its weights are the group softmax,
+ * whose gradient reaches experts that were not kept; not built).
  */
 int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out, const int32_t* sel,
                        const float* p_tilde, const void* x, const void* w_router, float* d_hard,
@@ -322,7 +332,9 @@ int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void
  * head outputs, then one final linear projection; GQE study note §3-2 (5) and
  * (7): in GQE the concatenation is of the kG+2 slots).  The weighted slot(s)
  * are not read: they are formed from the hard slots inside the call exactly
- * as gqe_assemble forms them.
+ * as gqe_assemble forms them.  Route modes 2 and 3 have no weighted slot: the
+ * slots are projected as given (mode 3: pass the scaled hard slots that
+ * gqe_attn_prefill or gqe_attn_decode write).
  * In:  out [B*T, S, d_head] fp32 with the hard and shared slots written (as
  *      gqe_attn_prefill_heads or gqe_attn_decode leave them);
  *      p_tilde [B*T, G, k] fp32; w_o [d_model, S*d_head] (dtype), row-major.

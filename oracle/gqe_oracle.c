@@ -49,7 +49,9 @@ typedef struct {
 
 /* Weighted slots: route_mode 0 one summed over groups ([note] §3-2 (4)), 1 one
  * per group, 2 none (the "hard concat only" row of the [note] §5-1 ablation
- * table). */
+ * table), 3 none (the "weighted concat, no renormalized slot" row, read as:
+ * each hard slot scaled by its kept expert's group softmax probability, not
+ * renormalised over the kept ones, and no weighted-sum slot). */
 static int ora_nroute(const ora_desc* D)
 {
     return D->route_mode == 0 ? 1 : D->route_mode == 1 ? D->H_kv : 0;
@@ -78,7 +80,8 @@ static double dot(const double* a, const double* b, int64_t n)
  *   logits[t, n]   s_{t,g,e} = r_g(x_t)_e, the router score       ([note] §3-2 (2))
  *   probs[t, n]    p_{t,g,e}: softmax over the E experts of group g ([note] §3-2 (2))
  *   sel[t, g, j]   S_{t,g} = TopK(p_{t,g,1:E}, k), ascending index  ([note] §3-2 (2))
- *   ptilde[t,g,j]  p renormalised over the kept experts              ([note] §3-2 (4))
+ *   ptilde[t,g,j]  p renormalised over the kept experts              ([note] §3-2 (4));
+ *                  in route mode 3 p itself (the group softmax of the kept expert)
  *   tie[t, g]      1 when the k-th and (k+1)-th largest logits are closer than
  *                  1e-6, so either choice is a correct selection.
  * Any output pointer except sel may be NULL.
@@ -131,7 +134,7 @@ int ora_route(const ora_desc* D, int64_t n_tok, const double* x, const double* w
                 if (chosen[e]) { sel[(t * G + g) * k + j] = e; den += p[e]; ++j; }
             if (ptilde)
                 for (j = 0; j < k; ++j)
-                    ptilde[(t * G + g) * k + j] = p[sel[(t * G + g) * k + j]] / den;
+                    ptilde[(t * G + g) * k + j] = p[sel[(t * G + g) * k + j]] / (D->route_mode == 3 ? 1.0 : den);
             if (logits) for (int e = 0; e < E; ++e) logits[t * N + g * E + e] = s[e];
             if (probs) for (int e = 0; e < E; ++e) probs[t * N + g * E + e] = p[e];
         }
@@ -241,6 +244,8 @@ static void attend(const double* q, const double* Kh, const double* Vh, int64_t 
  *   mode 0: out[kG]     h_route = sum_g sum_j ptilde * o, summed g then j
  *   mode 1: out[kG + g] per-group weighted sum sum_j ptilde * o
  *   mode 2: no weighted slot
+ *   mode 3: no weighted slot; hard slot g*k+j is ptilde[g*k+j] * o (ptilde
+ *           then holds the group softmax p of the kept expert)
  *   out[last]           the shared head (when present)
  * o_r [G*k, dh] holds the kept-expert outputs in hard-slot order.
  */
@@ -250,6 +255,9 @@ static void assemble(const ora_desc* D, const double* o_r, const double* o_sh, c
     const int G = D->H_kv, k = D->k, dh = D->d_head;
     const int nroute = ora_nroute(D);
     memcpy(out, o_r, sizeof(double) * (size_t)G * k * dh);
+    if (D->route_mode == 3)
+        for (int h = 0; h < G * k; ++h)
+            for (int d = 0; d < dh; ++d) out[h * dh + d] = pt[h] * o_r[h * dh + d];
     double* route = out + (int64_t)G * k * dh;
     for (int i = 0; i < nroute * dh; ++i) route[i] = 0.0;
     for (int g = 0; g < G && nroute; ++g)

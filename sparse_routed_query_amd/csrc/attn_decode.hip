@@ -326,8 +326,10 @@ __global__ __launch_bounds__(64 * kDcMergeWaves) void decode_merge_kernel(
             }
         }
         Ls = wave_sum(Ls);
-        // a length below 1 (outside the documented range) has no chunk: its slots are NaN
-        const float inv = nc > 0 ? 1.f / Ls : __builtin_nanf("");
+        // a length below 1 (outside the documented range) has no chunk: its slots are NaN;
+        // route mode 3 scales each hard slot by its kept expert's group softmax probability
+        const float scale = (route_mode == 3 && row < kG) ? p_tilde[(size_t)b * kG + row] : 1.f;
+        const float inv = nc > 0 ? scale / Ls : __builtin_nanf("");
         float* dst = out + ((size_t)b * S + (row < kG ? row : S - 1)) * D;
 #pragma unroll
         for (int d0 = 0; d0 < D; d0 += 64) {

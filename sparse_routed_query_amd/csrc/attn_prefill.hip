@@ -652,6 +652,17 @@ __global__ __launch_bounds__(256) void assemble_kernel(const float* __restrict__
     float* row = out + (size_t)tok * S * D + d;
     const float* pt = p_tilde + (size_t)tok * G * k;
     const int kG = k * G;
+    if (route_mode == 3) {
+        // weighted concatenation: every hard slot times its kept expert's
+        // (not renormalised) group softmax probability, in place
+        for (int h = 0; h < kG; ++h) {
+            f32x4 v = *(const f32x4*)(row + (size_t)h * D);
+            const float w = pt[h];
+            v = f32x4{v[0] * w, v[1] * w, v[2] * w, v[3] * w};
+            *(f32x4*)(row + (size_t)h * D) = v;
+        }
+        return;
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int h0 = 0; h0 < kG; h0 += 8) {
         f32x4 v[8];

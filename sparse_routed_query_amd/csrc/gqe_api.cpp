@@ -29,7 +29,7 @@ int check_desc(const gqe_desc* d, Shape& s)
     if (d->k < 1 || d->k > E) return GQE_ERR_INVALID;
     if (d->n_shared != 0 && d->n_shared != 1) return GQE_ERR_INVALID;
     if (d->causal != 0 && d->causal != 1) return GQE_ERR_INVALID;
-    if (d->route_mode < 0 || d->route_mode > 2) return GQE_ERR_INVALID;
+    if (d->route_mode < 0 || d->route_mode > 3) return GQE_ERR_INVALID;
     if (d->dtype != GQE_F32 && d->dtype != GQE_BF16) return GQE_ERR_INVALID;
     if (d->d_head != 32 && d->d_head != 64 && d->d_head != 128) return GQE_ERR_UNSUPPORTED;
     if (d->H_q > kMaxHq || d->k > kMaxK) return GQE_ERR_UNSUPPORTED;
@@ -39,7 +39,7 @@ int check_desc(const gqe_desc* d, Shape& s)
     if (BT * d->H_kv * d->k >= (1ll << 31) || (long long)d->T * d->k >= (1ll << 31) - 256) return GQE_ERR_UNSUPPORTED;
     s.B = d->B; s.T = d->T; s.dm = d->d_model; s.Hq = d->H_q; s.G = d->H_kv; s.E = E; s.k = d->k;
     s.D = d->d_head; s.ns = d->n_shared; s.causal = d->causal; s.mode = d->route_mode;
-    s.S = d->k * d->H_kv + (d->route_mode == 0 ? 1 : d->route_mode == 1 ? d->H_kv : 0) + d->n_shared;
+    s.S = d->k * d->H_kv + (d->route_mode == 0 ? 1 : d->route_mode == 1 ? d->H_kv : 0) + d->n_shared;   // modes 2, 3: none
     s.bf16 = d->dtype == GQE_BF16;
     s.BT = BT;
     return GQE_OK;
@@ -151,6 +151,7 @@ int gqe_route(const gqe_desc* desc, const void* x, const void* w_router, const f
     }
     gqe::RouteArgs a{x, w_router, b_router, sel, p_tilde, counts, offsets, rows, logits, workspace,
                      (int)s.BT, s.dm, s.G, s.E, s.k, s.bf16};
+    a.renorm = s.mode != 3;
     return launch_status(gqe::launch_route(a, (hipStream_t)stream));
 }
 
@@ -232,6 +233,9 @@ int gqe_route_backward(const gqe_desc* desc, const float* dout, const float* out
     Shape s;
     GQE_TRY(check_desc(desc, s));
     if (s.BT * s.dm >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    // route mode 3 scales the hard slots by the group softmax, whose gradient
+    // reaches experts that were not kept; not built
+    if (s.mode == 3) return GQE_ERR_UNSUPPORTED;
     if (s.BT == 0) return GQE_OK;
     GQE_TRY(need(dout));
     GQE_TRY(need(out));

@@ -21,6 +21,7 @@ struct RouteArgs {
     void* workspace;
     int BT, d_model, G, E, k;
     bool bf16;
+    bool renorm = true;   // false (route mode 3): p_tilde holds the group softmax of the kept experts
 };
 size_t route_workspace_bytes(int BT, int N);
 int launch_route(const RouteArgs& a, hipStream_t st);

@@ -42,7 +42,8 @@ struct OpTile {
     static constexpr int RB = BM / 64;   // 32-row blocks per wave
 };
 
-// Weighted slots of a route mode: one (0), one per group (1) or none (2).
+// Weighted slots of a route mode: one (0), one per group (1) or none (2, 3;
+// mode 3's hard slots arrive already scaled, as gqe_attn_prefill leaves them).
 __device__ __forceinline__ int op_nroute(int G, int mode) { return mode == 0 ? 1 : mode == 1 ? G : 0; }
 
 // Slot read at K stage i (0 <= i < S).  Modes 0 and 2: slot order (hard,

@@ -37,7 +37,7 @@ template <bool BF16, int NB>
 __global__ __launch_bounds__(256) void router_kernel(
     const void* __restrict__ xv, const void* __restrict__ wv, const float* __restrict__ bias,
     int32_t* __restrict__ sel, float* __restrict__ ptilde, double* __restrict__ logits_out,
-    int32_t* __restrict__ blk_counts, int BT, int d_model, int G, int E, int k)
+    int32_t* __restrict__ blk_counts, int BT, int d_model, int G, int E, int k, int renorm)
 {
     const int N = G * E;
     constexpr int nb = NB;         // 16-expert column blocks (<= 4)
@@ -152,11 +152,20 @@ __global__ __launch_bounds__(256) void router_kernel(
             chosen |= 1ull << best;
         }
         int j = 0;
-        double mk = -INFINITY;
-        for (int e = 0; e < E; ++e)
+        double mk = -INFINITY, ma = -INFINITY;
+        for (int e = 0; e < E; ++e) {
+            ma = fmax(ma, s[e]);
             if ((chosen >> e) & 1) { kept[j++] = e; mk = fmax(mk, s[e]); }
+        }
+        // p~ = softmax over the kept scores (renormalised), or in route mode 3
+        // the group softmax p itself, p[e] = exp(s_e - max) / sum over all E
         float ex[8], den = 0.f;
-        for (j = 0; j < k; ++j) { ex[j] = expf((float)(s[kept[j]] - mk)); den += ex[j]; }
+        const double mref = renorm ? mk : ma;
+        for (j = 0; j < k; ++j) { ex[j] = expf((float)(s[kept[j]] - mref)); den += ex[j]; }
+        if (!renorm) {
+            den = 0.f;
+            for (int e = 0; e < E; ++e) den += expf((float)(s[e] - mref));
+        }
         const size_t o = ((size_t)t * G + g) * k;
         for (j = 0; j < k; ++j) {
             sel[o + j] = kept[j];
@@ -380,7 +389,7 @@ int launch_route(const RouteArgs& a, hipStream_t st)
                        (a.bf16 ? (size_t)4 * 2 * nb * 4 * 64 * sizeof(double) : 0) + (size_t)N * sizeof(int);
     if (a.bf16) {
 #define GQE_ROUTER(NBV) router_kernel<true, NBV><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, \
-        a.p_tilde, a.logits, blk_counts, a.BT, a.d_model, a.G, a.E, a.k)
+        a.p_tilde, a.logits, blk_counts, a.BT, a.d_model, a.G, a.E, a.k, a.renorm ? 1 : 0)
         switch (nb) {
         case 1: GQE_ROUTER(1); break;
         case 2: GQE_ROUTER(2); break;
@@ -390,7 +399,7 @@ int launch_route(const RouteArgs& a, hipStream_t st)
 #undef GQE_ROUTER
     } else {
         router_kernel<false, 1><<<grid, 256, lds, st>>>(a.x, a.w_router, a.b_router, a.sel, a.p_tilde, a.logits,
-                                                      blk_counts, a.BT, a.d_model, a.G, a.E, a.k);
+                                                      blk_counts, a.BT, a.d_model, a.G, a.E, a.k, a.renorm ? 1 : 0);
     }
     if ((long long)nblk * N <= kFusedMax) {
         const int cgrid = (nblk + 2 * kCmpWaves - 1) / (2 * kCmpWaves);

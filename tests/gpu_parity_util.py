@@ -59,7 +59,8 @@ def agreed_routing(w: W.Workload, orc: dict, gpu_sel: np.ndarray):
         sel[mism] = gpu_sel[mism]
         probs = orc["probs"].reshape(-1, w.G, w.E)
         p = np.take_along_axis(probs, sel.astype(np.int64), -1)
-        pt[mism] = (p / p.sum(-1, keepdims=True))[mism]
+        # route mode 3 keeps the group softmax of the kept experts; the others renormalise it
+        pt[mism] = (p if w.route_mode == 3 else p / p.sum(-1, keepdims=True))[mism]
     return sel, pt, int(mism.sum())
 
 
@@ -167,7 +168,7 @@ def full_decode_check(w: W.Workload, inp: dict | None = None):
         sel[mism] = gsel[mism]
         probs = oracle.route(d, inp["x"].reshape(w.B, w.d_model), inp["w_router"], inp["b_router"])["probs"]
         p = np.take_along_axis(probs.reshape(w.B, w.G, w.E), sel.astype(np.int64), -1)
-        pt[mism] = (p / p.sum(-1, keepdims=True))[mism]
+        pt[mism] = (p if w.route_mode == 3 else p / p.sum(-1, keepdims=True))[mism]
         ref = oracle.decode(d, inp["x"], inp["w_router"], inp["b_router"], inp["w_q"], inp["k_cache"],
                             inp["v_cache"], inp["lens"], routing=dict(sel=sel, ptilde=pt))["out"]
     say(f"[{w.name}] decode: tie-substituted={int(mism.sum())}")
@@ -180,7 +181,7 @@ def gpu_out_proj(w: W.Workload, out_slots: torch.Tensor, p_tilde: torch.Tensor, 
     """gqe_out_proj on the given slots [B*T, S, d_head] with the weighted slot(s) set to NaN first, so
     that a read of them would show in y.  Returns (y, slots after the call) on the CPU."""
     d = G.desc_from(w)
-    kG, nr = w.k * w.G, (1, w.G, 0)[w.route_mode]
+    kG, nr = w.k * w.G, (1, w.G, 0, 0)[w.route_mode]
     o = out_slots.reshape(w.B * w.T, d.S, w.d_head).clone()
     o[:, kG:kG + nr] = float("nan")
     od = o.to(dev)
@@ -199,9 +200,13 @@ def check_out_proj(w: W.Workload, slots: torch.Tensor, p_tilde: torch.Tensor, w_
     S = oracle.num_slots(d)
     h_gpu = slots.reshape(-1, S, w.d_head)[tok].double().numpy()
     pt = p_tilde.reshape(-1, w.G, w.k)[tok].double().numpy()
-    h = oracle.assemble_rows(d, h_gpu, pt)
+    if w.route_mode == 3:
+        # no weighted slot to form: the slots (scaled hard slots, as gqe_attn_prefill leaves them) are projected
+        h, h_abs = h_gpu, np.abs(h_gpu)
+    else:
+        h = oracle.assemble_rows(d, h_gpu, pt)
+        h_abs = oracle.assemble_rows(d, np.abs(h_gpu), pt)    # weighted part: sum p~ |hard| bounds its error too
     y_ref = oracle.out_proj_rows(d, h, w_o)
-    h_abs = oracle.assemble_rows(d, np.abs(h_gpu), pt)        # weighted part: sum p~ |hard| bounds its error too
     mag = h_abs.reshape(len(tok), -1) @ np.abs(w_o.double().numpy()).T
     K = S * w.d_head
     eps = (2.0 ** -8 if w.dtype == "bf16" else 0.0) + (K + w.k * w.G + 1) * 2.0 ** -24

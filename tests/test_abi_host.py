@@ -54,7 +54,8 @@ def test_num_slots_and_workspace_sizes():
     assert G.gqe_num_slots(main(H_q=15)) == -1
     assert G.gqe_num_slots(main(route_mode=2)) == 9             # 8 hard + shared ("hard concat only")
     assert G.gqe_num_slots(main(route_mode=2, n_shared=0)) == 8
-    assert G.gqe_num_slots(main(route_mode=3)) == -1
+    assert G.gqe_num_slots(main(route_mode=3)) == 9             # 8 scaled hard + shared ("weighted concat")
+    assert G.gqe_num_slots(main(route_mode=4)) == -1
     nblk = (4 * 4096 + 31) // 32
     assert G.gqe_route_workspace_bytes(main()) >= 2 * nblk * 16 * 4
     dd = main(B=64, T=1)
@@ -70,7 +71,7 @@ def test_num_slots_and_workspace_sizes():
     (dict(k=3), INVALID),                    # k > E = 2
     (dict(n_shared=2), INVALID),
     (dict(causal=5), INVALID),
-    (dict(route_mode=3), INVALID),
+    (dict(route_mode=4), INVALID),
     (dict(B=-1), INVALID),
     (dict(d_head=96), UNSUPPORTED),
     (dict(d_model=1000), UNSUPPORTED),       # bf16 needs d_model % 64 == 0
@@ -303,3 +304,13 @@ def test_noalloc_decode_rejects_more_than_its_static_scratch():
     assert rc(big, lens=None) == INVALID
     assert rc(big, lens=MIS) == ALIGN
     assert lib.gqe_status_string(SCRATCH) == b"call needs more than the static scratch holds"
+
+
+def test_route_backward_rejects_the_weighted_concat_mode():
+    """Route mode 3 scales hard slots by the group softmax, whose gradient reaches experts that were not kept;
+    its routing backward is not built and is refused on the host."""
+    lib = G.load()
+    d = main(route_mode=3)
+    rc = lib.gqe_route_backward(ctypes.byref(d), A16, A16, A16, A16, A16, A16, A16, A16, None, None, None, None, 0,
+                                None)
+    assert rc == UNSUPPORTED

@@ -42,6 +42,7 @@ SHAPES = [
     small(d_head=32, name="d32"), small(d_head=128, name="d128"),
     small(route_mode=1, name="per_group_slots"),
     small(route_mode=2, name="hard_only"),
+    small(route_mode=3, name="weighted_concat"),
     small(n_shared=0, name="no_shared"),
     small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="kG8"),
     small(H_q=4, H_kv=1, k=2, name="G1"),

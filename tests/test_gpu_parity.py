@@ -68,6 +68,8 @@ EDGE = [
     small(n_shared=0, name="no_shared"),
     small(route_mode=1, name="per_group_slots"),
     small(route_mode=2, name="hard_only"), small(route_mode=2, n_shared=0, k=1, name="hard_only_no_shared"),
+    small(route_mode=3, name="weighted_concat"), small(route_mode=3, n_shared=0, zipf_s=1.2, name="weighted_concat_ns"),
+    small(dtype="f32", T=90, route_mode=3, name="f32_weighted_concat"),
     small(H_q=16, H_kv=4, k=2, zipf_s=1.2, name="zipf"),
     small(dtype="f32", T=100, d_model=96, name="f32_d64"),
     small(dtype="f32", T=70, d_head=128, d_model=64, k=1, name="f32_d128"),
@@ -206,7 +208,7 @@ def test_heads_then_assemble_equals_attn_prefill(w):
     out = torch.full_like(ref, float("nan"))
     G.gqe_attn_prefill_heads(d, q["q_routed"], q["q_shared"], di["k"], di["v"], out, G.prefill_workspace(d, "cuda"))
     kG = w.k * w.G
-    n_w = (1, w.G, 0)[w.route_mode]
+    n_w = (1, w.G, 0, 0)[w.route_mode]
     torch.cuda.synchronize()
     assert torch.isnan(out[:, :, kG:kG + n_w]).all(), "heads call wrote the weighted slots"
     G.gqe_assemble(d, r["p_tilde"], out)
@@ -272,6 +274,7 @@ def decode_case(**kw):
     decode_case(),
     decode_case(k=2, route_mode=1, name="dec_k2_mode1"),
     decode_case(k=2, route_mode=2, name="dec_k2_hard_only"),
+    decode_case(k=2, route_mode=3, name="dec_k2_weighted_concat"),
     decode_case(d_head=128, H_q=12, H_kv=3, k=3, name="dec_d128_dense"),
     decode_case(d_head=32, n_shared=0, name="dec_d32_noshared"),
     decode_case(dtype="f32", name="dec_f32"),

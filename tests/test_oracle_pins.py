@@ -302,6 +302,51 @@ def test_hard_concat_only_drops_the_weighted_slot():
     assert oracle.num_slots(d2) == kG + 1 and b.shape[1] == kG + 1
     assert np.array_equal(b[:, :kG], a[:, :kG]) and np.array_equal(b[:, kG], a[:, kG + 1])
 
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_weighted_concat_scales_each_hard_slot_by_its_group_softmax(k):
+    """Route mode 3 (the "weighted concat, no renormalized slot" row of [note] §5-1, read as each hard slot times
+    its kept expert's group softmax probability, no weighted-sum slot): the probabilities are torch's softmax of
+    the oracle's router scores over each group's E experts (not renormalised over the kept k), the head outputs
+    are mode 2's hard slots, and the slots of a group sum to (sum of the kept p) times mode 1's per-group
+    weighted slot, whose weights are renormalised."""
+    w = wl(H_q=12, H_kv=3, k=k, zipf_s=1.2)
+    inp = W.make_inputs(w)
+    d3 = oracle.desc(w.replace(route_mode=3))
+    kG = w.G * k
+    assert oracle.num_slots(d3) == kG + 1
+    r3 = oracle.prefill(d3, inp)
+    out3 = r3["out"]
+    logits = torch.from_numpy(oracle.route(oracle.desc(w), inp["x"], inp["w_router"], inp["b_router"])["logits"])
+    p = torch.softmax(logits.reshape(-1, w.G, w.E), dim=-1).numpy()
+    p_kept = np.take_along_axis(p, r3["sel"].astype(np.int64), -1)            # [BT, G, k]
+    np.testing.assert_allclose(r3["ptilde"], p_kept, rtol=1e-13, atol=1e-15)
+    out2 = oracle.prefill(oracle.desc(w.replace(route_mode=2)), inp)["out"]
+    np.testing.assert_allclose(out3[:, :kG], out2[:, :kG] * p_kept.reshape(-1, kG, 1), rtol=1e-13, atol=1e-15)
+    assert np.array_equal(out3[:, kG], out2[:, kG])                          # the shared slot, unchanged
+    out1 = oracle.prefill(oracle.desc(w.replace(route_mode=1)), inp)["out"]
+    grp = out3[:, :kG].reshape(-1, w.G, k, w.d_head).sum(axis=2)
+    want = out1[:, kG:kG + w.G] * p_kept.sum(-1)[..., None]
+    np.testing.assert_allclose(grp, want, rtol=1e-12, atol=1e-14)
+    if k == w.E:   # every expert kept: the kept probabilities sum to 1, so the sum is the weighted slot itself
+        np.testing.assert_allclose(grp, out1[:, kG:kG + w.G], rtol=1e-12, atol=1e-14)
+
+
+def test_weighted_concat_invariances():
+    """Mode 3 with one expert per group keeps the hard slot (p = 1), and a constant added to every score of a
+    group (a uniform router bias) changes no slot: the weights are a softmax over the group."""
+    w1 = wl(H_q=3, H_kv=3, k=1)
+    inp1 = W.make_inputs(w1)
+    a = oracle.prefill(oracle.desc(w1.replace(route_mode=3)), inp1)["out"]
+    b = oracle.prefill(oracle.desc(w1.replace(route_mode=2)), inp1)["out"]
+    assert np.array_equal(a, b)
+    w = wl(H_q=12, H_kv=3, k=2)
+    inp = W.make_inputs(w)
+    d3 = oracle.desc(w.replace(route_mode=3))
+    base = oracle.prefill(d3, inp)["out"]
+    shifted = dict(inp, b_router=torch.tensor([1.7] * 4 + [-0.9] * 4 + [3.1] * 4, dtype=torch.float32))
+    np.testing.assert_allclose(oracle.prefill(d3, shifted)["out"], base, rtol=1e-12, atol=1e-14)
+
+
 def test_permuting_experts_inside_a_group_keeps_weighted_and_shared_slots():
     w = wl(H_q=12, H_kv=3, k=2)
     inp = W.make_inputs(w)

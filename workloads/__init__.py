@@ -41,7 +41,8 @@ class Workload:
     w_std: float           # std of W_router, W_q
     n_shared: int = 1
     causal: int = 1
-    route_mode: int = 0    # 0: one summed weighted slot; 1: one weighted slot per group; 2: none
+    route_mode: int = 0    # 0: one summed weighted slot; 1: one weighted slot per group; 2: none;
+                           # 3: none, hard slots scaled by their group softmax probability
     zipf_s: float = 0.0    # >0: per-expert router bias ln(Zipf pmf) with this exponent
     decode: bool = False
     L_lo: int = 0          # decode: cache length drawn uniformly in [L_lo, L_hi]
@@ -62,7 +63,7 @@ class Workload:
 
     @property
     def n_slots(self) -> int:
-        return self.k * self.G + (1, self.G, 0)[self.route_mode] + self.n_shared
+        return self.k * self.G + (1, self.G, 0, 0)[self.route_mode] + self.n_shared
 
     @property
     def h_active(self) -> int:
@@ -198,13 +199,13 @@ def make_w_o(w: Workload, seed: Optional[int] = None) -> torch.Tensor:
     1000003), so the draws of ``make_inputs`` are unchanged."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed((w.seed if seed is None else seed) + 1000003)
-    S = w.k * w.G + (1, w.G, 0)[w.route_mode] + w.n_shared
+    S = w.k * w.G + (1, w.G, 0, 0)[w.route_mode] + w.n_shared
     return _randn(gen, (w.d_model, S * w.d_head), w.w_std).to(torch_dtype(w))
 
 
 def out_proj_flops(w: Workload, n_tok: Optional[int] = None) -> float:
     """Output-projection FLOPs: 2 * tokens * d_model * S * d_head."""
-    S = w.k * w.G + (1, w.G, 0)[w.route_mode] + w.n_shared
+    S = w.k * w.G + (1, w.G, 0, 0)[w.route_mode] + w.n_shared
     n = w.B * w.T if n_tok is None else n_tok
     return 2.0 * n * w.d_model * S * w.d_head
 
