@@ -309,22 +309,37 @@ def out_proj_leg(p, torch, steps):
 
 def kv_proj_leg(p, torch, steps):
     """The K and V projections ahead of the path (gqe_kv_proj) on the step's x: 2 * B*T * d_model * 2 *
-    H_kv * d_head FLOPs, bf16 MFMA with fp32 accumulation, outside the timed step."""
+    H_kv * d_head FLOPs, bf16 MFMA with fp32 accumulation, outside the timed step; and the whole Q/K/V
+    preamble in one launch (gqe_qkv_proj: kept experts, shared head, K and V from one read of x), without
+    and with the rotary embedding, against gqe_qproj + gqe_kv_proj."""
     import workloads as W
     w, G = p.w, p.G
     wk, wv = (t.to(p.x.device) for t in W.make_w_kv(w))
     k = torch.empty_like(p.k)
     v = torch.empty_like(p.v)
+    q = G.alloc_qproj(p.d, p.x.device)
+    r = p.r
 
     def kv():
         G.gqe_kv_proj(p.d, p.x, wk, wv, k, v)
 
-    warm([kv], torch)
-    (t,) = time_calls([kv], steps, torch)
+    def qkv():
+        G.gqe_qkv_proj(p.d, p.x, p.wq, wk, wv, r["sel"], r["counts"], r["offsets"], r["rows"], None, 0.0,
+                       q["q_routed"], q["q_shared"], k, v)
+
+    def qkv_rope():
+        G.gqe_qkv_proj(p.d, p.x, p.wq, wk, wv, r["sel"], r["counts"], r["offsets"], r["rows"], None, 10000.0,
+                       q["q_routed"], q["q_shared"], k, v)
+
+    warm([kv, p.qproj, qkv, qkv_rope], torch)
+    t, t_qp, t_qkv, t_rope = time_calls([kv, p.qproj, qkv, qkv_rope], steps, torch)
     fl = 2.0 * w.B * w.T * w.d_model * 2 * w.H_kv * w.d_head
+    fl_all = fl + W.qproj_flops(w)
     tf = fl / (t * 1e-3) / 1e12
     return {"workload": w.name, "kernel": f"qproj_bf16_kernel<{w.d_head}, 64> as dense heads (gqe_kv_proj)",
-            "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+            "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl,
+            "qkv_proj_us": t_qkv * 1e3, "qkv_proj_rope_us": t_rope * 1e3, "qproj_plus_kv_proj_us": (t + t_qp) * 1e3,
+            "qkv_proj_tflops": fl_all / (t_qkv * 1e-3) / 1e12, "qkv_proj_flops": fl_all}
 
 
 def route_backward_leg(p, torch, steps):

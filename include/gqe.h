@@ -325,6 +325,35 @@ int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void
                 void* stream);
 
 /*
+ * gqe_qkv_proj -- the whole Q/K/V preamble of the layer from one read of x
+ * (GQA tutorial, freeguideonline, "GQA 核心原理与计算流程" step 2: x is
+ * projected to Q, K and V; GQE study note §3-2 (2) and (5): only the kept
+ * experts and the shared head are projected for Q), in one launch: the kept
+ * experts over their compacted rows exactly as gqe_qproj, the shared head, and
+ * the H_kv K and V heads exactly as gqe_kv_proj, with the k*G + 1 + 2*H_kv
+ * projections of each x row served from one XCD's L2.
+ * Optional rotary position embedding (the pages give none; the RoFormer
+ * form, rotate-half pairing): with rope_base > 1, every routed and shared query
+ * row and every K row at position p has each pair (c, c + d_head/2),
+ * c < d_head/2, rotated by the angle p * rope_base^(-2c/d_head):
+ *   (u, w) -> (u cos - w sin, w cos + u sin),
+ * in fp32 on the fp32 sums before the one rounding to bf16 (V is not
+ * rotated).  Positions: positions[b*T + t] (int32, device, >= 0) or, with
+ * positions NULL, t.  A decode step passes T = 1 and positions = lens - 1.
+ * rope_base = 0 applies no rotation (then the outputs equal gqe_qproj's and
+ * gqe_kv_proj's bit for bit).
+ * In:  x [BT, d_model]; w_q [N + n_shared, d_head, d_model]; w_k, w_v [H_kv,
+ *      d_head, d_model] (dtype); sel, counts, offsets, rows from gqe_route.
+ * Out: q_routed [B, G, T, k, d_head], q_shared [B, T, d_head] (n_shared = 1),
+ *      k, v [B, H_kv, T, d_head] (dtype).
+ * Errors: rope_base not 0 and not above 1 (or not finite) is GQE_ERR_INVALID.
+ */
+int gqe_qkv_proj(const gqe_desc* desc, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                 const int32_t* sel, const int32_t* counts, const int32_t* offsets, const int32_t* rows,
+                 const int32_t* positions, float rope_base, void* q_routed, void* q_shared, void* k, void* v,
+                 void* stream);
+
+/*
  * gqe_out_proj -- the attention output projection, fused with slot assembly.
  * The S slots of a token are concatenated in slot order into h_t (width
  * S*d_head) and passed through one linear map, y_t = W_o h_t, no bias (GQA

@@ -65,6 +65,8 @@ def _load():
         lib.ora_out_proj_rows.restype = None
         lib.ora_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
         lib.ora_decode.restype = ctypes.c_int
+        lib.ora_rope.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_double, P]
+        lib.ora_rope.restype = None
         lib.ora_decode_given.argtypes = [P, P, P, P, P, ctypes.c_int32, P, P, P, P]
         lib.ora_decode_given.restype = ctypes.c_int
         lib.ora_num_slots.argtypes = [P]
@@ -207,6 +209,21 @@ def kv_proj(d: _Desc, x, w):
     return out
 
 
+def rope(rows, positions, base: float):
+    """Rotary position embedding of rows [..., d_head] at positions [...] (broadcast over the leading axes
+    of rows that positions does not cover), float64: pair (c, c + d_head/2) rotated by positions *
+    base^(-2c/d_head).  Returns a new array."""
+    lib = _load()
+    x = np.array(_f64(rows), dtype=np.float64, copy=True)
+    dh = x.shape[-1]
+    pos = np.asarray(positions, dtype=np.int32)
+    pos = np.broadcast_to(pos.reshape(pos.shape + (1,) * (x.ndim - 1 - pos.ndim)), x.shape[:-1])
+    flat = np.ascontiguousarray(x.reshape(-1, dh))
+    p = np.ascontiguousarray(pos.reshape(-1))
+    lib.ora_rope(flat.shape[0], dh, _ptr(p), float(base), _ptr(flat))
+    return flat.reshape(x.shape)
+
+
 def assemble_rows(d: _Desc, slots, ptilde):
     """The weighted slot(s) of token rows whose hard and shared slots are given.
 
@@ -280,5 +297,5 @@ def decode(d: _Desc, x, w_router, b_router, w_q, k_cache, v_cache, lens, routing
 
 
 __all__ = ["build", "desc", "num_slots", "num_threads", "route", "compact", "qproj_rows", "prefill_rows", "prefill",
-           "assemble_rows", "out_proj_rows", "kv_proj",
+           "assemble_rows", "out_proj_rows", "kv_proj", "rope",
            "decode", "TIE_MARGIN"]

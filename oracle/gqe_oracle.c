@@ -372,6 +372,27 @@ void ora_assemble_rows(const ora_desc* D, const double* ptilde, int64_t n_list, 
 }
 
 /*
+ * Rotary position embedding of n rows of width dh in place (the pages give
+ * none; the RoFormer form with rotate-half pairing is the reading taken):
+ * pair (c, c + dh/2), c < dh/2, of a row at position pos[r] is rotated by
+ * the angle pos * base^(-2c/dh):  (u, w) -> (u cos - w sin, w cos + u sin).
+ */
+void ora_rope(int64_t n, int dh, const int32_t* pos, double base, double* rowsv)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        double* x = rowsv + r * dh;
+        for (int c = 0; c < dh / 2; ++c) {
+            const double ang = (double)pos[r] * pow(base, -2.0 * c / dh);
+            const double cs = cos(ang), sn = sin(ang);
+            const double u = x[c], w = x[c + dh / 2];
+            x[c] = u * cs - w * sn;
+            x[c + dh / 2] = w * cs + u * sn;
+        }
+    }
+}
+
+/*
  * The attention output projection of n_list tokens: the S slots of a token,
  * concatenated in slot order into h_t of width S*d_head, times W_o
  * ([tut] "GQA 核心原理与计算流程", step 5: the head outputs are concatenated

@@ -323,6 +323,38 @@ int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void
     return launch_status(gqe::launch_kv_proj(a, (hipStream_t)stream));
 }
 
+int gqe_qkv_proj(const gqe_desc* desc, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                 const int32_t* sel, const int32_t* counts, const int32_t* offsets, const int32_t* rows,
+                 const int32_t* positions, float rope_base, void* q_routed, void* q_shared, void* k, void* v,
+                 void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!(rope_base == 0.f || rope_base > 1.f) || !(rope_base < 3.0e38f)) return GQE_ERR_INVALID;
+    if (s.BT * s.G >= (1ll << 31)) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(x));
+    GQE_TRY(need(w_q));
+    GQE_TRY(need(w_k));
+    GQE_TRY(need(w_v));
+    GQE_TRY(need(sel));
+    GQE_TRY(need(counts));
+    GQE_TRY(need(offsets));
+    GQE_TRY(need(rows));
+    GQE_TRY(maybe(positions));
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    gqe::QkvProjArgs a{};
+    a.x = x; a.w_q = w_q; a.w_k = w_k; a.w_v = w_v; a.sel = sel; a.counts = counts; a.offsets = offsets;
+    a.rows = rows; a.positions = positions; a.q_routed = q_routed; a.q_shared = q_shared; a.k = k; a.v = v;
+    a.rope_base = rope_base;
+    a.B = s.B; a.T = s.T; a.d_model = s.dm; a.G = s.G; a.E = s.E; a.k_ = s.k; a.d_head = s.D; a.n_shared = s.ns;
+    a.H_kv = s.G; a.bf16 = s.bf16;
+    return launch_status(gqe::launch_qkv_proj(a, (hipStream_t)stream));
+}
+
 int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
                  int32_t write_weighted, void* stream)
 {

@@ -92,6 +92,26 @@ struct KvProjArgs {
 };
 int launch_kv_proj(const KvProjArgs& a, hipStream_t st);
 
+struct QkvProjArgs {
+    const void* x;            // [B*T, d_model]
+    const void* w_q;          // [N + n_shared, d_head, d_model]
+    const void* w_k;          // [H_kv, d_head, d_model]
+    const void* w_v;
+    const int32_t* sel;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* rows;
+    const int32_t* positions; // [B*T] or NULL (position t)
+    void* q_routed;           // [B, G, T, k, d_head]
+    void* q_shared;           // [B, T, d_head] (n_shared = 1)
+    void* k;                  // [B, H_kv, T, d_head]
+    void* v;
+    float rope_base;          // 0: no rotary embedding
+    int B, T, d_model, G, E, k_, d_head, n_shared, H_kv;
+    bool bf16;
+};
+int launch_qkv_proj(const QkvProjArgs& a, hipStream_t st);
+
 struct PrefillArgs {
     const void* q_routed;   // NULL: the routed heads are not computed by this call
     const void* q_shared;   // NULL: the shared head is not computed by this call

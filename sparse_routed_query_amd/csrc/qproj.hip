@@ -23,20 +23,68 @@ namespace gqe {
 constexpr int kQpBM = 128;   // rows per tile of the fp32 kernel
 constexpr int kQpPad = 8;    // bf16 elements of row padding in LDS (16 bytes)
 
-// Destination element offset of row r of expert n's bucket.  Experts n >= N
-// are dense heads over every token, written as [B, H, T, d_head] with H = the
-// number of dense heads (1: the shared head, [B, T, d_head]; H_kv: the K or V
-// projection).
-__device__ __forceinline__ size_t qp_dst(int n, int N, int n_dense, int tok, const int32_t* __restrict__ sel,
-                                         int T, int G, int E, int k, int d_head)
+// Projections of one launch.  Expert indices: [0, N) the routed experts
+// (W_q rows n, compacted rows), then ns shared heads (W_q row block N), then
+// nkv K heads and nkv V heads (W_k, W_v), the dense ones over every token.
+struct QpArgs {
+    const uint16_t* x;            // bf16 kernel; the fp32 kernel reads xf etc.
+    const void* w_q;
+    const void* w_k;
+    const void* w_v;
+    const int32_t* sel;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* rows;
+    void* q_routed;               // NULL: the routed experts are left out
+    void* q_shared;               // [B, T, d_head]
+    void* k_out;                  // [B, nkv, T, d_head]
+    void* v_out;
+    const int32_t* positions;     // [B*T] rotary positions, NULL: t
+    int B, T, d_model, G, E, k, ns, nkv;
+    double rope_log2_base;        // > 0: rotate q (routed, shared) and K by the rotary embedding
+};
+
+__host__ __device__ __forceinline__ int qp_n_exp(const QpArgs& a) { return a.G * a.E + a.ns + 2 * a.nkv; }
+
+// Kind of expert n: 0 routed, 1 shared, 2 K head, 3 V head; h = the head within its kind.
+__device__ __forceinline__ int qp_kind(const QpArgs& a, int n, int& h)
 {
-    const int b = tok / T, t = tok - b * T;
-    if (n >= N) return (((size_t)b * n_dense + (n - N)) * T + t) * d_head;
-    const int g = n / E, e = n - g * E;
-    const int32_t* s = sel + ((size_t)tok * G + g) * k;
+    const int N = a.G * a.E;
+    if (n < N) { h = n; return 0; }
+    n -= N;
+    if (n < a.ns) { h = n; return 1; }
+    n -= a.ns;
+    if (n < a.nkv) { h = n; return 2; }
+    h = n - a.nkv;
+    return 3;
+}
+
+// Destination element offset of row r of expert n's bucket (token tok).
+__device__ __forceinline__ size_t qp_dst(const QpArgs& a, int kind, int h, int n, int tok, int d_head)
+{
+    const int b = tok / a.T, t = tok - b * a.T;
+    if (kind == 1) return ((size_t)b * a.T + t) * d_head;
+    if (kind >= 2) return (((size_t)b * a.nkv + h) * a.T + t) * d_head;
+    const int g = n / a.E, e = n - g * a.E;
+    const int32_t* s = a.sel + ((size_t)tok * a.G + g) * a.k;
     int j = 0;
-    for (int i = 0; i < k; ++i) j = s[i] == e ? i : j;
-    return ((((size_t)b * G + g) * T + t) * k + j) * d_head;
+    for (int i = 0; i < a.k; ++i) j = s[i] == e ? i : j;
+    return ((((size_t)b * a.G + g) * a.T + t) * a.k + j) * d_head;
+}
+
+// Rotary frequency of pair i of a d_head-wide row, base^(-2i/d_head), in
+// double (a float exponent would move the angle of a far position by ~1e-3).
+__device__ __forceinline__ double qp_rope_freq(int i, int d_head, double log2_base)
+{
+    return exp2(-(double)(2 * i) / (double)d_head * log2_base);
+}
+// The angle pos * freq reduced to [-pi, pi] in double, so that fp32 sin and
+// cos keep full accuracy at any position.
+__device__ __forceinline__ float qp_rope_angle(int pos, double freq)
+{
+    const double a = (double)pos * freq;
+    const double two_pi = 6.283185307179586476925;
+    return (float)(a - two_pi * rint(a * (1.0 / two_pi)));
 }
 
 // Work order.  Expert n has c_n = ceil(M_n / BM) row tiles (M_N = B*T for
@@ -82,6 +130,7 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane)
 __device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, bool routed, int BM,
                         int lane, int& n_out, int& tile_out)
 {
+    // n_exp <= 128: two candidate experts per lane
     auto ntiles = [&](int n) {
         if (n >= n_exp || (n < N && !routed)) return 0;
         const int M = n < N ? counts[n] : BT;
@@ -137,29 +186,31 @@ struct QpNT {
 // row segment) into registers while the previous stage is multiplied out of
 // LDS, then stored to LDS between two barriers.  Rows past the bucket's end
 // reload its last row and are not stored, so every load is unconditional.
+// The epilogue applies the rotary embedding in fp32 where asked (pairs
+// (c, c + D/2) of a row, which a lane holds in blocks j and j + NB/2, or at
+// D = 32 in lanes l and l ^ 16) and rounds once to bf16.
 template <int D, int BK>
-__global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wq, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
-    uint16_t* __restrict__ q_routed, uint16_t* __restrict__ q_shared, int B, int T, int d_model, int G, int E,
-    int k, int n_shared)
+__global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
 {
-    // q_routed == NULL: only the shared head; n_shared == 0: only the routed experts
     constexpr int NT = QpNT<D>::NT, BM = QpNT<D>::BM;
-    const int N = G * E, BT = B * T, n_exp = N + n_shared;
+    const int N = a.G * a.E, BT = a.B * a.T, n_exp = qp_n_exp(a), d_model = a.d_model;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int s_item[2];
     if (wave == 0) {
         int pn = -1, pt = 0;
-        if (!qp_plan(blockIdx.x, counts, N, n_exp, BT, q_routed != nullptr, BM, lane, pn, pt)) pn = -1;
+        if (!qp_plan(blockIdx.x, a.counts, N, n_exp, BT, a.q_routed != nullptr, BM, lane, pn, pt)) pn = -1;
         if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
     }
     __syncthreads();
     const int n = s_item[0];
     if (n < 0) return;
+    int h;
+    const int kind = qp_kind(a, n, h);
     const int row0 = s_item[1] * BM;
-    const int M = n < N ? counts[n] : BT;
-    const int base = n < N ? offsets[n] : 0;
+    const int M = kind == 0 ? a.counts[n] : BT;
+    const int base = kind == 0 ? a.offsets[n] : 0;
+    const uint16_t* wsrc = kind <= 1 ? (const uint16_t*)a.w_q + (size_t)(kind == 0 ? n : N + h) * D * d_model
+                                     : (const uint16_t*)(kind == 2 ? a.w_k : a.w_v) + (size_t)h * D * d_model;
     constexpr int P = BK + kQpPad;
     constexpr int NB = D / 32;
     constexpr int CPR = BK / 8;                           // 16-byte chunks per row of a stage
@@ -174,10 +225,10 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int rr = min(row0 + tid / CPR + i * (NT / CPR), M - 1);
-        const int tok = n < N ? rows[base + rr] : rr;
-        pa[i] = x + (size_t)tok * d_model + col;
+        const int tok = kind == 0 ? a.rows[base + rr] : rr;
+        pa[i] = a.x + (size_t)tok * d_model + col;
     }
-    const uint16_t* pb = wq + (size_t)n * D * d_model + (size_t)(tid / CPR) * d_model + col;
+    const uint16_t* pb = wsrc + (size_t)(tid / CPR) * d_model + col;
     u32x4 ra[ACH], rb[BCH];
     auto load = [&](int k0) {
 #pragma unroll
@@ -228,116 +279,191 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(
         } else {
 #pragma unroll
             for (int kk = 0; kk < BK; kk += 16) {
-                const bf16x8 a = ld_bf16x8(&sA[a_off + kk]);
+                const bf16x8 fa = ld_bf16x8(&sA[a_off + kk]);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) acc[j] = mfma32(a, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
+                for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
             }
         }
     }
 
-    // destinations of the tile's rows; rows past the bucket are not stored
+    // destinations (and rotary positions) of the tile's rows; rows past the bucket are not stored
     __shared__ size_t s_dst[BM];
+    __shared__ int s_pos[BM];
     const int m = wave * 32 + (lane & 31);
     if (lane < 32) {
         const int r = row0 + m;
         size_t o = ~(size_t)0;
-        if (r < M) o = qp_dst(n, N, n_shared, n < N ? rows[base + r] : r, sel, T, G, E, k, D);
+        int pos = 0;
+        if (r < M) {
+            const int tok = kind == 0 ? a.rows[base + r] : r;
+            o = qp_dst(a, kind, h, n, tok, D);
+            pos = a.positions ? a.positions[tok] : tok % a.T;
+        }
         s_dst[m] = o;
+        s_pos[m] = pos;
     }
     __syncthreads();
-    uint16_t* dst = n < N ? q_routed : q_shared;
+    uint16_t* dst = (uint16_t*)(kind == 0 ? a.q_routed : kind == 1 ? a.q_shared : kind == 2 ? a.k_out : a.v_out);
+    const bool rope = a.rope_log2_base > 0.0 && kind <= 2;
+    const int c0 = lane & 31;
+    // this lane's pair frequencies (pair 32 j + c0, or c0 mod 16 at D = 32)
+    double freq[NB > 1 ? NB / 2 : 1];
+    if (rope) {
+#pragma unroll
+        for (int j = 0; j < (NB > 1 ? NB / 2 : 1); ++j)
+            freq[j] = qp_rope_freq(NB > 1 ? 32 * j + c0 : (c0 & 15), D, a.rope_log2_base);
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int mm = wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const size_t o = s_dst[mm];
+        float v[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) v[j] = acc[j][e];
+        if (rope) {
+            const int pos = s_pos[mm];
+            if constexpr (NB == 1) {
+                // D = 32: column c pairs with c ^ 16, held by lane l ^ 16
+                const float other = __shfl_xor(v[0], 16);
+                float sn, cs;
+                sincosf(qp_rope_angle(pos, freq[0]), &sn, &cs);
+                v[0] = c0 < 16 ? v[0] * cs - other * sn : v[0] * cs + other * sn;
+            } else {
+#pragma unroll
+                for (int j = 0; j < NB / 2; ++j) {
+                    float sn, cs;
+                    sincosf(qp_rope_angle(pos, freq[j]), &sn, &cs);
+                    const float x1 = v[j], x2 = v[j + NB / 2];
+                    v[j] = x1 * cs - x2 * sn;
+                    v[j + NB / 2] = x2 * cs + x1 * sn;
+                }
+            }
+        }
         if (o == ~(size_t)0) continue;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) dst[o + j * 32 + (lane & 31)] = __builtin_bit_cast(uint16_t, f2bf(acc[j][e]));
+        for (int j = 0; j < NB; ++j) dst[o + j * 32 + c0] = __builtin_bit_cast(uint16_t, f2bf(v[j]));
     }
 }
 
-// fp32 projection: one thread per output element, fp32 FMA chain.
-__global__ __launch_bounds__(256) void qproj_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ wq, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, const int32_t* __restrict__ rows,
-    float* __restrict__ q_routed, float* __restrict__ q_shared, int B, int T, int d_model, int G, int E, int k,
-    int d_head, int n_shared)
+// fp32 projection: one thread per output element, fp32 FMA chain (two chains
+// where the rotary embedding needs the partner element of the pair).
+__global__ __launch_bounds__(256) void qproj_f32_kernel(const QpArgs a, const float* __restrict__ x, int d_head)
 {
-    const int N = G * E, BT = B * T, n_exp = N + n_shared;
+    const int N = a.G * a.E, BT = a.B * a.T, n_exp = qp_n_exp(a);
     const int n = blockIdx.x % n_exp;
-    if (n < N && !q_routed) return;
+    int h;
+    const int kind = qp_kind(a, n, h);
+    if (kind == 0 && !a.q_routed) return;
     const int row0 = (blockIdx.x / n_exp) * kQpBM;
-    const int M = n < N ? counts[n] : BT;
+    const int M = kind == 0 ? a.counts[n] : BT;
     if (row0 >= M) return;
-    const int base = n < N ? offsets[n] : 0;
-    const float* wn = wq + (size_t)n * d_head * d_model;
+    const int base = kind == 0 ? a.offsets[n] : 0;
+    const int d_model = a.d_model;
+    const float* wn = kind <= 1 ? (const float*)a.w_q + (size_t)(kind == 0 ? n : N + h) * d_head * d_model
+                                : (const float*)(kind == 2 ? a.w_k : a.w_v) + (size_t)h * d_head * d_model;
+    float* dst = (float*)(kind == 0 ? a.q_routed : kind == 1 ? a.q_shared : kind == 2 ? a.k_out : a.v_out);
+    const bool rope = a.rope_log2_base > 0.0 && kind <= 2;
+    const int half = d_head / 2;
     for (int idx = threadIdx.x; idx < kQpBM * d_head; idx += 256) {
         const int r = row0 + idx / d_head, d = idx % d_head;
         if (r >= M) break;
-        const int tok = n < N ? rows[base + r] : r;
+        const int tok = kind == 0 ? a.rows[base + r] : r;
         const float* xr = x + (size_t)tok * d_model;
-        const float* wr = wn + (size_t)d * d_model;
-        float s = 0.f;
-        for (int i = 0; i < d_model; ++i) s = fmaf(xr[i], wr[i], s);
-        float* dst = n < N ? q_routed : q_shared;
-        dst[qp_dst(n, N, n_shared, tok, sel, T, G, E, k, d_head) + d] = s;
+        auto dotw = [&](int dd) {
+            const float* wr = wn + (size_t)dd * d_model;
+            float s = 0.f;
+            for (int i = 0; i < d_model; ++i) s = fmaf(xr[i], wr[i], s);
+            return s;
+        };
+        float s = dotw(d);
+        if (rope) {
+            const int pos = a.positions ? a.positions[tok] : tok % a.T;
+            const float other = dotw(d < half ? d + half : d - half);
+            float sn, cs;
+            sincosf(qp_rope_angle(pos, qp_rope_freq(d % half, d_head, a.rope_log2_base)), &sn, &cs);
+            s = d < half ? s * cs - other * sn : s * cs + other * sn;
+        }
+        dst[qp_dst(a, kind, h, n, tok, d_head) + d] = s;
     }
 }
 
-int launch_qproj(const QprojArgs& a, hipStream_t st)
+static int launch_qp(const QpArgs& q, int d_head, bool bf16, hipStream_t st)
 {
-    // a NULL q_shared leaves the shared head out of this call (n_shared = 0 below)
-    const int ns = a.q_shared ? a.n_shared : 0;
-    const bool routed = a.q_routed != nullptr;
-    const int N = a.G * a.E, BT = a.B * a.T, n_exp = N + ns;
-    if (BT == 0 || (!routed && ns == 0)) return 0;
-    const int tiles = (BT + kQpBM - 1) / kQpBM;
-    const int grid = tiles * n_exp;
-    // bf16: an upper bound on the number of tiles over all buckets, rounded to the 8 XCDs
-    auto grid_bf16_for = [&](int BM) {
-        const long long um = (routed ? (long long)BT * a.G * a.k / BM + N : 0) + (long long)ns * ((BT + BM - 1) / BM);
-        return (int)(8 * ((um + 7) / 8));
-    };
-    if (a.bf16) {
-        const uint16_t* x = (const uint16_t*)a.x;
-        const uint16_t* w = (const uint16_t*)a.w_q;
-        uint16_t* qr = (uint16_t*)a.q_routed;
-        uint16_t* qs = (uint16_t*)a.q_shared;
-#define GQE_QP(D) qproj_bf16_kernel<D, 64><<<grid_bf16_for(QpNT<D>::BM), QpNT<D>::NT, 0, st>>>(x, w, a.sel, a.counts, a.offsets, a.rows, qr, qs, \
-                                                                  a.B, a.T, a.d_model, a.G, a.E, a.k, ns)
-        switch (a.d_head) {   // d_model is a multiple of the 64-wide stage (checked by the API)
-        case 32: GQE_QP(32); break;
-        case 64: GQE_QP(64); break;
-        case 128: GQE_QP(128); break;
+    const int N = q.G * q.E, BT = q.B * q.T, n_exp = qp_n_exp(q);
+    const bool routed = q.q_routed != nullptr;
+    if (BT == 0 || (!routed && q.ns + q.nkv == 0)) return 0;
+    if (n_exp > 128) return -2;
+    if (bf16) {
+        // an upper bound on the number of tiles over all buckets, rounded to the 8 XCDs
+        auto grid_for = [&](int BM) {
+            const long long um = (routed ? (long long)BT * q.G * q.k / BM + N : 0) +
+                                 (long long)(q.ns + 2 * q.nkv) * ((BT + BM - 1) / BM);
+            return (int)(8 * ((um + 7) / 8));
+        };
+        switch (d_head) {   // d_model is a multiple of the 64-wide stage (checked by the API)
+        case 32: qproj_bf16_kernel<32, 64><<<grid_for(QpNT<32>::BM), QpNT<32>::NT, 0, st>>>(q); break;
+        case 64: qproj_bf16_kernel<64, 64><<<grid_for(QpNT<64>::BM), QpNT<64>::NT, 0, st>>>(q); break;
+        case 128: qproj_bf16_kernel<128, 64><<<grid_for(QpNT<128>::BM), QpNT<128>::NT, 0, st>>>(q); break;
         default: return -2;
         }
-#undef GQE_QP
     } else {
-        qproj_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, (const float*)a.w_q, a.sel, a.counts, a.offsets,
-                                               a.rows, (float*)a.q_routed, (float*)a.q_shared, a.B, a.T, a.d_model,
-                                               a.G, a.E, a.k, a.d_head, ns);
+        const int tiles = (BT + kQpBM - 1) / kQpBM;
+        qproj_f32_kernel<<<tiles * n_exp, 256, 0, st>>>(q, (const float*)q.x, d_head);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+static QpArgs qp_args(const void* x, int B, int T, int d_model, int G, int E, int k)
+{
+    QpArgs q{};
+    q.x = (const uint16_t*)x;
+    q.B = B; q.T = T; q.d_model = d_model; q.G = G; q.E = E; q.k = k;
+    return q;
+}
+
+int launch_qproj(const QprojArgs& a, hipStream_t st)
+{
+    // a NULL q_shared leaves the shared head out of this call
+    QpArgs q = qp_args(a.x, a.B, a.T, a.d_model, a.G, a.E, a.k);
+    q.w_q = a.w_q; q.sel = a.sel; q.counts = a.counts; q.offsets = a.offsets; q.rows = a.rows;
+    q.q_routed = a.q_routed; q.q_shared = a.q_shared;
+    q.ns = a.q_shared ? a.n_shared : 0;
+    return launch_qp(q, a.d_head, a.bf16, st);
+}
+
 // K and V projections (GQA tutorial, freeguideonline, "GQA 核心原理与计算流程"
-// step 2): the same kernel with no routed experts and H_kv dense heads over
-// every token, once for K and once for V, written as [B, H_kv, T, d_head].
+// step 2): the same kernel with no routed experts and 2 H_kv dense heads over
+// every token in one launch, written as [B, H_kv, T, d_head].
 int launch_kv_proj(const KvProjArgs& a, hipStream_t st)
 {
-    for (int which = 0; which < 2; ++which) {
-        QprojArgs q{};
-        q.x = a.x;
-        q.w_q = which ? a.w_v : a.w_k;
-        q.q_routed = nullptr;
-        q.q_shared = which ? a.v : a.k;
-        q.B = a.B; q.T = a.T; q.d_model = a.d_model; q.G = 0; q.E = 1; q.k = 1; q.d_head = a.d_head;
-        q.n_shared = a.H_kv;
-        q.bf16 = a.bf16;
-        const int rc = launch_qproj(q, st);
-        if (rc) return rc;
-    }
-    return 0;
+    QpArgs q = qp_args(a.x, a.B, a.T, a.d_model, 0, 1, 1);
+    q.w_k = a.w_k; q.w_v = a.w_v; q.k_out = a.k; q.v_out = a.v;
+    q.nkv = a.H_kv;   // at most 64 (the descriptor's limit), so one plan covers both
+    return launch_qp(q, a.d_head, a.bf16, st);
+}
+
+// The whole Q/K/V preamble from one read of x: the routed experts over their
+// compacted rows, the shared head, and the K and V heads in one launch, so
+// the k*G + 1 + 2*H_kv projections of every x row are served from one XCD's
+// L2; the rotary embedding, when asked, is applied to q and K in fp32 before
+// the one bf16 rounding.
+int launch_qkv_proj(const QkvProjArgs& a, hipStream_t st)
+{
+    QpArgs q = qp_args(a.x, a.B, a.T, a.d_model, a.G, a.E, a.k_);
+    q.w_q = a.w_q; q.w_k = a.w_k; q.w_v = a.w_v;
+    q.sel = a.sel; q.counts = a.counts; q.offsets = a.offsets; q.rows = a.rows;
+    q.q_routed = a.q_routed; q.q_shared = a.n_shared ? a.q_shared : nullptr; q.k_out = a.k; q.v_out = a.v;
+    q.ns = a.n_shared ? 1 : 0;
+    q.nkv = a.H_kv;
+    q.positions = a.positions;
+    q.rope_log2_base = a.rope_base > 0.f ? log2((double)a.rope_base) : 0.0;
+    if (qp_n_exp(q) <= 128) return launch_qp(q, a.d_head, a.bf16, st);
+    // more experts than one plan covers: the queries, then K and V
+    QpArgs qq = q, qkv = q;
+    qq.nkv = 0;
+    qkv.q_routed = nullptr; qkv.ns = 0; qkv.G = 0; qkv.E = 1;
+    const int rc = launch_qp(qq, a.d_head, a.bf16, st);
+    return rc ? rc : launch_qp(qkv, a.d_head, a.bf16, st);
 }
 
 }  // namespace gqe

@@ -32,7 +32,7 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
            "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
-           "gqe_attn_decode_noalloc")
+           "gqe_attn_decode_noalloc", "gqe_qkv_proj")
 
 
 class GqeError(RuntimeError):
@@ -129,6 +129,8 @@ def load():
         lib.gqe_decode_workspace_bytes.restype = Z
         lib.gqe_attn_decode.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P, Z, P]
         lib.gqe_attn_decode.restype = I
+        lib.gqe_qkv_proj.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P]
+        lib.gqe_qkv_proj.restype = I
         lib.gqe_attn_decode_noalloc.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P]
         lib.gqe_attn_decode_noalloc.restype = I
         i32 = ctypes.c_int32
@@ -365,6 +367,19 @@ def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, o
     _check("gqe_attn_decode", rc)
 
 
+def gqe_qkv_proj(desc, x, w_q, w_k, w_v, sel, counts, offsets, rows, positions, rope_base, q_routed, q_shared, k, v,
+                 stream=None):
+    """The Q/K/V preamble in one launch, optionally with the rotary embedding (rope_base > 1; 0 = none)."""
+    dt = desc.torch_dtype
+    rc = load().gqe_qkv_proj(ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_q, dt, "w_q"), _ptr(w_k, dt, "w_k"),
+                             _ptr(w_v, dt, "w_v"), _ptr(sel, torch.int32, "sel"), _ptr(counts, torch.int32, "counts"),
+                             _ptr(offsets, torch.int32, "offsets"), _ptr(rows, torch.int32, "rows"),
+                             _ptr(positions, torch.int32, "positions"), float(rope_base),
+                             _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"),
+                             _ptr(v, dt, "v"), _stream(stream))
+    _check("gqe_qkv_proj", rc)
+
+
 def gqe_attn_decode_noalloc(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, stream=None):
     """gqe_attn_decode with its partials in the library's static device scratch (no workspace)."""
     dt = desc.torch_dtype
@@ -414,6 +429,17 @@ def route(desc, x, w_router, b_router=None, logits=False, bufs=None, stream=None
     gqe_route(desc, x, w_router, b_router, r["sel"], r["p_tilde"], r["counts"], r["offsets"], r["rows"],
               r["logits"], r["workspace"], stream)
     return r
+
+
+def qkv_proj(desc, x, w_q, w_k, w_v, r: dict, positions=None, rope_base=0.0, stream=None) -> dict:
+    """q_routed, q_shared, k, v of x in one launch (rotary embedding when rope_base > 1)."""
+    q = alloc_qproj(desc, x.device)
+    shape = (desc.B, desc.H_kv, desc.T, desc.d_head)
+    k = torch.empty(shape, dtype=desc.torch_dtype, device=x.device)
+    v = torch.empty(shape, dtype=desc.torch_dtype, device=x.device)
+    gqe_qkv_proj(desc, x, w_q, w_k, w_v, r["sel"], r["counts"], r["offsets"], r["rows"], positions, rope_base,
+                 q["q_routed"], q["q_shared"], k, v, stream)
+    return dict(q, k=k, v=v)
 
 
 def qproj(desc, x, w_q, r: dict, bufs=None, stream=None) -> dict:

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -314,3 +314,21 @@ def test_route_backward_rejects_the_weighted_concat_mode():
     rc = lib.gqe_route_backward(ctypes.byref(d), A16, A16, A16, A16, A16, A16, A16, A16, None, None, None, None, 0,
                                 None)
     assert rc == UNSUPPORTED
+
+
+def test_qkv_proj_rejects_bad_rope_base_and_pointers():
+    lib = G.load()
+    d = main()
+
+    def rc(base, positions=None, x=A16, qs=A16):
+        return lib.gqe_qkv_proj(ctypes.byref(d), x, A16, A16, A16, A16, A16, A16, A16, positions, ctypes.c_float(base),
+                                A16, qs, A16, A16, None)
+
+    assert rc(1.0) == INVALID                    # base 1: every pair the same frequency
+    assert rc(0.5) == INVALID
+    assert rc(-3.0) == INVALID
+    assert rc(float("nan")) == INVALID
+    assert rc(float("inf")) == INVALID
+    assert rc(10000.0, x=None) == INVALID
+    assert rc(10000.0, qs=None) == INVALID       # the shared head is on
+    assert rc(10000.0, positions=MIS) == ALIGN

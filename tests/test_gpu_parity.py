@@ -543,3 +543,107 @@ def test_decode_input_audit_counts_bad_lengths_and_page_ids():
     table[6, 1] = -5          # not used by a length of 64
     table[7, 1] = num_pages + 3   # used (length 65 reaches column 1)
     assert G.check_decode_inputs(d, good.cuda(), max_pages * P, table.cuda(), num_pages, P) == (0, 4)
+
+
+# ---------------------------------------------------------------- fused Q/K/V preamble, rotary embedding
+
+def qkv_case(w, rope_base=0.0, positions=None):
+    """gqe_route, then gqe_qkv_proj on the workload's x, W_q and seeded W_k / W_v."""
+    inp = W.make_inputs(w)
+    wk, wv = W.make_w_kv(w)
+    d = G.desc_from(w)
+    dev = "cuda"
+    x = inp["x"].reshape(-1, w.d_model).to(dev)
+    br = inp["b_router"].to(dev) if inp["b_router"] is not None else None
+    r = G.route(d, x, inp["w_router"].to(dev), br)
+    pos = positions.to(dev) if positions is not None else None
+    out = G.qkv_proj(d, x, inp["w_q"].to(dev), wk.to(dev), wv.to(dev), r, pos, rope_base)
+    torch.cuda.synchronize()
+    return inp, wk, wv, d, r, {k: v.cpu() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("w", [small(), small(d_head=32, name="d32"), small(d_head=128, name="d128"),
+                               small(dtype="f32", T=90, name="f32")], ids=lambda w: w.name)
+def test_qkv_proj_without_rotation_equals_separate_projections(w):
+    """One launch of every projection gives, bit for bit, what gqe_qproj and gqe_kv_proj give."""
+    inp, wk, wv, d, r, out = qkv_case(w)
+    dev = "cuda"
+    x = inp["x"].reshape(-1, w.d_model).to(dev)
+    q = G.qproj(d, x, inp["w_q"].to(dev), r)
+    k, v = G.kv_proj(d, x, wk.to(dev), wv.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(out["q_routed"], q["q_routed"].cpu()) and torch.equal(out["q_shared"], q["q_shared"].cpu())
+    assert torch.equal(out["k"], k.cpu()) and torch.equal(out["v"], v.cpu())
+
+
+def check_rotated(w, got, ref_plain, pos, base, what):
+    """got (GPU, rotated) against the oracle's rotation of the oracle's unrotated projection ref_plain
+    (float64, [..., d_head]): bf16 rounding of the result (2^-8 relative), the fp32 rotation and angle
+    (1e-5 of the pair's magnitude) and 1e-4 absolute; fp32 1e-5 of max|ref|."""
+    ref = oracle.rope(ref_plain, pos, base) if base else ref_plain
+    g = got.double().numpy()
+    err = np.abs(g - ref)
+    h = w.d_head // 2
+    pair = np.abs(ref_plain[..., :h]) + np.abs(ref_plain[..., h:])
+    mag = np.concatenate([pair, pair], axis=-1)
+    if w.dtype == "bf16":
+        lim = 2.0 ** -8 * np.abs(ref) + 1e-5 * mag + 1e-4
+    else:
+        lim = 1e-5 * max(1e-30, np.abs(ref).max()) + 1e-6 * mag
+    say(f"[{w.name}] {what}: max-abs={err.max():.3e} max err/bound={(err / lim).max():.3f}")
+    assert (err <= lim).all()
+
+
+@pytest.mark.parametrize("w,base,given", [
+    (small(), 10000.0, False), (small(d_head=32, name="d32"), 10000.0, True),
+    (small(d_head=128, k=1, name="d128"), 500000.0, False), (small(T=64, name="short_base"), 10.0, True),
+    (small(dtype="f32", T=90, name="f32"), 10000.0, True),
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_qkv_proj_rotary_against_the_oracle(w, base, given):
+    """Routed and shared queries and K rotated by position (given, or t), V not rotated, against the
+    oracle's projections rotated by oracle.rope."""
+    positions = None
+    if given:
+        positions = torch.randint(0, 70000, (w.B * w.T,), dtype=torch.int32, generator=torch.Generator().manual_seed(4))
+    inp, wk, wv, d, r, out = qkv_case(w, base, positions)
+    agreed = check_route(w, inp, dict(sel=r["sel"].cpu(), p_tilde=r["p_tilde"].cpu(), counts=r["counts"].cpu(),
+                                      offsets=r["offsets"].cpu(), rows=r["rows"].cpu()))
+    od = oracle.desc(w)
+    tok = np.arange(w.B * w.T)
+    pos = positions.numpy() if given else tok % w.T
+    qr, qs = oracle.qproj_rows(od, inp["x"], inp["w_q"], agreed["sel"], tok)
+    b, t = tok // w.T, tok % w.T
+    check_rotated(w, out["q_routed"][b, :, t], qr, pos, base, "q_routed")
+    check_rotated(w, out["q_shared"][b, t], qs, pos, base, "q_shared")
+    kp = oracle.kv_proj(od, inp["x"], wk)                         # [B, H_kv, T, d_head]
+    kpos = pos.reshape(w.B, 1, w.T)
+    check_rotated(w, out["k"], kp, np.broadcast_to(kpos, kp.shape[:-1]), base, "k")
+    check_rotated(w, out["v"], oracle.kv_proj(od, inp["x"], wv), None, 0.0, "v")
+
+
+def test_rotary_layer_prefill_and_decode():
+    """x -> route -> rotated Q/K/V (one launch) -> attention: the slots against the oracle's attention of the
+    GPU's rotated queries and keys; and a decode step at position L-1 (T = 1, positions = L - 1) against the
+    cache of those rotated keys equals prefill row L-1."""
+    w = small(B=2, T=300, name="rope_layer")
+    base = 10000.0
+    inp, wk, wv, d, r, out = qkv_case(w, base)
+    dev = "cuda"
+    slots = G.attn_prefill(d, {"q_routed": out["q_routed"].to(dev), "q_shared": out["q_shared"].to(dev)},
+                           out["k"].to(dev), out["v"].to(dev), r["p_tilde"])
+    torch.cuda.synchronize()
+    gpu = dict(q_routed=out["q_routed"], q_shared=out["q_shared"], out=slots.cpu())
+    agreed = dict(ptilde=r["p_tilde"].cpu().double().numpy())
+    check_prefill_given_q(w, dict(inp, k=out["k"], v=out["v"]), gpu, agreed, np.arange(w.B * w.T))
+    lens = torch.tensor([300, 41], dtype=torch.int32)
+    dw = w.replace(T=1, decode=True, L_max=300, name="rope_decode")
+    dd = G.desc_from(dw)
+    xs = inp["x"][torch.arange(2), lens.long() - 1].reshape(2, -1).to(dev)
+    rd = G.route(dd, xs, inp["w_router"].to(dev))
+    qd = G.qkv_proj(dd, xs, inp["w_q"].to(dev), wk.to(dev), wv.to(dev), rd, (lens - 1).to(dev), base)
+    dec = G.attn_decode(dd, qd, out["k"].to(dev), out["v"].to(dev), lens.to(dev), rd["p_tilde"])
+    torch.cuda.synchronize()
+    ref = slots.cpu().reshape(2, 300, d.S, w.d_head)[torch.arange(2), lens.long() - 1]
+    # the decode step's rotated K of the new token equals the prefill's at that position
+    assert torch.equal(qd["k"].cpu()[:, :, 0], out["k"][torch.arange(2), :, lens.long() - 1])
+    check_out(dw, dec.cpu().numpy(), ref.double().numpy(), "rotary decode vs prefill row")

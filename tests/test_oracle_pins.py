@@ -435,6 +435,34 @@ def test_output_projection_closed_forms_and_torch():
     np.testing.assert_allclose(oracle.out_proj_rows(dm, hm, wom), (torch.from_numpy(hm.reshape(n, -1)) @ wom.T).numpy(),
                                rtol=1e-12, atol=1e-13)
 
+# ---------------------------------------------------------------- rotary embedding (next-step row, reading)
+
+def test_rotary_embedding_pins():
+    """oracle.rope (the RoFormer rotary embedding with rotate-half pairing; the pages give no positional
+    encoding, so the form is a reading) against numpy's complex exponential, and its invariants: position 0
+    is the identity, each pair keeps its norm, pair 0 turns by the position in radians, rotations compose by
+    adding positions, and a score of a rotated query and key depends only on their relative position."""
+    rng = np.random.default_rng(3)
+    dh, base = 16, 10000.0
+    x = rng.standard_normal((6, dh))
+    pos = np.array([0, 1, 5, 100, 4095, 32767])
+    y = oracle.rope(x, pos, base)
+    freq = base ** (-2.0 * np.arange(dh // 2) / dh)
+    z = (x[:, :dh // 2] + 1j * x[:, dh // 2:]) * np.exp(1j * pos[:, None] * freq[None, :])
+    np.testing.assert_allclose(y, np.concatenate([z.real, z.imag], axis=1), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(y[0], x[0])
+    np.testing.assert_allclose(y[:, :8] ** 2 + y[:, 8:] ** 2, x[:, :8] ** 2 + x[:, 8:] ** 2, rtol=1e-12)
+    e = np.zeros((1, dh)); e[0, 0] = 1.0
+    r = oracle.rope(e, np.array([3]), base)
+    assert abs(r[0, 0] - np.cos(3.0)) < 1e-15 and abs(r[0, dh // 2] - np.sin(3.0)) < 1e-15
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, np.full(6, 7), base), pos, base),
+                               oracle.rope(x, pos + 7, base), rtol=1e-10, atol=1e-10)
+    q, k = rng.standard_normal((1, dh)), rng.standard_normal((1, dh))
+    for pq, pk, c in [(10, 3, 50), (0, 7, 1000), (300, 300, 12345)]:
+        s1 = float((oracle.rope(q, [pq], base) * oracle.rope(k, [pk], base)).sum())
+        s2 = float((oracle.rope(q, [pq + c], base) * oracle.rope(k, [pk + c], base)).sum())
+        assert abs(s1 - s2) < 1e-10 * (np.abs(q).sum() * np.abs(k).sum())
+
 # ---------------------------------------------------------------- decode
 
 def test_decode_equals_last_prefill_row():
