@@ -31,7 +31,9 @@ divided by the whole step's time).  The same JSON line carries:
   route_backward  the backward through slot assembly and routing
                 (gqe_route_backward) on the step's outputs, GB/s against HBM;
   attn_backward the attention backward (gqe_attn_backward) on the step's
-                query rows and slots, TFLOP/s against the bf16 peak.
+                query rows and slots, TFLOP/s against the bf16 peak;
+  proj_backward the projections' backward (gqe_qkv_proj_backward: dW_q,
+                dW_k, dW_v, dx) on the step's routing, against the bf16 peak.
 
 --graph also times the step replayed from one HIP graph of the four calls
 (on this stack replaying is not faster than launching them one by one).
@@ -460,6 +462,43 @@ def prefill_leg(w, inp, torch, dev, steps, traffic_key=None):
             "expert_rows": counts}
 
 
+def proj_backward_leg(p, torch, steps):
+    """The projections' backward (gqe_qkv_proj_backward) on the step's routing and x with seeded gradients of
+    q, K and V: dW_q, dW_k, dW_v and dx, each 2 * d_head * d_model * B*T * (k*G + 1 + 2*H_kv) FLOPs
+    (unselected experts cost nothing), against the bf16 peak."""
+    import workloads as W
+    w, G = p.w, p.G
+    dev = p.x.device
+    wk, wv = (t.to(dev) for t in W.make_w_kv(w))
+    gen = torch.Generator(device="cpu").manual_seed(13)
+    B, T, D = w.B, w.T, w.d_head
+    dqr = torch.randn((B, w.G, T * w.k, D), generator=gen).to(dev)
+    dqs = torch.randn((B, T, D), generator=gen).to(dev)
+    dk = torch.randn((B, w.G, T, D), generator=gen).to(dev)
+    dv = torch.randn((B, w.G, T, D), generator=gen).to(dev)
+    f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+    dwq, dwk, dwv, dx = f32(*p.wq.shape), f32(*wk.shape), f32(*wv.shape), f32(B * T, w.d_model)
+    nws = G.gqe_qkv_proj_backward_workspace_bytes(p.d, True)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    r = p.r
+
+    def bwd():
+        G.gqe_qkv_proj_backward(p.d, p.x, p.wq, wk, wv, r["sel"], r["counts"], r["offsets"], r["rows"], None, 0.0,
+                                dqr, dqs, dk, dv, dwq, dwk, dwv, dx, ws)
+
+    def bwd_dw():
+        G.gqe_qkv_proj_backward(p.d, p.x, p.wq, wk, wv, r["sel"], r["counts"], r["offsets"], r["rows"], None, 0.0,
+                                dqr, dqs, dk, dv, dwq, dwk, dwv, None, ws)
+
+    warm([bwd, bwd_dw], torch)
+    t, t_dw = time_calls([bwd, bwd_dw], steps, torch)
+    fl_one = 2.0 * D * w.d_model * B * T * (w.k * w.G + w.n_shared + 2 * w.G)
+    tf = 2 * fl_one / (t * 1e-3) / 1e12
+    return {"workload": w.name, "kernel": f"pb_dw_kernel<{D}> + pb_dx_kernel<{D}> (gqe_qkv_proj_backward)",
+            "us": t * 1e3, "dw_us": t_dw * 1e3, "dx_us": (t - t_dw) * 1e3, "tflops": tf,
+            "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": 2 * fl_one}
+
+
 def long_context_leg(torch, dev, steps):
     import workloads as W
     w = W.WORKLOADS["long_32k"]
@@ -612,6 +651,7 @@ def main():
     line["kv_proj"] = kv_proj_leg(p, torch, max(10, args.steps))
     line["route_backward"] = route_backward_leg(p, torch, max(10, args.steps))
     line["attn_backward"] = attn_backward_leg(p, torch, max(10, args.steps))
+    line["proj_backward"] = proj_backward_leg(p, torch, max(10, args.steps))
     del p
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -354,6 +354,45 @@ int gqe_qkv_proj(const gqe_desc* desc, const void* x, const void* w_q, const voi
                  void* stream);
 
 /*
+ * gqe_qkv_proj_backward -- gradients of the Q/K/V preamble's weights and of x,
+ * given the gradients of its outputs (from gqe_attn_backward): the backward
+ * of gqe_qkv_proj with the same routing, positions and rope_base.  With the
+ * kept sets fixed (each kept expert its own projection of x_t, GQE study note
+ * §3-2 (2); unselected experts get no gradient) and R_t the rotary embedding
+ * of the forward (identity when rope_base = 0):
+ *   dw_q[n] = sum over tokens t that kept n of (R_t^T dq_{t,n})^T x_t,
+ *   dw_q[N] = sum over t of (R_t^T dq_sh_t)^T x_t,
+ *   dw_k[h] = sum_t (R_t^T dk_{t,h})^T x_t,   dw_v[h] = sum_t dv_{t,h}^T x_t,
+ *   dx_t = sum_{kept n} W_q[n]^T R_t^T dq_{t,n} + W_q[N]^T R_t^T dq_sh_t
+ *          + sum_h (W_k[h]^T R_t^T dk_{t,h} + W_v[h]^T dv_{t,h}).
+ * (The router's share of dx comes from gqe_route_backward; add the two.)
+ * bf16 only (GQE_ERR_UNSUPPORTED for fp32): the fp32 gradients are rotated
+ * back in fp32 and rounded to bf16 for the MFMA products, which accumulate in
+ * fp32; deterministic (fixed order, no atomics).
+ * In:  x [BT, d_model], w_q [N + n_shared, d_head, d_model], w_k, w_v [H_kv,
+ *      d_head, d_model] (bf16); sel, counts, offsets, rows from gqe_route;
+ *      positions and rope_base as given to gqe_qkv_proj;
+ *      dq_routed [B, G, T*k, d_head] and dq_shared [B, T, d_head] fp32 (as
+ *      gqe_attn_backward gives them; dq_shared only with n_shared = 1);
+ *      dk, dv [B, H_kv, T, d_head] fp32, both or neither (NULL: the K/V
+ *      projections are left out, of dx too).
+ * Out (each may be NULL to skip it): dw_q [N + n_shared, d_head, d_model],
+ *      dw_k, dw_v [H_kv, d_head, d_model] (need dk, dv), dx [BT, d_model],
+ *      all fp32, every element written.
+ * Workspace: NULL, or gqe_qkv_proj_backward_workspace_bytes(desc, dk != NULL)
+ *      bytes (a smaller size returns GQE_ERR_WORKSPACE): with it the weight
+ *      gradient splits each head's rows into chunks, summed in chunk order
+ *      (the same definition; only the grouping of the fp32 sums differs), so
+ *      that the launch fills the chip.  No initialisation needed.
+ */
+size_t gqe_qkv_proj_backward_workspace_bytes(const gqe_desc* desc, int32_t with_kv);
+int gqe_qkv_proj_backward(const gqe_desc* desc, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                          const int32_t* sel, const int32_t* counts, const int32_t* offsets, const int32_t* rows,
+                          const int32_t* positions, float rope_base, const float* dq_routed, const float* dq_shared,
+                          const float* dk, const float* dv, float* dw_q, float* dw_k, float* dw_v, float* dx,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gqe_out_proj -- the attention output projection, fused with slot assembly.
  * The S slots of a token are concatenated in slot order into h_t (width
  * S*d_head) and passed through one linear map, y_t = W_o h_t, no bias (GQA

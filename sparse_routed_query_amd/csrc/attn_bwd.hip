@@ -36,32 +36,8 @@ constexpr int kAbTile = 64;
 __device__ __forceinline__ bf16x8 frag_row(const uint16_t* p) { return ld_bf16x8(p); }
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-// B fragment read across a row-major LDS tile M[k][n] (pitch in elements) with
-// two transposing reads.  Within each 16-lane group, lane i of
-// ds_read_b64_tr_b16 receives, as its element j, element i % 4 of the 8 bytes
-// that lane 4 j + i / 4 addresses; pointing lane 4 j + q at
-// M[k0 + 4 (l/32) + j][n + 4 q .. +3] gives lane l column n0 + l%32 and rows
-// k0 + 4 (l/32) + 0..3, then (second read) 8 rows further.  In the MFMA's k
-// order, rows 4-7 and 8-11 of each 16-row block are therefore swapped; the A
-// operand is stored with the same swap (kpos), so the products are unchanged.
-typedef short ab_s16x4 __attribute__((ext_vector_type(4)));
-typedef short ab_s16x8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* M, int pitch, int k0, int n0, int lane)
-{
-    typedef __attribute__((address_space(3))) ab_s16x4 lds_s16x4;
-    const int s16 = lane & 15;
-    const uint16_t* p = M + (k0 + 4 * (lane >> 5) + (s16 >> 2)) * pitch + n0 + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);
-    const ab_s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-    const ab_s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * pitch));
-    const ab_s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
-// storage position of contraction index k (0..63) in an A-operand tile read by frag_row
-__device__ __forceinline__ int kpos(int k)
-{
-    const int b = k & 12;
-    return b == 4 ? k + 4 : b == 8 ? k - 4 : k;
-}
+// frag_tr (gqe_device.h) reads fragments across a row-major tile; the A
+// operand read by frag_row is stored with the same k swap (kpos).
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, f2bf(f)); }
 

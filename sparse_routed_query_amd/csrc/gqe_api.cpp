@@ -355,6 +355,65 @@ int gqe_qkv_proj(const gqe_desc* desc, const void* x, const void* w_q, const voi
     return launch_status(gqe::launch_qkv_proj(a, (hipStream_t)stream));
 }
 
+size_t gqe_qkv_proj_backward_workspace_bytes(const gqe_desc* desc, int32_t with_kv)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK || !s.bf16 || s.BT == 0) return 0;
+    gqe::ProjBwdArgs a{};
+    a.B = s.B; a.T = s.T; a.d_model = s.dm; a.G = s.G; a.E = s.E; a.k = s.k; a.D = s.D; a.ns = s.ns;
+    a.nkv = with_kv ? s.G : 0;
+    return gqe::proj_bwd_workspace_bytes(a);
+}
+
+int gqe_qkv_proj_backward(const gqe_desc* desc, const void* x, const void* w_q, const void* w_k, const void* w_v,
+                          const int32_t* sel, const int32_t* counts, const int32_t* offsets, const int32_t* rows,
+                          const int32_t* positions, float rope_base, const float* dq_routed, const float* dq_shared,
+                          const float* dk, const float* dv, float* dw_q, float* dw_k, float* dw_v, float* dx,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!s.bf16) return GQE_ERR_UNSUPPORTED;
+    if (!(rope_base == 0.f || rope_base > 1.f) || !(rope_base < 3.0e38f)) return GQE_ERR_INVALID;
+    if ((dk == nullptr) != (dv == nullptr)) return GQE_ERR_INVALID;
+    if (!dk && (dw_k || dw_v)) return GQE_ERR_INVALID;
+    if (s.BT * s.G >= (1ll << 31) || s.BT * s.dm >= (1ll << 40)) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    if (!dw_q && !dw_k && !dw_v && !dx) return GQE_OK;
+    GQE_TRY(need(sel));
+    GQE_TRY(need(counts));
+    GQE_TRY(need(offsets));
+    GQE_TRY(need(rows));
+    GQE_TRY(maybe(positions));
+    GQE_TRY(need(dq_routed));
+    if (s.ns) GQE_TRY(need(dq_shared));
+    GQE_TRY(maybe(dk));
+    GQE_TRY(maybe(dv));
+    GQE_TRY(maybe(dw_q));
+    GQE_TRY(maybe(dw_k));
+    GQE_TRY(maybe(dw_v));
+    GQE_TRY(maybe(dx));
+    GQE_TRY(maybe(workspace));
+    if (dw_q || dw_k || dw_v) GQE_TRY(need(x));
+    if (dx) {
+        GQE_TRY(need(w_q));
+        if (dk) {
+            GQE_TRY(need(w_k));
+            GQE_TRY(need(w_v));
+        }
+    }
+    gqe::ProjBwdArgs a{};
+    a.x = (const uint16_t*)x; a.w_q = (const uint16_t*)w_q; a.w_k = (const uint16_t*)w_k;
+    a.w_v = (const uint16_t*)w_v; a.sel = sel; a.counts = counts; a.offsets = offsets; a.rows = rows;
+    a.positions = positions; a.dq_routed = dq_routed; a.dq_shared = dq_shared; a.dk = dk; a.dv = dv;
+    a.dw_q = dw_q; a.dw_k = dw_k; a.dw_v = dw_v; a.dx = dx;
+    a.B = s.B; a.T = s.T; a.d_model = s.dm; a.G = s.G; a.E = s.E; a.k = s.k; a.D = s.D; a.ns = s.ns;
+    a.nkv = dk ? s.G : 0;
+    a.rope_log2_base = rope_base > 0.f ? log2((double)rope_base) : 0.0;
+    if (workspace && workspace_bytes < gqe::proj_bwd_workspace_bytes(a)) return GQE_ERR_WORKSPACE;
+    return launch_status(gqe::launch_proj_bwd(a, workspace, workspace_bytes, (hipStream_t)stream));
+}
+
 int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_o, float* y,
                  int32_t write_weighted, void* stream)
 {

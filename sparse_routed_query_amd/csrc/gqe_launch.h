@@ -112,6 +112,34 @@ struct QkvProjArgs {
 };
 int launch_qkv_proj(const QkvProjArgs& a, hipStream_t st);
 
+// Backward of the Q/K/V projections.  Heads: [0, N) routed experts, ns shared,
+// nkv K heads, nkv V heads (nkv = 0 when dk / dv are not given).
+struct ProjBwdArgs {
+    const uint16_t* x;          // [B*T, d_model] bf16
+    const uint16_t* w_q;        // [N + ns, D, d_model]
+    const uint16_t* w_k;        // [H_kv, D, d_model]
+    const uint16_t* w_v;
+    const int32_t* sel;
+    const int32_t* counts;
+    const int32_t* offsets;
+    const int32_t* rows;
+    const int32_t* positions;   // [B*T] or NULL (t)
+    const float* dq_routed;     // [B, G, T*k, D]
+    const float* dq_shared;     // [B, T, D]
+    const float* dk;            // [B, H_kv, T, D]
+    const float* dv;
+    float* dw_q;                // [N + ns, D, d_model] or NULL
+    float* dw_k;                // [H_kv, D, d_model] or NULL
+    float* dw_v;
+    float* dx;                  // [B*T, d_model] or NULL
+    int B, T, d_model, G, E, k, D, ns, nkv;
+    double rope_log2_base;      // > 0: the forward rotated q and K
+};
+// Bytes of workspace that let the weight gradient split each head's rows into
+// chunks (0: one chunk is enough).
+size_t proj_bwd_workspace_bytes(const ProjBwdArgs& a);
+int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st);
+
 struct PrefillArgs {
     const void* q_routed;   // NULL: the routed heads are not computed by this call
     const void* q_shared;   // NULL: the shared head is not computed by this call

@@ -72,20 +72,11 @@ __device__ __forceinline__ size_t qp_dst(const QpArgs& a, int kind, int h, int n
     return ((((size_t)b * a.G + g) * a.T + t) * a.k + j) * d_head;
 }
 
-// Rotary frequency of pair i of a d_head-wide row, base^(-2i/d_head), in
-// double (a float exponent would move the angle of a far position by ~1e-3).
 __device__ __forceinline__ double qp_rope_freq(int i, int d_head, double log2_base)
 {
-    return exp2(-(double)(2 * i) / (double)d_head * log2_base);
+    return rope_freq(i, d_head, log2_base);
 }
-// The angle pos * freq reduced to [-pi, pi] in double, so that fp32 sin and
-// cos keep full accuracy at any position.
-__device__ __forceinline__ float qp_rope_angle(int pos, double freq)
-{
-    const double a = (double)pos * freq;
-    const double two_pi = 6.283185307179586476925;
-    return (float)(a - two_pi * rint(a * (1.0 / two_pi)));
-}
+__device__ __forceinline__ float qp_rope_angle(int pos, double freq) { return rope_angle(pos, freq); }
 
 // Work order.  Expert n has c_n = ceil(M_n / BM) row tiles (M_N = B*T for
 // the shared head).  Tiles are ordered in rounds r = 0..R-1, R = max c_n:

@@ -32,7 +32,8 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_prefill_heads", "gqe_assemble", "gqe_out_proj", "gqe_decode_workspace_bytes", "gqe_attn_decode",
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
            "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
-           "gqe_attn_decode_noalloc", "gqe_qkv_proj")
+           "gqe_attn_decode_noalloc", "gqe_qkv_proj", "gqe_qkv_proj_backward",
+           "gqe_qkv_proj_backward_workspace_bytes")
 
 
 class GqeError(RuntimeError):
@@ -131,6 +132,11 @@ def load():
         lib.gqe_attn_decode.restype = I
         lib.gqe_qkv_proj.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P]
         lib.gqe_qkv_proj.restype = I
+        lib.gqe_qkv_proj_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P,
+                                              Z, P]
+        lib.gqe_qkv_proj_backward.restype = I
+        lib.gqe_qkv_proj_backward_workspace_bytes.argtypes = [D, ctypes.c_int32]
+        lib.gqe_qkv_proj_backward_workspace_bytes.restype = Z
         lib.gqe_attn_decode_noalloc.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P]
         lib.gqe_attn_decode_noalloc.restype = I
         i32 = ctypes.c_int32
@@ -378,6 +384,42 @@ def gqe_qkv_proj(desc, x, w_q, w_k, w_v, sel, counts, offsets, rows, positions, 
                              _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"),
                              _ptr(v, dt, "v"), _stream(stream))
     _check("gqe_qkv_proj", rc)
+
+
+def gqe_qkv_proj_backward_workspace_bytes(desc, with_kv: bool) -> int:
+    return load().gqe_qkv_proj_backward_workspace_bytes(ctypes.byref(desc), int(bool(with_kv)))
+
+
+def gqe_qkv_proj_backward(desc, x, w_q, w_k, w_v, sel, counts, offsets, rows, positions, rope_base, dq_routed,
+                          dq_shared, dk, dv, dw_q, dw_k, dw_v, dx, workspace=None, stream=None):
+    """Gradients of the projection weights and of x from the gradients of q, K and V."""
+    dt = desc.torch_dtype
+    f = torch.float32
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().gqe_qkv_proj_backward(
+        ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_q, dt, "w_q"), _ptr(w_k, dt, "w_k"), _ptr(w_v, dt, "w_v"),
+        _ptr(sel, torch.int32, "sel"), _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(rows, torch.int32, "rows"), _ptr(positions, torch.int32, "positions"), float(rope_base),
+        _ptr(dq_routed, f, "dq_routed"), _ptr(dq_shared, f, "dq_shared"), _ptr(dk, f, "dk"), _ptr(dv, f, "dv"),
+        _ptr(dw_q, f, "dw_q"), _ptr(dw_k, f, "dw_k"), _ptr(dw_v, f, "dw_v"), _ptr(dx, f, "dx"),
+        _ptr(workspace, None, "workspace"), ws_bytes, _stream(stream))
+    _check("gqe_qkv_proj_backward", rc)
+
+
+def qkv_proj_backward(desc, x, w_q, w_k, w_v, r: dict, dq_routed, dq_shared, dk=None, dv=None, positions=None,
+                      rope_base=0.0, use_workspace=True, stream=None) -> dict:
+    """Allocating wrapper: dw_q, dw_k, dw_v (with dk, dv) and dx, fp32."""
+    dev = x.device
+    nws = gqe_qkv_proj_backward_workspace_bytes(desc, dk is not None) if use_workspace else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+    f = torch.float32
+    dw_q = torch.empty(tuple(w_q.shape), dtype=f, device=dev)
+    dw_k = torch.empty(tuple(w_k.shape), dtype=f, device=dev) if dk is not None else None
+    dw_v = torch.empty(tuple(w_v.shape), dtype=f, device=dev) if dk is not None else None
+    dx = torch.empty((desc.B * desc.T, desc.d_model), dtype=f, device=dev)
+    gqe_qkv_proj_backward(desc, x, w_q, w_k, w_v, r["sel"], r["counts"], r["offsets"], r["rows"], positions, rope_base,
+                          dq_routed, dq_shared, dk, dv, dw_q, dw_k, dw_v, dx, ws, stream)
+    return dict(dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dx=dx)
 
 
 def gqe_attn_decode_noalloc(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, stream=None):

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n

@@ -748,3 +748,83 @@ def test_expert_importance(zipf):
     # a zero router spreads it evenly
     r0 = oracle.route(d, inp["x"], np.zeros_like(inp["w_router"].double().numpy()))
     np.testing.assert_allclose(oracle.expert_importance(d, r0["probs"]), BT / E, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- projections' backward (next-step row)
+
+def _proj_case(rope_base, k=1, H_q=6, H_kv=3):
+    from oracle.proj_backward import qkv_proj_backward
+    w = wl(H_q=H_q, H_kv=H_kv, k=k, B=2, T=5, d_model=8, d_head=4)
+    inp = W.make_inputs(w)
+    wk, wv = W.make_w_kv(w)
+    sel = oracle.route(oracle.desc(w), inp["x"], inp["w_router"])["sel"]
+    rng = np.random.default_rng(11)
+    B, T, G, D = w.B, w.T, w.G, w.d_head
+    dqr = rng.standard_normal((B, G, T * w.k, D))
+    dqs = rng.standard_normal((B, T, D))
+    dk, dv = rng.standard_normal((B, G, T, D)), rng.standard_normal((B, G, T, D))
+    pos = rng.integers(0, 50, B * T)
+    x, wq = inp["x"].double().numpy().reshape(B * T, -1), inp["w_q"].double().numpy()
+    wkn, wvn = wk.double().numpy(), wv.double().numpy()
+    g = qkv_proj_backward(w, x, wq, wkn, wvn, sel, dqr, dqs, dk, dv, pos, rope_base)
+    d = oracle.desc(w)
+
+    def loss(x_, wq_, wk_, wv_):
+        # the forward through the C oracle's projections and its rotation
+        qr, qs = oracle.qproj_rows(d, x_, wq_, sel)                    # [BT, G, k, D], [BT, D]
+        K = oracle.kv_proj(d, x_, wk_)                                  # [B, H, T, D]
+        V = oracle.kv_proj(d, x_, wv_)
+        if rope_base:
+            qr = oracle.rope(qr, pos, rope_base)
+            qs = oracle.rope(qs, pos, rope_base)
+            K = oracle.rope(K, np.broadcast_to(pos.reshape(B, 1, T), K.shape[:-1]), rope_base)
+        dq_tok = dqr.reshape(B, G, T, w.k, D).transpose(0, 2, 1, 3, 4).reshape(B * T, G, w.k, D)
+        return float((qr * dq_tok).sum() + (qs * dqs.reshape(B * T, D)).sum() + (K * dk).sum() + (V * dv).sum())
+
+    return w, sel, x, wq, wkn, wvn, g, loss
+
+
+@pytest.mark.parametrize("rope_base", [0.0, 100.0])
+def test_projection_backward_matches_finite_differences(rope_base):
+    """oracle.proj_backward (fp64 autograd) against central differences of the loss through the C oracle's
+    projections and rotation, for entries of x and of every weight; the loss is bilinear in (x, W), so the
+    differences are exact up to rounding.  Experts no token kept get exactly zero weight gradient."""
+    w, sel, x, wq, wk, wv, g, loss = _proj_case(rope_base)
+    h = 1e-3
+    args = [x, wq, wk, wv]
+    for ai, name, idx in [(0, "dx", (3, 5)), (0, "dx", (9, 0)), (1, "dw_q", (0, 1, 2)), (1, "dw_q", (4, 3, 7)),
+                          (1, "dw_q", (w.N, 2, 6)), (2, "dw_k", (1, 0, 4)), (3, "dw_v", (2, 3, 1))]:
+        plus = [a.copy() for a in args]; minus = [a.copy() for a in args]
+        plus[ai][idx] += h; minus[ai][idx] -= h
+        fd = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert abs(fd - g[name][idx]) <= 1e-9 * max(1.0, abs(fd)), (name, idx, fd, g[name][idx])
+    kept = np.zeros(w.N, dtype=bool)
+    kept[(np.arange(w.G)[None, :, None] * w.E + sel).reshape(-1)] = True
+    for n in range(w.N):
+        if not kept[n]:
+            assert not g["dw_q"][n].any()
+
+
+def test_projection_backward_all_experts_kept_is_a_plain_matmul():
+    """With k = E every token keeps every expert and no rotation: dW_q[n] = dq_n^T X, dx = sum_n dq_n W_q[n]
+    + the K/V terms, as plain matrix products (torch fp64)."""
+    w, sel, x, wq, wk, wv, g, _ = _proj_case(0.0, k=2, H_q=6, H_kv=3)
+    from oracle.proj_backward import qkv_proj_backward  # noqa: F401  (the case above already ran it)
+    B, T, G, E, D = w.B, w.T, w.G, w.E, w.d_head
+    rng = np.random.default_rng(11)
+    dqr = rng.standard_normal((B, G, T * w.k, D))
+    dqs = rng.standard_normal((B, T, D))
+    dk, dv = rng.standard_normal((B, G, T, D)), rng.standard_normal((B, G, T, D))
+    # with k = E the kept experts of a group, in ascending order, are all of them: j = e
+    assert (np.sort(sel, axis=-1) == np.arange(E)).all()
+    dq_tok = dqr.reshape(B, G, T, E, D).transpose(0, 2, 1, 3, 4).reshape(B * T, G * E, D)   # expert n = g E + e
+    X = torch.from_numpy(x)
+    for n in range(w.N):
+        np.testing.assert_allclose(g["dw_q"][n], (torch.from_numpy(dq_tok[:, n]).T @ X).numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dw_q"][w.N], (torch.from_numpy(dqs.reshape(B * T, D)).T @ X).numpy(), rtol=1e-12,
+                               atol=1e-12)
+    dk_tok = dk.transpose(0, 2, 1, 3).reshape(B * T, G, D)
+    dv_tok = dv.transpose(0, 2, 1, 3).reshape(B * T, G, D)
+    dx = sum(dq_tok[:, n] @ wq[n] for n in range(w.N)) + dqs.reshape(B * T, D) @ wq[w.N]
+    dx = dx + sum(dk_tok[:, h] @ wk[h] + dv_tok[:, h] @ wv[h] for h in range(G))
+    np.testing.assert_allclose(g["dx"], dx, rtol=1e-12, atol=1e-12)
