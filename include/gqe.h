@@ -456,6 +456,31 @@ int gqe_check_decode_inputs(const gqe_desc* desc, const int32_t* lens, int32_t L
                             const int32_t* block_table, int32_t num_pages, int32_t page_size,
                             int32_t max_pages, int32_t* bad, void* stream);
 
+/*
+ * gqe_decode_route_qproj -- the decode step's routing and query projection in
+ * one launch, for one new token per sequence (desc->T == 1): what gqe_route
+ * and gqe_qproj compute for it (GQE study note §3-2 (2), (4), (5): scores,
+ * in-group softmax, the top k with lower-index ties, the weights renormalised
+ * over the kept ones -- route mode 3: not renormalised --, then only the kept
+ * experts' and the shared head's query rows), without the compaction, which
+ * decode does not need.  bf16 scores are exact products added in double in a
+ * fixed tree order (gqe_route instead adds fp32 partial sums of up to 32
+ * products, so the two can differ by that rounding and split a near-tie
+ * differently; each agrees with the exact score to well under 1e-6);
+ * fp32 scores take gqe_route's fp64 FMA chain, bit for bit.  Each query
+ * row is an fp32 sum rounded once (bf16).
+ * Optional rotary embedding of the query rows (as gqe_qkv_proj) at
+ * positions[b] (required when rope_base > 1; a decode step passes lens - 1).
+ * In:  x [B, d_model], w_router [N, d_model], b_router [N] or NULL,
+ *      w_q [N + n_shared, d_head, d_model] (dtype).
+ * Out: sel [B, G, k] int32, p_tilde [B, G, k] fp32, q_routed [B, G, 1, k,
+ *      d_head], q_shared [B, 1, d_head] (n_shared = 1), logits [B, N] fp64
+ *      or NULL.
+ */
+int gqe_decode_route_qproj(const gqe_desc* desc, const void* x, const void* w_router, const float* b_router,
+                           const void* w_q, const int32_t* positions, float rope_base, int32_t* sel, float* p_tilde,
+                           void* q_routed, void* q_shared, double* logits, void* stream);
+
 /* Bytes of device workspace gqe_attn_decode needs for a cache of L_max positions. */
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max);
 

@@ -465,6 +465,35 @@ int gqe_attn_decode(const gqe_desc* desc, const void* q_routed, const void* q_sh
     return launch_status(gqe::launch_decode(a, (hipStream_t)stream));
 }
 
+int gqe_decode_route_qproj(const gqe_desc* desc, const void* x, const void* w_router, const float* b_router,
+                           const void* w_q, const int32_t* positions, float rope_base, int32_t* sel, float* p_tilde,
+                           void* q_routed, void* q_shared, double* logits, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (s.T != 1) return GQE_ERR_INVALID;
+    if (!(rope_base == 0.f || rope_base > 1.f) || !(rope_base < 3.0e38f)) return GQE_ERR_INVALID;
+    if (rope_base > 0.f && !positions) return GQE_ERR_INVALID;
+    if (s.B == 0) return GQE_OK;
+    GQE_TRY(need(x));
+    GQE_TRY(need(w_router));
+    GQE_TRY(maybe(b_router));
+    GQE_TRY(need(w_q));
+    GQE_TRY(maybe(positions));
+    GQE_TRY(need(sel));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(q_routed));
+    if (s.ns) GQE_TRY(need(q_shared));
+    GQE_TRY(maybe(logits));
+    gqe::DecodePreArgs a{};
+    a.x = x; a.w_router = w_router; a.b_router = b_router; a.w_q = w_q; a.positions = positions; a.sel = sel;
+    a.p_tilde = p_tilde; a.q_routed = q_routed; a.q_shared = s.ns ? q_shared : nullptr; a.logits = logits;
+    a.B = s.B; a.d_model = s.dm; a.G = s.G; a.E = s.E; a.k = s.k; a.d_head = s.D; a.bf16 = s.bf16;
+    a.renorm = s.mode != 3;
+    a.rope_log2_base = rope_base > 0.f ? log2((double)rope_base) : 0.0;
+    return launch_status(gqe::launch_decode_preamble(a, (hipStream_t)stream));
+}
+
 int gqe_attn_decode_noalloc(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k_cache,
                             const void* v_cache, int32_t L_max, const int32_t* lens, const float* p_tilde, float* out,
                             void* stream)

@@ -192,6 +192,23 @@ struct DecodeArgs {
     const int32_t* block_table = nullptr;
     int page_shift = 0, max_pages = 0, num_pages = 0;
 };
+struct DecodePreArgs {
+    const void* x;            // [B, d_model]
+    const void* w_router;     // [N, d_model]
+    const float* b_router;    // [N] or NULL
+    const void* w_q;          // [N + n_shared, d_head, d_model]
+    const int32_t* positions; // [B] rotary positions (needed when rope_log2_base > 0)
+    int32_t* sel;             // [B, G, k]
+    float* p_tilde;           // [B, G, k]
+    void* q_routed;           // [B, G, 1, k, d_head]
+    void* q_shared;           // [B, 1, d_head] or NULL (no shared head)
+    double* logits;           // [B, N] or NULL
+    int B, d_model, G, E, k, d_head;
+    bool bf16, renorm;
+    double rope_log2_base;
+};
+int launch_decode_preamble(const DecodePreArgs& a, hipStream_t st);
+
 size_t decode_workspace_bytes(int B, int G, int k, int n_shared, int d_head, int L_max, bool bf16);
 // Size of the static device array gqe_attn_decode_noalloc keeps its partials in.
 constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;

@@ -33,7 +33,7 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
            "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
            "gqe_attn_decode_noalloc", "gqe_qkv_proj", "gqe_qkv_proj_backward",
-           "gqe_qkv_proj_backward_workspace_bytes")
+           "gqe_qkv_proj_backward_workspace_bytes", "gqe_decode_route_qproj")
 
 
 class GqeError(RuntimeError):
@@ -135,6 +135,8 @@ def load():
         lib.gqe_qkv_proj_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P, P,
                                               Z, P]
         lib.gqe_qkv_proj_backward.restype = I
+        lib.gqe_decode_route_qproj.argtypes = [D, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P]
+        lib.gqe_decode_route_qproj.restype = I
         lib.gqe_qkv_proj_backward_workspace_bytes.argtypes = [D, ctypes.c_int32]
         lib.gqe_qkv_proj_backward_workspace_bytes.restype = Z
         lib.gqe_attn_decode_noalloc.argtypes = [D, P, P, P, P, ctypes.c_int32, P, P, P, P]
@@ -386,6 +388,34 @@ def gqe_qkv_proj(desc, x, w_q, w_k, w_v, sel, counts, offsets, rows, positions, 
     _check("gqe_qkv_proj", rc)
 
 
+def gqe_decode_route_qproj(desc, x, w_router, b_router, w_q, positions, rope_base, sel, p_tilde, q_routed, q_shared,
+                           logits=None, stream=None):
+    """Routing and query projection of one new token per sequence in one launch (desc.T == 1)."""
+    dt = desc.torch_dtype
+    rc = load().gqe_decode_route_qproj(ctypes.byref(desc), _ptr(x, dt, "x"), _ptr(w_router, dt, "w_router"),
+                                       _ptr(b_router, torch.float32, "b_router"), _ptr(w_q, dt, "w_q"),
+                                       _ptr(positions, torch.int32, "positions"), float(rope_base),
+                                       _ptr(sel, torch.int32, "sel"), _ptr(p_tilde, torch.float32, "p_tilde"),
+                                       _ptr(q_routed, dt, "q_routed"), _ptr(q_shared, dt, "q_shared"),
+                                       _ptr(logits, torch.float64, "logits"), _stream(stream))
+    _check("gqe_decode_route_qproj", rc)
+
+
+def decode_route_qproj(desc, x, w_router, b_router, w_q, positions=None, rope_base=0.0, logits=False,
+                       stream=None) -> dict:
+    """Allocating wrapper: sel, p_tilde, q_routed, q_shared (and logits) of one new token per sequence."""
+    dev = x.device
+    B, G, k, D = desc.B, desc.H_kv, desc.k, desc.d_head
+    res = dict(sel=torch.empty((B, G, k), dtype=torch.int32, device=dev),
+               p_tilde=torch.empty((B, G, k), dtype=torch.float32, device=dev),
+               q_routed=torch.empty((B, G, 1, k, D), dtype=desc.torch_dtype, device=dev),
+               q_shared=torch.empty((B, 1, D), dtype=desc.torch_dtype, device=dev) if desc.n_shared else None,
+               logits=torch.empty((B, desc.H_q), dtype=torch.float64, device=dev) if logits else None)
+    gqe_decode_route_qproj(desc, x, w_router, b_router, w_q, positions, rope_base, res["sel"], res["p_tilde"],
+                           res["q_routed"], res["q_shared"], res["logits"], stream)
+    return res
+
+
 def gqe_qkv_proj_backward_workspace_bytes(desc, with_kv: bool) -> int:
     return load().gqe_qkv_proj_backward_workspace_bytes(ctypes.byref(desc), int(bool(with_kv)))
 
@@ -542,9 +572,18 @@ def prefill(desc, x, w_router, b_router, w_q, k, v, logits=False, stream=None) -
     return dict(r, **q, out=out)
 
 
-def decode(desc, x, w_router, b_router, w_q, k_cache, v_cache, lens, stream=None) -> dict:
-    """Whole decode step for one new token per sequence (desc.T == 1)."""
-    r = route(desc, x, w_router, b_router, stream=stream)
-    q = qproj(desc, x, w_q, r, stream=stream)
+def decode(desc, x, w_router, b_router, w_q, k_cache, v_cache, lens, positions=None, rope_base=0.0,
+           fused=True, stream=None) -> dict:
+    """Whole decode step for one new token per sequence (desc.T == 1): routing and query projection in one
+    launch (gqe_decode_route_qproj), then the attention.  fused=False takes gqe_route + gqe_qproj instead
+    (no rotary embedding there)."""
+    if fused:
+        r = decode_route_qproj(desc, x, w_router, b_router, w_q, positions, rope_base, logits=True, stream=stream)
+        q = dict(q_routed=r.pop("q_routed"), q_shared=r.pop("q_shared"))
+    else:
+        if rope_base:
+            raise ValueError("the rotary embedding needs the fused decode preamble")
+        r = route(desc, x, w_router, b_router, logits=True, stream=stream)
+        q = qproj(desc, x, w_q, r, stream=stream)
     out = attn_decode(desc, q, k_cache, v_cache, lens, r["p_tilde"], stream=stream)
     return dict(r, **q, out=out)

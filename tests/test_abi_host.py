@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -314,6 +314,27 @@ def test_route_backward_rejects_the_weighted_concat_mode():
     rc = lib.gqe_route_backward(ctypes.byref(d), A16, A16, A16, A16, A16, A16, A16, A16, None, None, None, None, 0,
                                 None)
     assert rc == UNSUPPORTED
+
+
+def test_decode_route_qproj_rejects_prefill_shapes_bad_rope_base_and_pointers():
+    lib = G.load()
+
+    def rc(d, base=0.0, positions=None, x=A16, qs=A16, sel=A16):
+        return lib.gqe_decode_route_qproj(ctypes.byref(d), x, A16, None, A16, positions, ctypes.c_float(base), sel,
+                                          A16, A16, qs, None, None)
+
+    dec = main(B=64, T=1)
+    assert rc(main()) == INVALID                 # T = 4096: one token per sequence only
+    assert rc(main(B=64, T=2)) == INVALID
+    assert rc(dec, 10000.0) == INVALID           # rotation needs the positions
+    assert rc(dec, 1.0, A16) == INVALID
+    assert rc(dec, float("nan"), A16) == INVALID
+    assert rc(dec, float("inf"), A16) == INVALID
+    assert rc(dec, x=None) == INVALID
+    assert rc(dec, sel=None) == INVALID
+    assert rc(dec, qs=None) == INVALID           # the shared head is on
+    assert rc(dec, 10000.0, MIS) == ALIGN
+    assert rc(main(B=0, T=1), x=None) == OK      # empty batch: nothing to do, no pointer read
 
 
 def test_qkv_proj_rejects_bad_rope_base_and_pointers():

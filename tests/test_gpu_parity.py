@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_parity_util import (check_out, check_prefill_given_q, check_qproj, check_route, full_decode_check,
+from gpu_parity_util import (LOGIT_TOL, PT_TOL, agreed_routing, check_out, check_prefill_given_q, check_qproj,
+                             check_route, full_decode_check,
                              full_prefill_check, gpu_decode, gpu_prefill, say)
 import sparse_routed_query_amd.gqe as G
 
@@ -383,6 +384,106 @@ def test_large_scores_move_the_softmax_reference():
     tok = np.arange(w.B * w.T)
     check_qproj(w, inp, gpu, agreed, tok)
     check_prefill_given_q(w, inp, gpu, agreed, tok)
+
+
+# ---------------------------------------------------------------- decode: routing + query projection, one launch
+
+def decode_pre(w, inp, positions=None, base=0.0):
+    d = G.desc_from(w)
+    dev = "cuda"
+    x = inp["x"].reshape(w.B, w.d_model).to(dev)
+    br = inp["b_router"].to(dev) if inp["b_router"] is not None else None
+    pos = positions.to(dev) if positions is not None else None
+    res = G.decode_route_qproj(d, x, inp["w_router"].to(dev), br, inp["w_q"].to(dev), pos, base, logits=True)
+    torch.cuda.synchronize()
+    return {k: (v.cpu() if v is not None else None) for k, v in res.items()}
+
+
+def check_decode_pre(w, inp, got, positions=None, base=0.0):
+    """Routing against oracle.route (GPU choice accepted only at a flagged tie), logits and p~ within the
+    routing tolerances, query rows against the oracle's projection of the agreed selection (rotated by
+    oracle.rope when base > 1)."""
+    od = oracle.desc(w)
+    orc = oracle.route(od, inp["x"].reshape(w.B, w.d_model), inp["w_router"], inp["b_router"])
+    sel, pt, n_sub = agreed_routing(w, orc, got["sel"].numpy())
+    dlog = float(np.abs(got["logits"].numpy() - orc["logits"]).max())
+    dpt = float(np.abs(got["p_tilde"].numpy().astype(np.float64) - pt).max())
+    say(f"[{w.name}] decode preamble route: tie-substituted={n_sub} max|dlogit|={dlog:.3e} max|dp~|={dpt:.3e}")
+    assert dlog < LOGIT_TOL and dpt <= PT_TOL
+    tok = np.arange(w.B)
+    qr, qs = oracle.qproj_rows(od, inp["x"], inp["w_q"], sel, tok)
+    pos = positions.numpy() if positions is not None else None
+    check_rotated(w, got["q_routed"][:, :, 0], qr, pos, base, "decode preamble q_routed")
+    if w.n_shared:
+        check_rotated(w, got["q_shared"][:, 0], qs, pos, base, "decode preamble q_shared")
+
+
+DEC_PRE = [decode_case(), decode_case(k=2, route_mode=1, name="dec_k2_mode1"),
+           decode_case(k=2, route_mode=2, name="dec_k2_hard_only"),
+           decode_case(k=2, route_mode=3, name="dec_k2_weighted_concat"),
+           decode_case(d_head=128, H_q=12, H_kv=3, k=3, name="dec_d128"),
+           decode_case(d_head=32, n_shared=0, name="dec_d32_noshared"),
+           decode_case(H_q=64, H_kv=1, k=8, d_model=320, name="dec_e64_k8"),
+           decode_case(dtype="f32", name="dec_f32"),
+           decode_case(dtype="f32", d_model=90, d_head=128, H_q=12, H_kv=4, k=2, name="dec_f32_dm90"),
+           decode_case(B=300, d_model=1024, H_q=16, H_kv=8, name="dec_b300"),
+           W.WORKLOADS["decode_b64"]]
+
+
+@pytest.mark.parametrize("w", DEC_PRE, ids=lambda w: w.name)
+def test_decode_route_qproj_against_the_oracle(w):
+    inp = W.make_inputs(w)
+    check_decode_pre(w, inp, decode_pre(w, inp))
+
+
+@pytest.mark.parametrize("w", [decode_case(name="dec_rope"), decode_case(d_head=128, k=2, name="dec_rope_d128"),
+                               decode_case(dtype="f32", d_head=32, name="dec_rope_f32")], ids=lambda w: w.name)
+def test_decode_route_qproj_rotary_against_the_oracle(w):
+    inp = W.make_inputs(w)
+    pos = (inp["lens"] - 1).to(torch.int32)
+    pos[0] = 65535          # a large position: the angle's rounding grows with it
+    for base in (10000.0, 500000.0):
+        check_decode_pre(w, inp, decode_pre(w, inp, pos, base), pos, base)
+
+
+@pytest.mark.parametrize("w", [decode_case(dtype="f32", name="dec_f32"),
+                               decode_case(dtype="f32", k=2, route_mode=3, name="dec_f32_mode3")],
+                         ids=lambda w: w.name)
+def test_decode_route_qproj_fp32_routing_is_gqe_routes_bit_for_bit(w):
+    """fp32 scores take gqe_route's own fp64 FMA chain, so logits, selection and p~ agree to the bit."""
+    inp = W.make_inputs(w)
+    got = decode_pre(w, inp)
+    dev = "cuda"
+    r = G.route(G.desc_from(w), inp["x"].reshape(w.B, w.d_model).to(dev), inp["w_router"].to(dev),
+                inp["b_router"].to(dev) if inp["b_router"] is not None else None, logits=True)
+    torch.cuda.synchronize()
+    for key in ("logits", "sel", "p_tilde"):
+        assert torch.equal(got[key], r[key].cpu()), key
+
+
+def test_fused_and_composed_decode_steps_agree():
+    """G.decode's one-launch preamble and gqe_route + gqe_qproj give the same slots (same selection; query
+    rows within one bf16 rounding of each other, so the slots within the decode tolerance)."""
+    w = W.WORKLOADS["decode_b64"]
+    inp = W.make_inputs(w)
+    d = G.desc_from(w)
+    di = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    args = (d, di["x"].reshape(w.B, w.d_model), di["w_router"], di["b_router"], di["w_q"], di["k_cache"],
+            di["v_cache"], di["lens"])
+    a, b = G.decode(*args), G.decode(*args, fused=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a["sel"], b["sel"])
+    check_out(w, a["out"].cpu().numpy(), b["out"].cpu().double().numpy(), "fused vs composed decode")
+
+
+def test_decode_route_qproj_empty_batch():
+    w = decode_case(B=0, name="dec_empty")
+    d = G.desc_from(w)
+    res = G.decode_route_qproj(d, torch.empty((0, w.d_model), dtype=torch.bfloat16, device="cuda"),
+                               torch.zeros((w.H_q, w.d_model), dtype=torch.bfloat16, device="cuda"), None,
+                               torch.zeros((w.H_q + 1, w.d_head, w.d_model), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert res["sel"].numel() == 0 and res["q_routed"].numel() == 0
 
 
 # ---------------------------------------------------------------- paged decode
