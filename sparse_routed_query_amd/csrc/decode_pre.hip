@@ -6,10 +6,10 @@
 // embedding of the queries at the token's position.
 //
 // One workgroup per (sequence, group) and one more per sequence for the
-// shared head.  The token's x row is read once into registers; scores are
-// exact products summed in double (fp32 inputs: one fp64 FMA chain per score
-// in index order, as gqe_route does); each kept expert's d_head x d_model
-// weight rows are read with 16-byte loads, 32 lanes per row, and reduced
+// shared head.  bf16 scores are exact products summed in double in a fixed
+// order (fp32: one fp64 FMA chain per score in index order, as gqe_route
+// does); the top k is picked in parallel by rank.  Each weight row is read by
+// 32 lanes with 16-byte loads, about 16 of them in flight a lane, and reduced
 // across those lanes in a fixed order.  With this launch a decode step is
 // route+project, then the attention: no compaction (decode needs none).
 #include "gqe_device.h"
@@ -40,21 +40,18 @@ template <typename ET, int D>
 __global__ __launch_bounds__(256) void decode_preamble_kernel(const DecodePreArgs a)
 {
     constexpr int VEC = 16 / sizeof(ET);          // elements per 16-byte load
-    constexpr int PER = 32 * VEC;                 // elements of a row one 32-lane group covers per pass
     const int b = blockIdx.x, gg = blockIdx.y;
     const int G = a.G, E = a.E, k = a.k, N = G * E, dm = a.d_model;
     const bool shared = gg == G;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int sub = tid & 31, grp = tid >> 5;     // 8 groups of 32 lanes
     const ET* xb = (const ET*)a.x + (size_t)b * dm;
-    __shared__ double s_red[4][kDpMaxE];
+    __shared__ double s_sc[kDpMaxE];
     __shared__ int s_sel[8];
-    __shared__ float s_q[8 + 1][D];
+    __shared__ float s_q[8][D];
 
     int nsel = 0;   // kept rows this workgroup projects
     if (!shared) {
         // ---- scores of the group's E experts
-        const float* bias = a.b_router ? a.b_router + gg * E : nullptr;
         if constexpr (sizeof(ET) == 4) {
             // fp32: one fp64 FMA chain per score, in index order (bit for bit gqe_route's)
             if (tid < E) {
@@ -62,70 +59,76 @@ __global__ __launch_bounds__(256) void decode_preamble_kernel(const DecodePreArg
                 const float* wr = (const float*)a.w_router + (size_t)(gg * E + tid) * dm;
                 double s = 0.0;
                 for (int i = 0; i < dm; ++i) s = fma((double)xr[i], (double)wr[i], s);
-                s_red[0][tid] = s;
+                s_sc[tid] = s;
             }
         } else {
-            // bf16: exact products added in double, each wave over a quarter of d_model,
-            // then the lanes and the waves in a fixed order
-            for (int e0 = 0; e0 < E; e0 += 4) {
-                double p[4] = {0.0, 0.0, 0.0, 0.0};
-                for (int i = tid; i < dm; i += 256) {
-                    const float xv = bf2f(((const uint16_t*)xb)[i]);
+            // bf16: four experts per wave at a time, each lane over 8-element chunks (d_model is a
+            // multiple of 64); exact products added in double, then the lanes in a fixed tree
+            const uint16_t* wq0 = (const uint16_t*)a.w_router + (size_t)gg * E * dm;
+            for (int e0 = 4 * wave; e0 < E; e0 += 16) {
+                double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+                for (int col = 8 * lane; col < dm; col += 512) {
+                    const u32x4 xv = ld_u32x4(xb + col);
+                    u32x4 wv[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        if (e0 + c < E)
-                            p[c] += (double)(xv * bf2f(((const uint16_t*)a.w_router)[(size_t)(gg * E + e0 + c) * dm + i]));
+                        wv[c] = e0 + c < E ? ld_u32x4(wq0 + (size_t)(e0 + c) * dm + col) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            acc[c] += (double)(dp_elem<uint16_t>(xv, i) * dp_elem<uint16_t>(wv[c], i));
                 }
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    double v = p[c];
+                    double v = acc[c];
 #pragma unroll
                     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-                    if (lane == 0 && e0 + c < E) s_red[wave][e0 + c] = v;
+                    if (lane == 0 && e0 + c < E) s_sc[e0 + c] = v;
                 }
             }
-            __syncthreads();
-            if (tid < E) s_red[0][tid] = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
-        }
-        // the bias and the logits output, one expert a thread
-        if (tid < E) {
-            const double v = s_red[0][tid] + (bias ? (double)bias[tid] : 0.0);
-            s_red[0][tid] = v;
-            if (a.logits) a.logits[(size_t)b * N + gg * E + tid] = v;
         }
         __syncthreads();
-        // ---- softmax, top-k (lower index wins ties), weights: one thread, scores read from LDS
-        if (tid == 0) {
-            const double* s = s_red[0];
-            uint64_t chosen = 0;
-            double mk = -INFINITY, ma = -INFINITY;
-            for (int r = 0; r < k; ++r) {
-                int best = -1;
-                double bv = 0.0;
-                for (int e = 0; e < E; ++e) {
-                    if ((chosen >> e) & 1) continue;
-                    if (best < 0 || s[e] > bv) { best = e; bv = s[e]; }
-                }
-                chosen |= 1ull << best;
-                mk = fmax(mk, bv);
+        // ---- bias, logits, then the selection in parallel (wave 0, one expert a lane): expert e is kept
+        // when fewer than k experts rank above it (higher score, or equal score and lower index), which is
+        // the k largest with lower-index ties; the kept ones are numbered in ascending index.
+        if (wave == 0) {
+            const bool live = lane < E;
+            double se = 0.0;
+            if (live) {
+                se = s_sc[lane] + (a.b_router ? (double)a.b_router[gg * E + lane] : 0.0);
+                if (a.logits) a.logits[(size_t)b * N + gg * E + lane] = se;
             }
-            for (int e = 0; e < E; ++e) ma = fmax(ma, s[e]);
+            // every lane's score, with the bias, from its owner lane
+            int rank = 0;
+            for (int f = 0; f < E; ++f) {
+                const double sf = __shfl(se, f);
+                rank += (sf > se) || (sf == se && f < lane);
+            }
+            const bool kept = live && rank < k;
+            const uint64_t mask = __ballot(kept);
+            double mk = kept ? se : -INFINITY, ma = live ? se : -INFINITY;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                mk = fmax(mk, __shfl_xor(mk, o));
+                ma = fmax(ma, __shfl_xor(ma, o));
+            }
             const double mref = a.renorm ? mk : ma;
+            const float ex = live ? expf((float)(se - mref)) : 0.f;
+            // the denominator in ascending index, the same in every lane: the kept terms (or, not
+            // renormalised, all E)
             float den = 0.f;
-            if (a.renorm) {
-                for (int e = 0; e < E; ++e)
-                    if ((chosen >> e) & 1) den += expf((float)(s[e] - mref));
-            } else {
-                for (int e = 0; e < E; ++e) den += expf((float)(s[e] - mref));
-            }
-            const size_t o = ((size_t)b * G + gg) * k;
-            int j = 0;
             for (int e = 0; e < E; ++e) {
-                if (!((chosen >> e) & 1)) continue;
-                a.sel[o + j] = e;
-                a.p_tilde[o + j] = expf((float)(s[e] - mref)) / den;
-                s_sel[j] = gg * E + e;
-                ++j;
+                const float v = __shfl(ex, e);
+                if (!a.renorm || ((mask >> e) & 1)) den += v;
+            }
+            if (kept) {
+                const int j = __popcll(mask & ((1ull << lane) - 1));
+                const size_t o = ((size_t)b * G + gg) * k + j;
+                a.sel[o] = lane;
+                a.p_tilde[o] = ex / den;
+                s_sel[j] = gg * E + lane;
             }
         }
         __syncthreads();
@@ -136,32 +139,54 @@ __global__ __launch_bounds__(256) void decode_preamble_kernel(const DecodePreArg
         nsel = 1;
     }
 
-    // ---- projections: each 32-lane group one weight row per pass, 8 rows at a time.
-    // 16-byte loads when d_model is a multiple of VEC (always for bf16, whose d_model is a
-    // multiple of 64): a lane's chunk is then wholly inside or past the row; else one element a lane.
+    // ---- projections: each 32-lane group owns rows grp, grp + 8, ... of the d_head rows of each kept
+    // expert (or the shared head); a sweep loads U column chunks of 16 bytes of each of its rows at once
+    // (about 16 loads in flight a lane), x's chunks alongside.  16-byte loads when d_model is a
+    // multiple of VEC (always for bf16, whose d_model is a multiple of 64): a lane's chunk is then wholly
+    // inside or past the row; else one element a lane.
+    constexpr int RPG = D / 8;                     // rows per 32-lane group
+    constexpr int U = RPG >= 16 ? 1 : 16 / RPG;    // column chunks per sweep
+    constexpr int PER = 32 * VEC;                  // columns one chunk of the 32 lanes covers
+    const int sub = tid & 31, grp = tid >> 5;
     const bool vec = dm % VEC == 0;
-    const int passes = (dm + PER - 1) / PER;
     for (int j = 0; j < nsel; ++j) {
-        const ET* w = (const ET*)a.w_q + (size_t)s_sel[j] * D * dm;
-        for (int d0 = 0; d0 < D; d0 += 8) {
-            const int d = d0 + grp;
-            float acc = 0.f;
-            if (vec) {
-                const ET* wr = w + (size_t)d * dm + sub * VEC;
-                for (int p = 0; p < passes; ++p) {
-                    if (sub * VEC + p * PER >= dm) break;
-                    const u32x4 wv = ld_u32x4(wr + p * PER);
-                    const u32x4 xv = ld_u32x4(xb + sub * VEC + p * PER);
+        const ET* w = (const ET*)a.w_q + ((size_t)s_sel[j] * D + grp) * dm;
+        float acc[RPG];
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) acc = fmaf(dp_elem<ET>(xv, i), dp_elem<ET>(wv, i), acc);
+        for (int i = 0; i < RPG; ++i) acc[i] = 0.f;
+        if (vec) {
+            for (int c0 = sub * VEC; c0 < dm; c0 += U * PER) {
+                u32x4 xv[U], wv[U][RPG];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int col = c0 + u * PER;
+                    const bool in = col < dm;
+                    xv[u] = in ? ld_u32x4(xb + col) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int i = 0; i < RPG; ++i)
+                        wv[u][i] = in ? ld_u32x4(w + (size_t)(8 * i) * dm + col) : u32x4{0u, 0u, 0u, 0u};
                 }
-            } else {
-                const ET* wr = w + (size_t)d * dm;
-                for (int i = sub; i < dm; i += 32) acc = fmaf(elem_f32(xb[i]), elem_f32(wr[i]), acc);
-            }
 #pragma unroll
-            for (int o = 16; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-            if (sub == 0) s_q[j][d] = acc;
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int i = 0; i < RPG; ++i)
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            acc[i] = fmaf(dp_elem<ET>(xv[u], e), dp_elem<ET>(wv[u][i], e), acc[i]);
+            }
+        } else {
+            for (int col = sub; col < dm; col += 32) {
+                const float xv = elem_f32(xb[col]);
+#pragma unroll
+                for (int i = 0; i < RPG; ++i) acc[i] = fmaf(xv, elem_f32(w[(size_t)(8 * i) * dm + col]), acc[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RPG; ++i) {
+            float v = acc[i];
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o);
+            if (sub == 0) s_q[j][grp + 8 * i] = v;
         }
     }
     __syncthreads();
