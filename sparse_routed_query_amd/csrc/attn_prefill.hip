@@ -514,11 +514,20 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 
     if (w.part >= 0) {
         // Split tile: publish this part's state, then take a ticket; the part
-        // that draws the second ticket merges, the first one is done.  The
-        // state moves with agent-scope stores and loads, each coherent across
-        // the XCDs' L2 caches on its own, so no fence has to write back or
-        // invalidate a whole L2; the wait below makes the stores complete
-        // before the ticket is taken.
+        // that draws the second ticket merges, the first one is done.
+        // Ordering, argued at the instruction level (the atomics are relaxed,
+        // so the HIP memory model alone does not give it): the agent-scope
+        // stores and loads are emitted with the device-scope cache bit (sc1),
+        // so a store is acknowledged only once it is visible device-wide and
+        // a load is served from the device-coherent level, never from a stale
+        // line of this XCD's L2; vmcnt counts stores on CDNA, so the wait
+        // below returns only after every state store of the wave has been
+        // acknowledged, and the barrier makes that true of all four waves
+        // before thread 0's ticket atomic is issued; the merging part issues
+        // its loads only after its own ticket has returned (through LDS and a
+        // barrier), i.e. after the other part's ticket and so after its
+        // acknowledged stores.  Release/acquire would add an L2 write-back
+        // and invalidate to every split tile (measured 3.5x slower).
         __shared__ int s_ticket;
         typedef unsigned long long u64;
         constexpr int NQ = D / 4;   // 8-byte words of output accumulators per thread
