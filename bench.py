@@ -389,10 +389,11 @@ def route_backward_leg(p, torch, steps):
 
 
 def attn_backward_leg(p, torch, steps):
-    """The attention backward (gqe_attn_backward) on the step's own query rows, K, V and slots with seeded slot
-    gradients.  Algorithmic work: the four products dV = P^T dO, dP = dO V^T, dq = dS K, dK = dS^T q over the
-    causal scores, twice the forward's attention FLOPs (recomputing S, which the implementation does twice,
-    is not counted); against the bf16 peak."""
+    """The attention backward on the step's own query rows, K, V and slots with seeded slot gradients, given
+    the forward's row statistics (gqe_attn_backward_lse; the forward that keeps them, and the backward that
+    recomputes them, timed beside it).  Algorithmic work: the four products dV = P^T dO, dP = dO V^T,
+    dq = dS K, dK = dS^T q over the causal scores, twice the forward's attention FLOPs (recomputing S, which
+    the implementation does in both kernels, is not counted); against the bf16 peak."""
     import workloads as W
     w, G = p.w, p.G
     BT, S, D, kG = w.B * w.T, p.d.S, w.d_head, w.k * w.G
@@ -404,16 +405,29 @@ def attn_backward_leg(p, torch, steps):
     dqr, dqs = f32(w.B, w.G, w.T * w.k, D), f32(w.B, w.T, D)
     dk, dv = f32(w.B, w.G, w.T, D), f32(w.B, w.G, w.T, D)
     ws = torch.empty(G.gqe_attn_backward_workspace_bytes(p.d), dtype=torch.uint8, device=p.x.device)
+    # the forward's row statistics, from the statistics-keeping attention call on the same rows
+    lse = torch.empty(G.lse_rows(p.d), dtype=torch.float32, device=p.x.device)
+    slots = torch.empty_like(out)
+    G.gqe_attn_prefill_heads_lse(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, slots, lse, p.ws)
 
     def bwd():
         G.gqe_attn_backward(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, out, d_hard, dout, dqr, dqs, dk, dv, ws)
 
-    warm([bwd], torch)
-    (t,) = time_calls([bwd], steps, torch)
+    def bwd_lse():
+        G.gqe_attn_backward_lse(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, out, d_hard, dout, lse, dqr, dqs, dk,
+                                dv, ws)
+
+    def fwd_lse():
+        G.gqe_attn_prefill_heads_lse(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, slots, lse, p.ws)
+
+    warm([bwd, bwd_lse, fwd_lse], torch)
+    t, t_lse, t_fwd = time_calls([bwd, bwd_lse, fwd_lse], steps, torch)
     fl = 2.0 * W.attention_flops(w)
-    tf = fl / (t * 1e-3) / 1e12
-    return {"workload": w.name, "kernel": "attn_bwd_dq_kernel<%d> + attn_bwd_dkdv_kernel<%d> (gqe_attn_backward)" % (D, D),
-            "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl}
+    tf = fl / (t_lse * 1e-3) / 1e12
+    return {"workload": w.name,
+            "kernel": "attn_bwd_dq_kernel<%d> + attn_bwd_dkdv_kernel<%d> (gqe_attn_backward_lse)" % (D, D),
+            "us": t_lse * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl,
+            "recompute_statistics_us": t * 1e3, "forward_keeping_statistics_us": t_fwd * 1e3}
 
 
 def ceilings_leg(torch, dev):

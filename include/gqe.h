@@ -223,6 +223,22 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
                            size_t workspace_bytes, void* stream);
 
 /*
+ * gqe_attn_prefill_heads_lse -- gqe_attn_prefill_heads (same slots, bit for
+ * bit) that also keeps each query row's softmax statistic for the backward:
+ *   lse[r] = log2 sum_s 2^(q_r . K_s log2(e) / sqrt(d_head))   (keys s as masked)
+ * i.e. the base-2 log of the softmax denominator of the attention equation
+ * (GQE study note §1-1), formed from the running reference and row sum the
+ * kernel already holds.  bf16 only (GQE_ERR_UNSUPPORTED for fp32).
+ * Out: lse [B*G*T*k + B*T] fp32: routed row t*k + j of (b, g) at
+ *      (b*G + g)*T*k + t*k + j, then shared row (b, t) at B*G*T*k + b*T + t;
+ *      only the rows this call computes are written.
+ * Everything else: as gqe_attn_prefill_heads.
+ */
+int gqe_attn_prefill_heads_lse(const gqe_desc* desc, const void* q_routed, const void* q_shared,
+                               const void* k, const void* v, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * gqe_assemble -- the weighted slot(s) of B*T output rows from their hard
  * slots (GQE study note §3-2 (4)):
  *   mode 0: out[t, kG]   = sum_g sum_j p~[t,g,j] out[t, g*k+j]
@@ -276,6 +292,19 @@ int gqe_attn_backward(const gqe_desc* desc, const void* q_routed, const void* q_
                       const void* v, const float* out, const float* d_hard, const float* dout,
                       float* dq_routed, float* dq_shared, float* dk, float* dv, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * gqe_attn_backward_lse -- gqe_attn_backward given the forward's row
+ * statistics (lse as gqe_attn_prefill_heads_lse wrote them, every row), so
+ * the pass that recomputes them from q K^T is skipped.  Same definitions and
+ * outputs; the results differ from gqe_attn_backward's only by the rounding
+ * of lse (forward's reference + log2 of its row sum, against the backward's
+ * recomputation).  lse is read, not written.  Workspace: as gqe_attn_backward.
+ */
+int gqe_attn_backward_lse(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                          const void* v, const float* out, const float* d_hard, const float* dout,
+                          const float* lse, float* dq_routed, float* dq_shared, float* dk, float* dv,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace gqe_route_backward needs when it computes dw_router. */
 size_t gqe_route_backward_workspace_bytes(const gqe_desc* desc);

@@ -84,4 +84,19 @@ def attention_backward(w, q_routed, q_shared, K, V, d_hard, dout, heads=None):
     return dict(dq_routed=dq_r, dq_shared=dq_s, dk=dk, dv=dv)
 
 
-__all__ = ["head_backward", "attention_backward"]
+def row_lse2(q, K, kk, causal=True):
+    """The base-2 log of each row's softmax denominator (GQE study note §1-1 attention equation):
+    lse[r] = log2 sum_s exp(q_r . K_s / sqrt(d)) over the keys row r sees (r // kk >= s when causal), which is
+    the statistic that turns a row's scores into its softmax, P[r, s] = 2^(q_r . K_s log2(e) / sqrt(d) - lse[r]).
+    q [R, d], K [T, d].  Returns float64 numpy [R]."""
+    q, K = _f64(q), _f64(K)
+    R, d = q.shape
+    T = K.shape[0]
+    S = (q @ K.T) / np.sqrt(d)
+    if causal:
+        pos = torch.arange(R) // kk
+        S = S.masked_fill(torch.arange(T)[None, :] > pos[:, None], float("-inf"))
+    return (torch.logsumexp(S, dim=-1) / np.log(2.0)).numpy()
+
+
+__all__ = ["head_backward", "attention_backward", "row_lse2"]

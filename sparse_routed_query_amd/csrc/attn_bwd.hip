@@ -303,6 +303,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
 
     KeyRegs<D> rk, rv;
     keys_load<D>(Kh, 0, T, rk);
+    if (a.lse_given) keys_load<D>(Vh, 0, T, rv);
     load_rows<D>(rs, r0, sQ, sdO, s_dp);
     __syncthreads();
     if (tid < kAbTile) {
@@ -311,8 +312,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         s_delta[tid] = dsum;
     }
     keys_store<D>(rk, sK);
+    if (a.lse_given) keys_store<D>(rv, sV);
     __syncthreads();
 
+    if (a.lse_given) {
+        // the forward's log-sum-exp of each row; only Delta goes to the workspace
+        if (tid < kAbTile) {
+            const int r = r0 + tid;
+            s_lse[tid] = r < rs.R ? rs.lse[r] : INFINITY;   // (rows past R weigh nothing)
+            if (r < rs.R) rs.delta[r] = s_delta[tid];
+        }
+        __syncthreads();
+    } else {
     // pass 1: the rows' base-2 log-sum-exp.  Its last step fetches pass 2's first K and V tiles.
     float m = -1e30f, l = 0.f;
     for (int kt = 0; kt < nkt; ++kt) {
@@ -368,6 +379,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
             }
         }
         __syncthreads();
+    }
     }
 
     // pass 2: dq = dS K / sqrt(d)

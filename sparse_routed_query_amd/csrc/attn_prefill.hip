@@ -230,6 +230,7 @@ struct PfParams {
     float* out;
     int* ctr;      // one counter per split pair (even before a launch, even after)
     float* part;   // pf_part_floats<D>() floats per part of each split pair
+    float* lse;    // NULL, or each row's base-2 log-sum-exp: routed rows [B, G, T*k], then shared rows [B, T]
     int S;
     float qscale;  // log2(e) / sqrt(d)
     PfSched sc;
@@ -560,6 +561,7 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         const bool first = w.part == 0;
         const float a0 = first ? a_me : a_o, a1 = first ? a_o : a_me;
         l_half = fmaf(first ? l_half : l_o, a0, (first ? l_o : l_half) * a1);
+        m_ref = mm;
 #pragma unroll
         for (int c = 0; c < NQ; ++c) {
             const f32x2 y = __builtin_bit_cast(f32x2, ov[c]);
@@ -576,6 +578,12 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     if (!qvalid) return;
     const float l = half_sum(l_half);
     const float inv = 1.f / l;
+    if (p.lse && lh == 0) {
+        // log2 of the row's sum of 2^(s log2(e)/sqrt(d)): the reference plus log2 of the sum
+        const size_t ri = shared ? (size_t)p.sc.B * G * T * k + (size_t)w.b * T + qrow
+                                 : ((size_t)w.b * G + w.h) * (size_t)R + qrow;
+        p.lse[ri] = m_ref + log2f(l);
+    }
     const int t = qrow / kk, jj = qrow - t * kk;
     float* dst = out + (((size_t)w.b * T + t) * S + slot0 + jj) * D;
 #pragma unroll
@@ -786,6 +794,7 @@ int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
 {
     const long long BT = (long long)a.B * a.T;
     if (BT == 0) return 0;
+    if (a.lse && !a.bf16) return -2;
     if (a.bf16) {
         const bool split = a.workspace != nullptr &&
                            prefill_workspace_bytes(a.B, a.T, a.G, a.k, a.d_head, a.n_shared, a.causal, true) > 0;
@@ -799,6 +808,7 @@ int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
                           a.q_shared != nullptr);
         prm.ctr = split ? (int*)a.workspace : nullptr;
         prm.part = split ? (float*)((char*)a.workspace + pf_ctr_bytes(pf_pairs(prm.sc))) : nullptr;
+        prm.lse = a.lse;
         prm.S = a.S;
         prm.qscale = 1.4426950408889634f / sqrtf((float)a.d_head);
         const long long items = pf_count_ge(prm.sc, 1);

@@ -73,7 +73,7 @@ size_t prefill_ws_bytes(const Shape& s)
 
 int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k, const void* v,
                    const float* p_tilde, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                   bool assemble)
+                   bool assemble, float* lse = nullptr)
 {
     Shape s;
     GQE_TRY(check_desc(desc, s));
@@ -93,8 +93,47 @@ int prefill_common(const gqe_desc* desc, const void* q_routed, const void* q_sha
     if (workspace && workspace_bytes < prefill_ws_bytes(s)) return GQE_ERR_WORKSPACE;
     gqe::PrefillArgs a{q_routed, shared ? q_shared : nullptr, k, v, p_tilde, out, workspace,
                        s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, s.mode, s.S, s.bf16};
+    a.lse = lse;
     return launch_status(assemble ? gqe::launch_prefill(a, (hipStream_t)stream)
                                   : gqe::launch_prefill_heads(a, (hipStream_t)stream));
+}
+
+int attn_backward_common(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                         const void* v, const float* out, const float* d_hard, const float* dout, const float* lse,
+                         float* dq_routed, float* dq_shared, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!s.bf16) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(q_routed));
+    GQE_TRY(need(k));
+    GQE_TRY(need(v));
+    GQE_TRY(need(out));
+    GQE_TRY(need(d_hard));
+    GQE_TRY(need(dq_routed));
+    GQE_TRY(need(dk));
+    GQE_TRY(need(dv));
+    if (s.ns) {
+        GQE_TRY(need(q_shared));
+        GQE_TRY(need(dout));
+        GQE_TRY(need(dq_shared));
+    }
+    if (!workspace) return GQE_ERR_WORKSPACE;
+    GQE_TRY(need(workspace));
+    if (workspace_bytes < gqe::attn_bwd_workspace_bytes(s.B, s.T, s.G, s.k, s.ns)) return GQE_ERR_WORKSPACE;
+    const long long rows = (long long)s.B * s.G * s.T * s.k + (s.ns ? s.BT : 0);
+    gqe::AttnBwdArgs a{q_routed, s.ns ? q_shared : nullptr, k, v, out, d_hard, s.ns ? dout : nullptr, dq_routed,
+                       s.ns ? dq_shared : nullptr, dk, dv, (float*)workspace, (float*)workspace + rows,
+                       s.B, s.T, s.G, s.k, s.S, s.D, s.causal, s.ns,
+                       1.4426950408889634f / sqrtf((float)s.D), 1.f / sqrtf((float)s.D)};
+    if (lse) {
+        // the forward's statistics take the workspace's first half's place; the kernels do not write them
+        a.lse = const_cast<float*>(lse);
+        a.lse_given = true;
+    }
+    return launch_status(gqe::launch_attn_bwd(a, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -208,6 +247,19 @@ int gqe_attn_prefill_heads(const gqe_desc* desc, const void* q_routed, const voi
     return prefill_common(desc, q_routed, q_shared, k, v, nullptr, out, workspace, workspace_bytes, stream, false);
 }
 
+int gqe_attn_prefill_heads_lse(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                               const void* v, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (!s.bf16) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(lse));
+    return prefill_common(desc, q_routed, q_shared, k, v, nullptr, out, workspace, workspace_bytes, stream, false,
+                          lse);
+}
+
 int gqe_assemble(const gqe_desc* desc, const float* p_tilde, float* out, void* stream)
 {
     Shape s;
@@ -275,37 +327,29 @@ size_t gqe_attn_backward_workspace_bytes(const gqe_desc* desc)
     return gqe::attn_bwd_workspace_bytes(s.B, s.T, s.G, s.k, s.ns);
 }
 
+
 int gqe_attn_backward(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
                       const void* v, const float* out, const float* d_hard, const float* dout, float* dq_routed,
                       float* dq_shared, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return attn_backward_common(desc, q_routed, q_shared, k, v, out, d_hard, dout, nullptr, dq_routed, dq_shared, dk,
+                                dv, workspace, workspace_bytes, stream);
+}
+
+int gqe_attn_backward_lse(const gqe_desc* desc, const void* q_routed, const void* q_shared, const void* k,
+                          const void* v, const float* out, const float* d_hard, const float* dout, const float* lse,
+                          float* dq_routed, float* dq_shared, float* dk, float* dv, void* workspace,
+                          size_t workspace_bytes, void* stream)
 {
     Shape s;
     GQE_TRY(check_desc(desc, s));
     if (!s.bf16) return GQE_ERR_UNSUPPORTED;
     if (s.BT == 0) return GQE_OK;
-    GQE_TRY(need(q_routed));
-    GQE_TRY(need(k));
-    GQE_TRY(need(v));
-    GQE_TRY(need(out));
-    GQE_TRY(need(d_hard));
-    GQE_TRY(need(dq_routed));
-    GQE_TRY(need(dk));
-    GQE_TRY(need(dv));
-    if (s.ns) {
-        GQE_TRY(need(q_shared));
-        GQE_TRY(need(dout));
-        GQE_TRY(need(dq_shared));
-    }
-    if (!workspace) return GQE_ERR_WORKSPACE;
-    GQE_TRY(need(workspace));
-    if (workspace_bytes < gqe::attn_bwd_workspace_bytes(s.B, s.T, s.G, s.k, s.ns)) return GQE_ERR_WORKSPACE;
-    const long long rows = (long long)s.B * s.G * s.T * s.k + (s.ns ? s.BT : 0);
-    gqe::AttnBwdArgs a{q_routed, s.ns ? q_shared : nullptr, k, v, out, d_hard, s.ns ? dout : nullptr, dq_routed,
-                       s.ns ? dq_shared : nullptr, dk, dv, (float*)workspace, (float*)workspace + rows,
-                       s.B, s.T, s.G, s.k, s.S, s.D, s.causal, s.ns,
-                       1.4426950408889634f / sqrtf((float)s.D), 1.f / sqrtf((float)s.D)};
-    return launch_status(gqe::launch_attn_bwd(a, (hipStream_t)stream));
+    GQE_TRY(need(lse));
+    return attn_backward_common(desc, q_routed, q_shared, k, v, out, d_hard, dout, lse, dq_routed, dq_shared, dk, dv,
+                                workspace, workspace_bytes, stream);
 }
+
 
 int gqe_kv_proj(const gqe_desc* desc, const void* x, const void* w_k, const void* w_v, void* k, void* v,
                 void* stream)

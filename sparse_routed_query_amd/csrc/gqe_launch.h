@@ -73,10 +73,12 @@ struct AttnBwdArgs {
     float* dq_shared;       // [B, T, d_head] (n_shared = 1)
     float* dk;              // [B, G, T, d_head]
     float* dv;              // [B, G, T, d_head]
-    float* lse;             // workspace: one base-2 log-sum-exp per row (routed rows, then shared)
+    float* lse;             // one base-2 log-sum-exp per row (routed rows, then shared): the workspace,
+                            // or the forward's own when lse_given
     float* delta;           // workspace: one <dO, O> per row
     int B, T, G, k, S, d_head, causal, n_shared;
     float qscale2, inv_sqrt_d;
+    bool lse_given = false; // lse holds the forward's values: the dq kernel reads them instead of recomputing
 };
 size_t attn_bwd_workspace_bytes(int B, int T, int G, int k, int n_shared);
 int launch_attn_bwd(const AttnBwdArgs& a, hipStream_t st);
@@ -150,6 +152,7 @@ struct PrefillArgs {
     void* workspace;   // NULL: no split tiles; else prefill_workspace_bytes() bytes, counters even
     int B, T, G, k, d_head, n_shared, causal, route_mode, S;
     bool bf16;
+    float* lse = nullptr;   // bf16 only: each row's base-2 log-sum-exp (routed rows, then shared rows)
 };
 size_t prefill_workspace_bytes(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool bf16);
 // The launch's work items in launch order, 5 ints each (b, h, tile, part, pair);

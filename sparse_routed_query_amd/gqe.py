@@ -33,7 +33,8 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_attn_decode_paged", "gqe_kv_proj", "gqe_check_decode_inputs", "gqe_route_backward_workspace_bytes",
            "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
            "gqe_attn_decode_noalloc", "gqe_qkv_proj", "gqe_qkv_proj_backward",
-           "gqe_qkv_proj_backward_workspace_bytes", "gqe_decode_route_qproj")
+           "gqe_qkv_proj_backward_workspace_bytes", "gqe_decode_route_qproj", "gqe_attn_prefill_heads_lse",
+           "gqe_attn_backward_lse")
 
 
 class GqeError(RuntimeError):
@@ -122,6 +123,10 @@ def load():
         lib.gqe_attn_backward_workspace_bytes.restype = Z
         lib.gqe_attn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.gqe_attn_backward.restype = I
+        lib.gqe_attn_prefill_heads_lse.argtypes = [D, P, P, P, P, P, P, P, Z, P]
+        lib.gqe_attn_prefill_heads_lse.restype = I
+        lib.gqe_attn_backward_lse.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+        lib.gqe_attn_backward_lse.restype = I
         lib.gqe_kv_proj.argtypes = [D, P, P, P, P, P, P]
         lib.gqe_kv_proj.restype = I
         lib.gqe_out_proj.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
@@ -246,6 +251,21 @@ def gqe_attn_prefill_heads(desc, q_routed, q_shared, k, v, out, workspace=None, 
     _check("gqe_attn_prefill_heads", rc)
 
 
+def gqe_attn_prefill_heads_lse(desc, q_routed, q_shared, k, v, out, lse, workspace=None, stream=None):
+    dt = desc.torch_dtype
+    wp, wb = _ws(workspace)
+    rc = load().gqe_attn_prefill_heads_lse(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"),
+                                           _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"), _ptr(v, dt, "v"),
+                                           _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"), wp, wb,
+                                           _stream(stream))
+    _check("gqe_attn_prefill_heads_lse", rc)
+
+
+def lse_rows(desc) -> int:
+    """Number of rows of the attention statistics: routed rows, then shared rows."""
+    return desc.B * desc.H_kv * desc.T * desc.k + (desc.B * desc.T if desc.n_shared else 0)
+
+
 def gqe_assemble(desc, p_tilde, out, stream=None):
     rc = load().gqe_assemble(ctypes.byref(desc), _ptr(p_tilde, torch.float32, "p_tilde"),
                              _ptr(out, torch.float32, "out"), _stream(stream))
@@ -326,15 +346,35 @@ def gqe_attn_backward(desc, q_routed, q_shared, k, v, out, d_hard, dout, dq_rout
     _check("gqe_attn_backward", rc)
 
 
-def attn_backward(desc, q_routed, q_shared, k, v, out, d_hard, dout, stream=None) -> dict:
+def gqe_attn_backward_lse(desc, q_routed, q_shared, k, v, out, d_hard, dout, lse, dq_routed, dq_shared, dk, dv,
+                          workspace, stream=None):
+    dt = desc.torch_dtype
+    rc = load().gqe_attn_backward_lse(ctypes.byref(desc), _ptr(q_routed, dt, "q_routed"),
+                                      _ptr(q_shared, dt, "q_shared"), _ptr(k, dt, "k"), _ptr(v, dt, "v"),
+                                      _ptr(out, torch.float32, "out"), _ptr(d_hard, torch.float32, "d_hard"),
+                                      _ptr(dout, torch.float32, "dout"), _ptr(lse, torch.float32, "lse"),
+                                      _ptr(dq_routed, torch.float32, "dq_routed"),
+                                      _ptr(dq_shared, torch.float32, "dq_shared"), _ptr(dk, torch.float32, "dk"),
+                                      _ptr(dv, torch.float32, "dv"), _ptr(workspace, torch.uint8, "workspace"),
+                                      workspace.numel(), _stream(stream))
+    _check("gqe_attn_backward_lse", rc)
+
+
+def attn_backward(desc, q_routed, q_shared, k, v, out, d_hard, dout, lse=None, stream=None) -> dict:
     """Gradients of the attention: dq_routed [B, G, T*k, d], dq_shared [B, T, d] or None, dk, dv [B, H_kv, T, d]
-    (fp32; allocates its outputs and workspace)."""
+    (fp32; allocates its outputs and workspace).  lse: the forward's row statistics
+    (gqe_attn_prefill_heads_lse), which skips their recomputation."""
     B, T, G, k_, D = desc.B, desc.T, desc.H_kv, desc.k, desc.d_head
     dev = d_hard.device
     e = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
     res = dict(dq_routed=e(B, G, T * k_, D), dq_shared=e(B, T, D) if desc.n_shared else None, dk=e(B, G, T, D),
                dv=e(B, G, T, D))
     ws = torch.empty(gqe_attn_backward_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    if lse is not None:
+        gqe_attn_backward_lse(desc, q_routed, q_shared if desc.n_shared else None, k, v, out, d_hard,
+                              dout if desc.n_shared else None, lse, res["dq_routed"], res["dq_shared"], res["dk"],
+                              res["dv"], ws, stream)
+        return res
     gqe_attn_backward(desc, q_routed, q_shared if desc.n_shared else None, k, v, out, d_hard,
                       dout if desc.n_shared else None, res["dq_routed"], res["dq_shared"], res["dk"], res["dv"], ws,
                       stream)

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 26
+    assert len(names) == 28
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -335,6 +335,22 @@ def test_decode_route_qproj_rejects_prefill_shapes_bad_rope_base_and_pointers():
     assert rc(dec, qs=None) == INVALID           # the shared head is on
     assert rc(dec, 10000.0, MIS) == ALIGN
     assert rc(main(B=0, T=1), x=None) == OK      # empty batch: nothing to do, no pointer read
+
+
+def test_attention_lse_entries_reject_fp32_and_missing_statistics():
+    lib = G.load()
+    d = main()
+    f32 = main(dtype="f32")
+    heads = lambda desc, lse=A16: lib.gqe_attn_prefill_heads_lse(ctypes.byref(desc), A16, A16, A16, A16, A16, lse,  # noqa: E731
+                                                                None, 0, None)
+    assert heads(f32) == UNSUPPORTED
+    assert heads(d, None) == INVALID
+    assert heads(d, MIS) == ALIGN
+    bwd = lambda desc, lse=A16, ws=A16: lib.gqe_attn_backward_lse(  # noqa: E731
+        ctypes.byref(desc), A16, A16, A16, A16, A16, A16, A16, lse, A16, A16, A16, A16, ws, 1 << 40, None)
+    assert bwd(f32) == UNSUPPORTED
+    assert bwd(d, None) == INVALID
+    assert bwd(d, ws=None) == WORKSPACE
 
 
 def test_qkv_proj_rejects_bad_rope_base_and_pointers():

@@ -17,7 +17,7 @@ import torch
 
 import workloads as W
 from gpu_parity_util import gpu_prefill, say
-from oracle.attn_backward import head_backward
+from oracle.attn_backward import head_backward, row_lse2
 import sparse_routed_query_amd.gqe as G
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +44,50 @@ def check(name, got, ref, bound):
     assert r <= 1.0, name
 
 
-def run_case(w, heads=None):
+def forward_lse(w, inp, gpu, split=True):
+    """gqe_attn_prefill_heads_lse on the forward's own queries: checks that its slots are gqe_attn_prefill_heads'
+    bit for bit (same workspace choice) and returns the row statistics (device tensor)."""
+    d = G.desc_from(w)
+    qr = gpu["q_routed"].cuda()
+    qs = gpu["q_shared"].cuda() if w.n_shared else None
+    k, v = inp["k"].cuda(), inp["v"].cuda()
+    shape = (w.B * w.T, d.S, w.d_head)
+    out_a = torch.full(shape, float("nan"), device="cuda")
+    out_b = out_a.clone()
+    lse = torch.full((G.lse_rows(d),), float("nan"), device="cuda")
+    nws = G.gqe_attn_prefill_workspace_bytes(d) if split else 0
+    ws = torch.zeros(max(nws, 256), dtype=torch.uint8, device="cuda") if nws else None
+    G.gqe_attn_prefill_heads(d, qr, qs, k, v, out_a, ws)
+    G.gqe_attn_prefill_heads_lse(d, qr, qs, k, v, out_b, lse, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(out_a, nan=0.0), torch.nan_to_num(out_b, nan=0.0))
+    return lse
+
+
+def check_lse(w, inp, gpu, lse, heads):
+    """The forward's row statistics against the oracle's (base-2 log of each row's softmax denominator): the
+    GPU forms the scores in fp32 from the bf16 rows, so 2e-4 absolute."""
+    B, T, Gn, k = w.B, w.T, w.H_kv, w.k
+    got = lse.cpu().double().numpy()
+    nr = B * Gn * T * k
+    Kf = inp["k"].double().numpy()
+    worst = 0.0
+    for b, h in heads:
+        if h < Gn:
+            q = gpu["q_routed"].double().numpy().reshape(B, Gn, T * k, -1)[b, h]
+            ref = row_lse2(q, Kf[b, h], k, w.causal)
+            g = got[(b * Gn + h) * T * k:(b * Gn + h + 1) * T * k]
+        else:
+            q = gpu["q_shared"].double().numpy().reshape(B, T, -1)[b]
+            ref = row_lse2(q, Kf[b, 0], 1, w.causal)
+            g = got[nr + b * T:nr + (b + 1) * T]
+        assert np.isfinite(g).all()
+        worst = max(worst, float(np.abs(g - ref).max()))
+    say(f"[{w.name}] forward row statistics: max-abs error {worst:.2e} over {len(heads)} heads")
+    assert worst <= 2e-4
+
+
+def run_case(w, heads=None, use_lse=False):
     inp = W.make_inputs(w)
     gpu = gpu_prefill(w, inp)
     d = G.desc_from(w)
@@ -54,13 +97,18 @@ def run_case(w, heads=None):
     d_hard = torch.from_numpy(rng.standard_normal((BT, kG, D)).astype(np.float32))
     dout = torch.from_numpy(rng.standard_normal((BT, S, D)).astype(np.float32))
     qs = gpu["q_shared"] if w.n_shared else None
-    say(f"[{w.name}] attention backward (B={B}, T={T}, G={Gn}, k={k}, d={D}, causal={w.causal})")
-    res = G.attn_backward(d, gpu["q_routed"].cuda(), qs.cuda() if qs is not None else None, inp["k"].cuda(),
-                          inp["v"].cuda(), gpu["out"].reshape(BT, S, D).cuda(), d_hard.cuda(), dout.cuda())
-    torch.cuda.synchronize()
-    res = {key: (v.cpu().numpy() if v is not None else None) for key, v in res.items()}
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Gn + (1 if w.n_shared else 0))]
+    lse = None
+    if use_lse:
+        lse = forward_lse(w, inp, gpu)
+        check_lse(w, inp, gpu, lse, heads)
+    say(f"[{w.name}] attention backward (B={B}, T={T}, G={Gn}, k={k}, d={D}, causal={w.causal}, "
+        f"forward statistics given={use_lse})")
+    res = G.attn_backward(d, gpu["q_routed"].cuda(), qs.cuda() if qs is not None else None, inp["k"].cuda(),
+                          inp["v"].cuda(), gpu["out"].reshape(BT, S, D).cuda(), d_hard.cuda(), dout.cuda(), lse=lse)
+    torch.cuda.synchronize()
+    res = {key: (v.cpu().numpy() if v is not None else None) for key, v in res.items()}
     Kf, Vf = inp["k"].double().numpy(), inp["v"].double().numpy()
     qr = gpu["q_routed"].double().numpy().reshape(B, Gn, T * k, D)
     out = gpu["out"].double().numpy().reshape(B, T, S, D)
@@ -101,6 +149,43 @@ def run_case(w, heads=None):
 ], ids=lambda w: w.name)
 def test_attention_backward(w):
     run_case(w)
+
+
+@pytest.mark.parametrize("w", [
+    small(), small(causal=0, name="noncausal"), small(n_shared=0, name="no_shared"),
+    small(d_head=32, name="d32"), small(d_head=128, name="d128"), small(H_q=16, H_kv=4, k=3, name="E4k3"),
+    small(B=1, T=1, name="T1"), small(B=1, T=2304, H_q=4, H_kv=1, k=1, name="split_tiles"),
+], ids=lambda w: w.name)
+def test_attention_backward_given_the_forward_statistics(w):
+    """gqe_attn_prefill_heads_lse's row statistics against the oracle's, its slots equal to
+    gqe_attn_prefill_heads', then gqe_attn_backward_lse against fp64 autograd at the same bounds."""
+    run_case(w, use_lse=True)
+
+
+def test_attention_backward_full_size_given_the_forward_statistics():
+    w = W.WORKLOADS["main_250m"]
+    run_case(w, heads=[(0, 0), (0, w.H_kv), (2, 5)], use_lse=True)
+
+
+def test_backward_with_and_without_the_forward_statistics_agree():
+    """The two entry points differ only by the rounding of the statistics (recomputed or the forward's)."""
+    w = small(T=700, name="lse_vs_recompute")
+    inp = W.make_inputs(w)
+    gpu = gpu_prefill(w, inp)
+    d = G.desc_from(w)
+    BT, S, D = w.B * w.T, d.S, w.d_head
+    g = torch.Generator().manual_seed(5)
+    d_hard = torch.randn((BT, w.k * w.H_kv, D), generator=g).cuda()
+    dout = torch.randn((BT, S, D), generator=g).cuda()
+    lse = forward_lse(w, inp, gpu)
+    args = (d, gpu["q_routed"].cuda(), gpu["q_shared"].cuda(), inp["k"].cuda(), inp["v"].cuda(),
+            gpu["out"].reshape(BT, S, D).cuda(), d_hard, dout)
+    a, b = G.attn_backward(*args), G.attn_backward(*args, lse=lse)
+    torch.cuda.synchronize()
+    for key in a:
+        rel = float((a[key] - b[key]).norm() / a[key].norm())
+        say(f"  {key}: relative rms difference {rel:.2e}")
+        assert rel <= 1e-3, key
 
 
 def test_attention_backward_full_size_sampled_heads():

@@ -616,7 +616,7 @@ def test_router_backward_closed_forms():
 
 # ---------------------------------------------------------------- attention backward (oracle/attn_backward.py)
 
-from oracle.attn_backward import attention_backward, head_backward  # noqa: E402
+from oracle.attn_backward import attention_backward, head_backward, row_lse2  # noqa: E402
 
 
 def _attn_bwd_case(k=2, E=2, G=2, T=5, d=3, seed=11, causal=1):
@@ -669,6 +669,34 @@ def test_attention_backward_matches_finite_differences_of_the_forward(causal):
         for idx in itertools.product(*[range(s) for s in arr.shape]):
             f = fd(arr, idx)
             assert abs(f - grad[idx]) <= 1e-6 * max(1.0, abs(f)), (idx, f, grad[idx])
+
+
+def test_row_statistic_closed_forms():
+    """row_lse2 against closed forms: with every score equal to c a row over n keys has log2(n) + c log2(e);
+    its 2^(s log2(e) - lse) are the softmax of the row (they sum to one and equal torch's); shifting every
+    key's score by a constant shifts lse by that constant times log2(e)."""
+    rng = np.random.default_rng(7)
+    d, T, kk = 16, 9, 2
+    q = np.zeros((T * kk, d))
+    q[:, 0] = 1.0
+    K = np.zeros((T, d))
+    K[:, 0] = 0.75 * np.sqrt(d)                       # every score q.K/sqrt(d) = 0.75
+    lse = row_lse2(q, K, kk, causal=True)
+    n = np.arange(T * kk) // kk + 1
+    assert np.allclose(lse, np.log2(n) + 0.75 / np.log(2.0), rtol=0, atol=1e-12)
+    assert np.allclose(row_lse2(q, K, kk, causal=False), np.log2(T) + 0.75 / np.log(2.0), rtol=0, atol=1e-12)
+    q = rng.standard_normal((T * kk, d))
+    K = rng.standard_normal((T, d))
+    lse = row_lse2(q, K, kk, causal=True)
+    S = q @ K.T / np.sqrt(d)
+    mask = np.arange(T)[None, :] > (np.arange(T * kk) // kk)[:, None]
+    P = np.where(mask, 0.0, np.exp2(S / np.log(2.0) - lse[:, None]))
+    assert np.allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    ref = torch.softmax(torch.from_numpy(np.where(mask, -np.inf, S)), dim=-1).numpy()
+    assert np.allclose(P, ref, rtol=0, atol=1e-12)
+    u = rng.standard_normal(d)
+    shift = (q @ u) / np.sqrt(d)                      # K_s + u moves every score of row r by q_r.u/sqrt(d)
+    assert np.allclose(row_lse2(q, K + u, kk, causal=True) - lse, shift / np.log(2.0), rtol=0, atol=1e-10)
 
 
 def test_attention_backward_single_key():
