@@ -345,6 +345,22 @@ __global__ __launch_bounds__(64 * kCmpWaves) void compact_kernel(const int32_t* 
     // 2. scatter: wave ballots rank the token among its block's tokens that kept each expert
     const uint32_t below = (1u << hl) - 1u;
     const int* my_sel = s_sel[bi * kRouteTok + hl];
+    if (staged) {
+        // kept experts from LDS only, so no wait on global memory sits between the stores
+        // (a load's wait would also wait for every store issued before it): first the token's
+        // kept experts as one mask over the N <= 64 experts, then one ballot per expert, skipping
+        // the experts no token of the wave kept
+        uint64_t kept = 0;
+        if (valid)
+            for (int j = 0; j < Gk; ++j) kept |= 1ull << ((j / k) * E + my_sel[j]);
+        for (int n = 0; n < N; ++n) {
+            const bool has = (kept >> n) & 1;
+            const uint64_t m = __ballot(has);
+            if (m == 0) continue;
+            if (has) rows[s_base[bi][n] + __popc((uint32_t)(m >> (32 * half)) & below)] = t;
+        }
+        return;
+    }
     for (int g = 0; g < G; ++g) {
         int kept[8];
         for (int j = 0; j < k; ++j)
