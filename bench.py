@@ -299,16 +299,21 @@ def decode_leg(torch, dev, steps):
 
 
 def out_proj_leg(p, torch, steps):
-    """The attention output projection fused with slot assembly (gqe_out_proj) on the step's own slots:
-    y = W_o h over the S = kG+2 concatenated slots, bf16 MFMA with fp32 accumulation.  Timed beside it,
-    for context only, hipBLASLt's plain bf16 GEMM (torch.mm) of slots that were already assembled and
-    cast to bf16, with a bf16 result: it does neither the assembly nor the fp32 output."""
+    """The attention output projection fused with slot assembly on the step's own slots: y = W_o h over the
+    S = kG+2 concatenated slots, bf16 MFMA with fp32 accumulation, from W_o packed once into fragment order
+    (gqe_out_proj_packed; the row-major call gqe_out_proj timed beside it).  Timed beside them, for context
+    only, hipBLASLt's plain bf16 GEMM (torch.mm) of slots that were already assembled and cast to bf16, with
+    a bf16 result: it does neither the assembly nor the fp32 output."""
     import workloads as W
     w, G = p.w, p.G
     wo = W.make_w_o(w).to(p.x.device)
+    wp = G.out_proj_pack(p.d, wo)
     BT = w.B * w.T
     y = torch.empty((BT, w.d_model), dtype=torch.float32, device=p.x.device)
     slots = p.out.view(BT, -1)
+
+    def op_packed():
+        G.gqe_out_proj_packed(p.d, p.out, p.r["p_tilde"], wp, y, False)
 
     def op():
         G.gqe_out_proj(p.d, p.out, p.r["p_tilde"], wo, y, False)
@@ -319,12 +324,17 @@ def out_proj_leg(p, torch, steps):
     def lib():
         torch.mm(hb, wt)
 
-    warm([op, lib], torch)
-    t_op, t_lib = time_calls([op, lib], steps, torch)
+    warm([op_packed, op, lib], torch)
+    t_pk, t_op, t_lib = time_calls([op_packed, op, lib], steps, torch)
     fl = W.out_proj_flops(w)
-    tf = fl / (t_op * 1e-3) / 1e12
-    return {"workload": w.name, "kernel": f"out_proj_bf16_kernel<{w.d_head}> (gqe_out_proj)", "us": t_op * 1e3,
-            "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl, "shape_mnk": [BT, w.d_model, slots.shape[1]],
+    tf = fl / (t_pk * 1e-3) / 1e12
+    # HBM floor of the call: the fp32 hard and shared slots read once, y written once (fp32)
+    hbm_bytes = BT * (p.d.S - (1 if w.route_mode == 0 else w.G if w.route_mode == 1 else 0)) * w.d_head * 4 \
+        + BT * w.d_model * 4
+    return {"workload": w.name, "kernel": f"out_proj_tile_kernel<{w.d_head}, packed> (gqe_out_proj_packed)",
+            "us": t_pk * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl,
+            "shape_mnk": [BT, w.d_model, slots.shape[1]], "row_major_weights_us": t_op * 1e3,
+            "hbm_floor_bytes": hbm_bytes, "hbm_floor_us_at_8tbs": hbm_bytes / 8e12 * 1e6,
             "context_torch_mm_bf16_us": t_lib * 1e3}
 
 

@@ -446,6 +446,29 @@ int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const v
                  int32_t write_weighted, void* stream);
 
 /*
+ * Packed output-projection weights (bf16 only).  The same projection as
+ * gqe_out_proj (GQA tutorial step 5; GQE study note §3-2 (5), (7)) with W_o
+ * first rearranged once into the order the kernel's matrix-core fragments are
+ * read in, so that every weight load is a run of consecutive bytes:
+ *   packed[((ct*(K/16) + ks)*2 + cb)*512 + (32*h + c)*8 + e]
+ *     = W_o[64*ct + 32*cb + c][16*ks + 8*h + e],   K = S*d_head,
+ *   c < 32, h < 2, e < 8.
+ * gqe_out_proj_packed_bytes: bytes of the packed weights (d_model*K*2), or 0
+ *   when this shape has no packed form (fp32, or K too large for the
+ *   kernel's 64-token tile of bf16 slots to fit in LDS: 64*(K+8)*2 bytes
+ *   above 160 KiB) -- use gqe_out_proj there.
+ * gqe_out_proj_pack: w_o [d_model, K] bf16 -> w_packed (caller-owned, that
+ *   many bytes); GQE_ERR_UNSUPPORTED where the size is 0.
+ * gqe_out_proj_packed: y and the optional weighted-slot write-back exactly as
+ *   gqe_out_proj defines them (the same bf16 rounding of every slot value;
+ *   fp32 sums in a different order), from the packed weights.
+ */
+size_t gqe_out_proj_packed_bytes(const gqe_desc* desc);
+int gqe_out_proj_pack(const gqe_desc* desc, const void* w_o, void* w_packed, void* stream);
+int gqe_out_proj_packed(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_packed, float* y,
+                        int32_t write_weighted, void* stream);
+
+/*
  * gqe_attn_decode_paged -- gqe_attn_decode over a paged KV cache, the layout
  * of paged attention (GQA tutorial, freeguideonline, "推理优化：连续批处理与
  * 分页注意力": GQA pairs with continuous batching and paged attention, the

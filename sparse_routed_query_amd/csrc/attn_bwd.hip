@@ -24,6 +24,8 @@
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
+#include <atomic>
+
 namespace gqe {
 
 namespace {
@@ -566,12 +568,17 @@ static int launch_attn_bwd_d(AttnBwdArgs a, hipStream_t st)
     const long long nq = (long long)a.B * a.G * ntr + (a.n_shared ? (long long)a.B * nts : 0);
     const long long nkv = (long long)a.B * a.G * nts;
     const int lq = ab_lds_bytes<D>(true), lkv = ab_lds_bytes<D>(false);
-    if (lq > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dq_kernel<D>,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, lq) != hipSuccess)
-        return -1;
-    if (lkv > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dkdv_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lkv) != hipSuccess)
-        return -1;
+    // LDS limits raised once per kernel (their sizes are fixed per d_head)
+    static std::atomic<int> raised{0};
+    if (!raised.load(std::memory_order_acquire)) {
+        if (lq > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dq_kernel<D>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, lq) != hipSuccess)
+            return -1;
+        if (lkv > 65536 && hipFuncSetAttribute((const void*)&attn_bwd_dkdv_kernel<D>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, lkv) != hipSuccess)
+            return -1;
+        raised.store(1, std::memory_order_release);
+    }
     attn_bwd_dq_kernel<D><<<(unsigned)nq, 256, lq, st>>>(a);
     attn_bwd_dkdv_kernel<D><<<(unsigned)nkv, 256, lkv, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -477,6 +477,47 @@ int gqe_out_proj(const gqe_desc* desc, float* out, const float* p_tilde, const v
     return launch_status(gqe::launch_out_proj(a, (hipStream_t)stream));
 }
 
+size_t gqe_out_proj_packed_bytes(const gqe_desc* desc)
+{
+    Shape s;
+    if (check_desc(desc, s) != GQE_OK || !s.bf16) return 0;
+    if ((long long)s.dm * s.S * s.D >= (1ll << 31) || !gqe::out_proj_tile_fits(s.S * s.D, s.dm)) return 0;
+    return (size_t)s.dm * s.S * s.D * 2;
+}
+
+int gqe_out_proj_pack(const gqe_desc* desc, const void* w_o, void* w_packed, void* stream)
+{
+    if (gqe_out_proj_packed_bytes(desc) == 0) {
+        Shape s;
+        GQE_TRY(check_desc(desc, s));
+        return GQE_ERR_UNSUPPORTED;
+    }
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    GQE_TRY(need(w_o));
+    GQE_TRY(need(w_packed));
+    return launch_status(gqe::launch_out_proj_pack(w_o, w_packed, s.dm, s.S * s.D, (hipStream_t)stream));
+}
+
+int gqe_out_proj_packed(const gqe_desc* desc, float* out, const float* p_tilde, const void* w_packed, float* y,
+                        int32_t write_weighted, void* stream)
+{
+    Shape s;
+    GQE_TRY(check_desc(desc, s));
+    if (write_weighted != 0 && write_weighted != 1) return GQE_ERR_INVALID;
+    if (gqe_out_proj_packed_bytes(desc) == 0) return GQE_ERR_UNSUPPORTED;
+    if (s.BT == 0) return GQE_OK;
+    GQE_TRY(need(out));
+    GQE_TRY(need(p_tilde));
+    GQE_TRY(need(w_packed));
+    GQE_TRY(need(y));
+    gqe::OutProjArgs a;
+    a.out = out; a.p_tilde = p_tilde; a.w_o = nullptr; a.w_packed = w_packed; a.y = y; a.BT = s.BT;
+    a.d_model = s.dm; a.G = s.G; a.k = s.k; a.d_head = s.D; a.n_shared = s.ns; a.route_mode = s.mode; a.S = s.S;
+    a.write_weighted = write_weighted; a.bf16 = true;
+    return launch_status(gqe::launch_out_proj(a, (hipStream_t)stream));
+}
+
 size_t gqe_decode_workspace_bytes(const gqe_desc* desc, int32_t L_max)
 {
     Shape s;

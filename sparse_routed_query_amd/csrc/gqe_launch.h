@@ -175,8 +175,12 @@ struct OutProjArgs {
     long long BT;
     int d_model, G, k, d_head, n_shared, route_mode, S, write_weighted;
     bool bf16;
+    const void* w_packed = nullptr;   // bf16: W_o in fragment order (launch_out_proj_pack); used instead of w_o
 };
 int launch_out_proj(const OutProjArgs& a, hipStream_t st);
+// Whether the token-tile kernel takes this shape (K = S * d_head): the packed form exists only then.
+bool out_proj_tile_fits(int K, int d_model);
+int launch_out_proj_pack(const void* w_o, void* w_packed, int d_model, int K, hipStream_t st);
 
 struct DecodeArgs {
     const void* q_routed;

@@ -23,6 +23,8 @@
 #include "gqe_device.h"
 #include "gqe_launch.h"
 
+#include <atomic>
+
 namespace gqe {
 
 constexpr int kOpBN = 128;   // output features per tile
@@ -209,6 +211,213 @@ __global__ __launch_bounds__(256, 2) void out_proj_bf16_kernel(float* __restrict
         }
 }
 
+// Token-tile kernel for K = S*d_head small enough that a tile's whole bf16
+// slot matrix fits in LDS: one workgroup of eight waves per 64 tokens, every
+// output feature.  Prologue: the tile's slots are read once (fp32, several
+// slots' loads in flight a thread), the weighted slot(s) formed in the fixed
+// order above, everything rounded to bf16 into LDS [64][K + 8].  Then each
+// wave walks its own 64-feature column tiles (tile w, w + 8, ...): 64 x 64
+// outputs as 2 x 2 blocks of 32x32x16 MFMA, the W_o fragments loaded straight
+// from global memory four k-steps ahead (each wave reads only its own
+// features, so nothing is shared and no barrier follows the prologue), the
+// slot fragments from LDS.  The slots are read from memory once instead of
+// once per column tile, as bf16 from LDS thereafter.
+//
+// PACKED: W_o in fragment order (gqe_out_proj_pack), so that each fragment
+// load of a wave is 1 KB of consecutive bytes; from the row-major W_o a load
+// touches 32 rows, 32 bytes each, and the four k-steps that share a 128-byte
+// line reach it at different times, so lines are fetched from L2 repeatedly.
+// Packed index of W_o[64 ct + 32 cb + c][16 ks + 8 h + e] (c < 32, h < 2,
+// e < 8): ((ct * K/16 + ks) * 2 + cb) * 512 + (32 h + c) * 8 + e.
+constexpr int kOtM = 64;                       // tokens per workgroup
+constexpr int kOtWaves = 8;
+constexpr int kOtPad = 8;                      // bf16 elements of row padding
+constexpr int kOtMaxLds = 160 * 1024;          // LDS of a gfx950 compute unit
+
+__host__ __device__ constexpr int ot_lds_bytes(int K) { return kOtM * (K + kOtPad) * 2; }
+bool out_proj_tile_fits(int K, int d_model) { return ot_lds_bytes(K) <= kOtMaxLds && d_model % 64 == 0; }
+
+template <int D, bool PACKED>
+__global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* __restrict__ out,
+                                                               const float* __restrict__ p_tilde,
+                                                               const uint16_t* __restrict__ w_o,
+                                                               float* __restrict__ y, long long BT, int d_model,
+                                                               int G, int k, int mode, int S, int write_weighted)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t sA[];
+    constexpr int LPR = D / 4, RPP = 64 * kOtWaves / LPR, NP = kOtM / RPP;
+    constexpr int SB = D == 32 ? 4 : NP >= 10 ? 1 : 10 / NP;   // slots whose loads are in flight together
+    const int K = S * D, PA = K + kOtPad;
+    const long long m0 = (long long)blockIdx.x * kOtM;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kG = G * k, nroute = op_nroute(G, mode);
+
+    // ---- prologue: slots -> bf16 LDS tile (rows past B*T read as zero and are never stored)
+    const int arow0 = tid / LPR, acol = (tid % LPR) * 4;
+    const int rows = (int)(BT - m0 < kOtM ? BT - m0 : kOtM);
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)(out + (size_t)m0 * S * D), 0,
+                                                                         rows * S * D * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc((void*)(p_tilde + (size_t)m0 * kG), 0,
+                                                                         rows * kG * 4, 0x00020000);
+    f32x4 wacc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) wacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < S; i0 += SB) {
+        f32x4 ra[SB][NP];
+        float rp[SB][NP];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            const int sl = i0 + u < S ? op_slot(i0 + u, G, k, mode) : kG;   // past S: a weighted-like no-load
+            const bool data = i0 + u < S && (sl < kG || sl >= kG + nroute);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                ra[u][p] = data ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                      rA, ((arow0 + RPP * p) * S * D + sl * D + acol) * 4, 0, 0))
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+                rp[u][p] = (data && sl < kG) ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rP, ((arow0 + RPP * p) * kG + sl) * 4, 0, 0))
+                                             : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            if (i0 + u >= S) break;
+            const int sl = op_slot(i0 + u, G, k, mode);
+            f32x4 av[NP];
+            if (sl < kG) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) {
+                    av[p] = ra[u][p];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) wacc[p][e] = fmaf(rp[u][p], ra[u][p][e], wacc[p][e]);
+                }
+            } else if (sl < kG + nroute) {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) av[p] = wacc[p];
+                if (write_weighted) {
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) {
+                        const long long t = m0 + arow0 + RPP * p;
+                        if (t < BT) *(f32x4*)(out + (size_t)t * S * D + (size_t)sl * D + acol) = wacc[p];
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < NP; ++p) wacc[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int p = 0; p < NP; ++p) av[p] = ra[u][p];
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const uint32_t lo = pack_bf2(av[p][0], av[p][1]), hi = pack_bf2(av[p][2], av[p][3]);
+                *(uint2*)&sA[(arow0 + RPP * p) * PA + sl * D + acol] = make_uint2(lo, hi);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- each wave: its 64-feature column tiles over the whole K
+    constexpr int KC = 4;                      // k-steps of W_o fragments loaded ahead
+    constexpr int BSTEP = PACKED ? 1024 : 16;  // elements between a lane's fragments of consecutive k-steps
+    const int NT = d_model / 64, KS = K / 16;
+    const uint16_t* a0p = sA + (lane & 31) * PA + 8 * (lane >> 5);
+    const uint16_t* a1p = a0p + 32 * PA;
+    for (int ct = wave; ct < NT; ct += kOtWaves) {
+        const int n0 = ct * 64;
+        const uint16_t* b0p = PACKED ? w_o + (size_t)n0 * K + lane * 8
+                                     : w_o + (size_t)(n0 + (lane & 31)) * K + 8 * (lane >> 5);
+        const uint16_t* b1p = PACKED ? b0p + 512 : b0p + (size_t)32 * K;
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        u32x4 bc[KC][2], bn[KC][2];
+#pragma unroll
+        for (int u = 0; u < KC; ++u) {
+            const int ks = min(u, KS - 1);
+            bc[u][0] = ld_u32x4(b0p + BSTEP * ks);
+            bc[u][1] = ld_u32x4(b1p + BSTEP * ks);
+        }
+        for (int c0 = 0; c0 < KS; c0 += KC) {
+            const bool more = c0 + KC < KS;
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < KC; ++u) {
+                    const int ks = min(c0 + KC + u, KS - 1);
+                    bn[u][0] = ld_u32x4(b0p + BSTEP * ks);
+                    bn[u][1] = ld_u32x4(b1p + BSTEP * ks);
+                }
+            }
+            if (c0 + KC <= KS) {
+                // a whole chunk: no per-step test, so the slot fragments' LDS reads are issued ahead
+                bf16x8 a0[KC], a1[KC];
+#pragma unroll
+                for (int u = 0; u < KC; ++u) {
+                    a0[u] = ld_bf16x8(a0p + 16 * (c0 + u));
+                    a1[u] = ld_bf16x8(a1p + 16 * (c0 + u));
+                }
+#pragma unroll
+                for (int u = 0; u < KC; ++u) {
+                    const bf16x8 b0 = __builtin_bit_cast(bf16x8, bc[u][0]), b1 = __builtin_bit_cast(bf16x8, bc[u][1]);
+                    acc[0][0] = mfma32(a0[u], b0, acc[0][0]);
+                    acc[0][1] = mfma32(a0[u], b1, acc[0][1]);
+                    acc[1][0] = mfma32(a1[u], b0, acc[1][0]);
+                    acc[1][1] = mfma32(a1[u], b1, acc[1][1]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < KC; ++u) {
+                    const int ks = c0 + u;
+                    if (ks < KS) {
+                        const bf16x8 a0 = ld_bf16x8(a0p + 16 * ks), a1 = ld_bf16x8(a1p + 16 * ks);
+                        const bf16x8 b0 = __builtin_bit_cast(bf16x8, bc[u][0]), b1 = __builtin_bit_cast(bf16x8, bc[u][1]);
+                        acc[0][0] = mfma32(a0, b0, acc[0][0]);
+                        acc[0][1] = mfma32(a0, b1, acc[0][1]);
+                        acc[1][0] = mfma32(a1, b0, acc[1][0]);
+                        acc[1][1] = mfma32(a1, b1, acc[1][1]);
+                    }
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int u = 0; u < KC; ++u) {
+                    bc[u][0] = bn[u][0];
+                    bc[u][1] = bn[u][1];
+                }
+            }
+        }
+        // element e of block (i, j): token 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, feature 32 j + lane % 32
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const long long t = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (t >= BT) continue;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) y[(size_t)t * d_model + n0 + 32 * j + (lane & 31)] = acc[i][j][e];
+            }
+    }
+}
+
+// W_o [d_model, K] bf16 -> fragment order (see PACKED above): one thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void out_proj_pack_kernel(const uint16_t* __restrict__ w_o, uint16_t* __restrict__ wp,
+                                                            int d_model, int K)
+{
+    const long long q = (long long)blockIdx.x * 256 + threadIdx.x;   // destination chunk
+    const int KS = K / 16;
+    if (q >= (long long)d_model * KS * 2) return;
+    const int l = (int)(q & 63);
+    const long long blk = q >> 6;                                    // (ct * KS + ks) * 2 + cb
+    const int cb = (int)(blk & 1);
+    const long long cs = blk >> 1;
+    const int ks = (int)(cs % KS), ct = (int)(cs / KS);
+    const int n = 64 * ct + 32 * cb + (l & 31);
+    *(u32x4*)(wp + q * 8) = ld_u32x4(w_o + (size_t)n * K + 16 * ks + 8 * (l >> 5));
+}
+
 // fp32: one thread per output element, fp32 FMA chain over the slots in the
 // stage order above; the thread of feature 0 also writes the weighted slot(s).
 __global__ __launch_bounds__(256) void out_proj_f32_kernel(float* __restrict__ out, const float* __restrict__ p_tilde,
@@ -246,6 +455,16 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(float* __restrict__ o
     y[(size_t)t * d_model + n] = s;
 }
 
+int launch_out_proj_pack(const void* w_o, void* w_packed, int d_model, int K, hipStream_t st)
+{
+    if (!out_proj_tile_fits(K, d_model) || K % 16) return -2;
+    const long long chunks = (long long)d_model * (K / 16) * 2;
+    if (chunks == 0) return 0;
+    out_proj_pack_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, st>>>((const uint16_t*)w_o, (uint16_t*)w_packed,
+                                                                           d_model, K);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_out_proj(const OutProjArgs& a, hipStream_t st)
 {
     if (a.BT == 0) return 0;
@@ -254,6 +473,40 @@ int launch_out_proj(const OutProjArgs& a, hipStream_t st)
         out_proj_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(a.out, a.p_tilde, (const float*)a.w_o, a.y,
                                                                            a.BT, a.d_model, a.G, a.k, a.d_head, a.route_mode,
                                                                            a.S, a.write_weighted);
+        return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+    // packed weights: the token-tile kernel (row-major W_o stays on the kernel below, which reads it
+    // through LDS with coalesced loads: 54 against 58 us for the tile kernel on main_250m)
+    const int K = a.S * a.d_head;
+    if (a.w_packed) {
+        if (!out_proj_tile_fits(K, a.d_model)) return -2;
+        const long long grid = (a.BT + kOtM - 1) / kOtM;
+        if (grid >= (1ll << 31)) return -2;
+        const int lds = ot_lds_bytes(K);
+        // the LDS limit is raised once per kernel to the largest tile that fits (setting it per call
+        // costs host time comparable to the kernel's)
+#define GQE_OT(D, PK)                                                                                                 \
+    do {                                                                                                              \
+        static std::atomic<int> raised{0};                                                                            \
+        if (lds > 65536 && !raised.load(std::memory_order_acquire)) {                                                 \
+            if (hipFuncSetAttribute((const void*)&out_proj_tile_kernel<D, PK>,                                         \
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, kOtMaxLds) != hipSuccess)             \
+                return -1;                                                                                            \
+            raised.store(1, std::memory_order_release);                                                               \
+        }                                                                                                             \
+        out_proj_tile_kernel<D, PK><<<(unsigned)grid, 64 * kOtWaves, lds, st>>>(                                      \
+            a.out, a.p_tilde, (const uint16_t*)(PK ? a.w_packed : a.w_o), a.y, a.BT, a.d_model, a.G, a.k,            \
+            a.route_mode, a.S, a.write_weighted);                                                                     \
+    } while (0)
+#define GQE_OT2(D) GQE_OT(D, true)
+        switch (a.d_head) {
+        case 32: GQE_OT2(32); break;
+        case 64: GQE_OT2(64); break;
+        case 128: GQE_OT2(128); break;
+        default: return -2;
+        }
+#undef GQE_OT2
+#undef GQE_OT
         return hipGetLastError() == hipSuccess ? 0 : -1;
     }
     const int nN = (a.d_model + kOpBN - 1) / kOpBN;

@@ -34,7 +34,7 @@ EXPORTS = ("gqe_num_slots", "gqe_status_string", "gqe_route_workspace_bytes", "g
            "gqe_route_backward", "gqe_attn_backward_workspace_bytes", "gqe_attn_backward", "gqe_route_stats",
            "gqe_attn_decode_noalloc", "gqe_qkv_proj", "gqe_qkv_proj_backward",
            "gqe_qkv_proj_backward_workspace_bytes", "gqe_decode_route_qproj", "gqe_attn_prefill_heads_lse",
-           "gqe_attn_backward_lse")
+           "gqe_attn_backward_lse", "gqe_out_proj_packed_bytes", "gqe_out_proj_pack", "gqe_out_proj_packed")
 
 
 class GqeError(RuntimeError):
@@ -123,6 +123,12 @@ def load():
         lib.gqe_attn_backward_workspace_bytes.restype = Z
         lib.gqe_attn_backward.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
         lib.gqe_attn_backward.restype = I
+        lib.gqe_out_proj_packed_bytes.argtypes = [D]
+        lib.gqe_out_proj_packed_bytes.restype = Z
+        lib.gqe_out_proj_pack.argtypes = [D, P, P, P]
+        lib.gqe_out_proj_pack.restype = I
+        lib.gqe_out_proj_packed.argtypes = [D, P, P, P, P, ctypes.c_int32, P]
+        lib.gqe_out_proj_packed.restype = I
         lib.gqe_attn_prefill_heads_lse.argtypes = [D, P, P, P, P, P, P, P, Z, P]
         lib.gqe_attn_prefill_heads_lse.restype = I
         lib.gqe_attn_backward_lse.argtypes = [D, P, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
@@ -404,6 +410,33 @@ def gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted=False, stream=None):
     _check("gqe_out_proj", rc)
 
 
+def gqe_out_proj_packed_bytes(desc) -> int:
+    return load().gqe_out_proj_packed_bytes(ctypes.byref(desc))
+
+
+def gqe_out_proj_pack(desc, w_o, w_packed, stream=None):
+    rc = load().gqe_out_proj_pack(ctypes.byref(desc), _ptr(w_o, desc.torch_dtype, "w_o"),
+                                  _ptr(w_packed, desc.torch_dtype, "w_packed"), _stream(stream))
+    _check("gqe_out_proj_pack", rc)
+
+
+def gqe_out_proj_packed(desc, out, p_tilde, w_packed, y, write_weighted=False, stream=None):
+    rc = load().gqe_out_proj_packed(ctypes.byref(desc), _ptr(out, torch.float32, "out"),
+                                    _ptr(p_tilde, torch.float32, "p_tilde"),
+                                    _ptr(w_packed, desc.torch_dtype, "w_packed"), _ptr(y, torch.float32, "y"),
+                                    int(bool(write_weighted)), _stream(stream))
+    _check("gqe_out_proj_packed", rc)
+
+
+def out_proj_pack(desc, w_o, stream=None) -> torch.Tensor:
+    """W_o rearranged into the packed order gqe_out_proj_packed reads (a tensor of W_o's shape and dtype)."""
+    if gqe_out_proj_packed_bytes(desc) == 0:
+        raise GqeError("gqe_out_proj_pack", -2)
+    w_packed = torch.empty_like(w_o)
+    gqe_out_proj_pack(desc, w_o, w_packed, stream)
+    return w_packed
+
+
 def gqe_attn_decode(desc, q_routed, q_shared, k_cache, v_cache, lens, p_tilde, out, workspace, stream=None):
     dt = desc.torch_dtype
     L_max = k_cache.shape[2]
@@ -596,11 +629,15 @@ def attn_decode(desc, q: dict, k_cache, v_cache, lens, p_tilde, out=None, worksp
     return out
 
 
-def out_proj(desc, out, p_tilde, w_o, y=None, write_weighted=False, stream=None) -> torch.Tensor:
-    """y = W_o h_t over the concatenated slots of every token (weighted slot(s) formed inside)."""
+def out_proj(desc, out, p_tilde, w_o, y=None, write_weighted=False, w_packed=None, stream=None) -> torch.Tensor:
+    """y = W_o h_t over the concatenated slots of every token (weighted slot(s) formed inside); with w_packed
+    (out_proj_pack's result) the packed-weight call."""
     if y is None:
         y = torch.empty((desc.B * desc.T, desc.d_model), dtype=torch.float32, device=out.device)
-    gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted, stream)
+    if w_packed is not None:
+        gqe_out_proj_packed(desc, out, p_tilde, w_packed, y, write_weighted, stream)
+    else:
+        gqe_out_proj(desc, out, p_tilde, w_o, y, write_weighted, stream)
     return y
 
 

@@ -177,15 +177,19 @@ def full_decode_check(w: W.Workload, inp: dict | None = None):
 
 
 def gpu_out_proj(w: W.Workload, out_slots: torch.Tensor, p_tilde: torch.Tensor, w_o: torch.Tensor,
-                 write_weighted: bool = True, dev="cuda"):
-    """gqe_out_proj on the given slots [B*T, S, d_head] with the weighted slot(s) set to NaN first, so
-    that a read of them would show in y.  Returns (y, slots after the call) on the CPU."""
+                 write_weighted: bool = True, dev="cuda", packed: bool = False):
+    """gqe_out_proj (packed: gqe_out_proj_pack, then gqe_out_proj_packed) on the given slots [B*T, S, d_head]
+    with the weighted slot(s) set to NaN first, so that a read of them would show in y.  Returns (y, slots
+    after the call) on the CPU."""
     d = G.desc_from(w)
     kG, nr = w.k * w.G, (1, w.G, 0, 0)[w.route_mode]
     o = out_slots.reshape(w.B * w.T, d.S, w.d_head).clone()
     o[:, kG:kG + nr] = float("nan")
     od = o.to(dev)
-    y = G.out_proj(d, od, p_tilde.reshape(w.B * w.T, w.G, w.k).to(dev), w_o.to(dev), write_weighted=write_weighted)
+    wd = w_o.to(dev)
+    wp = G.out_proj_pack(d, wd) if packed else None
+    y = G.out_proj(d, od, p_tilde.reshape(w.B * w.T, w.G, w.k).to(dev), wd, write_weighted=write_weighted,
+                   w_packed=wp)
     torch.cuda.synchronize()
     return y.cpu(), od.cpu()
 

@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = G.load()
     names = declared_functions()
-    assert len(names) == 28
+    assert len(names) == 31
     assert set(names) == set(G.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -351,6 +351,23 @@ def test_attention_lse_entries_reject_fp32_and_missing_statistics():
     assert bwd(f32) == UNSUPPORTED
     assert bwd(d, None) == INVALID
     assert bwd(d, ws=None) == WORKSPACE
+
+
+def test_out_proj_packed_sizes_and_rejects():
+    lib = G.load()
+    d = main()
+    K = d.H_kv * d.k * d.d_head + 2 * d.d_head                   # S = kG + 2 slots of d_head
+    assert G.gqe_out_proj_packed_bytes(d) == d.d_model * K * 2
+    assert G.gqe_out_proj_packed_bytes(main(dtype="f32")) == 0
+    assert G.gqe_out_proj_packed_bytes(main(H_q=32, H_kv=8, k=2, d_head=128)) == 0   # 64 x (2304 + 8) x 2 > 160 KiB
+    assert lib.gqe_out_proj_pack(ctypes.byref(main(dtype="f32")), A16, A16, None) == UNSUPPORTED
+    assert lib.gqe_out_proj_pack(ctypes.byref(d), None, A16, None) == INVALID
+    assert lib.gqe_out_proj_pack(ctypes.byref(d), A16, MIS, None) == ALIGN
+    op = lambda desc, wp=A16, ww=0: lib.gqe_out_proj_packed(ctypes.byref(desc), A16, A16, wp, A16, ww, None)  # noqa: E731
+    assert op(main(dtype="f32")) == UNSUPPORTED
+    assert op(d, ww=2) == INVALID
+    assert op(d, wp=None) == INVALID
+    assert op(main(B=0)) == OK
 
 
 def test_qkv_proj_rejects_bad_rope_base_and_pointers():

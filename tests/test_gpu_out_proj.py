@@ -11,6 +11,7 @@ import torch
 
 import workloads as W
 from gpu_parity_util import check_out_proj, gpu_decode, gpu_out_proj, gpu_prefill, say
+import sparse_routed_query_amd.gqe as G
 
 pytestmark = pytest.mark.gpu
 
@@ -22,12 +23,12 @@ def small(**kw):
     return W.Workload(**base)
 
 
-def run_and_check(w, tok=None):
+def run_and_check(w, tok=None, packed=False):
     inp = W.make_inputs(w)
     gpu = gpu_prefill(w, inp)
     wo = W.make_w_o(w)
     slots = gpu["out"].reshape(w.B * w.T, -1, w.d_head)
-    y, after = gpu_out_proj(w, slots, gpu["p_tilde"], wo)
+    y, after = gpu_out_proj(w, slots, gpu["p_tilde"], wo, packed=packed)
     # the weighted slot(s) written back are gqe_assemble's bits; the other slots are untouched
     assert torch.equal(after, slots)
     assert torch.isfinite(y).all()
@@ -58,12 +59,46 @@ def test_out_proj_every_token(w):
     run_and_check(w)
 
 
-def test_out_proj_main_250m_sampled():
+@pytest.mark.parametrize("w", [x for x in SHAPES if x.dtype == "bf16"], ids=lambda w: f"{w.name}-d{w.d_head}")
+def test_out_proj_packed_every_token(w):
+    """The packed-weight call against the oracle at the same bound, its weighted-slot write-back equal to the
+    plain call's bit for bit, and y within fp32 reordering of the plain call's."""
+    gpu, wo, slots, y = run_and_check(w, packed=True)
+    y2, after2 = gpu_out_proj(w, slots, gpu["p_tilde"], wo)
+    _, after = gpu_out_proj(w, slots, gpu["p_tilde"], wo, packed=True)
+    assert torch.equal(torch.nan_to_num(after, nan=7.0), torch.nan_to_num(after2, nan=7.0))
+    rel = float((y - y2).norm() / max(float(y2.norm()), 1e-30))
+    say(f"[{w.name}] packed vs plain: relative rms {rel:.2e}")
+    assert rel <= 1e-5
+
+
+def test_out_proj_pack_layout():
+    """gqe_out_proj_pack writes W_o[64 ct + 32 cb + c][16 ks + 8 h + e] at
+    ((ct K/16 + ks) 2 + cb) 512 + (32 h + c) 8 + e, the order the header defines."""
+    w = small(d_model=192, name="pack_layout")
+    d = G.desc_from(w)
+    wo = W.make_w_o(w)
+    got = G.out_proj_pack(d, wo.cuda()).cpu().reshape(-1)
+    dm, K = wo.shape
+    ref = wo.reshape(dm // 64, 2, 32, K // 16, 2, 8).permute(0, 3, 1, 4, 2, 5).reshape(-1)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_out_proj_packed_is_refused_where_it_has_no_form():
+    wide = small(H_q=32, H_kv=8, k=2, d_head=128, name="wide_k")   # K = 18 * 128: a 64-token tile exceeds LDS
+    assert G.gqe_out_proj_packed_bytes(G.desc_from(wide)) == 0
+    assert G.gqe_out_proj_packed_bytes(G.desc_from(small(dtype="f32", name="f32"))) == 0
+    with pytest.raises(G.GqeError):
+        G.out_proj_pack(G.desc_from(wide), W.make_w_o(wide).cuda())
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
+def test_out_proj_main_250m_sampled(packed):
     w = W.WORKLOADS["main_250m"]
     BT = w.B * w.T
     rng = np.random.default_rng(0)
     tok = np.unique(np.concatenate([np.arange(0, BT, BT // 256), rng.integers(0, BT, 128), [0, BT - 1]]))
-    run_and_check(w, tok)
+    run_and_check(w, tok, packed=packed)
 
 
 def test_out_proj_after_decode_and_without_write_back():
