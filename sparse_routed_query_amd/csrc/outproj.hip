@@ -320,6 +320,8 @@ __global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* 
     constexpr int KC = 4;                      // k-steps of W_o fragments loaded ahead
     constexpr int BSTEP = PACKED ? 1024 : 16;  // elements between a lane's fragments of consecutive k-steps
     const int NT = d_model / 64, KS = K / 16;
+    const __amdgpu_buffer_rsrc_t rY = __builtin_amdgcn_make_buffer_rsrc((void*)(y + (size_t)m0 * d_model), 0,
+                                                                         rows * d_model * 4, 0x00020000);
     const uint16_t* a0p = sA + (lane & 31) * PA + 8 * (lane >> 5);
     const uint16_t* a1p = a0p + 32 * PA;
     for (int ct = wave; ct < NT; ct += kOtWaves) {
@@ -334,23 +336,18 @@ __global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* 
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-        u32x4 bc[KC][2], bn[KC][2];
+        // W_o fragments in two register sets used in turn: the loads of the next chunk of KC k-steps
+        // are issued before the current chunk's products
+        u32x4 bA[KC][2], bB[KC][2];
+        auto load_b = [&](u32x4 (&b)[KC][2], int c0) {
 #pragma unroll
-        for (int u = 0; u < KC; ++u) {
-            const int ks = min(u, KS - 1);
-            bc[u][0] = ld_u32x4(b0p + BSTEP * ks);
-            bc[u][1] = ld_u32x4(b1p + BSTEP * ks);
-        }
-        for (int c0 = 0; c0 < KS; c0 += KC) {
-            const bool more = c0 + KC < KS;
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < KC; ++u) {
-                    const int ks = min(c0 + KC + u, KS - 1);
-                    bn[u][0] = ld_u32x4(b0p + BSTEP * ks);
-                    bn[u][1] = ld_u32x4(b1p + BSTEP * ks);
-                }
+            for (int u = 0; u < KC; ++u) {
+                const int ks = min(c0 + u, KS - 1);
+                b[u][0] = ld_u32x4(b0p + BSTEP * ks);
+                b[u][1] = ld_u32x4(b1p + BSTEP * ks);
             }
+        };
+        auto mma = [&](const u32x4 (&b)[KC][2], int c0) {
             if (c0 + KC <= KS) {
                 // a whole chunk: no per-step test, so the slot fragments' LDS reads are issued ahead
                 bf16x8 a0[KC], a1[KC];
@@ -361,7 +358,7 @@ __global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* 
                 }
 #pragma unroll
                 for (int u = 0; u < KC; ++u) {
-                    const bf16x8 b0 = __builtin_bit_cast(bf16x8, bc[u][0]), b1 = __builtin_bit_cast(bf16x8, bc[u][1]);
+                    const bf16x8 b0 = __builtin_bit_cast(bf16x8, b[u][0]), b1 = __builtin_bit_cast(bf16x8, b[u][1]);
                     acc[0][0] = mfma32(a0[u], b0, acc[0][0]);
                     acc[0][1] = mfma32(a0[u], b1, acc[0][1]);
                     acc[1][0] = mfma32(a1[u], b0, acc[1][0]);
@@ -373,7 +370,7 @@ __global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* 
                     const int ks = c0 + u;
                     if (ks < KS) {
                         const bf16x8 a0 = ld_bf16x8(a0p + 16 * ks), a1 = ld_bf16x8(a1p + 16 * ks);
-                        const bf16x8 b0 = __builtin_bit_cast(bf16x8, bc[u][0]), b1 = __builtin_bit_cast(bf16x8, bc[u][1]);
+                        const bf16x8 b0 = __builtin_bit_cast(bf16x8, b[u][0]), b1 = __builtin_bit_cast(bf16x8, b[u][1]);
                         acc[0][0] = mfma32(a0, b0, acc[0][0]);
                         acc[0][1] = mfma32(a0, b1, acc[0][1]);
                         acc[1][0] = mfma32(a1, b0, acc[1][0]);
@@ -381,24 +378,28 @@ __global__ __launch_bounds__(64 * kOtWaves, 1) void out_proj_tile_kernel(float* 
                     }
                 }
             }
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < KC; ++u) {
-                    bc[u][0] = bn[u][0];
-                    bc[u][1] = bn[u][1];
-                }
-            }
+        };
+        // (loads past the last k-step repeat it, in bounds, and are not used)
+        load_b(bA, 0);
+        for (int c0 = 0; c0 < KS; c0 += 2 * KC) {
+            load_b(bB, c0 + KC);
+            mma(bA, c0);
+            load_b(bA, c0 + 2 * KC);
+            mma(bB, c0 + KC);
         }
-        // element e of block (i, j): token 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, feature 32 j + lane % 32
+        // element e of block (i, j): token 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, feature 32 j + lane % 32;
+        // buffer stores over the tile's rows, so rows past B*T are dropped without a branch (the value goes
+        // through __float_as_uint: this compiler's __builtin_bit_cast of a vector element reads element 0)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const long long t = m0 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (t >= BT) continue;
+            for (int e = 0; e < 16; ++e)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) y[(size_t)t * d_model + n0 + 32 * j + (lane & 31)] = acc[i][j][e];
-            }
+                for (int j = 0; j < 2; ++j) {
+                    const int r = 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e]), rY,
+                                                          (r * d_model + n0 + 32 * j + (lane & 31)) * 4, 0, 0);
+                }
     }
 }
 
