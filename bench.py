@@ -367,7 +367,7 @@ def kv_proj_leg(p, torch, steps):
     fl = 2.0 * w.B * w.T * w.d_model * 2 * w.H_kv * w.d_head
     fl_all = fl + W.qproj_flops(w)
     tf = fl / (t * 1e-3) / 1e12
-    return {"workload": w.name, "kernel": f"qproj_bf16_kernel<{w.d_head}, 64> as dense heads (gqe_kv_proj)",
+    return {"workload": w.name, "kernel": f"kv_dense_kernel<{w.d_head}> (gqe_kv_proj)",
             "us": t * 1e3, "tflops": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": fl,
             "qkv_proj_us": t_qkv * 1e3, "qkv_proj_rope_us": t_rope * 1e3, "qproj_plus_kv_proj_us": (t + t_qp) * 1e3,
             "qkv_proj_tflops": fl_all / (t_qkv * 1e-3) / 1e12, "qkv_proj_flops": fl_all}

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libgqe.so")
 CALIB_SRC = "calib.hip"
 CALIB_LIB = os.path.join(HERE, "libgqe_calib.so")
 SOURCES = ["gqe_api.cpp", "route.hip", "qproj.hip", "attn_prefill.hip", "attn_decode.hip", "outproj.hip",
-           "route_bwd.hip", "attn_bwd.hip", "proj_bwd.hip", "decode_pre.hip"]
+           "route_bwd.hip", "attn_bwd.hip", "proj_bwd.hip", "decode_pre.hip", "kvproj.hip"]
 ARCH = os.environ.get("GQE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

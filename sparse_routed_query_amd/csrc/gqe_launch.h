@@ -94,6 +94,19 @@ struct KvProjArgs {
 };
 int launch_kv_proj(const KvProjArgs& a, hipStream_t st);
 
+// K and V of every token as one dense GEMM (bf16): kvproj.hip.
+struct KvDenseArgs {
+    const uint16_t* x;          // [B*T, d_model]
+    const uint16_t* w_k;        // [H, d_head, d_model]
+    const uint16_t* w_v;
+    void* k_out;                // [B, H, T, d_head]
+    void* v_out;
+    const int32_t* positions;   // [B*T] or NULL (position t)
+    int B, T, d_model, H, d_head;
+    double rope_log2_base;      // 0: no rotary embedding of K
+};
+int launch_kv_dense(const KvDenseArgs& a, hipStream_t st);
+
 struct QkvProjArgs {
     const void* x;            // [B*T, d_model]
     const void* w_q;          // [N + n_shared, d_head, d_model]

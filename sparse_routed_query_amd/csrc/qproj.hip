@@ -425,8 +425,23 @@ int launch_qproj(const QprojArgs& a, hipStream_t st)
 // K and V projections (GQA tutorial, freeguideonline, "GQA 核心原理与计算流程"
 // step 2): the same kernel with no routed experts and 2 H_kv dense heads over
 // every token in one launch, written as [B, H_kv, T, d_head].
+static KvDenseArgs kv_dense_args(const void* x, const void* w_k, const void* w_v, void* k, void* v,
+                                 const int32_t* positions, int B, int T, int d_model, int H, int d_head,
+                                 double rope_log2_base)
+{
+    KvDenseArgs d{};
+    d.x = (const uint16_t*)x; d.w_k = (const uint16_t*)w_k; d.w_v = (const uint16_t*)w_v; d.k_out = k; d.v_out = v;
+    d.positions = positions; d.B = B; d.T = T; d.d_model = d_model; d.H = H; d.d_head = d_head;
+    d.rope_log2_base = rope_log2_base;
+    return d;
+}
+
 int launch_kv_proj(const KvProjArgs& a, hipStream_t st)
 {
+    // bf16: one dense GEMM over every token (kvproj.hip)
+    if (a.bf16)
+        return launch_kv_dense(kv_dense_args(a.x, a.w_k, a.w_v, a.k, a.v, nullptr, a.B, a.T, a.d_model, a.H_kv,
+                                             a.d_head, 0.0), st);
     QpArgs q = qp_args(a.x, a.B, a.T, a.d_model, 0, 1, 1);
     q.w_k = a.w_k; q.w_v = a.w_v; q.k_out = a.k; q.v_out = a.v;
     q.nkv = a.H_kv;   // at most 64 (the descriptor's limit), so one plan covers both
@@ -448,6 +463,14 @@ int launch_qkv_proj(const QkvProjArgs& a, hipStream_t st)
     q.nkv = a.H_kv;
     q.positions = a.positions;
     q.rope_log2_base = a.rope_base > 0.f ? log2((double)a.rope_base) : 0.0;
+    if (a.bf16) {
+        // the queries over their compacted rows, then K and V as one dense GEMM
+        QpArgs qq = q;
+        qq.nkv = 0;
+        const int rc = launch_qp(qq, a.d_head, true, st);
+        return rc ? rc : launch_kv_dense(kv_dense_args(a.x, a.w_k, a.w_v, a.k, a.v, a.positions, a.B, a.T,
+                                                       a.d_model, a.H_kv, a.d_head, q.rope_log2_base), st);
+    }
     if (qp_n_exp(q) <= 128) return launch_qp(q, a.d_head, a.bf16, st);
     // more experts than one plan covers: the queries, then K and V
     QpArgs qq = q, qkv = q;
