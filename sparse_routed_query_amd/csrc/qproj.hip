@@ -304,35 +304,54 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
         for (int j = 0; j < (NB > 1 ? NB / 2 : 1); ++j)
             freq[j] = qp_rope_freq(NB > 1 ? 32 * j + c0 : (c0 & 15), D, a.rope_log2_base);
     }
+    // results leave through the wave's own LDS region, 16 rows at a time, so every global store is 16 bytes
+    // of one output row (the stage buffers are free: every wave passed the barrier above)
+    constexpr int RPC = D + 8;                          // region pitch (bf16)
+    constexpr int CH = D / 8;                           // 16-byte chunks per row
+    uint16_t* reg = sA + wave * 16 * RPC;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int mm = wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const size_t o = s_dst[mm];
-        float v[NB];
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) v[j] = acc[j][e];
-        if (rope) {
-            const int pos = s_pos[mm];
-            if constexpr (NB == 1) {
-                // D = 32: column c pairs with c ^ 16, held by lane l ^ 16
-                const float other = __shfl_xor(v[0], 16);
-                float sn, cs;
-                sincosf(qp_rope_angle(pos, freq[0]), &sn, &cs);
-                v[0] = c0 < 16 ? v[0] * cs - other * sn : v[0] * cs + other * sn;
-            } else {
+        for (int e = 8 * p; e < 8 * p + 8; ++e) {
+            const int mm = wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            float v[NB];
 #pragma unroll
-                for (int j = 0; j < NB / 2; ++j) {
+            for (int j = 0; j < NB; ++j) v[j] = acc[j][e];
+            if (rope) {
+                const int pos = s_pos[mm];
+                if constexpr (NB == 1) {
+                    // D = 32: column c pairs with c ^ 16, held by lane l ^ 16
+                    const float other = __shfl_xor(v[0], 16);
                     float sn, cs;
-                    sincosf(qp_rope_angle(pos, freq[j]), &sn, &cs);
-                    const float x1 = v[j], x2 = v[j + NB / 2];
-                    v[j] = x1 * cs - x2 * sn;
-                    v[j + NB / 2] = x2 * cs + x1 * sn;
+                    sincosf(qp_rope_angle(pos, freq[0]), &sn, &cs);
+                    v[0] = c0 < 16 ? v[0] * cs - other * sn : v[0] * cs + other * sn;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NB / 2; ++j) {
+                        float sn, cs;
+                        sincosf(qp_rope_angle(pos, freq[j]), &sn, &cs);
+                        const float x1 = v[j], x2 = v[j + NB / 2];
+                        v[j] = x1 * cs - x2 * sn;
+                        v[j + NB / 2] = x2 * cs + x1 * sn;
+                    }
                 }
             }
-        }
-        if (o == ~(size_t)0) continue;
+            const int rl = 8 * ((e >> 2) & 1) + 4 * (lane >> 5) + (e & 3);   // row within the 16
 #pragma unroll
-        for (int j = 0; j < NB; ++j) dst[o + j * 32 + c0] = __builtin_bit_cast(uint16_t, f2bf(v[j]));
+            for (int j = 0; j < NB; ++j) reg[rl * RPC + j * 32 + c0] = __builtin_bit_cast(uint16_t, f2bf(v[j]));
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int q = 0; q < 16 * CH / 64; ++q) {
+            const int idx = lane + 64 * q, rl = idx / CH, ch = idx % CH;
+            const size_t o = s_dst[wave * 32 + 16 * p + rl];
+            if (o != ~(size_t)0) *(u32x4*)&dst[o + 8 * ch] = *(const u32x4*)&reg[rl * RPC + 8 * ch];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
