@@ -173,13 +173,15 @@ struct QpNT {
 };
 // One workgroup computes a BM-row tile of one expert: Q = X[rows] W_q[n]^T,
 // each wave 32 rows.  Per stage of BK columns of d_model the x rows and the
-// weight slice are loaded with 16-byte coalesced loads (16 lanes per 256-byte
+// weight slice are loaded with 16-byte coalesced loads (8 lanes per 128-byte
 // row segment) into registers while the previous stage is multiplied out of
-// LDS, then stored to LDS between two barriers.  Rows past the bucket's end
-// reload its last row and are not stored, so every load is unconditional.
-// The epilogue applies the rotary embedding in fp32 where asked (pairs
-// (c, c + D/2) of a row, which a lane holds in blocks j and j + NB/2, or at
-// D = 32 in lanes l and l ^ 16) and rounds once to bf16.
+// LDS, then stored to LDS (d_head <= 64: one buffer between two barriers;
+// 128: the other of two buffers, mid-stage, one barrier).  Rows past the
+// bucket's end reload its last row and are not stored, so every load is
+// unconditional.  The epilogue applies the rotary embedding in fp32 where
+// asked (pairs (c, c + D/2) of a row, which a lane holds in blocks j and
+// j + NB/2, or at D = 32 in lanes l and l ^ 16), rounds once to bf16 and
+// writes each row through LDS as 16-byte stores.
 template <int D, int BK>
 __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
 {
@@ -207,8 +209,13 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
     constexpr int CPR = BK / 8;                           // 16-byte chunks per row of a stage
     constexpr int ACH = BM * CPR / NT;                    // A chunks per thread
     constexpr int BCH = D * CPR / NT;                     // B chunks per thread
-    __shared__ __attribute__((aligned(16))) uint16_t sA[BM * P];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[D * P];
+    // the stages of x rows and weight rows in LDS: at d_head 128 two, used in turn with one barrier per
+    // stage (one workgroup of eight waves per compute unit); below, one stage between two barriers, which
+    // keeps more workgroups on a compute unit (two buffers cost 10 % at d_head 64 and gain 17 % at 128)
+    constexpr bool DB = D >= 128;
+    constexpr int STG = (BM + D) * P;
+    __shared__ __attribute__((aligned(16))) uint16_t sS[(DB ? 2 : 1) * STG];
+    uint16_t* const sA = sS;   // stage 0's x rows; the epilogue's regions
 
     // row pointers of this thread's A chunks (rows tid / CPR + i * 256 / CPR)
     const int col = (tid % CPR) * 8;
@@ -228,11 +235,11 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
         for (int i = 0; i < BCH; ++i) rb[i] = ld_u32x4(pb + (size_t)i * (NT / CPR) * d_model + k0);
     };
     const int w_off = (tid / CPR) * P + col;
-    auto store = [&]() {
+    auto store = [&](uint16_t* buf) {
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) *(u32x4*)&sA[w_off + i * (NT / CPR) * P] = ra[i];
+        for (int i = 0; i < ACH; ++i) *(u32x4*)&buf[w_off + i * (NT / CPR) * P] = ra[i];
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) *(u32x4*)&sB[w_off + i * (NT / CPR) * P] = rb[i];
+        for (int i = 0; i < BCH; ++i) *(u32x4*)&buf[BM * P + w_off + i * (NT / CPR) * P] = rb[i];
     };
 
     f32x16 acc[NB];
@@ -244,36 +251,41 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
     const int nst = d_model / BK;
     const int a_off = (wave * 32 + (lane & 31)) * P + 8 * (lane >> 5);
     const int b_off = (lane & 31) * P + 8 * (lane >> 5);
-    load(0);
-    for (int st = 0; st < nst; ++st) {
-        __syncthreads();
-        store();
-        __syncthreads();
-        if (st + 1 < nst) load((st + 1) * BK);
-        if constexpr (D >= 128) {
-            // all fragments of the stage first, so the reads overlap each other
-            // and the MFMAs wait only for their own operands (at d = 64 the
-            // extra registers cost a wave per SIMD, which costs more)
-            bf16x8 fa[BK / 16], fb[BK / 16][NB];
+    auto mma = [&](const uint16_t* buf, int kk) {
+        const uint16_t* bA = buf;
+        const uint16_t* bB = buf + BM * P;
+        const bf16x8 fa = ld_bf16x8(&bA[a_off + kk]);
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                fa[kk] = ld_bf16x8(&sA[a_off + 16 * kk]);
+        for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa, ld_bf16x8(&bB[b_off + j * 32 * P + kk]), acc[j]);
+    };
+    if constexpr (DB) {
+        load(0);
+        store(sS);
+        if (nst > 1) load(BK);
+        __syncthreads();
+        for (int st = 0; st < nst; ++st) {
+            const uint16_t* cur = sS + (st & 1) * STG;
 #pragma unroll
-                for (int j = 0; j < NB; ++j) fb[kk][j] = ld_bf16x8(&sB[b_off + j * 32 * P + 16 * kk]);
+            for (int kk = 0; kk < BK / 2; kk += 16) mma(cur, kk);
+            // the next stage into the other buffer (its readers passed the last barrier), then its successor's
+            // loads
+            if (st + 1 < nst) {
+                store(sS + ((st + 1) & 1) * STG);
+                if (st + 2 < nst) load((st + 2) * BK);
             }
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk)
+            for (int kk = BK / 2; kk < BK; kk += 16) mma(cur, kk);
+            __syncthreads();
+        }
+    } else {
+        load(0);
+        for (int st = 0; st < nst; ++st) {
+            __syncthreads();
+            store(sS);
+            __syncthreads();
+            if (st + 1 < nst) load((st + 1) * BK);
 #pragma unroll
-                for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa[kk], fb[kk][j], acc[j]);
-            __builtin_amdgcn_sched_group_barrier(0x100, (BK / 16) * (NB + 1), 0);   // the LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, (BK / 16) * NB, 0);         // then the MFMAs
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 16) {
-                const bf16x8 fa = ld_bf16x8(&sA[a_off + kk]);
-#pragma unroll
-                for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa, ld_bf16x8(&sB[b_off + j * 32 * P + kk]), acc[j]);
-            }
+            for (int kk = 0; kk < BK; kk += 16) mma(sS, kk);
         }
     }
 
