@@ -345,6 +345,153 @@ __global__ __launch_bounds__(256, 2) void pb_dx_kernel(const ProjBwdArgs a, int 
         }
 }
 
+// dx at d_head 64 with wider tiles: one workgroup of four waves per 128 tokens x 256 columns, so the fp32
+// gradient rows are read once per 256 columns (not 128); one head per stage in two LDS buffers used in turn
+// (the next head is stored between the halves of the current one's products, one barrier per head); each
+// wave 64 tokens x 128 columns as 2 x 4 blocks, so every fragment read from LDS feeds two or four products;
+// dx leaves by buffer stores over the tile's rows.  The same products in the same order per output element
+// as pb_dx_kernel.
+struct PbDx64 {
+    static constexpr int D = 64, BM = 128, BN = 256;
+    static constexpr int PA = D + 8, PW = BN + 32;
+    static constexpr int STG = BM * PA + D * PW;            // bf16 elements of one stage
+    static constexpr int NA = BM * (D / 8) / 256;           // gradient pairs per thread and head
+    static constexpr int NW = D * (BN / 8) / 256;           // weight chunks per thread and head
+};
+
+__global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, int n_heads)
+{
+    using S = PbDx64;
+    constexpr int D = S::D, BM = S::BM, BN = S::BN, PA = S::PA, PW = S::PW, STG = S::STG, NA = S::NA, NW = S::NW;
+    const int d_model = a.d_model, BT = a.B * a.T, N = a.G * a.E;
+    const int ncol = (d_model + BN - 1) / BN;
+    const int tok0 = (blockIdx.x / ncol) * BM, col0 = (blockIdx.x % ncol) * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;   // 2 x 2 waves of 64 tokens x 128 columns
+    __shared__ __attribute__((aligned(16))) uint16_t sS[2 * STG];
+    // the tile's kept experts (G*k <= 16 of them per token), so that a routed head's row lookup reads LDS
+    // instead of waiting on a global load before the gradient load it addresses
+    constexpr int KMAX = 16;
+    __shared__ int s_sel[BM * KMAX];
+    const int Gk = a.G * a.k;
+    const bool staged = Gk <= KMAX;
+    if (staged)
+        for (int i = tid; i < BM * Gk; i += 256) {
+            const int m = i / Gk, tok = min(tok0 + m, BT - 1);
+            s_sel[m * KMAX + i % Gk] = a.sel[(size_t)tok * Gk + i % Gk];
+        }
+    __syncthreads();
+    // gradient row of head n for the tile's token m (as pb_src, with the kept experts from LDS)
+    auto src_of = [&](int kind, int h, int n, int m) -> const float* {
+        if (kind != 0 || !staged) return pb_src(a, kind, h, n, tok0 + m);
+        const int tok = tok0 + m, b = tok / a.T, t = tok - b * a.T;
+        const int g = n / a.E, e = n - g * a.E;
+        int j = -1;
+        for (int i = 0; i < a.k; ++i) j = s_sel[m * KMAX + g * a.k + i] == e ? i : j;
+        return j < 0 ? nullptr : a.dq_routed + ((((size_t)b * a.G + g) * a.T + t) * a.k + j) * D;
+    };
+
+    f32x4 au[NA], aw[NA];
+    u32x4 wr[NW];
+    auto load = [&](int n) {
+        int h;
+        const int kind = pb_kind(a, n, h);
+        const bool rot = a.rope_log2_base > 0.0 && kind <= 2;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
+            const int tok = tok0 + m;
+            const float* src = nullptr;
+            int pos = 0;
+            if (tok < BT) {
+                src = src_of(kind, h, n, m);
+                pos = a.positions ? a.positions[tok] : tok % a.T;
+            }
+            pb_load_pair(a, src, rot, pos, d0, au[i], aw[i]);
+        }
+        const uint16_t* w = (kind <= 1 ? a.w_q + (size_t)(kind == 0 ? n : N + h) * D * d_model
+                                       : (kind == 2 ? a.w_k : a.w_v) + (size_t)h * D * d_model);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int task = tid + 256 * i, d = task / (BN / 8);
+            const int c = min(col0 + (task % (BN / 8)) * 8, d_model - 8);
+            wr[i] = ld_u32x4(w + (size_t)d * d_model + c);
+        }
+    };
+    auto store = [&](uint16_t* buf) {
+        uint16_t* sA = buf;
+        uint16_t* sW = buf + BM * PA;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
+            *(uint64_t*)&sA[m * PA + d0] = pb_pack4(au[i]);
+            *(uint64_t*)&sA[m * PA + d0 + D / 2] = pb_pack4(aw[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int task = tid + 256 * i, d = task / (BN / 8), c = (task % (BN / 8)) * 8;
+            *(u32x4*)&sW[d * PW + c] = wr[i];
+        }
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    auto mma = [&](const uint16_t* buf, int c) {
+        const uint16_t* sA = buf;
+        const uint16_t* sW = buf + BM * PA;
+        bf16x8 fa[2], fb[4];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) fa[mi] = frag_perm(sA, PA, 64 * wm + 32 * mi, 16 * c, lane);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) fb[ni] = frag_tr(sW, PW, 16 * c, 128 * wn + 32 * ni, lane);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma32(fa[mi], fb[ni], acc[mi][ni]);
+    };
+
+    load(0);
+    store(sS);
+    if (n_heads > 1) load(1);
+    __syncthreads();
+    for (int n = 0; n < n_heads; ++n) {
+        const uint16_t* cur = sS + (n & 1) * STG;
+        mma(cur, 0);
+        mma(cur, 1);
+        // the next head into the other buffer (its readers passed the last barrier), then its successor's loads
+        if (n + 1 < n_heads) {
+            store(sS + ((n + 1) & 1) * STG);
+            if (n + 2 < n_heads) load(n + 2);
+        }
+        mma(cur, 2);
+        mma(cur, 3);
+        __syncthreads();
+    }
+
+    // element e of block (mi, ni): token 64 wm + 32 mi + 8 (e / 4) + 4 (lane / 32) + e % 4,
+    // column 128 wn + 32 ni + lane % 32; buffer stores over the tile's rows and columns
+    const int rows = min(BM, BT - tok0);
+    const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dx + (size_t)tok0 * d_model), 0,
+                                                                         rows * d_model * 4, 0x00020000);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int col = col0 + 128 * wn + 32 * ni + (lane & 31);
+            if (col >= d_model) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = 64 * wm + 32 * mi + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mi][ni][e]), rD, (r * d_model + col) * 4, 0, 0);
+            }
+        }
+}
+
 // Row chunks of the weight gradient: enough workgroups for the chip (about
 // four per compute unit), at most 16.
 static int pb_nchunk(const ProjBwdArgs& a)
@@ -385,7 +532,11 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
             pb_dw_reduce_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a, nc, part);
         }
     }
-    if (a.dx) {
+    if (a.dx && a.D == 64) {
+        const int ncol = (a.d_model + PbDx64::BN - 1) / PbDx64::BN;
+        const unsigned grid = (unsigned)(((BT + PbDx64::BM - 1) / PbDx64::BM) * ncol);
+        pb_dx64_kernel<<<grid, 256, 0, st>>>(a, n_heads);
+    } else if (a.dx) {
         const int ncol = (a.d_model + 127) / 128, bm = a.D >= 128 ? 64 : 128;
         const unsigned grid = (unsigned)(((BT + bm - 1) / bm) * ncol);
         switch (a.D) {
