@@ -364,8 +364,13 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
     using S = PbDx64;
     constexpr int D = S::D, BM = S::BM, BN = S::BN, PA = S::PA, PW = S::PW, STG = S::STG, NA = S::NA, NW = S::NW;
     const int d_model = a.d_model, BT = a.B * a.T, N = a.G * a.E;
-    const int ncol = (d_model + BN - 1) / BN;
-    const int tok0 = (blockIdx.x / ncol) * BM, col0 = (blockIdx.x % ncol) * BN;
+    const int ncol = (d_model + BN - 1) / BN, nM = (BT + BM - 1) / BM;
+    // workgroup -> tile: the column tiles of a token tile get indices 8 apart, so they run on one XCD and
+    // its L2 serves their shared gradient rows
+    const int L = blockIdx.x, xcd = L & 7, rr = L >> 3;
+    const int tm = (rr / ncol) * 8 + xcd;
+    if (tm >= nM) return;
+    const int tok0 = tm * BM, col0 = (rr % ncol) * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;   // 2 x 2 waves of 64 tokens x 128 columns
     __shared__ __attribute__((aligned(16))) uint16_t sS[2 * STG];
@@ -533,8 +538,8 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
         }
     }
     if (a.dx && a.D == 64) {
-        const int ncol = (a.d_model + PbDx64::BN - 1) / PbDx64::BN;
-        const unsigned grid = (unsigned)(((BT + PbDx64::BM - 1) / PbDx64::BM) * ncol);
+        const int ncol = (a.d_model + PbDx64::BN - 1) / PbDx64::BN, nM = (BT + PbDx64::BM - 1) / PbDx64::BM;
+        const unsigned grid = (unsigned)(8 * ((nM + 7) / 8) * ncol);
         pb_dx64_kernel<<<grid, 256, 0, st>>>(a, n_heads);
     } else if (a.dx) {
         const int ncol = (a.d_model + 127) / 128, bm = a.D >= 128 ? 64 : 128;
