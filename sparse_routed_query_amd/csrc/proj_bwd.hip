@@ -103,7 +103,7 @@ struct PbDw {
     static constexpr int NX = SR * (BN / 8) / 256;    // x chunks per thread and stage
 };
 
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(256, D >= 64 ? 2 : 3) void pb_dw_kernel(const ProjBwdArgs a, int nchunk, float* part)
 {
     using S = PbDw<D>;
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, D >= 64 ? 2 : 3) void pb_dw_kernel(const ProjB
     const int r_lo = min(ch * per, Mh);
     const int M = min(per, Mh - r_lo);
     const int base = (kind == 0 ? a.offsets[n] : 0) + r_lo;
-    const bool rot = a.rope_log2_base > 0.0 && kind <= 2;
+    const bool rot = ROT && kind <= 2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ __attribute__((aligned(16))) uint16_t sQ[SR * PQ];
     __shared__ __attribute__((aligned(16))) uint16_t sX[SR * PX];
@@ -249,7 +249,7 @@ struct PbDx {
     static constexpr int NW = D * (BN / 8) / 256;     // weight chunks per thread and head
 };
 
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(256, 2) void pb_dx_kernel(const ProjBwdArgs a, int n_heads)
 {
     using S = PbDx<D>;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void pb_dx_kernel(const ProjBwdArgs a, int 
     auto load = [&](int n) {
         int h;
         const int kind = pb_kind(a, n, h);
-        const bool rot = a.rope_log2_base > 0.0 && kind <= 2;
+        const bool rot = ROT && kind <= 2;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
@@ -359,6 +359,7 @@ struct PbDx64 {
     static constexpr int NW = D * (BN / 8) / 256;           // weight chunks per thread and head
 };
 
+template <bool ROT>
 __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, int n_heads)
 {
     using S = PbDx64;
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
     auto load = [&](int n) {
         int h;
         const int kind = pb_kind(a, n, h);
-        const bool rot = a.rope_log2_base > 0.0 && kind <= 2;
+        const bool rot = ROT && kind <= 2;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
@@ -520,6 +521,8 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
     const int BT = a.B * a.T;
     if (BT == 0) return 0;
     const int n_heads = a.G * a.E + a.ns + 2 * a.nkv;
+    // kernels without the rotary code when it is off (inlined per row, it made them several times larger)
+    const bool rot = a.rope_log2_base > 0.0;
     if (a.dw_q || a.dw_k || a.dw_v) {
         const size_t need = proj_bwd_workspace_bytes(a);
         const int nc = (need > 0 && workspace && workspace_bytes >= need) ? pb_nchunk(a) : 1;
@@ -527,9 +530,12 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
         const int ncol = (a.d_model + 255) / 256;
         const unsigned grid = (unsigned)(n_heads * ncol * nc);
         switch (a.D) {
-        case 32: pb_dw_kernel<32><<<grid, 256, 0, st>>>(a, nc, part); break;
-        case 64: pb_dw_kernel<64><<<grid, 256, 0, st>>>(a, nc, part); break;
-        case 128: pb_dw_kernel<128><<<grid, 256, 0, st>>>(a, nc, part); break;
+        case 32: rot ? pb_dw_kernel<32, true><<<grid, 256, 0, st>>>(a, nc, part)
+                     : pb_dw_kernel<32, false><<<grid, 256, 0, st>>>(a, nc, part); break;
+        case 64: rot ? pb_dw_kernel<64, true><<<grid, 256, 0, st>>>(a, nc, part)
+                     : pb_dw_kernel<64, false><<<grid, 256, 0, st>>>(a, nc, part); break;
+        case 128: rot ? pb_dw_kernel<128, true><<<grid, 256, 0, st>>>(a, nc, part)
+                      : pb_dw_kernel<128, false><<<grid, 256, 0, st>>>(a, nc, part); break;
         default: return -2;
         }
         if (nc > 1) {
@@ -540,14 +546,18 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
     if (a.dx && a.D == 64) {
         const int ncol = (a.d_model + PbDx64::BN - 1) / PbDx64::BN, nM = (BT + PbDx64::BM - 1) / PbDx64::BM;
         const unsigned grid = (unsigned)(8 * ((nM + 7) / 8) * ncol);
-        pb_dx64_kernel<<<grid, 256, 0, st>>>(a, n_heads);
+        rot ? pb_dx64_kernel<true><<<grid, 256, 0, st>>>(a, n_heads)
+            : pb_dx64_kernel<false><<<grid, 256, 0, st>>>(a, n_heads);
     } else if (a.dx) {
         const int ncol = (a.d_model + 127) / 128, bm = a.D >= 128 ? 64 : 128;
         const unsigned grid = (unsigned)(((BT + bm - 1) / bm) * ncol);
         switch (a.D) {
-        case 32: pb_dx_kernel<32><<<grid, 256, 0, st>>>(a, n_heads); break;
-        case 64: pb_dx_kernel<64><<<grid, 256, 0, st>>>(a, n_heads); break;
-        case 128: pb_dx_kernel<128><<<grid, 256, 0, st>>>(a, n_heads); break;
+        case 32: rot ? pb_dx_kernel<32, true><<<grid, 256, 0, st>>>(a, n_heads)
+                     : pb_dx_kernel<32, false><<<grid, 256, 0, st>>>(a, n_heads); break;
+        case 64: rot ? pb_dx_kernel<64, true><<<grid, 256, 0, st>>>(a, n_heads)
+                     : pb_dx_kernel<64, false><<<grid, 256, 0, st>>>(a, n_heads); break;
+        case 128: rot ? pb_dx_kernel<128, true><<<grid, 256, 0, st>>>(a, n_heads)
+                      : pb_dx_kernel<128, false><<<grid, 256, 0, st>>>(a, n_heads); break;
         default: return -2;
         }
     }
