@@ -118,16 +118,17 @@ __device__ __forceinline__ int wave_scan_i(int v, int lane)
     return v;
 }
 
-__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int n_exp, int BT, bool routed, int BM,
-                        int lane, int& n_out, int& tile_out)
+__device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int N,
+                        int n_exp, int BT, bool routed, int BM, int lane, int& n_out, int& tile_out, int& m_out,
+                        int& base_out)
 {
-    // n_exp <= 128: two candidate experts per lane
-    auto ntiles = [&](int n) {
-        if (n >= n_exp || (n < N && !routed)) return 0;
-        const int M = n < N ? counts[n] : BT;
-        return (M + BM - 1) / BM;
-    };
-    const int c0 = ntiles(lane), c1 = ntiles(lane + 64);
+    // n_exp <= 128: two candidate experts per lane, with their row counts and bucket starts (loaded together,
+    // so the chosen expert's need no second round trip)
+    auto rows_of = [&](int n) { return n >= n_exp || (n < N && !routed) ? 0 : n < N ? counts[n] : BT; };
+    auto start_of = [&](int n) { return n < N && routed ? offsets[n] : 0; };
+    const int m0 = rows_of(lane), m1 = rows_of(lane + 64);
+    const int s0 = start_of(lane), s1 = start_of(lane + 64);
+    const int c0 = (m0 + BM - 1) / BM, c1 = (m1 + BM - 1) / BM;
     const int U = wave_sum_i(c0 + c1);
     const int R = wave_max_i(max(c0, c1));
     const int chunk = (U + 7) / 8;
@@ -149,6 +150,8 @@ __device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int 
         const int ln = __ffsll((long long)m) - 1;
         n = ln;
         tile = __shfl(b0, ln) + rem - (__shfl(p0, ln) - __shfl(k0, ln));
+        m_out = __shfl(m0, ln);
+        base_out = __shfl(s0, ln);
     } else {
         rem -= t0;
         const int p1 = wave_scan_i(k1, lane);
@@ -156,6 +159,8 @@ __device__ bool qp_plan(int bid, const int32_t* __restrict__ counts, int N, int 
         const int ln = __ffsll((long long)m) - 1;
         n = ln + 64;
         tile = __shfl(b1, ln) + rem - (__shfl(p1, ln) - __shfl(k1, ln));
+        m_out = __shfl(m1, ln);
+        base_out = __shfl(s1, ln);
     }
     n_out = n;
     tile_out = tile;
@@ -188,20 +193,19 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
     constexpr int NT = QpNT<D>::NT, BM = QpNT<D>::BM;
     const int N = a.G * a.E, BT = a.B * a.T, n_exp = qp_n_exp(a), d_model = a.d_model;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    __shared__ int s_item[2];
+    __shared__ int s_item[4];
     if (wave == 0) {
-        int pn = -1, pt = 0;
-        if (!qp_plan(blockIdx.x, a.counts, N, n_exp, BT, a.q_routed != nullptr, BM, lane, pn, pt)) pn = -1;
-        if (lane == 0) { s_item[0] = pn; s_item[1] = pt; }
+        int pn = -1, pt = 0, pm = 0, pb = 0;
+        if (!qp_plan(blockIdx.x, a.counts, a.offsets, N, n_exp, BT, a.q_routed != nullptr, BM, lane, pn, pt, pm, pb))
+            pn = -1;
+        if (lane == 0) { s_item[0] = pn; s_item[1] = pt; s_item[2] = pm; s_item[3] = pb; }
     }
     __syncthreads();
     const int n = s_item[0];
     if (n < 0) return;
     int h;
     const int kind = qp_kind(a, n, h);
-    const int row0 = s_item[1] * BM;
-    const int M = kind == 0 ? a.counts[n] : BT;
-    const int base = kind == 0 ? a.offsets[n] : 0;
+    const int row0 = s_item[1] * BM, M = s_item[2], base = s_item[3];
     const uint16_t* wsrc = kind <= 1 ? (const uint16_t*)a.w_q + (size_t)(kind == 0 ? n : N + h) * D * d_model
                                      : (const uint16_t*)(kind == 2 ? a.w_k : a.w_v) + (size_t)h * D * d_model;
     constexpr int P = BK + kQpPad;
@@ -258,8 +262,27 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa, ld_bf16x8(&bB[b_off + j * 32 * P + kk]), acc[j]);
     };
+    // destinations (and rotary positions) of the tile's rows, looked up while the first stage loads (the
+    // barriers of the stage loop publish them); rows past the bucket are not stored
+    __shared__ size_t s_dst[BM];
+    __shared__ int s_pos[BM];
+    auto lookup = [&]() {
+        for (int m = tid; m < BM; m += NT) {
+            const int r = row0 + m;
+            size_t o = ~(size_t)0;
+            int pos = 0;
+            if (r < M) {
+                const int tok = kind == 0 ? a.rows[base + r] : r;
+                o = qp_dst(a, kind, h, n, tok, D);
+                pos = a.positions ? a.positions[tok] : tok % a.T;
+            }
+            s_dst[m] = o;
+            s_pos[m] = pos;
+        }
+    };
     if constexpr (DB) {
         load(0);
+        lookup();
         store(sS);
         if (nst > 1) load(BK);
         __syncthreads();
@@ -279,6 +302,7 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
         }
     } else {
         load(0);
+        lookup();
         for (int st = 0; st < nst; ++st) {
             __syncthreads();
             store(sS);
@@ -289,22 +313,7 @@ __global__ __launch_bounds__(QpNT<D>::NT) void qproj_bf16_kernel(const QpArgs a)
         }
     }
 
-    // destinations (and rotary positions) of the tile's rows; rows past the bucket are not stored
-    __shared__ size_t s_dst[BM];
-    __shared__ int s_pos[BM];
-    const int m = wave * 32 + (lane & 31);
-    if (lane < 32) {
-        const int r = row0 + m;
-        size_t o = ~(size_t)0;
-        int pos = 0;
-        if (r < M) {
-            const int tok = kind == 0 ? a.rows[base + r] : r;
-            o = qp_dst(a, kind, h, n, tok, D);
-            pos = a.positions ? a.positions[tok] : tok % a.T;
-        }
-        s_dst[m] = o;
-        s_pos[m] = pos;
-    }
+    // every wave is past its last read of the stage buffers before they hold the results
     __syncthreads();
     uint16_t* dst = (uint16_t*)(kind == 0 ? a.q_routed : kind == 1 ? a.q_shared : kind == 2 ? a.k_out : a.v_out);
     const bool rope = a.rope_log2_base > 0.0 && kind <= 2;
