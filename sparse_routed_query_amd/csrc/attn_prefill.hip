@@ -106,6 +106,7 @@ __host__ __device__ __forceinline__ long long pf_count_ge(const PfSched& p, int 
 // pf_count_ge(p, s) > id.
 __host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, long long id, int s)
 {
+    const long long gid = id;
     id -= pf_count_ge(p, s + 1);
     PfItem w{0, 0, 0, -1, -1};
     for (int l = 0; l < 2; ++l) {
@@ -127,11 +128,15 @@ __host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, lon
             if (id < n) {
                 const int i = e - 1 - (int)(id / per);
                 const int rem = (int)(id % per);
-                // split tiles come part-major (all part 0s, then all part 1s):
-                // workgroup j runs on XCD j mod 8, so with cnt a multiple of 8
-                // both halves and the whole tiles of a head keep to the same
-                // XCDs, whose L2 then serves the head's K/V to all of them
-                const int bh = sp ? rem % (int)cnt : rem;
+                // a tile's items come as runs of cnt consecutive workgroups, one
+                // per head (split tiles part-major: all part 0s, then all part
+                // 1s).  Workgroup j runs on XCD j mod 8, so when cnt is a
+                // multiple of 8 the run's workgroup j takes head
+                // 8 floor(r / 8) + j mod 8 (r its rank in the run): every item
+                // of a head, whole or either half, then runs on XCD head mod 8,
+                // whose L2 serves the head's K/V to all of them
+                const int r = sp ? rem % (int)cnt : rem;
+                const int bh = cnt % 8 == 0 ? (r & ~7) | (int)(gid & 7) : r;
                 w.tile = i;
                 w.part = sp ? rem / (int)cnt : -1;
                 if (l == 0) {

@@ -215,7 +215,11 @@ def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=7
     tiles of 64 and its first row sees key 64*(nkv//2), provided the longest
     tile needs more key tiles than the average load of 768 workgroup slots;
     sorted by item size (larger part), routed before shared, split before
-    whole, tile descending, split tiles by part then head."""
+    whole, tile descending, split tiles by part then head.  Then, since
+    workgroup j runs on XCD j mod 8: in each run of one tile's items over a
+    number of heads that is a multiple of 8, the item at position j takes the
+    run's head 8*(r//8) + j%8 (r its rank in the run), so all items of a head
+    run on one XCD."""
     def nkv_of(i, kk):
         if not causal:
             return -(-T // 64)
@@ -238,19 +242,25 @@ def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=7
         first_split = nt
         while split and first_split > 0 and can(first_split - 1):
             first_split -= 1
+        base = n_pairs_r if lst else 0
         for i in range(nt):
             n = nkv(i)
-            for hi, (b, h) in enumerate(heads):
+            for hi in range(len(heads)):
                 if i >= first_split:
-                    pair = (n_pairs_r if lst else 0) + (i - first_split) * len(heads) + hi
                     for part in (0, 1):   # part-major: all part 0s of a tile, then all part 1s
-                        items.append(((-(n - n // 2), lst, 0, -i, part, hi), (b, h, i, part, pair)))
+                        items.append(((-(n - n // 2), lst, 0, -i, part, hi), (heads, hi, i, part, base, first_split)))
                 else:
-                    items.append(((-n, lst, 1, -i, hi, 0), (b, h, i, -1, -1)))
+                    items.append(((-n, lst, 1, -i, hi, 0), (heads, hi, i, -1, base, first_split)))
         if lst == 0:
             n_pairs_r = (nt - first_split) * len(heads)
-    items.sort()
-    return [it for _, it in items]
+    items.sort(key=lambda it: it[0])
+    out = []
+    for j, (_, (heads, r, i, part, base, first_split)) in enumerate(items):
+        hi = 8 * (r // 8) + j % 8 if len(heads) % 8 == 0 else r
+        b, h = heads[hi]
+        pair = base + (i - first_split) * len(heads) + hi if part >= 0 else -1
+        out.append((b, h, i, part, pair))
+    return out
 
 
 @pytest.mark.parametrize("shape", [
@@ -270,6 +280,8 @@ def test_prefill_plan_matches_its_definition(shape):
         want = plan_reference(shape["B"], shape["T"], 8, shape["k"], shape["n_shared"], shape["causal"], split)
         assert got == want, (split, len(got), len(want))
     plan = G.gqe_attn_prefill_plan(d, True)
+    # 8 groups per batch here, so every routed head's items (whole or either half) share one XCD, j mod 8
+    assert all(j % 8 == (int(r[0]) * 8 + int(r[1])) % 8 for j, r in enumerate(plan) if r[1] < 8)
     pairs = sorted((int(r[4]), int(r[3])) for r in plan if r[3] >= 0)
     n_pairs = len(pairs) // 2
     assert pairs == [(p, part) for p in range(n_pairs) for part in (0, 1)]
