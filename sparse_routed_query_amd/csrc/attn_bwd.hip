@@ -6,10 +6,11 @@
 // Per head, with S = q K^T / sqrt(d), P = softmax(S) (masked), O = P V:
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Delta),  Delta_r = <dO_r, O_r>,
 //   dq = dS K / sqrt(d),   dK = dS^T q / sqrt(d).
-// The forward keeps no row statistics, so the dq kernel first recomputes each
-// row's log-sum-exp (base 2) and Delta, writes them to the workspace for the
-// dK/dV kernel, then forms dq.  No atomics: every output element is written by
-// one workgroup, with its sums in a fixed order.
+// Unless the forward kept its row statistics, the dq kernel first recomputes
+// each row's log-sum-exp (base 2); it writes Delta (and the recomputed
+// statistic) to the workspace for the dK/dV kernel, then forms dq.  No
+// atomics: every output element is written by one workgroup, with its sums in
+// a fixed order.
 //
 // Both kernels: 256 threads = 4 waves, tiles of 64 query rows x 64 keys,
 // 32x32x16 bf16 MFMA.  Score tiles are formed transposed (S^T = K q^T), so a
@@ -60,6 +61,7 @@ struct RowSet {
     float* lse;            // row r's base-2 log-sum-exp at lse[r], Delta at delta[r]
     float* delta;
     int R, kk;
+    int kshift;            // log2(kk) when kk is a power of two, else -1
 };
 
 __device__ __forceinline__ RowSet row_set(const AttnBwdArgs& a, int b, int h)
@@ -79,6 +81,7 @@ __device__ __forceinline__ RowSet row_set(const AttnBwdArgs& a, int b, int h)
         rs.delta = a.delta + base;
         rs.R = T * k;
         rs.kk = k;
+        rs.kshift = (k & (k - 1)) == 0 ? __builtin_ctz(k) : -1;
     } else {
         const long long base = (long long)b * T;
         rs.q = (const uint16_t*)a.q_shared + base * D;
@@ -91,6 +94,7 @@ __device__ __forceinline__ RowSet row_set(const AttnBwdArgs& a, int b, int h)
         rs.delta = a.delta + nrouted + base;
         rs.R = T;
         rs.kk = 1;
+        rs.kshift = 0;
     }
     return rs;
 }
@@ -181,17 +185,14 @@ __device__ __forceinline__ void rows_load(const RowSet& rs, int r0, RowRegs<D>& 
     constexpr int CPR = D / 8;
 #pragma unroll
     for (int i = 0; i < RowRegs<D>::N; ++i) {
-        const int c = threadIdx.x + 256 * i, row = c / CPR, d0 = (c % CPR) * 8, rr = r0 + row;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        r.q[i] = u32x4{0u, 0u, 0u, 0u};
-        r.g[2 * i] = r.g[2 * i + 1] = z;
-        if (rr < rs.R) {
-            r.q[i] = ld_u32x4(rs.q + (size_t)rr * D + d0);
-            const int t = rr / rs.kk, j = rr - t * rs.kk;
-            const float* g = rs.dO + (size_t)t * rs.dO_stride + (size_t)j * D + d0;
-            r.g[2 * i] = *(const f32x4*)g;
-            r.g[2 * i + 1] = *(const f32x4*)(g + 4);
-        }
+        // rows past R read row R - 1: their log-sum-exp is +inf (below), so their P and dS are 0 and they add
+        // nothing, and every load is unconditional
+        const int c = threadIdx.x + 256 * i, row = c / CPR, d0 = (c % CPR) * 8, rr = min(r0 + row, rs.R - 1);
+        r.q[i] = ld_u32x4(rs.q + (size_t)rr * D + d0);
+        const int t = rs.kshift >= 0 ? rr >> rs.kshift : rr / rs.kk, j = rr - t * rs.kk;
+        const float* g = rs.dO + (size_t)t * rs.dO_stride + (size_t)j * D + d0;
+        r.g[2 * i] = *(const f32x4*)g;
+        r.g[2 * i + 1] = *(const f32x4*)(g + 4);
     }
     const int rr = r0 + (int)threadIdx.x;
     r.lse = INFINITY;   // (rows past R weigh nothing)
@@ -247,10 +248,21 @@ __device__ __forceinline__ f32x16 gemm_az(f32x16 c, const uint16_t* A, int m0, c
     return c;
 }
 
+// C[m][n] += sum over the 64 rows k of A[k][m] Z[k][n]: A a row-major [64][64+8] tile and Z a row-major
+// [64][D+8] tile, both read across (columns m0 + l%32 and n0 + l%32) in frag_tr's k order
+template <int D>
+__device__ __forceinline__ f32x16 gemm_tt(f32x16 c, const uint16_t* A, int m0, const uint16_t* Z, int n0, int lane)
+{
+    constexpr int P = D + 8, PS = kAbTile + 8;
+#pragma unroll
+    for (int s = 0; s < kAbTile / 16; ++s) c = mfma32(frag_tr(A, PS, 16 * s, m0, lane), frag_tr(Z, P, 16 * s, n0, lane), c);
+    return c;
+}
+
 template <int D>
 constexpr int ab_lds_bytes(bool dq)
 {
-    // q, dO, K, V tiles; then dS (dq kernel) or P^T and dS^T (dK/dV kernel); then row data
+    // q, dO, K, V tiles; then dS (dq kernel) or P and dS (dK/dV kernel); then row data
     return 4 * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 +
            (dq ? kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 : 0) + 2 * kAbTile * 4;
 }
@@ -451,8 +463,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
     uint16_t* sdO = sQ + kAbTile * P;
     uint16_t* sK = sdO + kAbTile * P;
     uint16_t* sV = sK + kAbTile * P;
-    uint16_t* sP = sV + kAbTile * P;          // P^T [key][row]
-    uint16_t* sD = sP + kAbTile * PS;         // dS^T [key][row]
+    uint16_t* sP = sV + kAbTile * P;          // P [row][key]
+    uint16_t* sD = sP + kAbTile * PS;         // dS [row][key]
     float* s_lse = (float*)(sD + kAbTile * PS);
     float* s_delta = s_lse + kAbTile;
 
@@ -502,33 +514,32 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
         const float lse_r = s_lse[row], dl_r = s_delta[row];
         const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
-        // a tile whose keys all lie inside T and before its first row's position needs no mask
-        if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk)) {
+        // P and dS as bf16 in [row][key] order, four consecutive keys per 8-byte store; a tile whose keys all
+        // lie inside T and before its first row's position needs no mask (the mask is a select, not a branch)
+        const bool need_mask = s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kl = wk * 32 + acc_row(i, lane);
-                const int key = s0 + kl;
-                const bool ok = key < T && (!a.causal || key <= tq);
-                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r) : 0.f;
-                sP[kl * PS + kpos(row)] = bf16_bits(pv);
-                sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
-            }
-        } else {
+        for (int i4 = 0; i4 < 4; ++i4) {
+            float pv[4], ds[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kl = wk * 32 + acc_row(i, lane);
-                const float pv = __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r);
-                sP[kl * PS + kpos(row)] = bf16_bits(pv);
-                sD[kl * PS + kpos(row)] = bf16_bits(pv * (dp[i] - dl_r));
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                const int key = s0 + wk * 32 + acc_row(i, lane);
+                const bool ok = !need_mask || (key < T && (!a.causal || key <= tq));
+                const float ex = __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r);
+                pv[e] = ok ? ex : 0.f;
+                ds[e] = pv[e] * (dp[i] - dl_r);
             }
+            const int off = row * PS + wk * 32 + acc_row(4 * i4, lane);
+            *(uint2*)(sP + off) = make_uint2(pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3]));
+            *(uint2*)(sD + off) = make_uint2(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]));
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int blk = wave + 4 * j;
             if (blk < 2 * (D / 32)) {
-                dv[j] = gemm_az<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
-                dk[j] = gemm_az<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
+                dv[j] = gemm_tt<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
+                dk[j] = gemm_tt<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
             }
         }
         __syncthreads();

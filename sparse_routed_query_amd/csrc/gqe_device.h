@@ -18,9 +18,13 @@ __device__ __forceinline__ float bf2f(uint16_t u) { return __builtin_bit_cast(fl
 __device__ __forceinline__ float bf2f(bf16 b) { return bf2f(__builtin_bit_cast(uint16_t, b)); }
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 f2bf(float f) { return (bf16)f; }
+// two floats rounded to bf16 (nearest even, as f2bf), lo in the low half: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi)
 {
-    return (uint32_t)__builtin_bit_cast(uint16_t, f2bf(lo)) | ((uint32_t)__builtin_bit_cast(uint16_t, f2bf(hi)) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const void* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
