@@ -262,8 +262,9 @@ __device__ __forceinline__ f32x16 gemm_tt(f32x16 c, const uint16_t* A, int m0, c
 template <int D>
 constexpr int ab_lds_bytes(bool dq)
 {
-    // q, dO, K, V tiles; then dS (dq kernel) or P and dS (dK/dV kernel); then row data
-    return 4 * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 +
+    // q, dO, K (dq kernel only), V tiles; then dS (dq kernel) or P and dS (dK/dV kernel, whose K tile is staged
+    // there once and then held in registers); then row data
+    return (dq ? 4 : 3) * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 +
            (dq ? kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 : 0) + 2 * kAbTile * 4;
 }
 
@@ -454,19 +455,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
     }
 }
 
+// Three workgroups per compute unit (two at d_head 128): the key tile is fixed per workgroup, so each wave
+// keeps its 32 keys' K fragments in registers and K needs no LDS of its own.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
+__global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
 {
     constexpr int P = D + 8, PS = kAbTile + 8, NBW = (2 * (D / 32) + 3) / 4;
     extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
     uint16_t* sQ = s_ab;
     uint16_t* sdO = sQ + kAbTile * P;
-    uint16_t* sK = sdO + kAbTile * P;
-    uint16_t* sV = sK + kAbTile * P;
-    uint16_t* sP = sV + kAbTile * P;          // P [row][key]
+    uint16_t* sV = sdO + kAbTile * P;
+    uint16_t* sP = sV + kAbTile * P;          // P [row][key]; before the loop, the K tile
     uint16_t* sD = sP + kAbTile * PS;         // dS [row][key]
     float* s_lse = (float*)(sD + kAbTile * PS);
     float* s_delta = s_lse + kAbTile;
+    static_assert(kAbTile * P <= 2 * kAbTile * PS, "the K tile is staged in the P and dS region");
 
     const int T = a.T, G = a.G;
     const int nkt = (T + kAbTile - 1) / kAbTile;
@@ -479,7 +482,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
     const int wk = wave & 1, wr = wave >> 1;
     const int row = wr * 32 + (lane & 31);
 
-    load_keys<D>((const uint16_t*)a.k_ + ((size_t)b * G + g) * T * D, s0, T, sK);
+    load_keys<D>((const uint16_t*)a.k_ + ((size_t)b * G + g) * T * D, s0, T, sP);
     load_keys<D>((const uint16_t*)a.v_ + ((size_t)b * G + g) * T * D, s0, T, sV);
 
     f32x16 dk[NBW], dv[NBW];
@@ -499,6 +502,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
     RowRegs<D> rr;
     if (nit > 0) rows_load<D>(rs0, a0 * kAbTile, rr);
     __syncthreads();
+    // this wave's K fragments (keys wk * 32 + l % 32), read once; the region then holds P and dS
+    bf16x8 kf[D / 16];
+    {
+        const uint16_t* xa = sP + (wk * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) kf[st] = frag_row(xa + 16 * st);
+    }
     if (nit > 0) rows_store<D>(rr, sQ, sdO, s_lse, s_delta);
     __syncthreads();
     for (int it = 0; it < nit; ++it) {
@@ -512,7 +522,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
         }
         const int tq = (r0 + row) / rs.kk;
         const float lse_r = s_lse[row], dl_r = s_delta[row];
-        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        f32x16 c;
+        {
+            const uint16_t* yb = sQ + (wr * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = 0.f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) c = mfma32(kf[st], frag_row(yb + 16 * st), c);
+        }
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
         // P and dS as bf16 in [row][key] order, four consecutive keys per 8-byte store; a tile whose keys all
         // lie inside T and before its first row's position needs no mask (the mask is a select, not a branch)
