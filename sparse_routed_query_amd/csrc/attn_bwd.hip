@@ -262,29 +262,40 @@ __device__ __forceinline__ f32x16 gemm_tt(f32x16 c, const uint16_t* A, int m0, c
 template <int D>
 constexpr int ab_lds_bytes(bool dq)
 {
-    // q, dO, K (dq kernel only), V tiles; then dS (dq kernel) or P and dS (dK/dV kernel, whose K tile is staged
-    // there once and then held in registers); then row data
-    return (dq ? 4 : 3) * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 +
-           (dq ? kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 : 0) + 2 * kAbTile * 4;
+    // dK/dV kernel: q, dO, V tiles, then P and dS (where the K tile is staged once before it is held in
+    // registers), then row data.  dq kernel at d_head <= 64: dO, K, V tiles, then dS (where q is staged once
+    // before it is held in registers), then row data.  dq kernel at d_head 128: q, dO, K, V, dS, then the
+    // partial sums of Delta and of the row statistics, then row data.
+    if (!dq) return 3 * kAbTile * (D + 8) * 2 + 2 * kAbTile * (kAbTile + 8) * 2 + 2 * kAbTile * 4;
+    if (D <= 64) return 3 * kAbTile * (D + 8) * 2 + kAbTile * (kAbTile + 8) * 2 + 2 * kAbTile * 4;
+    return 4 * kAbTile * (D + 8) * 2 + kAbTile * (kAbTile + 8) * 2 + kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 +
+           2 * kAbTile * 4;
 }
 
 }  // namespace
 
+// At d_head <= 64 the query tile's fragments are held in registers (each wave's 32 rows, read once), which
+// with the scratch of the prologue and of pass 1's end kept in regions free at those times leaves 37 KB of
+// LDS and room for four workgroups per compute unit.
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
+__global__ __launch_bounds__(256, D <= 64 ? 4 : 1) void attn_bwd_dq_kernel(const AttnBwdArgs a)
 {
     constexpr int P = D + 8, PS = kAbTile + 8, CPR = D / 8, NBW = (2 * (D / 32) + 3) / 4;
+    constexpr bool QR = D <= 64;
     extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
-    uint16_t* sQ = s_ab;
-    uint16_t* sdO = sQ + kAbTile * P;
+    uint16_t* sdO = s_ab;
     uint16_t* sK = sdO + kAbTile * P;
     uint16_t* sV = sK + kAbTile * P;
     uint16_t* sS = sV + kAbTile * P;
-    float* s_dp = (float*)(sS + kAbTile * PS);
-    float* s_m = s_dp + kAbTile * CPR;            // [4][32]
-    float* s_l = s_m + 4 * 32;                    // [4][32]
-    float* s_lse = s_l + 4 * 32;                  // [64]
-    float* s_delta = s_lse + kAbTile;             // [64]
+    uint16_t* sQ = QR ? sS : sS + kAbTile * PS;                // QR: staged in the dS region
+    float* s_tail = (float*)(QR ? sS + kAbTile * PS : sQ + kAbTile * P);
+    float* s_dp = QR ? (float*)sK : s_tail;                    // prologue only (QR: before K is stored)
+    float* s_m = QR ? (float*)sS : s_dp + kAbTile * CPR;      // [4][32], end of pass 1 only
+    float* s_l = s_m + 4 * 32;                                 // [4][32]
+    float* s_lse = QR ? s_tail : s_l + 4 * 32;                 // [64]
+    float* s_delta = s_lse + kAbTile;                          // [64]
+    static_assert(!QR || (kAbTile * P <= kAbTile * PS && kAbTile * CPR * 4 <= kAbTile * P * 2 &&
+                          2 * 4 * 32 * 4 <= kAbTile * PS * 2), "aliased regions fit");
 
     const int T = a.T, G = a.G;
     const int ntr = (T * a.k + kAbTile - 1) / kAbTile, nts = (T + kAbTile - 1) / kAbTile;
@@ -326,6 +337,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         for (int c = 0; c < CPR; ++c) dsum += s_dp[tid * CPR + c];
         s_delta[tid] = dsum;
     }
+    // QR: this wave's query fragments (rows wr * 32 + l % 32), read before K and dS overwrite the staging
+    bf16x8 qf[QR ? D / 16 : 1];
+    if constexpr (QR) {
+        const uint16_t* yb = sQ + (wr * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) qf[st] = frag_row(yb + 16 * st);
+        __syncthreads();
+    }
+    // S^T quadrant of this wave (keys wk * 32 .., rows wr * 32 ..) against the K tile in LDS
+    auto scores = [&]() -> f32x16 {
+        if constexpr (QR) {
+            f32x16 c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = 0.f;
+            const uint16_t* xa = sK + (wk * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) c = mfma32(frag_row(xa + 16 * st), qf[st], c);
+            return c;
+        } else {
+            return quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        }
+    };
     keys_store<D>(rk, sK);
     if (a.lse_given) keys_store<D>(rv, sV);
     __syncthreads();
@@ -346,7 +379,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
         const bool more = kt + 1 < nkt;
         keys_load<D>(Kh, more ? s0 + kAbTile : 0, T, rk);
         if (!more) keys_load<D>(Vh, 0, T, rv);
-        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        const f32x16 c = scores();
         float sv[16], mt = -INFINITY;
         if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk)) {
 #pragma unroll
@@ -411,7 +444,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const AttnBwdArgs a)
             keys_load<D>(Kh, s0 + kAbTile, T, rk);
             keys_load<D>(Vh, s0 + kAbTile, T, rv);
         }
-        const f32x16 c = quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
+        const f32x16 c = scores();
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
         // dS[row][key] as bf16, four consecutive keys per 8-byte store
         const bool need_mask = s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk);
