@@ -263,39 +263,34 @@ template <int D>
 constexpr int ab_lds_bytes(bool dq)
 {
     // dK/dV kernel: q, dO, V tiles, then P and dS (where the K tile is staged once before it is held in
-    // registers), then row data.  dq kernel at d_head <= 64: dO, K, V tiles, then dS (where q is staged once
-    // before it is held in registers), then row data.  dq kernel at d_head 128: q, dO, K, V, dS, then the
-    // partial sums of Delta and of the row statistics, then row data.
-    if (!dq) return 3 * kAbTile * (D + 8) * 2 + 2 * kAbTile * (kAbTile + 8) * 2 + 2 * kAbTile * 4;
-    if (D <= 64) return 3 * kAbTile * (D + 8) * 2 + kAbTile * (kAbTile + 8) * 2 + 2 * kAbTile * 4;
-    return 4 * kAbTile * (D + 8) * 2 + kAbTile * (kAbTile + 8) * 2 + kAbTile * (D / 8) * 4 + 4 * 2 * 32 * 4 +
-           2 * kAbTile * 4;
+    // registers), then row data.  dq kernel: dO, K, V tiles, then dS, then row data (q is staged once, in
+    // the dS region or at d_head 128 the K region, before it is held in registers).
+    return 3 * kAbTile * (D + 8) * 2 + (dq ? 1 : 2) * kAbTile * (kAbTile + 8) * 2 + 2 * kAbTile * 4;
 }
 
 }  // namespace
 
-// At d_head <= 64 the query tile's fragments are held in registers (each wave's 32 rows, read once), which
-// with the scratch of the prologue and of pass 1's end kept in regions free at those times leaves 37 KB of
-// LDS and room for four workgroups per compute unit.
+// The query tile's fragments are held in registers (each wave's 32 rows, read once); with the scratch of
+// the prologue and of pass 1's end kept in regions free at those times, the kernel needs 37 KB of LDS at
+// d_head 64 (four workgroups per compute unit) and 62 KB at 128 (two).
 template <int D>
-__global__ __launch_bounds__(256, D <= 64 ? 4 : 1) void attn_bwd_dq_kernel(const AttnBwdArgs a)
+__global__ __launch_bounds__(256, D <= 64 ? 4 : 2) void attn_bwd_dq_kernel(const AttnBwdArgs a)
 {
     constexpr int P = D + 8, PS = kAbTile + 8, CPR = D / 8, NBW = (2 * (D / 32) + 3) / 4;
-    constexpr bool QR = D <= 64;
+    constexpr bool QS = kAbTile * P <= kAbTile * PS;   // q staged in the dS region, else in the K region
     extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
     uint16_t* sdO = s_ab;
     uint16_t* sK = sdO + kAbTile * P;
     uint16_t* sV = sK + kAbTile * P;
     uint16_t* sS = sV + kAbTile * P;
-    uint16_t* sQ = QR ? sS : sS + kAbTile * PS;                // QR: staged in the dS region
-    float* s_tail = (float*)(QR ? sS + kAbTile * PS : sQ + kAbTile * P);
-    float* s_dp = QR ? (float*)sK : s_tail;                    // prologue only (QR: before K is stored)
-    float* s_m = QR ? (float*)sS : s_dp + kAbTile * CPR;      // [4][32], end of pass 1 only
-    float* s_l = s_m + 4 * 32;                                 // [4][32]
-    float* s_lse = QR ? s_tail : s_l + 4 * 32;                 // [64]
-    float* s_delta = s_lse + kAbTile;                          // [64]
-    static_assert(!QR || (kAbTile * P <= kAbTile * PS && kAbTile * CPR * 4 <= kAbTile * P * 2 &&
-                          2 * 4 * 32 * 4 <= kAbTile * PS * 2), "aliased regions fit");
+    uint16_t* sQ = QS ? sS : sK;                                // staging, read once before K and dS are written
+    float* s_dp = (float*)(QS ? sK : sV);                       // prologue only, before K and V are stored
+    float* s_m = (float*)sS;                                    // [4][32], end of pass 1 only
+    float* s_l = s_m + 4 * 32;                                  // [4][32]
+    float* s_lse = (float*)(sS + kAbTile * PS);                 // [64]
+    float* s_delta = s_lse + kAbTile;                           // [64]
+    static_assert(kAbTile * CPR * 4 <= kAbTile * P * 2 && 2 * 4 * 32 * 4 <= kAbTile * PS * 2,
+                  "aliased regions fit");
 
     const int T = a.T, G = a.G;
     const int ntr = (T * a.k + kAbTile - 1) / kAbTile, nts = (T + kAbTile - 1) / kAbTile;
@@ -337,27 +332,23 @@ __global__ __launch_bounds__(256, D <= 64 ? 4 : 1) void attn_bwd_dq_kernel(const
         for (int c = 0; c < CPR; ++c) dsum += s_dp[tid * CPR + c];
         s_delta[tid] = dsum;
     }
-    // QR: this wave's query fragments (rows wr * 32 + l % 32), read before K and dS overwrite the staging
-    bf16x8 qf[QR ? D / 16 : 1];
-    if constexpr (QR) {
+    // this wave's query fragments (rows wr * 32 + l % 32), read before K, V and dS overwrite the staging
+    bf16x8 qf[D / 16];
+    {
         const uint16_t* yb = sQ + (wr * 32 + (lane & 31)) * P + 8 * (lane >> 5);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) qf[st] = frag_row(yb + 16 * st);
-        __syncthreads();
     }
+    __syncthreads();
     // S^T quadrant of this wave (keys wk * 32 .., rows wr * 32 ..) against the K tile in LDS
     auto scores = [&]() -> f32x16 {
-        if constexpr (QR) {
-            f32x16 c;
+        f32x16 c;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) c[r] = 0.f;
-            const uint16_t* xa = sK + (wk * 32 + (lane & 31)) * P + 8 * (lane >> 5);
+        for (int r = 0; r < 16; ++r) c[r] = 0.f;
+        const uint16_t* xa = sK + (wk * 32 + (lane & 31)) * P + 8 * (lane >> 5);
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) c = mfma32(frag_row(xa + 16 * st), qf[st], c);
-            return c;
-        } else {
-            return quad_xyT<D>(sK, wk * 32, sQ, wr * 32, lane);
-        }
+        for (int st = 0; st < D / 16; ++st) c = mfma32(frag_row(xa + 16 * st), qf[st], c);
+        return c;
     };
     keys_store<D>(rk, sK);
     if (a.lse_given) keys_store<D>(rv, sV);
