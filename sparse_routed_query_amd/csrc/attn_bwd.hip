@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 4 : 2) void attn_bwd_dq_kernel(const
 template <int D>
 __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(const AttnBwdArgs a)
 {
-    constexpr int P = D + 8, PS = kAbTile + 8, NBW = (2 * (D / 32) + 3) / 4;
+    constexpr int P = D + 8, PS = kAbTile + 8, NB = D / 32;
     extern __shared__ __attribute__((aligned(16))) uint16_t s_ab[];
     uint16_t* sQ = s_ab;
     uint16_t* sdO = sQ + kAbTile * P;
@@ -509,11 +509,14 @@ __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(co
     load_keys<D>((const uint16_t*)a.k_ + ((size_t)b * G + g) * T * D, s0, T, sP);
     load_keys<D>((const uint16_t*)a.v_ + ((size_t)b * G + g) * T * D, s0, T, sV);
 
-    f32x16 dk[NBW], dv[NBW];
+    // products: waves 0, 1 form dV, waves 2, 3 dK, each for keys 32 (wave & 1) .. and every d, so each
+    // P^T or dS^T fragment read from LDS feeds all D / 32 blocks
+    const bool is_dk = wave >= 2;
+    f32x16 acc[NB];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dk[j][r] = dv[j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
     // the row tiles that see this key tile: the group's routed rows, then (KV head 0) the shared rows
     const RowSet rs0 = row_set(a, b, g);
@@ -575,12 +578,14 @@ __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(co
             *(uint2*)(sD + off) = make_uint2(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]));
         }
         __syncthreads();
+        {
+            const uint16_t* src = is_dk ? sD : sP;   // dS^T q or P^T dO
+            const uint16_t* z = is_dk ? sQ : sdO;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            const int blk = wave + 4 * j;
-            if (blk < 2 * (D / 32)) {
-                dv[j] = gemm_tt<D>(dv[j], sP, (blk & 1) * 32, sdO, (blk >> 1) * 32, lane);
-                dk[j] = gemm_tt<D>(dk[j], sD, (blk & 1) * 32, sQ, (blk >> 1) * 32, lane);
+            for (int st = 0; st < kAbTile / 16; ++st) {
+                const bf16x8 fa = frag_tr(src, PS, 16 * st, wk * 32, lane);
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[j] = mfma32(fa, frag_tr(z, P, 16 * st, 32 * j, lane), acc[j]);
             }
         }
         __syncthreads();
@@ -589,20 +594,15 @@ __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(co
             __syncthreads();
         }
     }
-    float* dkh = a.dk + ((size_t)b * G + g) * T * D;
-    float* dvh = a.dv + ((size_t)b * G + g) * T * D;
+    float* dst = (is_dk ? a.dk : a.dv) + ((size_t)b * G + g) * T * D;
+    const float scale = is_dk ? a.inv_sqrt_d : 1.f;
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        const int blk = wave + 4 * j;
-        if (blk >= 2 * (D / 32)) continue;
-        const int d = (blk >> 1) * 32 + (lane & 31);
+    for (int j = 0; j < NB; ++j) {
+        const int d = 32 * j + (lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = s0 + (blk & 1) * 32 + acc_row(i, lane);
-            if (key < T) {
-                dkh[(size_t)key * D + d] = dk[j][i] * a.inv_sqrt_d;
-                dvh[(size_t)key * D + d] = dv[j][i];
-            }
+            const int key = s0 + wk * 32 + acc_row(i, lane);
+            if (key < T) dst[(size_t)key * D + d] = acc[j][i] * scale;
         }
     }
 }
