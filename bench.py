@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--graph", action="store_true", help="also time the step replayed from one HIP graph")
     ap.add_argument("--only", choices=["step", "prefill", "outproj", "decode", "copy", "qproj", "prefill_wide",
-                                       "qproj_wide", "prefill_long"], default=None,
+                                       "qproj_wide", "prefill_long", "attn_bwd"], default=None,
                     help="run just one call --steps times (for profiler counter runs) and print nothing else")
     return ap.parse_args()
 
@@ -563,8 +563,8 @@ def wide_leg(torch, dev, steps):
 def only(args, torch):
     """One call repeated, for rocprofv3 counter runs: the whole prefill step, the
     prefill attention and assembly calls on the main shape, the decode step
-    (one-launch preamble and attention), or a plain 256 MiB device copy (the calibration kernel for FETCH_SIZE /
-    WRITE_SIZE)."""
+    (one-launch preamble and attention), the attention backward given the forward's statistics (main shape), or
+    a plain 256 MiB device copy (the calibration kernel for FETCH_SIZE / WRITE_SIZE)."""
     import workloads as W
     import sparse_routed_query_amd.gqe as G
     dev = "cuda:0"
@@ -592,14 +592,32 @@ def only(args, torch):
         p.route()
         for _ in range(args.steps):
             p.qproj()
+    elif args.only == "attn_bwd":
+        # gqe_attn_backward_lse on main_250m's own rows, K, V and slots, given the forward's statistics
+        w = W.WORKLOADS["main_250m"]
+        p = Prefill(w, W.make_inputs(w), dev)
+        p.step()
+        BT, S, D = w.B * w.T, p.d.S, w.d_head
+        gen = torch.Generator(device="cpu").manual_seed(9)
+        d_hard = torch.randn((BT, w.k * w.G, D), generator=gen).to(dev)
+        dout = torch.randn((BT, S, D), generator=gen).to(dev)
+        lse = torch.empty(G.lse_rows(p.d), dtype=torch.float32, device=dev)
+        slots = torch.empty_like(p.out)
+        G.gqe_attn_prefill_heads_lse(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, slots, lse, p.ws)
+        f32 = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)  # noqa: E731
+        grads = (f32(w.B, w.G, w.T * w.k, D), f32(w.B, w.T, D), f32(w.B, w.G, w.T, D), f32(w.B, w.G, w.T, D))
+        ws = torch.empty(G.gqe_attn_backward_workspace_bytes(p.d), dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            G.gqe_attn_backward_lse(p.d, p.q["q_routed"], p.q["q_shared"], p.k, p.v, p.out.view(BT, S, D), d_hard,
+                                    dout, lse, *grads, ws)
     elif args.only == "outproj":
         w = W.WORKLOADS["main_250m"]
         p = Prefill(w, W.make_inputs(w), dev)
         p.step()
-        wo = W.make_w_o(w).to(dev)
+        wp = G.out_proj_pack(p.d, W.make_w_o(w).to(dev))
         y = torch.empty((w.B * w.T, w.d_model), dtype=torch.float32, device=dev)
         for _ in range(args.steps):
-            G.gqe_out_proj(p.d, p.out, p.r["p_tilde"], wo, y, False)
+            G.gqe_out_proj_packed(p.d, p.out, p.r["p_tilde"], wp, y, False)
     else:
         w = W.WORKLOADS["decode_b64"]
         inp = W.make_inputs(w)
