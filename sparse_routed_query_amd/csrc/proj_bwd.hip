@@ -22,9 +22,11 @@
 // dw kernel: one workgroup per (head, 256 columns of d_model, row chunk): a
 //   chunk of the head's rows (its compacted bucket, or every token) in
 //   stages of 64, both operands read across their stored rows with
-//   transposing LDS reads; with a workspace the rows are cut into up to 16
-//   chunks whose partial sums a second kernel adds in chunk order (so the
-//   launch has enough workgroups), else one chunk writes dW directly.
+//   transposing LDS reads; at d_head <= 64 the dense heads (shared, K, V)
+//   go two to a workgroup, sharing each staged x tile; with a workspace the
+//   rows are cut into up to 16 chunks whose partial sums a second kernel
+//   adds in chunk order (so the launch has enough workgroups), else one
+//   chunk writes dW directly.
 // dx kernel: one workgroup per (128 tokens, 64 at d_head 128; 128 columns): the heads in turn,
 //   each a stage of [tokens x D] gradient rows (zero where the token did
 //   not keep the expert) against the head's [D x 128] weight slice.
@@ -211,6 +213,135 @@ __global__ __launch_bounds__(256, D >= 64 ? 2 : 3) void pb_dw_kernel(const ProjB
                 dst[(size_t)d * d_model + col] = acc[mi][ni][e];
             }
         }
+}
+
+// dW of the dense heads (shared, K, V: every token is a row of each) two at a time: the two heads' gradient
+// rows of a stage are staged beside one x tile, so each x fragment read feeds both heads' products and a
+// stage moves 2 KB per MFMA instead of 3 KB (the kernel is bound by what its compute unit can load).
+// Dense head j (0 <= j < ns + 2 nkv) is head N + j; workgroup pair p takes j = 2p, 2p + 1.
+template <int D, bool ROT>
+__global__ __launch_bounds__(256, 2) void pb_dw2_kernel(const ProjBwdArgs a, int nchunk, float* part)
+{
+    using S = PbDw<D>;
+    constexpr int BN = S::BN, SR = S::SR, PQ = S::PQ, PX = S::PX, MI = S::MI, NI = S::NI, NQ = S::NQ, NX = S::NX;
+    const int d_model = a.d_model, BT = a.B * a.T, N = a.G * a.E, ndense = a.ns + 2 * a.nkv;
+    const int ncol = (d_model + BN - 1) / BN;
+    const int ch = blockIdx.x % nchunk, rest = blockIdx.x / nchunk;
+    const int pr = rest / ncol, col0 = (rest % ncol) * BN;
+    const bool two = 2 * pr + 1 < ndense;
+    int nh[2], kind[2], hh[2];
+    float* dw[2];
+    bool rot[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        nh[u] = N + min(2 * pr + u, ndense - 1);
+        kind[u] = pb_kind(a, nh[u], hh[u]);
+        dw[u] = kind[u] == 1 ? a.dw_q : kind[u] == 2 ? a.dw_k : a.dw_v;
+        rot[u] = ROT && kind[u] <= 2;
+    }
+    if (!dw[0] && (!two || !dw[1])) return;
+    const int per = ((BT + nchunk - 1) / nchunk + SR - 1) / SR * SR;
+    const int r_lo = min(ch * per, BT);
+    const int M = min(per, BT - r_lo);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * SR * PQ];
+    __shared__ __attribute__((aligned(16))) uint16_t sX[SR * PX];
+
+    f32x4 qu[2][NQ], qw[2][NQ];
+    u32x4 xr[NX];
+    auto load = [&](int r0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int task = tid + 256 * i, rr = task / (D / 8), d0 = (task % (D / 8)) * 4;
+                const int r = r0 + rr;
+                const float* src = nullptr;
+                int pos = 0;
+                if (r < M) {
+                    const int tok = r_lo + r;
+                    src = pb_src(a, kind[u], hh[u], nh[u], tok);
+                    pos = a.positions ? a.positions[tok] : tok % a.T;
+                }
+                pb_load_pair(a, src, rot[u], pos, d0, qu[u][i], qw[u][i]);
+            }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int task = tid + 256 * i, rr = task / (BN / 8);
+            const int tok = r_lo + min(r0 + rr, M - 1);
+            const int c = min(col0 + (task % (BN / 8)) * 8, d_model - 8);
+            xr[i] = ld_u32x4(a.x + (size_t)tok * d_model + c);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int task = tid + 256 * i, rr = task / (D / 8), d0 = (task % (D / 8)) * 4;
+                *(uint64_t*)&sQ[u * SR * PQ + rr * PQ + d0] = pb_pack4(qu[u][i]);
+                *(uint64_t*)&sQ[u * SR * PQ + rr * PQ + d0 + D / 2] = pb_pack4(qw[u][i]);
+            }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int task = tid + 256 * i, rr = task / (BN / 8), c = (task % (BN / 8)) * 8;
+            *(u32x4*)&sX[rr * PX + c] = xr[i];
+        }
+    };
+
+    f32x16 acc[2][MI][NI];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[u][mi][ni][e] = 0.f;
+
+    const int nst = (M + SR - 1) / SR;
+    if (nst > 0) load(0);
+    for (int st = 0; st < nst; ++st) {
+        __syncthreads();
+        store();
+        __syncthreads();
+        if (st + 1 < nst) load((st + 1) * SR);
+#pragma unroll
+        for (int c = 0; c < SR / 16; ++c) {
+            bf16x8 fb[NI];
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) fb[ni] = frag_tr(sX, PX, 16 * c, 32 * (wave * NI + ni), lane);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                bf16x8 fa[MI];
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) fa[mi] = frag_tr(sQ + u * SR * PQ, PQ, 16 * c, 32 * mi, lane);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) acc[u][mi][ni] = mfma32(fa[mi], fb[ni], acc[u][mi][ni]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (!dw[u] || (u == 1 && !two)) continue;
+        float* dst = nchunk == 1 ? dw[u] + (size_t)(kind[u] == 1 ? N + hh[u] : hh[u]) * D * d_model
+                                 : part + ((size_t)nh[u] * nchunk + ch) * D * d_model;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int col = col0 + 32 * (wave * NI + ni) + (lane & 31);
+                if (col >= d_model) continue;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int d = 32 * mi + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    dst[(size_t)d * d_model + col] = acc[u][mi][ni][e];
+                }
+            }
+    }
 }
 
 // dW[head] = the sum of its nchunk partials in chunk order, four columns per thread.
@@ -516,6 +647,16 @@ size_t proj_bwd_workspace_bytes(const ProjBwdArgs& a)
     return (size_t)n_heads * nc * a.D * a.d_model * sizeof(float);
 }
 
+// dW launches: the routed experts (all heads at d_head 128) one per workgroup, then the dense-head pairs
+template <int D, bool ROT>
+static void pb_dw_launch(const ProjBwdArgs& a, int nc, float* part, unsigned grid1, unsigned grid2, hipStream_t st)
+{
+    if (grid1) pb_dw_kernel<D, ROT><<<grid1, 256, 0, st>>>(a, nc, part);
+    if constexpr (D <= 64) {
+        if (grid2) pb_dw2_kernel<D, ROT><<<grid2, 256, 0, st>>>(a, nc, part);
+    }
+}
+
 int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_bytes, hipStream_t st)
 {
     const int BT = a.B * a.T;
@@ -528,14 +669,19 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
         const int nc = (need > 0 && workspace && workspace_bytes >= need) ? pb_nchunk(a) : 1;
         float* part = (float*)workspace;
         const int ncol = (a.d_model + 255) / 256;
-        const unsigned grid = (unsigned)(n_heads * ncol * nc);
+        // the routed experts one per workgroup (each over its own rows); at d_head <= 64 the dense heads two
+        // per workgroup (at 128 the two heads' accumulators would not fit the registers)
+        const int N = a.G * a.E, ndense = a.ns + 2 * a.nkv;
+        const bool pairs = a.D <= 64;
+        const unsigned grid1 = (unsigned)((pairs ? N : n_heads) * ncol * nc);
+        const unsigned grid2 = pairs ? (unsigned)(((ndense + 1) / 2) * ncol * nc) : 0u;
         switch (a.D) {
-        case 32: rot ? pb_dw_kernel<32, true><<<grid, 256, 0, st>>>(a, nc, part)
-                     : pb_dw_kernel<32, false><<<grid, 256, 0, st>>>(a, nc, part); break;
-        case 64: rot ? pb_dw_kernel<64, true><<<grid, 256, 0, st>>>(a, nc, part)
-                     : pb_dw_kernel<64, false><<<grid, 256, 0, st>>>(a, nc, part); break;
-        case 128: rot ? pb_dw_kernel<128, true><<<grid, 256, 0, st>>>(a, nc, part)
-                      : pb_dw_kernel<128, false><<<grid, 256, 0, st>>>(a, nc, part); break;
+        case 32: rot ? pb_dw_launch<32, true>(a, nc, part, grid1, grid2, st)
+                     : pb_dw_launch<32, false>(a, nc, part, grid1, grid2, st); break;
+        case 64: rot ? pb_dw_launch<64, true>(a, nc, part, grid1, grid2, st)
+                     : pb_dw_launch<64, false>(a, nc, part, grid1, grid2, st); break;
+        case 128: rot ? pb_dw_launch<128, true>(a, nc, part, grid1, grid2, st)
+                      : pb_dw_launch<128, false>(a, nc, part, grid1, grid2, st); break;
         default: return -2;
         }
         if (nc > 1) {
