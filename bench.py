@@ -537,7 +537,8 @@ def proj_backward_leg(p, torch, steps):
     t, t_dw = time_calls([bwd, bwd_dw], steps, torch)
     fl_one = 2.0 * D * w.d_model * B * T * (w.k * w.G + w.n_shared + 2 * w.G)
     tf = 2 * fl_one / (t * 1e-3) / 1e12
-    return {"workload": w.name, "kernel": f"pb_dw_kernel<{D}> + {'pb_dx64_kernel' if D == 64 else f'pb_dx_kernel<{D}>'} (gqe_qkv_proj_backward)",
+    return {"workload": w.name, "kernel": f"pb_dw_kernel<{D}>{f' + pb_dw2_kernel<{D}>' if D <= 64 else ''} + "
+                      f"{'pb_dx64_kernel' if D == 64 else f'pb_dx_kernel<{D}>'} (gqe_qkv_proj_backward)",
             "us": t * 1e3, "dw_us": t_dw * 1e3, "dx_us": (t - t_dw) * 1e3, "tflops": tf,
             "frac": tf / MFMA_BF16_PEAK_TFLOPS, "flops": 2 * fl_one}
 
