@@ -99,6 +99,9 @@ __device__ __forceinline__ RowSet row_set(const AttnBwdArgs& a, int b, int h)
     return rs;
 }
 
+// position t of row r of a row set (r = t kk + j)
+__device__ __forceinline__ int row_pos(const RowSet& rs, int r) { return rs.kshift >= 0 ? r >> rs.kshift : r / rs.kk; }
+
 // rows r0 .. r0+63 of a row set into LDS: q (bf16) and dO (rounded to bf16);
 // rows past R are zero.  With s_dp, also the partial <dO, O> of each 8-wide chunk.
 template <int D>
@@ -189,7 +192,7 @@ __device__ __forceinline__ void rows_load(const RowSet& rs, int r0, RowRegs<D>& 
         // nothing, and every load is unconditional
         const int c = threadIdx.x + 256 * i, row = c / CPR, d0 = (c % CPR) * 8, rr = min(r0 + row, rs.R - 1);
         r.q[i] = ld_u32x4(rs.q + (size_t)rr * D + d0);
-        const int t = rs.kshift >= 0 ? rr >> rs.kshift : rr / rs.kk, j = rr - t * rs.kk;
+        const int t = row_pos(rs, rr), j = rr - t * rs.kk;
         const float* g = rs.dO + (size_t)t * rs.dO_stride + (size_t)j * D + d0;
         r.g[2 * i] = *(const f32x4*)g;
         r.g[2 * i + 1] = *(const f32x4*)(g + 4);
@@ -437,22 +440,30 @@ __global__ __launch_bounds__(256, D <= 64 ? 4 : 2) void attn_bwd_dq_kernel(const
         }
         const f32x16 c = scores();
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
-        // dS[row][key] as bf16, four consecutive keys per 8-byte store
-        const bool need_mask = s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk);
+        // dS[row][key] as bf16, four consecutive keys per 8-byte store; the mask (a select after an
+        // unconditional exp2) only on tiles that reach past T or the row's position
+        auto d_s = [&](bool masked) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            float v[4];
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                const int key = s0 + wk * 32 + acc_row(i, lane);
-                const bool ok = !need_mask || (key < T && (!a.causal || key <= tq));
-                const float pv = ok ? __builtin_amdgcn_exp2f(c[i] * qs2 - lse_r) : 0.f;
-                v[e] = pv * (dp[i] - dl_r);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e;
+                    float pv = __builtin_amdgcn_exp2f(c[i] * qs2 - lse_r);
+                    if (masked) {
+                        const int key = s0 + wk * 32 + acc_row(i, lane);
+                        pv = key < T && (!a.causal || key <= tq) ? pv : 0.f;
+                    }
+                    v[e] = pv * (dp[i] - dl_r);
+                }
+                const int k0 = wk * 32 + acc_row(4 * i4, lane);   // (kpos moves whole 4-key blocks)
+                *(uint2*)(sS + row * PS + kpos(k0)) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
             }
-            const int k0 = wk * 32 + acc_row(4 * i4, lane);   // (kpos moves whole 4-key blocks)
-            *(uint2*)(sS + row * PS + kpos(k0)) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-        }
+        };
+        if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > row_pos(rs, r0)))
+            d_s(true);
+        else
+            d_s(false);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(co
             const bool nx0 = it + 1 < c0;
             rows_load<D>(nx0 ? rs0 : rs1, (nx0 ? a0 + it + 1 : a1 + it + 1 - c0) * kAbTile, rr);
         }
-        const int tq = (r0 + row) / rs.kk;
+        const int tq = row_pos(rs, r0 + row);
         const float lse_r = s_lse[row], dl_r = s_delta[row];
         f32x16 c;
         {
@@ -560,23 +571,31 @@ __global__ __launch_bounds__(256, D >= 128 ? 2 : 3) void attn_bwd_dkdv_kernel(co
         const f32x16 dp = quad_xyT<D>(sV, wk * 32, sdO, wr * 32, lane);
         // P and dS as bf16 in [row][key] order, four consecutive keys per 8-byte store; a tile whose keys all
         // lie inside T and before its first row's position needs no mask (the mask is a select, not a branch)
-        const bool need_mask = s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > r0 / rs.kk);
+        auto p_ds = [&](bool masked) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            float pv[4], ds[4];
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float pv[4], ds[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                const int key = s0 + wk * 32 + acc_row(i, lane);
-                const bool ok = !need_mask || (key < T && (!a.causal || key <= tq));
-                const float ex = __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r);
-                pv[e] = ok ? ex : 0.f;
-                ds[e] = pv[e] * (dp[i] - dl_r);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e;
+                    const float ex = __builtin_amdgcn_exp2f(c[i] * a.qscale2 - lse_r);
+                    if (masked) {
+                        const int key = s0 + wk * 32 + acc_row(i, lane);
+                        pv[e] = key < T && (!a.causal || key <= tq) ? ex : 0.f;
+                    } else {
+                        pv[e] = ex;
+                    }
+                    ds[e] = pv[e] * (dp[i] - dl_r);
+                }
+                const int off = row * PS + wk * 32 + acc_row(4 * i4, lane);
+                *(uint2*)(sP + off) = make_uint2(pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3]));
+                *(uint2*)(sD + off) = make_uint2(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]));
             }
-            const int off = row * PS + wk * 32 + acc_row(4 * i4, lane);
-            *(uint2*)(sP + off) = make_uint2(pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3]));
-            *(uint2*)(sD + off) = make_uint2(pack_bf2(ds[0], ds[1]), pack_bf2(ds[2], ds[3]));
-        }
+        };
+        if (s0 + kAbTile > T || (a.causal && s0 + kAbTile - 1 > row_pos(rs, r0)))
+            p_ds(true);
+        else
+            p_ds(false);
         __syncthreads();
         {
             const uint16_t* src = is_dk ? sD : sP;   // dS^T q or P^T dO
