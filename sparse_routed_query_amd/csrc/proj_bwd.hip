@@ -87,6 +87,9 @@ __device__ __forceinline__ void pb_load_pair(const ProjBwdArgs& a, const float* 
     }
 }
 
+// a gradient row of zeros: the row a token that did not keep a routed expert reads (at most 128 wide)
+__device__ __attribute__((aligned(16))) const float pb_zero_row[128] = {};
+
 __device__ __forceinline__ uint64_t pb_pack4(const f32x4& v)
 {
     return (uint64_t)pack_bf2(v[0], v[1]) | ((uint64_t)pack_bf2(v[2], v[3]) << 32);
@@ -518,15 +521,20 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
             s_sel[m * KMAX + i % Gk] = a.sel[(size_t)tok * Gk + i % Gk];
         }
     __syncthreads();
-    // gradient row of head n for the tile's token m (as pb_src, with the kept experts from LDS)
-    auto src_of = [&](int kind, int h, int n, int m) -> const float* {
-        if (kind != 0 || !staged) return pb_src(a, kind, h, n, tok0 + m);
-        const int tok = tok0 + m, b = tok / a.T, t = tok - b * a.T;
-        const int g = n / a.E, e = n - g * a.E;
-        int j = -1;
-        for (int i = 0; i < a.k; ++i) j = s_sel[m * KMAX + g * a.k + i] == e ? i : j;
-        return j < 0 ? nullptr : a.dq_routed + ((((size_t)b * a.G + g) * a.T + t) * a.k + j) * D;
-    };
+    // per load task: its tile row and the parts of its gradient-row offsets that no head changes (tokens past
+    // B*T use the last token: their dx rows are never stored), so a head's row address is one multiply-add
+    const int T = a.T, G = a.G, k = a.k;
+    int tk[NA], pos[NA];
+    size_t rbase[NA], kvbase[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int task = tid + 256 * i, m = task / (D / 8);
+        const int tok = min(tok0 + m, BT - 1), b = tok / T, t = tok - b * T;
+        tk[i] = tok;
+        rbase[i] = ((size_t)b * G * T + t) * k;      // routed row (b, g, t, j) = rbase + g T k + j
+        kvbase[i] = (size_t)b * a.nkv * T + t;       // K/V row (b, h, t) = kvbase + h T
+        pos[i] = ROT ? (a.positions ? a.positions[tok] : t) : 0;
+    }
 
     f32x4 au[NA], aw[NA];
     u32x4 wr[NW];
@@ -534,17 +542,30 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
         int h;
         const int kind = pb_kind(a, n, h);
         const bool rot = ROT && kind <= 2;
+        const int g = n / a.E, e = n - g * a.E;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
-            const int tok = tok0 + m;
-            const float* src = nullptr;
-            int pos = 0;
-            if (tok < BT) {
-                src = src_of(kind, h, n, m);
-                pos = a.positions ? a.positions[tok] : tok % a.T;
+            const float* src;
+            if (kind == 0) {
+                // the token's rank of expert e among its kept experts of group g (from LDS when staged); a
+                // token that did not keep it reads a row of zeros
+                int j = -1;
+                if (staged && k == 1) {
+                    j = s_sel[m * KMAX + g] == e ? 0 : -1;
+                } else if (staged) {
+                    for (int r = 0; r < k; ++r) j = s_sel[m * KMAX + g * k + r] == e ? r : j;
+                } else {
+                    const int32_t* sl = a.sel + ((size_t)tk[i] * G + g) * k;
+                    for (int r = 0; r < k; ++r) j = sl[r] == e ? r : j;
+                }
+                src = j < 0 ? pb_zero_row : a.dq_routed + (rbase[i] + (size_t)g * T * k + j) * D;
+            } else if (kind == 1) {
+                src = a.dq_shared + (size_t)tk[i] * D;
+            } else {
+                src = (kind == 2 ? a.dk : a.dv) + (kvbase[i] + (size_t)h * T) * D;
             }
-            pb_load_pair(a, src, rot, pos, d0, au[i], aw[i]);
+            pb_load_pair(a, src, rot, pos[i], d0, au[i], aw[i]);
         }
         const uint16_t* w = (kind <= 1 ? a.w_q + (size_t)(kind == 0 ? n : N + h) * D * d_model
                                        : (kind == 2 ? a.w_k : a.w_v) + (size_t)h * D * d_model);
