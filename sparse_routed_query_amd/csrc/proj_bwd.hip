@@ -479,25 +479,27 @@ __global__ __launch_bounds__(256, 2) void pb_dx_kernel(const ProjBwdArgs a, int 
         }
 }
 
-// dx at d_head 64 with wider tiles: one workgroup of four waves per 128 tokens x 256 columns, so the fp32
-// gradient rows are read once per 256 columns (not 128); one head per stage in two LDS buffers used in turn
+// dx at d_head 64 with wider tiles: one workgroup of eight waves (two per SIMD) per 256 tokens x 256
+// columns, so the fp32 gradient rows are read once per 256 columns (not 128) and each weight tile serves 256
+// tokens; one head per stage in two LDS buffers used in turn
 // (the next head is stored between the halves of the current one's products, one barrier per head); each
 // wave 64 tokens x 128 columns as 2 x 4 blocks, so every fragment read from LDS feeds two or four products;
 // dx leaves by buffer stores over the tile's rows.  The same products in the same order per output element
 // as pb_dx_kernel.
 struct PbDx64 {
-    static constexpr int D = 64, BM = 128, BN = 256;
+    static constexpr int D = 64, BM = 256, BN = 256, NT = 512;
     static constexpr int PA = D + 8, PW = BN + 32;
     static constexpr int STG = BM * PA + D * PW;            // bf16 elements of one stage
-    static constexpr int NA = BM * (D / 8) / 256;           // gradient pairs per thread and head
-    static constexpr int NW = D * (BN / 8) / 256;           // weight chunks per thread and head
+    static constexpr int NA = BM * (D / 8) / NT;            // gradient pairs per thread and head
+    static constexpr int NW = D * (BN / 8) / NT;            // weight chunks per thread and head
 };
 
 template <bool ROT>
-__global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, int n_heads)
+__global__ __launch_bounds__(512, 1) void pb_dx64_kernel(const ProjBwdArgs a, int n_heads)
 {
     using S = PbDx64;
-    constexpr int D = S::D, BM = S::BM, BN = S::BN, PA = S::PA, PW = S::PW, STG = S::STG, NA = S::NA, NW = S::NW;
+    constexpr int D = S::D, BM = S::BM, BN = S::BN, NT = S::NT, PA = S::PA, PW = S::PW, STG = S::STG, NA = S::NA,
+                  NW = S::NW;
     const int d_model = a.d_model, BT = a.B * a.T, N = a.G * a.E;
     const int ncol = (d_model + BN - 1) / BN, nM = (BT + BM - 1) / BM;
     // workgroup -> tile: the column tiles of a token tile get indices 8 apart, so they run on one XCD and
@@ -507,16 +509,16 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
     if (tm >= nM) return;
     const int tok0 = tm * BM, col0 = (rr % ncol) * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;   // 2 x 2 waves of 64 tokens x 128 columns
+    const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 waves of 64 tokens x 128 columns
     __shared__ __attribute__((aligned(16))) uint16_t sS[2 * STG];
     // the tile's kept experts (G*k <= 16 of them per token), so that a routed head's row lookup reads LDS
     // instead of waiting on a global load before the gradient load it addresses
     constexpr int KMAX = 16;
-    __shared__ int s_sel[BM * KMAX];
+    __shared__ int8_t s_sel[BM * KMAX];   // expert indices (< 128)
     const int Gk = a.G * a.k;
     const bool staged = Gk <= KMAX;
     if (staged)
-        for (int i = tid; i < BM * Gk; i += 256) {
+        for (int i = tid; i < BM * Gk; i += NT) {
             const int m = i / Gk, tok = min(tok0 + m, BT - 1);
             s_sel[m * KMAX + i % Gk] = a.sel[(size_t)tok * Gk + i % Gk];
         }
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
     size_t rbase[NA], kvbase[NA];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const int task = tid + 256 * i, m = task / (D / 8);
+        const int task = tid + NT * i, m = task / (D / 8);
         const int tok = min(tok0 + m, BT - 1), b = tok / T, t = tok - b * T;
         tk[i] = tok;
         rbase[i] = ((size_t)b * G * T + t) * k;      // routed row (b, g, t, j) = rbase + g T k + j
@@ -545,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
         const int g = n / a.E, e = n - g * a.E;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
+            const int task = tid + NT * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
             const float* src;
             if (kind == 0) {
                 // the token's rank of expert e among its kept experts of group g (from LDS when staged); a
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
                                        : (kind == 2 ? a.w_k : a.w_v) + (size_t)h * D * d_model);
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int task = tid + 256 * i, d = task / (BN / 8);
+            const int task = tid + NT * i, d = task / (BN / 8);
             const int c = min(col0 + (task % (BN / 8)) * 8, d_model - 8);
             wr[i] = ld_u32x4(w + (size_t)d * d_model + c);
         }
@@ -581,13 +583,13 @@ __global__ __launch_bounds__(256, 1) void pb_dx64_kernel(const ProjBwdArgs a, in
         uint16_t* sW = buf + BM * PA;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int task = tid + 256 * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
+            const int task = tid + NT * i, m = task / (D / 8), d0 = (task % (D / 8)) * 4;
             *(uint64_t*)&sA[m * PA + d0] = pb_pack4(au[i]);
             *(uint64_t*)&sA[m * PA + d0 + D / 2] = pb_pack4(aw[i]);
         }
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int task = tid + 256 * i, d = task / (BN / 8), c = (task % (BN / 8)) * 8;
+            const int task = tid + NT * i, d = task / (BN / 8), c = (task % (BN / 8)) * 8;
             *(u32x4*)&sW[d * PW + c] = wr[i];
         }
     };
@@ -713,8 +715,8 @@ int launch_proj_bwd(const ProjBwdArgs& a, void* workspace, size_t workspace_byte
     if (a.dx && a.D == 64) {
         const int ncol = (a.d_model + PbDx64::BN - 1) / PbDx64::BN, nM = (BT + PbDx64::BM - 1) / PbDx64::BM;
         const unsigned grid = (unsigned)(8 * ((nM + 7) / 8) * ncol);
-        rot ? pb_dx64_kernel<true><<<grid, 256, 0, st>>>(a, n_heads)
-            : pb_dx64_kernel<false><<<grid, 256, 0, st>>>(a, n_heads);
+        rot ? pb_dx64_kernel<true><<<grid, PbDx64::NT, 0, st>>>(a, n_heads)
+            : pb_dx64_kernel<false><<<grid, PbDx64::NT, 0, st>>>(a, n_heads);
     } else if (a.dx) {
         const int ncol = (a.d_model + 127) / 128, bm = a.D >= 128 ? 64 : 128;
         const unsigned grid = (unsigned)(((BT + bm - 1) / bm) * ncol);
