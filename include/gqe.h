@@ -171,7 +171,8 @@ size_t gqe_attn_prefill_workspace_bytes(const gqe_desc* desc);
  * in launch order (for inspection and host tests; computes nothing on the GPU).
  * split != 0 gives the plan used with a workspace.  Writes at most max_items
  * items of 5 int32 each to `items` (host memory, may be NULL):
- *   b, head (H_kv = the shared head), query tile (128 rows), part (-1 whole
+ *   b, head (H_kv = the shared head), query tile (128 rows; 256 at d_head
+ *   128, where a workgroup has eight waves instead of four), part (-1 whole
  *   tile, 0 / 1 first / second half of its key tiles), split-pair index (-1
  *   for a whole tile).
  * Items are ordered by decreasing number of key tiles.  Returns the number of

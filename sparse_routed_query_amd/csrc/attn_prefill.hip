@@ -36,15 +36,19 @@
 
 namespace gqe {
 
-constexpr int kPfBM = 128;   // query rows per workgroup (4 waves x 32)
+// Query rows per workgroup (waves of 32 rows): 256 at d_head 128, where the
+// registers allow two waves per SIMD either way and eight waves of one tile
+// halve the K/V tile loads per query row; 128 otherwise (three workgroups of
+// four waves per compute unit).
+__host__ __device__ constexpr int pf_bm(int d_head) { return d_head == 128 ? 256 : 128; }
 constexpr int kPfBN = 64;    // keys per iteration
 constexpr int kPfPad = 8;    // LDS row padding in bf16 elements
 
 // Key tiles needed by query tile i of a head with kk rows per position.
-__host__ __device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal)
+__host__ __device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int causal, int bm)
 {
     if (!causal) return (T + kPfBN - 1) / kPfBN;
-    const int last_row = min(R - 1, (i + 1) * kPfBM - 1);
+    const int last_row = min(R - 1, (i + 1) * bm - 1);
     return (last_row / kk) / kPfBN + 1;
 }
 
@@ -57,6 +61,7 @@ __host__ __device__ __forceinline__ int pf_nkv(int i, int kk, int R, int T, int 
 // tiles by part, then head.
 struct PfSched {
     int B, T, G, k, n_shared, causal;
+    int bm;         // query rows per tile (pf_bm)
     int ntr, nts;   // query tiles per routed / shared head
     int isr, iss;   // first split tile (== ntr / nts: none)
     int nkv_max;    // key tiles of the longest tile
@@ -76,14 +81,14 @@ struct PfItem {
 
 // Smallest tile index in [0, nt] whose key-tile count is at least n
 // (nkv is non-decreasing in the tile index).
-__host__ __device__ __forceinline__ int pf_first_ge(int n, int kk, int R, int nt, int T, int causal)
+__host__ __device__ __forceinline__ int pf_first_ge(int n, int kk, int R, int nt, int T, int causal, int bm)
 {
     if (!causal) return n <= (T + kPfBN - 1) / kPfBN ? 0 : nt;
     if (n <= 1) return 0;
-    // nkv(i) >= n  <=>  min(R - 1, 128 i + 127) >= 64 kk (n - 1)
+    // nkv(i) >= n  <=>  min(R - 1, bm i + bm - 1) >= 64 kk (n - 1)
     const long long need = (long long)kPfBN * kk * (n - 1);
     if (need > R - 1) return nt;
-    return (int)min((long long)nt, need / kPfBM);
+    return (int)min((long long)nt, need / bm);
 }
 
 // Number of work items whose size is at least s.
@@ -95,8 +100,8 @@ __host__ __device__ __forceinline__ long long pf_count_ge(const PfSched& p, int 
         const int kk = l ? 1 : p.k, nt = l ? p.nts : p.ntr, is = l ? p.iss : p.isr;
         const long long cnt = pf_heads(p, l);
         const int R = p.T * kk;
-        const int whole = max(0, is - pf_first_ge(s, kk, R, nt, p.T, p.causal));
-        const int split = max(0, nt - max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal)));
+        const int whole = max(0, is - pf_first_ge(s, kk, R, nt, p.T, p.causal, p.bm));
+        const int split = max(0, nt - max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal, p.bm)));
         n += (whole + 2ll * split) * cnt;
     }
     return n;
@@ -117,11 +122,11 @@ __host__ __device__ __forceinline__ PfItem pf_item_of_size(const PfSched& p, lon
             // tiles of this group whose item size is exactly s: [a, e)
             int a, e;
             if (sp) {
-                a = max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal));
-                e = max(is, pf_first_ge(2 * s + 1, kk, R, nt, p.T, p.causal));
+                a = max(is, pf_first_ge(2 * s - 1, kk, R, nt, p.T, p.causal, p.bm));
+                e = max(is, pf_first_ge(2 * s + 1, kk, R, nt, p.T, p.causal, p.bm));
             } else {
-                a = min(is, pf_first_ge(s, kk, R, nt, p.T, p.causal));
-                e = min(is, pf_first_ge(s + 1, kk, R, nt, p.T, p.causal));
+                a = min(is, pf_first_ge(s, kk, R, nt, p.T, p.causal, p.bm));
+                e = min(is, pf_first_ge(s + 1, kk, R, nt, p.T, p.causal, p.bm));
             }
             const long long per = cnt * (sp ? 2 : 1);
             const long long n = (long long)max(0, e - a) * per;
@@ -187,7 +192,7 @@ __device__ __forceinline__ PfItem pf_item_wave(const PfSched& p, long long id, i
 // Floats of one part's partial state: per thread, the output accumulators
 // (D / 2) and (reference, half row sum).
 template <int D>
-__host__ __device__ constexpr int pf_part_floats() { return 256 * (D / 2 + 2); }
+__host__ __device__ constexpr int pf_part_floats() { return 2 * pf_bm(D) * (D / 2 + 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -245,9 +250,10 @@ struct PfParams {
 template <int D>
 __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 {
+    constexpr int BM = pf_bm(D), NT = 2 * BM; // query rows and threads of the workgroup
     constexpr int P = D + kPfPad;           // LDS row pitch (elements)
     constexpr int NDB = D / 32;
-    constexpr int NCH = kPfBN * D / 8 / 256; // 16-byte chunks per thread for one K or V tile
+    constexpr int NCH = kPfBN * D / 8 / NT;  // 16-byte chunks per thread for one K or V tile
     const int T = p.sc.T, G = p.sc.G, k = p.sc.k, causal = p.sc.causal, S = p.S;
     const float qscale = p.qscale;
     const uint16_t* __restrict__ q_routed = p.q_routed;
@@ -268,8 +274,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     // wave-uniform, so that the per-wave tile limits and mask tests stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lh = lane >> 5;
-    const int r0 = w.tile * kPfBM;
-    const int nkv = pf_nkv(w.tile, kk, R, T, causal);
+    const int r0 = w.tile * BM;
+    const int nkv = pf_nkv(w.tile, kk, R, T, causal, BM);
     // key tiles of this work item: [kt0, kt1)
     const int kt0 = w.part == 1 ? nkv / 2 : 0;
     const int kt1 = w.part == 0 ? nkv / 2 : nkv;
@@ -300,10 +306,10 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
     }
 
     u32x4 rk[NCH], rv[NCH];
-    // Thread tid moves 16-byte chunks tid + 256 i of a tile: key row
+    // Thread tid moves 16-byte chunks tid + NT i of a tile: key row
     // srow + i * RPP, elements scol .. scol + 7.  A tile is contiguous in
-    // memory, so its chunks sit at tid * 8 + i * 256 * 8 from the tile start.
-    constexpr int RPP = 256 / (D / 8);       // key rows per 256 chunks
+    // memory, so its chunks sit at tid * 8 + i * NT * 8 from the tile start.
+    constexpr int RPP = NT / (D / 8);        // key rows per NT chunks
     const int srow = tid / (D / 8), scol = (tid % (D / 8)) * 8;
     // Buffer loads: the resource starts at the tile and covers the rest of the
     // head, so rows past T fall outside it and read as zero (their scores are
@@ -315,8 +321,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)(V + (size_t)p0 * D), 0, bytes, 0x00020000);
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, tid * 16 + i * 4096, 0, 0));
-            rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, tid * 16 + i * 4096, 0, 0));
+            rk[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, tid * 16 + i * NT * 16, 0, 0));
+            rv[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rV, tid * 16 + i * NT * 16, 0, 0));
         }
     };
     const int k_st = srow * P + scol, v_st = kPfBN * P + srow * PV + scol;   // store offsets in a stage
@@ -544,8 +550,8 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         u64* mine = (u64*)(p.part + ((size_t)w.pair * 2 + w.part) * pf_part_floats<D>());
 #pragma unroll
         for (int c = 0; c < NQ; ++c)
-            __hip_atomic_store(mine + c * 256 + tid, word(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + NQ * 256 + tid, __builtin_bit_cast(u64, f32x2{m_ref, l_half}), __ATOMIC_RELAXED,
+            __hip_atomic_store(mine + c * NT + tid, word(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + NQ * NT + tid, __builtin_bit_cast(u64, f32x2{m_ref, l_half}), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
@@ -556,7 +562,7 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         u64 ov[NQ + 1];
 #pragma unroll
         for (int c = 0; c <= NQ; ++c)
-            ov[c] = __hip_atomic_load(other + c * 256 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ov[c] = __hip_atomic_load(other + c * NT + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // part 0's term first, whichever part merges, so the result does not
         // depend on which part finished last
         const f32x2 ml = __builtin_bit_cast(f32x2, ov[NQ]);
@@ -602,9 +608,10 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
 }
 
 // At most 168 VGPRs for d <= 64 keeps three waves on each SIMD (the LDS of
-// three workgroups fits a compute unit); d = 128 runs two.
+// three workgroups fits a compute unit); d = 128 runs two (one workgroup of
+// eight waves).
 template <int D>
-__global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void prefill_bf16_kernel(const PfParams p)
+__global__ __launch_bounds__(2 * pf_bm(D), D <= 64 ? 3 : 1) void prefill_bf16_kernel(const PfParams p)
 {
     pf_item_run<D>(p, pf_item_wave(p.sc, blockIdx.x, threadIdx.x & 63));
 }
@@ -732,35 +739,37 @@ constexpr int kPfSlots = 3 * 256;
 // First split tile of a head: the split tiles are the suffix of tiles that
 // need more than kPfSplitTiles key tiles and whose first row sees the first
 // key of part 1 (so both parts start from a finite reference).
-static int pf_split_start(int nt, int kk, int T, int causal)
+static int pf_split_start(int nt, int kk, int T, int causal, int bm)
 {
     if (!causal) return nt;
     const int R = T * kk;
     int i = nt;
     while (i > 0) {
-        const int j = i - 1, n = pf_nkv(j, kk, R, T, causal);
-        const long long t0 = (long long)j * kPfBM / kk;
+        const int j = i - 1, n = pf_nkv(j, kk, R, T, causal, bm);
+        const long long t0 = (long long)j * bm / kk;
         if (n > kPfSplitTiles && (long long)kPfBN * (n / 2) <= t0) i = j; else break;
     }
     return i;
 }
 
-static PfSched pf_sched(int B, int T, int G, int k, int n_shared, int causal, bool split, bool routed = true,
-                        bool shared = true)
+static PfSched pf_sched(int B, int T, int G, int k, int n_shared, int causal, bool split, int bm,
+                        bool routed = true, bool shared = true)
 {
     PfSched sc;
+    sc.bm = bm;
     sc.B = B; sc.T = T; sc.G = G; sc.k = k; sc.n_shared = n_shared; sc.causal = causal;
     sc.routed = routed; sc.shared = shared;
-    sc.ntr = (T * k + kPfBM - 1) / kPfBM;
-    sc.nts = n_shared ? (T + kPfBM - 1) / kPfBM : 0;
+    sc.ntr = (T * k + bm - 1) / bm;
+    sc.nts = n_shared ? (T + bm - 1) / bm : 0;
     if (split && causal) {
         long long units = 0;   // key tiles over all query tiles
-        for (int i = 0; i < sc.ntr; ++i) units += (long long)pf_nkv(i, k, T * k, T, causal) * B * G;
-        for (int i = 0; i < sc.nts; ++i) units += (long long)pf_nkv(i, 1, T, T, causal) * B;
-        split = (long long)((T + kPfBN - 1) / kPfBN) * kPfSlots > units;
+        for (int i = 0; i < sc.ntr; ++i) units += (long long)pf_nkv(i, k, T * k, T, causal, bm) * B * G;
+        for (int i = 0; i < sc.nts; ++i) units += (long long)pf_nkv(i, 1, T, T, causal, bm) * B;
+        // (slots counted in 128-row tiles)
+        split = (long long)((T + kPfBN - 1) / kPfBN) * kPfSlots * 128 / bm > units;
     }
-    sc.isr = split ? pf_split_start(sc.ntr, k, T, causal) : sc.ntr;
-    sc.iss = split ? pf_split_start(sc.nts, 1, T, causal) : sc.nts;
+    sc.isr = split ? pf_split_start(sc.ntr, k, T, causal, bm) : sc.ntr;
+    sc.iss = split ? pf_split_start(sc.nts, 1, T, causal, bm) : sc.nts;
     sc.nkv_max = (T + kPfBN - 1) / kPfBN;
     return sc;
 }
@@ -776,16 +785,16 @@ static size_t pf_ctr_bytes(long long pairs) { return (size_t)((pairs * 4 + 255) 
 size_t prefill_workspace_bytes(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool bf16)
 {
     if (!bf16 || (long long)B * T == 0) return 0;
-    const long long pairs = pf_pairs(pf_sched(B, T, G, k, n_shared, causal, true));
+    const long long pairs = pf_pairs(pf_sched(B, T, G, k, n_shared, causal, true, pf_bm(d_head)));
     if (pairs == 0) return 0;
     const int pf = d_head == 32 ? pf_part_floats<32>() : d_head == 64 ? pf_part_floats<64>() : pf_part_floats<128>();
     return pf_ctr_bytes(pairs) + (size_t)pairs * 2 * pf * sizeof(float);
 }
 
-long long prefill_plan(int B, int T, int G, int k, int n_shared, int causal, bool split, int32_t* items,
+long long prefill_plan(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool split, int32_t* items,
                        long long max_items)
 {
-    const PfSched sc = pf_sched(B, T, G, k, n_shared, causal, split);
+    const PfSched sc = pf_sched(B, T, G, k, n_shared, causal, split, pf_bm(d_head));
     const long long n = (long long)B * T == 0 ? 0 : pf_count_ge(sc, 1);
     for (long long i = 0; items && i < n && i < max_items; ++i) {
         const PfItem w = pf_item(sc, i);
@@ -809,7 +818,7 @@ int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
         prm.kg = (const uint16_t*)a.kmat;
         prm.vg = (const uint16_t*)a.vmat;
         prm.out = a.out;
-        prm.sc = pf_sched(a.B, a.T, a.G, a.k, a.n_shared, a.causal, split, a.q_routed != nullptr,
+        prm.sc = pf_sched(a.B, a.T, a.G, a.k, a.n_shared, a.causal, split, pf_bm(a.d_head), a.q_routed != nullptr,
                           a.q_shared != nullptr);
         prm.ctr = split ? (int*)a.workspace : nullptr;
         prm.part = split ? (float*)((char*)a.workspace + pf_ctr_bytes(pf_pairs(prm.sc))) : nullptr;
@@ -821,9 +830,9 @@ int launch_prefill_heads(const PrefillArgs& a, hipStream_t st)
         if (items == 0) return 0;
         const int grid = (int)items;
         switch (a.d_head) {
-        case 32: prefill_bf16_kernel<32><<<grid, 256, 0, st>>>(prm); break;
-        case 64: prefill_bf16_kernel<64><<<grid, 256, 0, st>>>(prm); break;
-        case 128: prefill_bf16_kernel<128><<<grid, 256, 0, st>>>(prm); break;
+        case 32: prefill_bf16_kernel<32><<<grid, 2 * pf_bm(32), 0, st>>>(prm); break;
+        case 64: prefill_bf16_kernel<64><<<grid, 2 * pf_bm(64), 0, st>>>(prm); break;
+        case 128: prefill_bf16_kernel<128><<<grid, 2 * pf_bm(128), 0, st>>>(prm); break;
         default: return -2;
         }
     } else {

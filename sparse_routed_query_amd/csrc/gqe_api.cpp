@@ -231,7 +231,7 @@ int64_t gqe_attn_prefill_plan(const gqe_desc* desc, int split, int32_t* items, i
     GQE_TRY(check_desc(desc, s));
     if (!s.bf16) return GQE_ERR_UNSUPPORTED;
     if (max_items < 0) return GQE_ERR_INVALID;
-    return gqe::prefill_plan(s.B, s.T, s.G, s.k, s.ns, s.causal, split != 0 && prefill_ws_bytes(s) > 0, items,
+    return gqe::prefill_plan(s.B, s.T, s.G, s.k, s.D, s.ns, s.causal, split != 0 && prefill_ws_bytes(s) > 0, items,
                              max_items);
 }
 

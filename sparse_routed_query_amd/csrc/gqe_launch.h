@@ -170,7 +170,7 @@ struct PrefillArgs {
 size_t prefill_workspace_bytes(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool bf16);
 // The launch's work items in launch order, 5 ints each (b, h, tile, part, pair);
 // returns their number and writes at most max_items of them.
-long long prefill_plan(int B, int T, int G, int k, int n_shared, int causal, bool split, int32_t* items,
+long long prefill_plan(int B, int T, int G, int k, int d_head, int n_shared, int causal, bool split, int32_t* items,
                        long long max_items);
 // Attention only: hard and shared slots of `out`; the weighted slots are not written.
 int launch_prefill_heads(const PrefillArgs& a, hipStream_t st);

@@ -209,36 +209,41 @@ def test_python_binding_refuses_host_tensors():
 
 # ------------------------------------------------------------- prefill schedule
 
-def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=768):
+def plan_reference(B, T, G_, k, n_shared, causal, split, d_head=64, split_tiles=32, slots=768):
     """Work items of the prefill attention launch, written out directly: every
-    query tile of 128 rows, cut in two when it is causal, needs more than 32 key
-    tiles of 64 and its first row sees key 64*(nkv//2), provided the longest
-    tile needs more key tiles than the average load of 768 workgroup slots;
+    query tile of bm rows (256 at d_head 128, else 128), cut in two when it is
+    causal, needs more than 32 key tiles of 64 and its first row sees key
+    64*(nkv//2), provided the longest tile needs more key tiles than the average
+    load of 768 workgroup slots of 128 rows (768 * 128 / bm slots of bm rows);
     sorted by item size (larger part), routed before shared, split before
     whole, tile descending, split tiles by part then head.  Then, since
     workgroup j runs on XCD j mod 8: in each run of one tile's items over a
     number of heads that is a multiple of 8, the item at position j takes the
     run's head 8*(r//8) + j%8 (r its rank in the run), so all items of a head
     run on one XCD."""
+    bm = 256 if d_head == 128 else 128
+
     def nkv_of(i, kk):
         if not causal:
             return -(-T // 64)
-        return (min(T * kk - 1, 128 * (i + 1) - 1) // kk) // 64 + 1
-    units = sum(nkv_of(i, k) * B * G_ for i in range(-(-T * k // 128)))
-    units += sum(nkv_of(i, 1) * B for i in range(-(-T // 128))) if n_shared else 0
-    split = split and causal and -(-T // 64) * slots > units
+        return (min(T * kk - 1, bm * (i + 1) - 1) // kk) // 64 + 1
+    units = sum(nkv_of(i, k) * B * G_ for i in range(-(-T * k // bm)))
+    units += sum(nkv_of(i, 1) * B for i in range(-(-T // bm))) if n_shared else 0
+    split = split and causal and -(-T // 64) * slots * 128 // bm > units
     items = []
     n_pairs_r = 0
     for lst, (kk, heads) in enumerate(((k, [(b, g) for b in range(B) for g in range(G_)]),
                                        (1, [(b, G_) for b in range(B)] if n_shared else []))):
         R = T * kk
-        nt = -(-R // 128)
+        nt = -(-R // bm)
+
         def nkv(i):
             if not causal:
                 return -(-T // 64)
-            return (min(R - 1, 128 * (i + 1) - 1) // kk) // 64 + 1
+            return (min(R - 1, bm * (i + 1) - 1) // kk) // 64 + 1
+
         def can(i):
-            return causal and nkv(i) > split_tiles and 64 * (nkv(i) // 2) <= (128 * i) // kk
+            return causal and nkv(i) > split_tiles and 64 * (nkv(i) // 2) <= (bm * i) // kk
         first_split = nt
         while split and first_split > 0 and can(first_split - 1):
             first_split -= 1
@@ -271,13 +276,18 @@ def plan_reference(B, T, G_, k, n_shared, causal, split, split_tiles=32, slots=7
     dict(B=3, T=2100, k=1, n_shared=1, causal=0),     # non-causal: nothing split
     dict(B=2, T=300, k=2, n_shared=1, causal=1),      # short: nothing split
     dict(B=1, T=1, k=1, n_shared=1, causal=1),
+    dict(B=2, T=16384, k=2, n_shared=1, causal=1, d_head=128),   # wide_zipf's shape: 256-row tiles
+    dict(B=4, T=4096, k=1, n_shared=1, causal=1, d_head=128),
+    dict(B=2, T=700, k=3, n_shared=0, causal=1, d_head=128),
+    dict(B=1, T=5000, k=1, n_shared=1, causal=0, d_head=32),
 ])
 def test_prefill_plan_matches_its_definition(shape):
+    dh = shape.get("d_head", 64)
     d = main(B=shape["B"], T=shape["T"], k=shape["k"], H_q=8 * max(2, shape["k"]), n_shared=shape["n_shared"],
-             causal=shape["causal"])
+             causal=shape["causal"], d_head=dh)
     for split in (False, True):
         got = [tuple(int(x) for x in r) for r in G.gqe_attn_prefill_plan(d, split)]
-        want = plan_reference(shape["B"], shape["T"], 8, shape["k"], shape["n_shared"], shape["causal"], split)
+        want = plan_reference(shape["B"], shape["T"], 8, shape["k"], shape["n_shared"], shape["causal"], split, dh)
         assert got == want, (split, len(got), len(want))
     plan = G.gqe_attn_prefill_plan(d, True)
     # 8 groups per batch here, so every routed head's items (whole or either half) share one XCD, j mod 8
@@ -285,7 +295,8 @@ def test_prefill_plan_matches_its_definition(shape):
     pairs = sorted((int(r[4]), int(r[3])) for r in plan if r[3] >= 0)
     n_pairs = len(pairs) // 2
     assert pairs == [(p, part) for p in range(n_pairs) for part in (0, 1)]
-    want_bytes = 0 if n_pairs == 0 else -(-n_pairs * 4 // 256) * 256 + n_pairs * 2 * 256 * (64 // 2 + 2) * 4
+    threads = 512 if dh == 128 else 256   # two per query row of a tile
+    want_bytes = 0 if n_pairs == 0 else -(-n_pairs * 4 // 256) * 256 + n_pairs * 2 * threads * (dh // 2 + 2) * 4
     assert G.gqe_attn_prefill_workspace_bytes(d) == want_bytes
 
 
