@@ -8,10 +8,10 @@
 // §3-2 (3)-(5): hard slots, the router-weighted sum, the shared slot.
 //
 // bf16 kernel design (one workgroup = 4 waves = 128 query rows of one
-// (b, head); key tiles of 64):
+// (b, head), at d_head 128 8 waves = 256 rows; key tiles of 64):
 //   * Within a group the routed queries are a dense [T*k, d] matrix whose row
 //     r sits at position r / k, so all k kept rows of a position share every
-//     K/V tile staged in LDS -- each K/V tile is loaded once per 128 rows.
+//     K/V tile staged in LDS -- each K/V tile is loaded once per 128 (256) rows.
 //   * The wave computes S^T = K Q^T (32 keys x 32 queries per MFMA block), so a
 //     lane owns one query column: the row max and row sum need one exchange
 //     with lane l^32 and no LDS.  Q enters the product exactly as the
@@ -534,7 +534,7 @@ __device__ __forceinline__ void pf_item_run(const PfParams& p, const PfItem w)
         // a load is served from the device-coherent level, never from a stale
         // line of this XCD's L2; vmcnt counts stores on CDNA, so the wait
         // below returns only after every state store of the wave has been
-        // acknowledged, and the barrier makes that true of all four waves
+        // acknowledged, and the barrier makes that true of all the waves
         // before thread 0's ticket atomic is issued; the merging part issues
         // its loads only after its own ticket has returned (through LDS and a
         // barrier), i.e. after the other part's ticket and so after its
